@@ -1,0 +1,294 @@
+"""HiLS attention: plain fp64 CPU oracle.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import or call this
+module; only the tests, the smoke check and the benchmark's CPU-baseline leg
+use it. It shares no code with the HIP library.
+
+Source. "Hierarchical Sparse Attention Done Right: Toward Infinite Context
+Modeling" (arXiv 2607.02980v1), source-linked summary page, cited below as
+[HSADR <section>]. The page prints no equations, so each step restates the
+prose it follows:
+
+* keys are split into uniform chunks of S tokens; the local window is aligned
+  to chunk boundaries and never overlaps retrieved chunks [HSADR §2 Preliminary];
+* each query is scored against one learned summary key (landmark) per chunk;
+  the score stands in for the chunk's LogSumExp mass and is affine: a
+  query-summary relevance plus a per-chunk (entropy) bias [HSADR §3 Methodology,
+  "Method overview", "Linear surrogate for chunk mass"];
+* every query is routed over all chunk summaries and keeps the top-K chunks
+  [HSADR §3, "Sparse training"];
+* query heads of one GQA group share one retrieved chunk set [HSADR §4
+  Practical Design Choices, "Architecture" (GQA)];
+* the query attends to each retrieved chunk with its own softmax and the chunk
+  outputs are fused by a softmax over the retrieval scores (hierarchical
+  softmax) [HSADR Abstract; §3, "Hierarchical softmax"];
+* gradients of the LM loss reach the retrieval scores through the fusion
+  weights; unselected chunks get none [HSADR §3; §9 Discussion & Conclusion].
+
+Readings where the page is silent (each is listed with its reason in the
+design notes of the repository):
+
+* score s_{h,i,c} = scale * <q_{h,i}, lmk_c> + bias_c, with the token-logit
+  scale (default 1/sqrt(d)); bias is optional (absent = 0);
+* GQA group score = mean over the group's heads of s_{h,i,c}; selection takes
+  the top min(K, |C_i|) candidates by (group score rounded to fp32, descending;
+  chunk index ascending) -- the fp32 rounding is the precision the kernels
+  decide in; ``idx`` lists the chosen chunks in ascending order, padded with -1;
+* causal mode: query i sits at key position t_i = Lkv - Lq + i; its own chunk
+  o_i = floor(t_i / S) is never a candidate (its landmark would summarise
+  future tokens); candidates are chunks c < o_i. Non-causal mode: all complete
+  chunks are candidates and the trailing partial chunk (if any) is "own";
+* with keep_own_chunk the visible tokens of the own chunk are attended exactly
+  and enter the fusion with score = their exact LogSumExp (the one-chunk case
+  of the chunk-aligned local window); fusion weights are per head;
+* an empty fusion set gives O = 0 and LSE = -inf.
+
+Parity pins (what ties this oracle to something other than itself) live in
+tests/test_oracle_pins.py: dense attention (S = 1, all chunks), exact chunk mass
+= restricted softmax, top-1, weights summing to one, a hand-derived worked
+example, decode = last prefill row, ties, invariances, and central finite
+differences for every gradient.
+"""
+import math
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# positions and candidate sets  [HSADR §2 Preliminary; §3 "Sparse training"]
+# ----------------------------------------------------------------------------
+def query_layout(i, Lq, Lkv, S, causal):
+    """Return (candidate chunk ids, own-chunk token range [a, b)) for query i."""
+    NC = Lkv // S
+    if causal:
+        t = Lkv - Lq + i
+        own = t // S
+        cand = np.arange(0, min(own, NC))
+        own_rng = (own * S, t + 1)
+    else:
+        cand = np.arange(0, NC)
+        own_rng = (NC * S, Lkv)
+    return cand, own_rng
+
+
+def select_chunks(gbar, cand, K):
+    """Top-min(K, |cand|) by (fp32(gbar) desc, chunk id asc); returned ascending."""
+    if len(cand) == 0:
+        return np.zeros(0, dtype=np.int64)
+    g32 = np.asarray(gbar, dtype=np.float64).astype(np.float32).astype(np.float64)
+    order = np.lexsort((cand, -g32))          # primary key: -score, then chunk id
+    return np.sort(cand[order[:min(K, len(cand))]])
+
+
+def _logsumexp(x):
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return -math.inf
+    m = np.max(x)
+    if not np.isfinite(m):
+        return m
+    return m + math.log(np.sum(np.exp(x - m)))
+
+
+def _chunk_attention(q, k_blk, v_blk, scale):
+    """Independent softmax attention of one query over one chunk's tokens.
+
+    Returns (lse_c, o_c, p) with l_j = scale*<q,k_j>, lse_c = log sum exp l_j,
+    p_j = exp(l_j - lse_c), o_c = sum_j p_j v_j.  [HSADR §3 "Hierarchical softmax"]
+    """
+    logits = scale * (k_blk @ q)
+    lse = _logsumexp(logits)
+    p = np.exp(logits - lse)
+    return lse, p @ v_blk, p
+
+
+# ----------------------------------------------------------------------------
+# one query of one KV group: forward and (optionally) backward
+# ----------------------------------------------------------------------------
+def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale,
+               forced=None, dout=None):
+    """Forward (and backward if ``dout``) of query i for the G heads of one KV group.
+
+    qg: [G, d] query rows of the group; k, v: [Lkv, d] (indexable) this group's
+    cache; lmk: [NCcap, d]; bias: [NCcap] or None; forced: chunk ids to use
+    instead of the selection (ascending), or None.
+    Returns a dict with idx, out [G, d], lse [G], scores, and for backward dq
+    [G, d] and the lists of contributions to dk, dv (per token range), dlmk and
+    dbias (per chunk).
+    """
+    G, d = qg.shape
+    cand, (oa, ob) = query_layout(i, Lq, Lkv, S, causal)
+
+    # retrieval scores of every candidate, per head  [HSADR §3 "Linear surrogate"]
+    if len(cand):
+        s_all = scale * (qg @ lmk[cand].T)                  # [G, |C|]
+        if bias is not None:
+            s_all = s_all + bias[cand][None, :]
+        gbar = s_all.mean(axis=0)                           # group score [HSADR §4 GQA]
+    else:
+        s_all = np.zeros((G, 0))
+        gbar = np.zeros(0)
+
+    # top-K routing  [HSADR §3 "Sparse training"]
+    sel = select_chunks(gbar, cand, K) if forced is None else np.asarray(forced, dtype=np.int64)
+    idx = -np.ones(K, dtype=np.int64)
+    idx[:len(sel)] = sel
+    pos_in_cand = {int(c): n for n, c in enumerate(cand)}
+
+    # members of the fusion set: (kind, chunk id, token range)
+    members = [("ret", int(c), (int(c) * S, int(c) * S + S)) for c in sel]
+    if keep_own and ob > oa:
+        members.append(("own", -1, (oa, ob)))
+
+    out = np.zeros((G, d))
+    lse = np.full(G, -math.inf)
+    res = {"idx": idx, "out": out, "lse": lse, "gbar": gbar, "cand": cand}
+    if dout is not None:
+        res.update(dq=np.zeros((G, d)), dkv=[], dlmk=[], dbias=[])
+    if not members:
+        return res
+
+    for h in range(G):
+        q = qg[h]
+        parts = []
+        for kind, c, (a, b) in members:
+            kb = np.asarray(k[a:b], dtype=np.float64)
+            vb = np.asarray(v[a:b], dtype=np.float64)
+            lse_c, o_c, p = _chunk_attention(q, kb, vb, scale)
+            if kind == "ret":
+                if c in pos_in_cand:
+                    s_c = s_all[h, pos_in_cand[c]]
+                else:                                       # forced chunk outside C_i
+                    s_c = scale * float(q @ lmk[c]) + (0.0 if bias is None else float(bias[c]))
+            else:
+                s_c = lse_c                                  # exact mass of the own chunk
+            parts.append((kind, c, a, b, kb, vb, p, o_c, s_c))
+        # fusion by a softmax over the retrieval scores  [HSADR §3 "Hierarchical softmax"]
+        s_vec = np.array([pt[8] for pt in parts])
+        LSE = _logsumexp(s_vec)
+        w = np.exp(s_vec - LSE)
+        O = np.zeros(d)
+        for wc, pt in zip(w, parts):
+            O = O + wc * pt[7]
+        out[h] = O
+        lse[h] = LSE
+
+        if dout is None:
+            continue
+        # backward with the selection held fixed  [HSADR §3; §9]
+        g = np.asarray(dout[h], dtype=np.float64)
+        D = float(g @ O)
+        dq = np.zeros(d)
+        for wc, (kind, c, a, b, kb, vb, p, o_c, s_c) in zip(w, parts):
+            u = vb @ g                                       # <dO, v_j>
+            Dc = float(p @ u)                                # <dO, o_c>
+            if kind == "ret":
+                dl = wc * p * (u - Dc)                       # through the intra-chunk softmax
+                ds = wc * (Dc - D)                           # through the fusion softmax
+                dq = dq + scale * ds * np.asarray(lmk[c], dtype=np.float64)
+                res["dlmk"].append((c, scale * ds * q))
+                res["dbias"].append((c, ds))
+            else:
+                dl = wc * p * (u - D)                        # s_own = lse_own adds ds_own*p
+            dq = dq + scale * (dl @ kb)
+            res["dkv"].append((a, b, scale * np.outer(dl, q), np.outer(wc * p, g)))
+        res["dq"][h] = dq
+    return res
+
+
+# ----------------------------------------------------------------------------
+# whole-tensor entry points (the same names as the library, prefixed ref_)
+# ----------------------------------------------------------------------------
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def ref_forward(q, k, v, lmk, bias=None, *, chunk_size, top_k, causal=True,
+                keep_own_chunk=True, scale=None, queries=None, heads_kv=None,
+                batches=None, forced_idx=None):
+    """HiLS forward. q [B,Hq,Lq,d]; k, v [B,Hkv,Lkv,d]; lmk [B,Hkv,NCcap,d]; bias [B,Hkv,NCcap].
+
+    Returns out [B,Hq,nq,d], idx [B,Hkv,nq,K] (int64, -1 padded), lse [B,Hq,nq]
+    for the query positions ``queries`` (default: all).  ``forced_idx``
+    ([B,Hkv,nq,K], -1 padded) replaces the selection.  k and v may be lazy
+    indexable objects; only the rows of the used chunks are read.
+    """
+    B, Hq, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    S, K = int(chunk_size), int(top_k)
+    sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    qs = np.arange(Lq) if queries is None else np.asarray(queries)
+    bs = range(B) if batches is None else batches
+    gs = range(Hkv) if heads_kv is None else heads_kv
+    out = np.zeros((B, Hq, len(qs), d))
+    lse = np.full((B, Hq, len(qs)), -math.inf)
+    idx = -np.ones((B, Hkv, len(qs), K), dtype=np.int64)
+    for b in bs:
+        for g in gs:
+            kg, vg = k[b, g], v[b, g]
+            lg = _f64(lmk[b, g])
+            bg = None if bias is None else _f64(bias[b, g])
+            for n, i in enumerate(qs):
+                forced = None
+                if forced_idx is not None:
+                    f = np.asarray(forced_idx[b, g, n])
+                    forced = f[f >= 0]
+                r = hils_query(_f64(q[b, g * G:(g + 1) * G, i]), kg, vg, lg, bg, int(i),
+                               Lq=Lq, Lkv=Lkv, S=S, K=K, causal=bool(causal),
+                               keep_own=bool(keep_own_chunk), scale=sc, forced=forced)
+                idx[b, g, n] = r["idx"]
+                out[b, g * G:(g + 1) * G, n] = r["out"]
+                lse[b, g * G:(g + 1) * G, n] = r["lse"]
+    return out, idx, lse
+
+
+def ref_decode(q, k, v, lmk, bias=None, **kw):
+    """Single-token decode: q [B,Hq,1,d] sits at position Lkv-1 (its K/V already cached)."""
+    assert q.shape[2] == 1
+    kw = dict(kw)
+    kw["causal"] = True
+    return ref_forward(q, k, v, lmk, bias, **kw)
+
+
+def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
+                 keep_own_chunk=True, scale=None, forced_idx=None, queries=None):
+    """Gradients of sum(<dout, out>) for every input, selection held fixed.
+
+    Returns dq [B,Hq,Lq,d] (rows outside ``queries`` are zero), dk, dv
+    [B,Hkv,Lkv,d], dlmk [B,Hkv,NCcap,d], dbias [B,Hkv,NCcap] -- the last four
+    summed over the contributions of the queries in ``queries`` (default all).
+    """
+    B, Hq, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    S, K = int(chunk_size), int(top_k)
+    sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    qs = np.arange(Lq) if queries is None else np.asarray(queries)
+    dq = np.zeros((B, Hq, Lq, d))
+    dk = np.zeros((B, Hkv, Lkv, d))
+    dv = np.zeros((B, Hkv, Lkv, d))
+    dlmk = np.zeros(lmk.shape)
+    dbias = np.zeros(lmk.shape[:3])
+    for b in range(B):
+        for g in range(Hkv):
+            kg, vg = k[b, g], v[b, g]
+            lg = _f64(lmk[b, g])
+            bg = None if bias is None else _f64(bias[b, g])
+            for n, i in enumerate(qs):
+                forced = None
+                if forced_idx is not None:
+                    f = np.asarray(forced_idx[b, g, n])
+                    forced = f[f >= 0]
+                r = hils_query(_f64(q[b, g * G:(g + 1) * G, i]), kg, vg, lg, bg, int(i),
+                               Lq=Lq, Lkv=Lkv, S=S, K=K, causal=bool(causal),
+                               keep_own=bool(keep_own_chunk), scale=sc, forced=forced,
+                               dout=_f64(dout[b, g * G:(g + 1) * G, i]))
+                dq[b, g * G:(g + 1) * G, i] = r["dq"]
+                for a, e, dkp, dvp in r["dkv"]:
+                    dk[b, g, a:e] += dkp
+                    dv[b, g, a:e] += dvp
+                for c, val in r["dlmk"]:
+                    dlmk[b, g, c] += val
+                for c, val in r["dbias"]:
+                    dbias[b, g, c] += val
+    return dq, dk, dv, dlmk, dbias
