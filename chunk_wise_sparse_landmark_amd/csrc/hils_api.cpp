@@ -1,0 +1,217 @@
+// C ABI of the HiLS library: argument validation, workspace sizing, dispatch.
+// All checks run on the host before any launch; nothing throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "hils.h"
+#include "hils_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hils_status fail(hils_status s, const char* fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof(msg), fmt, ap);
+  va_end(ap);
+  g_last_error = msg;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_empty(const hils_params* p) {
+  return p->batch == 0 || p->heads_q == 0 || p->seq_q == 0;
+}
+
+// Shape checks shared by every entry point.  `op` is a hils_op.
+hils_status check_params(const hils_params* p, int op) {
+  if (!p) return fail(HILS_ERR_INVALID_ARG, "params is null");
+  if (p->batch < 0 || p->heads_q < 0 || p->heads_kv < 0 || p->head_dim < 0 || p->seq_q < 0 ||
+      p->seq_kv < 0 || p->num_landmarks < 0)
+    return fail(HILS_ERR_INVALID_ARG, "negative size");
+  if (p->dtype != HILS_F32 && p->dtype != HILS_BF16)
+    return fail(HILS_ERR_INVALID_ARG, "dtype %d is not HILS_F32 or HILS_BF16", p->dtype);
+  if (p->chunk_size < 1) return fail(HILS_ERR_INVALID_ARG, "chunk_size must be >= 1");
+  if (p->top_k < 1) return fail(HILS_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (p->causal != 0 && p->causal != 1) return fail(HILS_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->keep_own_chunk != 0 && p->keep_own_chunk != 1)
+    return fail(HILS_ERR_INVALID_ARG, "keep_own_chunk must be 0 or 1");
+  if (!std::isfinite(p->scale)) return fail(HILS_ERR_INVALID_ARG, "scale is not finite");
+  if (p->heads_kv == 0 && p->heads_q != 0)
+    return fail(HILS_ERR_INVALID_ARG, "heads_kv is 0 but heads_q is not");
+  if (p->heads_kv > 0 && p->heads_q % p->heads_kv != 0)
+    return fail(HILS_ERR_INVALID_ARG, "heads_q (%d) is not a multiple of heads_kv (%d)",
+                p->heads_q, p->heads_kv);
+  if (p->head_dim < 1) return fail(HILS_ERR_INVALID_ARG, "head_dim must be >= 1");
+  if (p->num_landmarks < p->seq_kv / p->chunk_size)
+    return fail(HILS_ERR_INVALID_ARG, "num_landmarks (%d) < seq_kv / chunk_size (%d)",
+                p->num_landmarks, p->seq_kv / p->chunk_size);
+  if (op == HILS_OP_DECODE && p->seq_q != 1 && !is_empty(p))
+    return fail(HILS_ERR_INVALID_ARG, "decode needs seq_q == 1 (got %d)", p->seq_q);
+  const int causal = op == HILS_OP_DECODE ? 1 : p->causal;
+  if (causal && p->seq_q > p->seq_kv)
+    return fail(HILS_ERR_INVALID_ARG, "causal call with seq_q (%d) > seq_kv (%d)", p->seq_q,
+                p->seq_kv);
+  if (p->top_k > hils::kMaxTopK)
+    return fail(HILS_ERR_UNSUPPORTED, "top_k %d > %d", p->top_k, hils::kMaxTopK);
+  if (p->head_dim > 256) return fail(HILS_ERR_UNSUPPORTED, "head_dim %d > 256", p->head_dim);
+  if (p->chunk_size > 256) return fail(HILS_ERR_UNSUPPORTED, "chunk_size %d > 256", p->chunk_size);
+  if (p->heads_kv > 0 && p->heads_q / p->heads_kv > 64)
+    return fail(HILS_ERR_UNSUPPORTED, "heads_q / heads_kv > 64");
+  if (op == HILS_OP_BACKWARD && (int64_t)p->chunk_size * p->head_dim > 8192)
+    return fail(HILS_ERR_UNSUPPORTED, "backward needs chunk_size * head_dim <= 8192");
+  return HILS_OK;
+}
+
+hils::Geometry geometry(const hils_params* p, int op) {
+  hils::Geometry g;
+  g.B = p->batch;
+  g.Hq = p->heads_q;
+  g.Hkv = p->heads_kv;
+  g.G = p->heads_kv > 0 ? p->heads_q / p->heads_kv : 1;
+  g.d = p->head_dim;
+  g.Lq = p->seq_q;
+  g.Lkv = p->seq_kv;
+  g.S = p->chunk_size;
+  g.K = p->top_k;
+  g.NC = p->seq_kv / p->chunk_size;
+  g.NCcap = p->num_landmarks;
+  g.causal = op == HILS_OP_DECODE ? 1 : p->causal;
+  g.keep_own = p->keep_own_chunk;
+  g.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
+  return g;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ws_bytes_for(const hils_params* p, int op) {
+  if (is_empty(p)) return 0;
+  hils::Geometry g = geometry(p, op);
+  const int bf16 = p->dtype == HILS_BF16;
+  switch (op) {
+    case HILS_OP_FORWARD:
+      return hils::prefill_fast_supported(g, bf16) ? round256(hils::prefill_fast_ws(g)) : 0;
+    case HILS_OP_DECODE:
+      return hils::decode_fast_supported(g, bf16) ? round256(hils::decode_fast_ws(g)) : 0;
+    case HILS_OP_BACKWARD:
+      return round256(hils::generic_backward_ws(g));
+    default:
+      return 0;
+  }
+}
+
+hils_status check_ws(const hils_params* p, int op, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_for(p, op);
+  if (need == 0) return HILS_OK;
+  if (!ws) return fail(HILS_ERR_WORKSPACE, "workspace of %zu bytes needed, got null", need);
+  if (ws_bytes < need)
+    return fail(HILS_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(HILS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return HILS_OK;
+}
+
+hils_status launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HILS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return HILS_OK;
+}
+
+hils_status forward_like(int op, const hils_params* p, const void* q, const void* k,
+                         const void* v, const void* lmk, const float* lmk_bias, void* out,
+                         int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  hils_status s = check_params(p, op);
+  if (s != HILS_OK) return s;
+  if (is_empty(p)) return HILS_OK;
+  if (!q || !k || !v || !lmk || !out || !sel_idx)
+    return fail(HILS_ERR_INVALID_ARG, "a required pointer (q, k, v, lmk, out, sel_idx) is null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lmk) || !aligned16(out) ||
+      !aligned16(sel_idx) || (lse && !aligned16(lse)) || (lmk_bias && !aligned16(lmk_bias)))
+    return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
+  s = check_ws(p, op, ws, ws_bytes);
+  if (s != HILS_OK) return s;
+  hils::Geometry g = geometry(p, op);
+  const int bf16 = p->dtype == HILS_BF16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipGetLastError();   // clear a stale error so it is not reported as ours
+  if (op == HILS_OP_DECODE && hils::decode_fast_supported(g, bf16))
+    return launch_status(hils::launch_decode_fast(g, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, st),
+                         "decode launch");
+  if (op == HILS_OP_FORWARD && hils::prefill_fast_supported(g, bf16))
+    return launch_status(hils::launch_prefill_fast(g, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, st),
+                         "prefill launch");
+  return launch_status(
+      hils::launch_generic_forward(g, bf16, q, k, v, lmk, lmk_bias, out, sel_idx, lse, st),
+      "forward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hils_workspace_size(const hils_params* p, int32_t op) {
+  if (op < HILS_OP_FORWARD || op > HILS_OP_BACKWARD) return 0;
+  if (check_params(p, op) != HILS_OK) return 0;
+  return ws_bytes_for(p, op);
+}
+
+hils_status hils_forward(const hils_params* p, const void* q, const void* k, const void* v,
+                         const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return forward_like(HILS_OP_FORWARD, p, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, ws_bytes,
+                      stream);
+}
+
+hils_status hils_decode(const hils_params* p, const void* q, const void* k, const void* v,
+                        const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return forward_like(HILS_OP_DECODE, p, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, ws_bytes,
+                      stream);
+}
+
+hils_status hils_backward(const hils_params* p, const void* q, const void* k, const void* v,
+                          const void* lmk, const float* lmk_bias, const void* out,
+                          const void* dout, const int32_t* sel_idx, const float* lse, void* dq,
+                          void* dk, void* dv, void* dlmk, float* dlmk_bias, void* ws,
+                          size_t ws_bytes, void* stream) {
+  hils_status s = check_params(p, HILS_OP_BACKWARD);
+  if (s != HILS_OK) return s;
+  if (is_empty(p)) return HILS_OK;
+  if (!q || !k || !v || !lmk || !out || !dout || !sel_idx || !lse || !dq || !dk || !dv || !dlmk)
+    return fail(HILS_ERR_INVALID_ARG, "a required pointer of hils_backward is null");
+  const void* ptrs[] = {q, k, v, lmk, out, dout, sel_idx, lse, dq, dk, dv, dlmk};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
+  if ((lmk_bias && !aligned16(lmk_bias)) || (dlmk_bias && !aligned16(dlmk_bias)))
+    return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
+  s = check_ws(p, HILS_OP_BACKWARD, ws, ws_bytes);
+  if (s != HILS_OK) return s;
+  hils::Geometry g = geometry(p, HILS_OP_BACKWARD);
+  const int bf16 = p->dtype == HILS_BF16;
+  hipGetLastError();
+  return launch_status(hils::launch_generic_backward(g, bf16, q, k, v, lmk, lmk_bias, dout, sel_idx,
+                                                     dq, dk, dv, dlmk, dlmk_bias, ws,
+                                                     reinterpret_cast<hipStream_t>(stream)),
+                       "backward launch");
+}
+
+const char* hils_status_string(hils_status s) {
+  switch (s) {
+    case HILS_OK: return "HILS_OK";
+    case HILS_ERR_INVALID_ARG: return "HILS_ERR_INVALID_ARG";
+    case HILS_ERR_UNSUPPORTED: return "HILS_ERR_UNSUPPORTED";
+    case HILS_ERR_WORKSPACE: return "HILS_ERR_WORKSPACE";
+    case HILS_ERR_HIP: return "HILS_ERR_HIP";
+  }
+  return "unknown hils_status";
+}
+
+const char* hils_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

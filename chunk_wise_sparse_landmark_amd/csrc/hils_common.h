@@ -1,0 +1,261 @@
+// Device helpers shared by the HiLS kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+constexpr int kWave = 64;
+constexpr int kMaxTopK = 64;
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static __forceinline__ float ld(const float* p) { return *p; }
+  __device__ static __forceinline__ void st(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float ld(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static __forceinline__ void st(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// ---------------------------------------------------------------- wave primitives
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+  lo = __shfl_xor(lo, m, kWave);
+  hi = __shfl_xor(hi, m, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
+  uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+  lo = __shfl(lo, src, kWave);
+  hi = __shfl(hi, src, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t y = shfl_xor_u64(x, m);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+// number of set bits of `mask` below this lane
+__device__ __forceinline__ int mask_rank(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+// ---------------------------------------------------------------- selection keys
+// Composite key: order-preserving fp32 score bits in the high word, and the
+// complemented chunk id in the low word, so that the larger key is the higher
+// score and, on equal scores, the lower chunk id.  Valid keys are never 0.
+__device__ __forceinline__ uint64_t make_key(float score, int idx) {
+  uint32_t u = __float_as_uint(score);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | (0xffffffffu - static_cast<uint32_t>(idx));
+}
+__device__ __forceinline__ int key_index(uint64_t key) {
+  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
+}
+__device__ __forceinline__ float key_score(uint64_t key) {
+  uint32_t u = static_cast<uint32_t>(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+
+// Bitonic sort of one key per lane, descending (lane 0 = largest).
+__device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t key) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t other = shfl_xor_u64(key, j);
+      bool lower = (lane & j) == 0;
+      bool keep_max = lower == ((lane & k) == 0);
+      uint64_t mx = other > key ? other : key;
+      uint64_t mn = other > key ? key : other;
+      key = keep_max ? mx : mn;
+    }
+  }
+  return key;
+}
+
+// Bitonic sort of R keys per lane (element e = r * 64 + lane), descending in e.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&keys)[R]) {
+  const int lane = lane_id();
+  constexpr int N = R * kWave;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kWave) {
+        const int jr = j / kWave;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if ((r & jr) == 0) {
+            const int e = r * kWave + lane;
+            const bool asc_blk = (e & k) == 0;   // lower element keeps the max
+            uint64_t a = keys[r], b = keys[r | jr];
+            uint64_t mx = a > b ? a : b, mn = a > b ? b : a;
+            keys[r] = asc_blk ? mx : mn;
+            keys[r | jr] = asc_blk ? mn : mx;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int e = r * kWave + lane;
+          uint64_t other = shfl_xor_u64(keys[r], j);
+          bool lower = (e & j) == 0;
+          bool keep_max = lower == ((e & k) == 0);
+          uint64_t mx = other > keys[r] ? other : keys[r];
+          uint64_t mn = other > keys[r] ? keys[r] : other;
+          keys[r] = keep_max ? mx : mn;
+        }
+      }
+    }
+  }
+}
+
+// Sort one key per lane, descending, by rank counting: every lane counts the
+// keys larger than its own (all 64 are read back from LDS as broadcasts) and
+// scatters its key to that rank.  Keys must be unique apart from 0 (empty),
+// which sorts last.  `buf` is 64 uint64 of LDS private to the calling wave.
+// The reads are independent, so the latency is one LDS round trip plus ~130
+// vector instructions, instead of the 21 dependent exchanges of a bitonic net.
+__device__ __forceinline__ uint64_t wave_rank_sort64(uint64_t key, uint64_t* buf) {
+  const int lane = lane_id();
+  buf[lane] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rank = 0;
+  const ulonglong2* b2 = reinterpret_cast<const ulonglong2*>(buf);
+#pragma unroll
+  for (int j = 0; j < kWave / 2; ++j) {
+    ulonglong2 kk = b2[j];
+    rank += (kk.x > key) + (kk.y > key);
+  }
+  const int nvalid = __popcll(__ballot(key != 0));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (key != 0) buf[rank] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint64_t out = lane < nvalid ? buf[lane] : 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return out;
+}
+
+// Top-K (K <= 64) of R keys per lane.  Returns, in lane l < K, the l-th largest
+// key (0 where fewer than l+1 valid keys exist); lanes >= K hold the following
+// keys in order.  `buf` is 64 uint64 of LDS private to the calling wave.
+//
+// tau = K-th largest of the lane maxima: the K lanes owning the largest maxima
+// each hold a key >= tau, so the top K keys are all >= tau.  When at most 64
+// keys qualify (always when K * R <= 64, and nearly always otherwise) they are
+// compacted and rank-sorted; otherwise all 64R keys go through a bitonic sort.
+template <int R>
+__device__ __forceinline__ uint64_t wave_topk(uint64_t (&keys)[R], int K, uint64_t* buf) {
+  const int lane = lane_id();
+  uint64_t lm = keys[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) lm = keys[r] > lm ? keys[r] : lm;
+  if (R == 1) return wave_rank_sort64(lm, buf);
+  uint64_t srt = wave_rank_sort64(lm, buf);
+  uint64_t tau = shfl_u64(srt, K - 1);
+  if (tau == 0) tau = 1;
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[r] >= tau));
+  if (cnt <= kWave) {
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      bool pred = keys[r] >= tau;
+      uint64_t m = __ballot(pred);
+      if (pred) buf[base + mask_rank(m)] = keys[r];
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint64_t key = lane < base ? buf[lane] : 0ull;
+    return wave_rank_sort64(key, buf);
+  }
+  wave_sort_desc<R>(keys);
+  return keys[0];
+}
+
+// ---------------------------------------------------------------- block reductions
+// 256-thread (4-wave) block sum / max; `red` is 4 floats of LDS.  All threads
+// receive the result.
+__device__ __forceinline__ float block_sum4(float x, float* red) {
+  x = wave_sum(x);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane_id() == 0) red[w] = x;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+__device__ __forceinline__ float block_max4(float x, float* red) {
+  x = wave_max(x);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane_id() == 0) red[w] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// ---------------------------------------------------------------- geometry
+struct Geometry {
+  int B, Hq, Hkv, G, d, Lq, Lkv, S, K, NC, NCcap, causal, keep_own;
+  float scale;
+  // candidate count and own-chunk token range [own_a, own_b) of query i
+  __device__ __forceinline__ void layout(int i, int& ncand, int& own_a, int& own_b) const {
+    if (causal) {
+      int t = Lkv - Lq + i;
+      int own = t / S;
+      ncand = own < NC ? own : NC;
+      own_a = own * S;
+      own_b = t + 1;
+    } else {
+      ncand = NC;
+      own_a = NC * S;
+      own_b = Lkv;
+    }
+    if (!keep_own) own_b = own_a;
+  }
+};
+
+}  // namespace hils

@@ -1,0 +1,361 @@
+// Split single-token decode for bf16, head_dim 128, chunk 64 (HBM-bound path).
+//
+// Method: Hierarchical Sparse Attention Done Right (arXiv 2607.02980v1, summary
+// page): landmark scores §3 "Linear surrogate for chunk mass", top-K routing §3
+// "Sparse training", GQA-shared selection §4 "Architecture", per-chunk softmax
+// and score-weighted fusion §3 "Hierarchical softmax".
+//
+// Three launches on the caller's stream:
+//  1. score_select  grid (nsplit, B*Hkv): each workgroup streams a contiguous
+//     range of landmark rows (16 lanes x 16 B per 256 B row, coalesced), forms
+//     the group score scale*<mean_h q_h, lmk_c> + bias_c (the group mean is
+//     linear in q), and keeps its local top-K as composite keys.
+//  2. merge         grid (B*Hkv): top-K of the nsplit local lists; writes the
+//     ascending chunk ids.
+//  3. attend        grid (K+1, B*Hkv): one workgroup per selected chunk (and
+//     one for the own chunk) reads the chunk's 16 KB of K and 16 KB of V once
+//     for all G heads, computes the chunk softmax and o_c, and writes
+//     (s_c, o_c); the last workgroup of each (b, kv head) fuses the partials
+//     with a log-sum-exp over the retrieval scores.
+#include "hils_common.h"
+#include "hils_kernels.h"
+
+namespace hils {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kS = 64;
+constexpr int kThreads = 256;
+constexpr int kMaxGd = 16;            // heads per KV group on this path
+constexpr int kPartStride = kD + 4;   // o[128], s, pad  (floats)
+
+struct DecodeWs {
+  uint64_t* lists;   // [B*Hkv][nsplit][K]
+  float* parts;      // [B*Hkv][K+1][G][kPartStride]
+  unsigned* counters;  // [B*Hkv]
+};
+
+__device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+  x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+  x[4] = __uint_as_float(u.z << 16); x[5] = __uint_as_float(u.z & 0xffff0000u);
+  x[6] = __uint_as_float(u.w << 16); x[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+// ----------------------------------------------------------------------------
+// 1. scores + local top-K.  R blocks of 64 candidates per wave.
+// ----------------------------------------------------------------------------
+template <int R>
+__global__ void __launch_bounds__(kThreads)
+decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ lmk,
+                    const float* __restrict__ bias, int ncand, int cps, int nsplit,
+                    uint64_t* __restrict__ lists, unsigned* __restrict__ counters) {
+  __shared__ uint64_t buf[4][kWave];
+  __shared__ uint64_t wl[4][kWave];
+  const int split = blockIdx.x, bkv = blockIdx.y;
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int sub = lane & 15, grp = lane >> 4;
+  if (split == 0 && tid == 0) counters[bkv] = 0u;
+
+  // this lane's 8 dims of the mean query
+  float qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int h = 0; h < g.G; ++h) {
+    float x[8];
+    load_bf16x8(q + (size_t)(b * g.Hq + kvh * g.G + h) * kD + sub * 8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[e] += x[e];
+  }
+  const float inv = g.scale / (float)g.G;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qb[e] *= inv;
+
+  const int c0 = split * cps;
+  const int c1 = min(c0 + cps, ncand);
+  const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
+  const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
+  uint64_t keys[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int base = c0 + (r * 4 + w) * kWave;   // this wave's block of 64
+    uint4 raw[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int c = base + grp * 16 + it;
+      raw[it] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+    float mine = 0.f;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const uint4 u = raw[it];
+      float s = qb[0] * __uint_as_float(u.x << 16) + qb[1] * __uint_as_float(u.x & 0xffff0000u)
+              + qb[2] * __uint_as_float(u.y << 16) + qb[3] * __uint_as_float(u.y & 0xffff0000u)
+              + qb[4] * __uint_as_float(u.z << 16) + qb[5] * __uint_as_float(u.z & 0xffff0000u)
+              + qb[6] * __uint_as_float(u.w << 16) + qb[7] * __uint_as_float(u.w & 0xffff0000u);
+      s += __shfl_xor(s, 8, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 1, kWave);
+      if (it == sub) mine = s;
+    }
+    const int c = base + lane;   // = base + grp*16 + sub
+    keys[r] = c < c1 ? make_key(mine + (bb ? bb[c] : 0.f), c) : 0ull;
+  }
+  uint64_t top = wave_topk<R>(keys, g.K, buf[w]);
+  wl[w][lane] = lane < g.K ? top : 0ull;
+  __syncthreads();
+  if (w == 0) {
+    uint64_t four[4] = {wl[0][lane], wl[1][lane], wl[2][lane], wl[3][lane]};
+    uint64_t t = wave_topk<4>(four, g.K, buf[0]);
+    if (lane < g.K) lists[((size_t)bkv * nsplit + split) * g.K + lane] = t;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 2. merge the nsplit local lists of one (b, kv head); write ascending ids.
+// ----------------------------------------------------------------------------
+constexpr int kMergeR = 15;   // + the running list = 16 keys per lane
+__global__ void __launch_bounds__(kThreads)
+decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
+             int32_t* __restrict__ sel_idx) {
+  __shared__ uint64_t buf[4][kWave];
+  __shared__ uint64_t wl[4][kWave];
+  const int bkv = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int n = nsplit * g.K;
+  const uint64_t* src = lists + (size_t)bkv * n;
+  uint64_t run = 0;
+  for (int base = w * kWave * kMergeR; base < n; base += 4 * kWave * kMergeR) {
+    uint64_t keys[kMergeR + 1];
+#pragma unroll
+    for (int r = 0; r < kMergeR; ++r) {
+      const int e = base + r * kWave + lane;
+      keys[r] = e < n ? src[e] : 0ull;
+    }
+    keys[kMergeR] = run;
+    run = wave_topk<kMergeR + 1>(keys, g.K, buf[w]);
+  }
+  wl[w][lane] = lane < g.K ? run : 0ull;
+  __syncthreads();
+  if (w == 0) {
+    uint64_t four[4] = {wl[0][lane], wl[1][lane], wl[2][lane], wl[3][lane]};
+    uint64_t top = wave_topk<4>(four, g.K, buf[0]);
+    uint64_t asc = (lane < g.K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
+    asc = wave_rank_sort64(asc, buf[0]);
+    if (lane < g.K) sel_idx[(size_t)bkv * g.K + lane] = asc ? (int)(0xffffffffull - (asc - 1)) : -1;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 3. per-chunk attention for the G heads + last-block fusion.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+decode_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
+              const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
+              float* __restrict__ parts, unsigned* __restrict__ counters,
+              uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+  __shared__ float qs[kMaxGd][kD];
+  __shared__ float lg[kMaxGd][kS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
+  __shared__ float sc[kMaxGd];
+  __shared__ int is_last;
+  const int slot = blockIdx.x, bkv = blockIdx.y;
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int G = g.G;
+  const int nslot = g.K + 1;
+
+  // which tokens: a selected chunk, or the own chunk's visible tokens
+  const int t = g.Lkv - 1;
+  int a = 0, n = 0, c = -1;
+  if (slot < g.K) {
+    c = sel_idx[(size_t)bkv * g.K + slot];
+    if (c >= 0) { a = c * kS; n = kS; }
+  } else if (g.keep_own) {
+    a = (t / kS) * kS;
+    n = t - a + 1;
+  }
+  float* part = parts + ((size_t)bkv * nslot + slot) * G * kPartStride;
+
+  if (n > 0) {
+    for (int x = tid; x < G * kD; x += kThreads)
+      qs[x / kD][x % kD] = bf16_to_f32(q[(size_t)(b * g.Hq + kvh * G) * kD + x]);
+    const uint16_t* Kc = k + ((size_t)bkv * g.Lkv + a) * kD;
+    const uint16_t* Vc = v + ((size_t)bkv * g.Lkv + a) * kD;
+    // stage V (16 B per thread per step); rows >= n are zero
+    for (int x = tid; x < kS * kD / 8; x += kThreads) {
+      const int row = x / (kD / 8);
+      uint4 u = row < n ? reinterpret_cast<const uint4*>(Vc)[x] : make_uint4(0, 0, 0, 0);
+      reinterpret_cast<uint4*>(vs)[x] = u;
+    }
+    // K: thread -> (key j = tid/4, quarter = tid%4 -> 32 dims)
+    const int j = tid >> 2, qd = tid & 3;
+    float kx[32];
+    if (j < n) {
+#pragma unroll
+      for (int p4 = 0; p4 < 4; ++p4) {
+        float x[8];
+        load_bf16x8(Kc + (size_t)j * kD + qd * 32 + p4 * 8, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kx[p4 * 8 + e] = x[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) kx[e] = 0.f;
+    }
+    __syncthreads();
+    for (int h = 0; h < G; ++h) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) s += qs[h][qd * 32 + e] * kx[e];
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      if (qd == 0) lg[h][j] = j < n ? g.scale * s : -INFINITY;
+    }
+    __syncthreads();
+    // softmax per head (wave w takes heads w, w+4, ...), and the retrieval score
+    for (int h = w; h < G; h += 4) {
+      const float l = lg[h][lane];
+      const float m = wave_max(l);
+      const float e = __expf(l - m);
+      const float z = wave_sum(e);
+      lg[h][lane] = e / z;
+      float s;
+      if (slot < g.K) {
+        const uint16_t* lr = lmk + ((size_t)bkv * g.NCcap + c) * kD;
+        float part_s = qs[h][2 * lane] * bf16_to_f32(lr[2 * lane]) +
+                       qs[h][2 * lane + 1] * bf16_to_f32(lr[2 * lane + 1]);
+        s = g.scale * wave_sum(part_s) + (bias ? bias[(size_t)bkv * g.NCcap + c] : 0.f);
+      } else {
+        s = m + __logf(z);   // own chunk: its exact log-sum-exp
+      }
+      if (lane == 0) sc[h] = s;
+    }
+    __syncthreads();
+    // o_c = P V : thread -> dims (2*dp, 2*dp+1) of heads hg, hg+4, ...
+    const int dp = tid & 63, hg = tid >> 6;
+    for (int h = hg; h < G; h += 4) {
+      float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+      for (int jj = 0; jj < kS; ++jj) {
+        const uint32_t pr = reinterpret_cast<const uint32_t*>(vs)[jj * (kD / 2) + dp];
+        const float pj = lg[h][jj];
+        o0 += pj * __uint_as_float(pr << 16);
+        o1 += pj * __uint_as_float(pr & 0xffff0000u);
+      }
+      float* ph = part + (size_t)h * kPartStride;
+      ph[2 * dp] = o0;
+      ph[2 * dp + 1] = o1;
+      if (dp == 0) ph[kD] = sc[h];
+    }
+  } else {
+    for (int h = tid; h < G; h += kThreads) part[(size_t)h * kPartStride + kD] = -INFINITY;
+  }
+
+  // last workgroup of this (b, kv head) fuses the K+1 partials
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(&counters[bkv], 1u) == (unsigned)(nslot - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  const float* pb = parts + (size_t)bkv * nslot * G * kPartStride;
+  const int dp = tid & 63, hg = tid >> 6;
+  for (int h = hg; h < G; h += 4) {
+    float m = -INFINITY;
+    for (int s = 0; s < nslot; ++s) m = fmaxf(m, __builtin_nontemporal_load(pb + ((size_t)s * G + h) * kPartStride + kD));
+    float z = 0.f, o0 = 0.f, o1 = 0.f;
+    if (m != -INFINITY) {
+      for (int s = 0; s < nslot; ++s) {
+        const float* ph = pb + ((size_t)s * G + h) * kPartStride;
+        const float sv = __builtin_nontemporal_load(ph + kD);
+        if (sv == -INFINITY) continue;
+        const float e = __expf(sv - m);
+        z += e;
+        o0 += e * __builtin_nontemporal_load(ph + 2 * dp);
+        o1 += e * __builtin_nontemporal_load(ph + 2 * dp + 1);
+      }
+    }
+    const size_t orow = (size_t)(b * g.Hq + kvh * G + h) * kD;
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    const uint32_t pk = (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
+    reinterpret_cast<uint32_t*>(out + orow)[dp] = pk;
+    if (dp == 0 && lse_out) lse_out[b * g.Hq + kvh * G + h] = z > 0.f ? m + __logf(z) : -INFINITY;
+  }
+  if (tid == 0) counters[bkv] = 0u;
+}
+
+struct DecodePlan {
+  int ncand, R, cps, nsplit;
+};
+
+DecodePlan plan(const Geometry& g) {
+  DecodePlan p;
+  const int t = g.Lkv - 1;
+  p.ncand = min(t / kS, g.NC);
+  const int bkv = g.B * g.Hkv;
+  // aim for about 1024 workgroups in the scoring launch
+  int want_splits = max(1, 1024 / max(1, bkv));
+  int per = (p.ncand + want_splits - 1) / want_splits;
+  int R = 1;
+  while (R < 8 && R * 256 < per) R <<= 1;
+  p.R = R;
+  p.cps = 256 * R;
+  p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
+  return p;
+}
+
+DecodeWs carve(const Geometry& g, const DecodePlan& p, void* ws) {
+  DecodeWs d;
+  char* c = reinterpret_cast<char*>(ws);
+  size_t off = 0;
+  d.lists = reinterpret_cast<uint64_t*>(c + off);
+  off += ((size_t)g.B * g.Hkv * p.nsplit * g.K * 8 + 255) & ~(size_t)255;
+  d.parts = reinterpret_cast<float*>(c + off);
+  off += ((size_t)g.B * g.Hkv * (g.K + 1) * g.G * kPartStride * 4 + 255) & ~(size_t)255;
+  d.counters = reinterpret_cast<unsigned*>(c + off);
+  return d;
+}
+
+}  // namespace
+
+bool decode_fast_supported(const Geometry& g, int bf16) {
+  return bf16 && g.d == kD && g.S == kS && g.G <= kMaxGd && g.K <= kMaxTopK && g.Lq == 1 &&
+         g.causal;
+}
+
+size_t decode_fast_ws(const Geometry& g) {
+  DecodePlan p = plan(g);
+  size_t off = ((size_t)g.B * g.Hkv * p.nsplit * g.K * 8 + 255) & ~(size_t)255;
+  off += ((size_t)g.B * g.Hkv * (g.K + 1) * g.G * kPartStride * 4 + 255) & ~(size_t)255;
+  off += (size_t)g.B * g.Hkv * 4;
+  return off;
+}
+
+hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, const void* v,
+                              const void* lmk, const float* bias, void* out, int32_t* sel_idx,
+                              float* lse, void* ws, hipStream_t st) {
+  DecodePlan p = plan(g);
+  DecodeWs d = carve(g, p, ws);
+  const int bkv = g.B * g.Hkv;
+  const uint16_t* Q = (const uint16_t*)q;
+  const uint16_t* Lm = (const uint16_t*)lmk;
+  dim3 g1(p.nsplit, bkv);
+  switch (p.R) {
+    case 1: hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
+    case 2: hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
+    case 4: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
+    default: hipLaunchKernelGGL(decode_score_select<8>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
+  }
+  hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kThreads), 0, st, g, p.nsplit, d.lists, sel_idx);
+  hipLaunchKernelGGL(decode_attend, dim3(g.K + 1, bkv), dim3(kThreads), 0, st, g, Q,
+                     (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts,
+                     d.counters, (uint16_t*)out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace hils

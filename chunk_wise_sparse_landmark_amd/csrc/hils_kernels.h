@@ -1,0 +1,35 @@
+// Host-side launchers of the HiLS kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hils_common.h"
+
+namespace hils {
+
+// shape-generic path (fp32 or bf16)
+hipError_t launch_generic_forward(const Geometry& g, int bf16, const void* q, const void* k,
+                                  const void* v, const void* lmk, const float* bias, void* out,
+                                  int32_t* sel_idx, float* lse, hipStream_t st);
+size_t generic_backward_ws(const Geometry& g);
+hipError_t launch_generic_backward(const Geometry& g, int bf16, const void* q, const void* k,
+                                   const void* v, const void* lmk, const float* bias,
+                                   const void* dout, const int32_t* sel_idx, void* dq, void* dk,
+                                   void* dv, void* dlmk, float* dbias, void* ws, hipStream_t st);
+
+// split decode path (bf16, d = 128, S = 64)
+bool decode_fast_supported(const Geometry& g, int bf16);
+size_t decode_fast_ws(const Geometry& g);
+hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, const void* v,
+                              const void* lmk, const float* bias, void* out, int32_t* sel_idx,
+                              float* lse, void* ws, hipStream_t st);
+
+// MFMA prefill path (bf16, d = 128, S = 64, causal, seq_q == seq_kv)
+bool prefill_fast_supported(const Geometry& g, int bf16);
+size_t prefill_fast_ws(const Geometry& g);
+hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, const void* v,
+                               const void* lmk, const float* bias, void* out, int32_t* sel_idx,
+                               float* lse, void* ws, hipStream_t st);
+
+}  // namespace hils

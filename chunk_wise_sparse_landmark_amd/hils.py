@@ -1,0 +1,184 @@
+"""Thin ctypes binding of libhils.so (argument marshalling only).
+
+The functions carry the C names: ``hils_forward``, ``hils_decode``,
+``hils_backward``, ``hils_workspace_size``.  Tensors must be contiguous
+torch tensors on a ROCm device (bf16 or fp32); outputs and the workspace are
+allocated with torch when not given, and every kernel runs on torch's current
+stream.  Nothing here computes any part of the method; a missing library is an
+error, never a fallback.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhils.so")
+
+HILS_OK, HILS_ERR_INVALID_ARG, HILS_ERR_UNSUPPORTED, HILS_ERR_WORKSPACE, HILS_ERR_HIP = range(5)
+HILS_F32, HILS_BF16 = 0, 1
+HILS_OP_FORWARD, HILS_OP_DECODE, HILS_OP_BACKWARD = 0, 1, 2
+
+EXPORTS = ("hils_workspace_size", "hils_forward", "hils_decode", "hils_backward",
+           "hils_status_string", "hils_last_error")
+
+
+class HilsParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("seq_q", ctypes.c_int32), ("seq_kv", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("num_landmarks", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("keep_own_chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+class HilsError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (_STATUS.get(status, status), msg))
+        self.status = status
+
+
+_STATUS = {0: "HILS_OK", 1: "HILS_ERR_INVALID_ARG", 2: "HILS_ERR_UNSUPPORTED",
+           3: "HILS_ERR_WORKSPACE", 4: "HILS_ERR_HIP"}
+_lib = None
+
+
+def load_library(path=None):
+    """Load libhils.so (built in-tree by chunk_wise_sparse_landmark_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libhils.so is not built (%s); run __graft_entry__.build()" % p)
+    lib = ctypes.CDLL(p)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    P = ctypes.POINTER(HilsParams)
+    lib.hils_workspace_size.argtypes = [P, i32]
+    lib.hils_workspace_size.restype = sz
+    lib.hils_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hils_forward.restype = ctypes.c_int
+    lib.hils_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hils_decode.restype = ctypes.c_int
+    lib.hils_backward.argtypes = [P] + [vp] * 14 + [vp, sz, vp]
+    lib.hils_backward.restype = ctypes.c_int
+    lib.hils_status_string.argtypes = [ctypes.c_int]
+    lib.hils_status_string.restype = ctypes.c_char_p
+    lib.hils_last_error.argtypes = []
+    lib.hils_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_params(*, batch, heads_q, heads_kv, head_dim, seq_q, seq_kv, chunk_size, top_k,
+                num_landmarks, causal=True, keep_own_chunk=True, scale=0.0, dtype=HILS_BF16):
+    return HilsParams(batch, heads_q, heads_kv, head_dim, seq_q, seq_kv, chunk_size, top_k,
+                      num_landmarks, int(bool(causal)), int(bool(keep_own_chunk)),
+                      float(scale or 0.0), dtype)
+
+
+def _check(status):
+    if status != HILS_OK:
+        msg = load_library().hils_last_error().decode()
+        raise HilsError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return HILS_BF16
+    if t.dtype == torch.float32:
+        return HILS_F32
+    raise TypeError("HiLS tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale):
+    for name, t in (("q", q), ("k", k), ("lmk", lmk)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    B, Hq, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    return make_params(batch=B, heads_q=Hq, heads_kv=Hkv, head_dim=d, seq_q=Lq, seq_kv=Lkv,
+                       chunk_size=chunk_size, top_k=top_k, num_landmarks=lmk.shape[2],
+                       causal=causal, keep_own_chunk=keep_own_chunk, scale=scale,
+                       dtype=_dtype_code(q))
+
+
+def hils_workspace_size(params, op):
+    return int(load_library().hils_workspace_size(ctypes.byref(params), op))
+
+
+def _workspace(params, op, device, ws):
+    need = hils_workspace_size(params, op)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, need if ws is None else ws.numel()
+
+
+def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_chunk, scale,
+         out, sel_idx, lse, ws, stream):
+    p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale)
+    B, Hq, Lq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hkv, Lq, top_k), dtype=torch.int32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
+    ws, nbytes = _workspace(p, op, dev, ws)
+    lib = load_library()
+    st = getattr(lib, entry)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lmk),
+                             _ptr(lmk_bias), _ptr(out), _ptr(sel_idx), _ptr(lse), _ptr(ws),
+                             nbytes, _stream(stream))
+    _check(st)
+    return out, sel_idx, lse
+
+
+def hils_forward(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, causal=True,
+                 keep_own_chunk=True, scale=0.0, out=None, sel_idx=None, lse=None, ws=None,
+                 stream=None):
+    """HiLS forward: returns (out [B,Hq,Lq,d], sel_idx int32 [B,Hkv,Lq,K], lse fp32 [B,Hq,Lq])."""
+    return _fwd("hils_forward", HILS_OP_FORWARD, q, k, v, lmk, lmk_bias, chunk_size, top_k,
+                causal, keep_own_chunk, scale, out, sel_idx, lse, ws, stream)
+
+
+def hils_decode(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, keep_own_chunk=True,
+                scale=0.0, out=None, sel_idx=None, lse=None, ws=None, stream=None):
+    """Single-token decode over the cache k, v (q: [B,Hq,1,d], position seq_kv-1)."""
+    return _fwd("hils_decode", HILS_OP_DECODE, q, k, v, lmk, lmk_bias, chunk_size, top_k,
+                True, keep_own_chunk, scale, out, sel_idx, lse, ws, stream)
+
+
+def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size, top_k,
+                  causal=True, keep_own_chunk=True, scale=0.0, need_dbias=None, ws=None,
+                  stream=None):
+    """Gradients (dq, dk, dv, dlmk, dbias-or-None) of <dout, out> with the selection fixed."""
+    p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale)
+    dq, dk, dv, dlmk = (torch.empty_like(t) for t in (q, k, v, lmk))
+    if need_dbias is None:
+        need_dbias = lmk_bias is not None
+    dbias = torch.empty(lmk.shape[:3], dtype=torch.float32, device=q.device) if need_dbias else None
+    ws, nbytes = _workspace(p, HILS_OP_BACKWARD, q.device, ws)
+    lib = load_library()
+    st = lib.hils_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lmk), _ptr(lmk_bias),
+                           _ptr(out), _ptr(dout), _ptr(sel_idx), _ptr(lse), _ptr(dq), _ptr(dk),
+                           _ptr(dv), _ptr(dlmk), _ptr(dbias), _ptr(ws), nbytes, _stream(stream))
+    _check(st)
+    return dq, dk, dv, dlmk, dbias
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

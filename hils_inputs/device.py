@@ -1,0 +1,73 @@
+"""Device copies of the synthetic inputs (torch tensors on a ROCm device).
+
+Small tensors are generated on the host and copied; large K/V caches are
+filled directly on the device by ``libhils_inputs.so`` with the same counter
+generator, so the host can regenerate any slice (LazyNormalBF16).
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from .configs import LazyNormalBF16, make_host_inputs
+from .gen import IH_INV_SD, f32_to_bf16_bits, TENSOR_IDS
+
+_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhils_inputs.so")
+_lib = None
+
+
+def _fill_lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError("libhils_inputs.so is not built; run __graft_entry__.build()")
+        _lib = ctypes.CDLL(_LIB)
+        _lib.hils_inputs_fill_normal.argtypes = [
+            ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+            ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        _lib.hils_inputs_fill_normal.restype = ctypes.c_int
+    return _lib
+
+
+def to_device(x, dtype, device):
+    """Host float32 array (representable in dtype) -> contiguous device tensor."""
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(np.ascontiguousarray(x, dtype=np.float32)).view(np.int16)
+        return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def fill_normal(t, seed, tid_name, offset=0, scale=1.0):
+    """Fill a contiguous bf16/fp32 device tensor with generated N(0, scale^2) values."""
+    assert t.is_contiguous()
+    as_bf16 = t.dtype == torch.bfloat16
+    st = torch.cuda.current_stream().cuda_stream
+    rc = _fill_lib().hils_inputs_fill_normal(
+        ctypes.c_void_p(t.data_ptr()), t.numel(), seed, TENSOR_IDS[tid_name], offset,
+        float(IH_INV_SD), float(scale), int(as_bf16), ctypes.c_void_p(st))
+    if rc != 0:
+        raise RuntimeError("device fill failed")
+    return t
+
+
+def make_device_inputs(cfg, device="cuda", host=None):
+    """Returns (host dict, device dict).  Lazy host K/V are filled on the device."""
+    host = make_host_inputs(cfg) if host is None else host
+    dt = cfg["dtype"]
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    dev = {}
+    for name in ("q", "lmk", "dout"):
+        if host.get(name) is not None:
+            dev[name] = to_device(host[name], dt, device)
+    dev["bias"] = None if host.get("bias") is None else torch.from_numpy(
+        np.ascontiguousarray(host["bias"], dtype=np.float32)).to(device)
+    for name in ("k", "v"):
+        x = host[name]
+        if isinstance(x, LazyNormalBF16):
+            t = torch.empty(x.shape, dtype=tdt, device=device)
+            fill_normal(t, cfg["seed"], name)
+            dev[name] = t
+        else:
+            dev[name] = to_device(x, dt, device)
+    return host, dev

@@ -1,0 +1,77 @@
+// Device fill for the seeded synthetic inputs: the same counter-based
+// generator as hils_inputs/gen.py (SplitMix64 finaliser, Irwin-Hall sum of four
+// 16-bit fields, one correctly rounded fp32 multiply, bf16 round-to-nearest-
+// even), so any slice can be regenerated on the host bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kTidMul = 0xD1B54A32D192ED03ull;
+
+__host__ __device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ inline float draw(uint64_t key, uint64_t n, float inv_sd, float scale, int scaled) {
+  const uint64_t u = mix64(key + (n + 1) * kGolden);
+  const int64_t s = (int64_t)(u & 0xffff) + (int64_t)((u >> 16) & 0xffff) +
+                    (int64_t)((u >> 32) & 0xffff) + (int64_t)((u >> 48) & 0xffff) - 131070;
+  float x = __fmul_rn((float)s, inv_sd);
+  if (scaled) x = __fmul_rn(x, scale);
+  return x;
+}
+
+__device__ inline uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__global__ void fill_bf16(uint16_t* dst, uint64_t n, uint64_t key, uint64_t offset, float inv_sd,
+                          float scale, int scaled) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 8;
+  for (uint64_t base = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; base < n;
+       base += stride) {
+    if (base + 8 <= n) {
+      uint32_t w[4];
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t lo = to_bf16(draw(key, offset + base + 2 * e, inv_sd, scale, scaled));
+        const uint16_t hi = to_bf16(draw(key, offset + base + 2 * e + 1, inv_sd, scale, scaled));
+        w[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + base) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (uint64_t e = base; e < n; ++e) dst[e] = to_bf16(draw(key, offset + e, inv_sd, scale, scaled));
+    }
+  }
+}
+
+__global__ void fill_f32(float* dst, uint64_t n, uint64_t key, uint64_t offset, float inv_sd,
+                         float scale, int scaled) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride)
+    dst[e] = draw(key, offset + e, inv_sd, scale, scaled);
+}
+
+}  // namespace
+
+extern "C" int hils_inputs_fill_normal(void* dst, uint64_t n, uint64_t seed, uint64_t tid,
+                                       uint64_t offset, float inv_sd, float scale, int as_bf16,
+                                       void* stream) {
+  const uint64_t key = mix64(seed * kGolden + tid * kTidMul);
+  const int scaled = scale != 1.0f;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int blocks = 8192;
+  if (n == 0) return 0;
+  if (as_bf16)
+    hipLaunchKernelGGL(fill_bf16, dim3(blocks), dim3(256), 0, st, (uint16_t*)dst, n, key, offset,
+                       inv_sd, scale, scaled);
+  else
+    hipLaunchKernelGGL(fill_f32, dim3(blocks), dim3(256), 0, st, (float*)dst, n, key, offset,
+                       inv_sd, scale, scaled);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}

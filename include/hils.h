@@ -1,0 +1,137 @@
+/*
+ * hils.h -- C ABI of the HiLS (Hierarchical Landmark Sparse) attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Hierarchical Sparse Attention Done Right: Toward Infinite Context
+ * Modeling" (arXiv 2607.02980v1), source-linked summary page, cited below as
+ * [HSADR <section>].  For every query i and query head h of KV group g:
+ *
+ *   candidates   C_i: complete chunks c (keys [cS, cS+S)) strictly before the
+ *                query's own chunk (causal), or all complete chunks
+ *                (non-causal)                         [HSADR §2 Preliminary]
+ *   score        s_{h,i,c} = scale * <q_{h,i}, lmk_{g,c}> + bias_{g,c}
+ *                (one landmark key per chunk; affine surrogate of the chunk's
+ *                LogSumExp mass)        [HSADR §3 "Linear surrogate for chunk mass"]
+ *   selection    T_{g,i} = top min(K, |C_i|) chunks by the fp32 group score
+ *                mean_{h in g} s_{h,i,c}, ties to the lower chunk id; the heads
+ *                of a group share it   [HSADR §3 "Sparse training"; §4 GQA]
+ *   attention    per chunk c in T (and the own chunk's visible tokens when
+ *                keep_own_chunk): l_j = scale*<q, k_j>, lse_c = log sum exp l_j,
+ *                o_c = sum_j exp(l_j - lse_c) v_j     [HSADR §3 "Hierarchical softmax"]
+ *   fusion       F = T + {own}; s_own = lse_own; LSE = log sum_{c in F} exp s_c;
+ *                O = sum_{c in F} exp(s_c - LSE) o_c  [HSADR Abstract; §3]
+ *   backward     gradients of <dO, O> for q, k, v, lmk, bias with the selection
+ *                held fixed; unselected chunks get none [HSADR §3; §9]
+ *
+ * Causal queries sit at key positions t_i = seq_kv - seq_q + i (prefill:
+ * seq_q == seq_kv; decode: seq_q == 1, t = seq_kv - 1).  Non-causal: the
+ * trailing partial chunk, if any, is the own chunk.  An empty fusion set gives
+ * O = 0 and LSE = -inf.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, out, dout, dq   [batch, heads_q,  seq_q,  head_dim]
+ *   k, v, dk, dv       [batch, heads_kv, seq_kv, head_dim]
+ *   lmk, dlmk          [batch, heads_kv, num_landmarks, head_dim]
+ *   lmk_bias, dbias    [batch, heads_kv, num_landmarks]          fp32, nullable
+ *   sel_idx            [batch, heads_kv, seq_q, top_k]           int32, ascending
+ *                                                               chunk ids, -1 padded
+ *   lse                [batch, heads_q,  seq_q]                  fp32
+ * dtype HILS_BF16: q, k, v, lmk, out, dout, dq, dk, dv, dlmk are bf16 (raw 16-bit
+ * patterns); arithmetic is fp32. HILS_F32: all of them fp32.
+ *
+ * Ownership and concurrency: every pointer is a device pointer owned by the
+ * caller.  The library allocates nothing and keeps no mutable global state;
+ * scratch memory is the caller's `ws` buffer of at least
+ * hils_workspace_size() bytes (256-byte aligned).  Work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream) and never synchronised;
+ * calls sharing one workspace must be ordered on one stream.
+ *
+ * Errors: arguments are validated before any launch.  A null required
+ * pointer, a negative size, heads_q % heads_kv != 0, chunk_size or top_k < 1,
+ * num_landmarks < seq_kv / chunk_size, a causal call with seq_q > seq_kv, a
+ * decode call with seq_q != 1, a base pointer not 16-byte aligned, or a
+ * workspace that is too small gives HILS_ERR_INVALID_ARG / HILS_ERR_WORKSPACE.
+ * Shapes the kernels do not cover (top_k > 64, head_dim > 256,
+ * chunk_size > 256, heads_q / heads_kv > 64, or a backward with
+ * chunk_size * head_dim > 8192) give HILS_ERR_UNSUPPORTED.  A failed launch
+ * gives HILS_ERR_HIP.  Nothing throws across the ABI; hils_last_error() holds
+ * a message for the calling thread.  Empty problems (batch, seq_q or heads
+ * equal to 0) are valid and launch nothing.
+ */
+#ifndef HILS_H_
+#define HILS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HILS_OK = 0,
+  HILS_ERR_INVALID_ARG = 1,
+  HILS_ERR_UNSUPPORTED = 2,
+  HILS_ERR_WORKSPACE = 3,
+  HILS_ERR_HIP = 4
+} hils_status;
+
+typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype;
+
+typedef enum { HILS_OP_FORWARD = 0, HILS_OP_DECODE = 1, HILS_OP_BACKWARD = 2 } hils_op;
+
+typedef struct {
+  int32_t batch;           /* B                                                  */
+  int32_t heads_q;         /* Hq; a multiple of heads_kv                         */
+  int32_t heads_kv;        /* Hkv; G = Hq / Hkv query heads share one chunk set  */
+  int32_t head_dim;        /* d                                                  */
+  int32_t seq_q;           /* queries per (batch, head)                          */
+  int32_t seq_kv;          /* keys per (batch, kv head)                          */
+  int32_t chunk_size;      /* S                                                  */
+  int32_t top_k;           /* K retrieved chunks per query (fewer if fewer exist)*/
+  int32_t num_landmarks;   /* landmark rows per (batch, kv head), >= seq_kv / S  */
+  int32_t causal;          /* 0 / 1                                              */
+  int32_t keep_own_chunk;  /* 0 / 1: attend the own chunk's visible tokens too   */
+  float scale;             /* token-logit and score scale; <= 0 means 1/sqrt(d)  */
+  int32_t dtype;           /* hils_dtype                                          */
+} hils_params;
+
+/* Bytes of workspace that `op` (hils_op) needs for these parameters; 0 when the
+ * parameters are invalid. */
+size_t hils_workspace_size(const hils_params* p, int32_t op);
+
+/* Forward pass (prefill or any seq_q): scores, group top-K selection, per-chunk
+ * attention and fusion [HSADR §3].  Writes out, sel_idx and (if non-null) lse. */
+hils_status hils_forward(const hils_params* p, const void* q, const void* k, const void* v,
+                         const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
+                         float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Single-token decode over a KV cache: seq_q must be 1 and causal is implied
+ * (the query is the newest token, at position seq_kv - 1, its K/V already in
+ * the cache).  Same math as hils_forward's last row; candidate scoring and
+ * chunk attention are split across the GPU and merged by log-sum-exp. */
+hils_status hils_decode(const hils_params* p, const void* q, const void* k, const void* v,
+                        const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
+                        float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass with the selection `sel_idx` (from hils_forward) held fixed
+ * [HSADR §3 "Hierarchical softmax"; §9].  Writes (overwrites) dq, dk, dv,
+ * dlmk and, if non-null, dlmk_bias.  `out` and `lse` are the forward's
+ * outputs; `lse` must be non-null. */
+hils_status hils_backward(const hils_params* p, const void* q, const void* k, const void* v,
+                          const void* lmk, const float* lmk_bias, const void* out,
+                          const void* dout, const int32_t* sel_idx, const float* lse,
+                          void* dq, void* dk, void* dv, void* dlmk, float* dlmk_bias,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* hils_status_string(hils_status s);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* hils_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HILS_H_ */

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before any launch
+(so these run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunk_wise_sparse_landmark_amd import hils as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hils.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(H.LIB_PATH), reason="libhils.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(hils_[a-z_]+)\s*\(", src,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_bound_entry_points():
+    assert _declared() == sorted(H.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = H.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_params_struct_layout_matches_header():
+    assert ctypes.sizeof(H.HilsParams) == 13 * 4
+
+
+def _p(**kw):
+    base = dict(batch=1, heads_q=4, heads_kv=2, head_dim=128, seq_q=256, seq_kv=256,
+                chunk_size=64, top_k=2, num_landmarks=4, causal=True, keep_own_chunk=True,
+                scale=0.0, dtype=H.HILS_BF16)
+    base.update(kw)
+    # raw struct: no normalisation of flag values
+    return H.HilsParams(base["batch"], base["heads_q"], base["heads_kv"], base["head_dim"],
+                        base["seq_q"], base["seq_kv"], base["chunk_size"], base["top_k"],
+                        base["num_landmarks"], int(base["causal"]), int(base["keep_own_chunk"]),
+                        base["scale"], base["dtype"])
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: every call below fails validation
+MIS = ctypes.c_void_p((1 << 20) + 4)   # not 16-byte aligned
+
+
+def _fwd(p, q=FAKE, k=FAKE, v=FAKE, lmk=FAKE, bias=None, out=FAKE, idx=FAKE, lse=None, ws=None,
+         ws_bytes=0, entry="hils_forward"):
+    lib = H.load_library()
+    return getattr(lib, entry)(ctypes.byref(p), q, k, v, lmk, bias, out, idx, lse, ws, ws_bytes,
+                               None)
+
+
+def _err():
+    return H.load_library().hils_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=3), H.HILS_ERR_INVALID_ARG),              # Hq % Hkv != 0
+    (dict(chunk_size=0), H.HILS_ERR_INVALID_ARG),
+    (dict(top_k=0), H.HILS_ERR_INVALID_ARG),
+    (dict(top_k=-3), H.HILS_ERR_INVALID_ARG),
+    (dict(num_landmarks=3), H.HILS_ERR_INVALID_ARG),        # < seq_kv / S
+    (dict(seq_q=512), H.HILS_ERR_INVALID_ARG),              # causal with seq_q > seq_kv
+    (dict(batch=-1), H.HILS_ERR_INVALID_ARG),
+    (dict(dtype=7), H.HILS_ERR_INVALID_ARG),
+    (dict(causal=2), H.HILS_ERR_INVALID_ARG),
+    (dict(top_k=65), H.HILS_ERR_UNSUPPORTED),
+    (dict(head_dim=512), H.HILS_ERR_UNSUPPORTED),
+    (dict(chunk_size=512, seq_kv=1024, seq_q=1024, num_landmarks=2), H.HILS_ERR_UNSUPPORTED),
+])
+def test_forward_rejects(kw, status):
+    assert _fwd(_p(**kw)) == status
+    assert _err()
+
+
+def test_null_and_misaligned_pointers():
+    assert _fwd(_p(), q=None) == H.HILS_ERR_INVALID_ARG
+    assert _fwd(_p(), idx=None) == H.HILS_ERR_INVALID_ARG
+    assert _fwd(_p(), k=MIS) == H.HILS_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    assert _fwd(H.make_params(batch=1, heads_q=32, heads_kv=8, head_dim=128, seq_q=1,
+                              seq_kv=4096, chunk_size=64, top_k=8, num_landmarks=64),
+                ws=None, entry="hils_decode") == H.HILS_ERR_WORKSPACE
+
+
+def test_decode_needs_one_query():
+    assert _fwd(_p(seq_q=2), entry="hils_decode") == H.HILS_ERR_INVALID_ARG
+    assert "seq_q" in _err()
+
+
+def test_workspace_too_small():
+    p = H.make_params(batch=2, heads_q=32, heads_kv=8, head_dim=128, seq_q=1, seq_kv=8192,
+                      chunk_size=64, top_k=16, num_landmarks=128)
+    need = H.hils_workspace_size(p, H.HILS_OP_DECODE)
+    assert need > 0 and need % 256 == 0
+    assert _fwd(p, ws=FAKE, ws_bytes=need - 1, entry="hils_decode") == H.HILS_ERR_WORKSPACE
+    assert _fwd(p, ws=ctypes.c_void_p((1 << 20) + 16), ws_bytes=need,
+                entry="hils_decode") == H.HILS_ERR_WORKSPACE
+
+
+def test_workspace_size_of_invalid_params_is_zero():
+    assert H.hils_workspace_size(_p(heads_q=3), H.HILS_OP_FORWARD) == 0
+    assert H.hils_workspace_size(_p(), 7) == 0
+
+
+def test_backward_rejections():
+    lib = H.load_library()
+    p = _p()
+    args = [FAKE] * 14 + [FAKE, 1 << 30, None]
+    args[4] = None                                   # lmk_bias may be null
+    args[8] = None                                   # lse is required
+    assert lib.hils_backward(ctypes.byref(p), *args) == H.HILS_ERR_INVALID_ARG
+    assert "null" in _err()
+    p2 = _p(chunk_size=128, head_dim=128, num_landmarks=2)
+    assert lib.hils_backward(ctypes.byref(p2), *args) == H.HILS_ERR_UNSUPPORTED
+
+
+def test_empty_problem_is_a_no_op():
+    assert _fwd(_p(batch=0), q=None, k=None, v=None, lmk=None, out=None, idx=None) == H.HILS_OK
+    assert _fwd(_p(seq_q=0), q=None, k=None, v=None, lmk=None, out=None, idx=None) == H.HILS_OK
+
+
+def test_status_strings():
+    lib = H.load_library()
+    for s in range(5):
+        assert lib.hils_status_string(s).decode().startswith("HILS_")

@@ -1,0 +1,132 @@
+"""GPU parity of the forward and decode entry points against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from hils_inputs.configs import config, make_host_inputs
+from hils_inputs.device import make_device_inputs, to_device
+from tests.parity import check_forward, to_np, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hl():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import chunk_wise_sparse_landmark_amd as m
+    m.load_library()
+    return m
+
+
+def _run(hl, cfg, dev, entry="forward", **over):
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], keep_own_chunk=bool(cfg["keep_own"]))
+    kw.update(over)
+    if entry == "forward":
+        out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"],
+                                        causal=bool(cfg["causal"]), **kw)
+    else:
+        out, idx, lse = hl.hils_decode(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"], **kw)
+    torch.cuda.synchronize()
+    return to_np(out), idx.cpu().numpy(), lse.cpu().numpy()
+
+
+def _case(**kw):
+    base = dict(B=1, Hq=2, Hkv=1, d=64, Lq=64, Lkv=64, S=16, K=2, causal=1, keep_own=1,
+                dtype="bf16", lmk="iid", seed=21)
+    base.update(kw)
+    return base
+
+
+def test_tiny_f32_forward(hl):
+    cfg = config("tiny_f32")
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev)
+    swaps = check_forward(host, cfg, out, idx, lse)
+    assert swaps == 0
+
+
+GENERIC_CASES = {
+    "causal_gqa3_ragged": _case(B=2, Hq=6, Hkv=2, d=64, Lq=237, Lkv=237, S=16, K=5),
+    "causal_suffix_queries": _case(B=1, Hq=4, Hkv=2, d=96, Lq=40, Lkv=300, S=32, K=3, bias=0.5),
+    "causal_no_own_chunk": _case(B=1, Hq=2, Hkv=2, d=32, Lq=130, Lkv=130, S=16, K=4, keep_own=0),
+    "noncausal_tail": _case(B=2, Hq=4, Hkv=4, d=128, Lq=33, Lkv=203, S=64, K=2, causal=0),
+    "f32_mha_k_exceeds": _case(B=1, Hq=3, Hkv=3, d=48, Lq=90, Lkv=90, S=8, K=20, dtype="f32"),
+    "bf16_d128_s64_k64": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1100, Lkv=1100, S=64, K=64,
+                               keep_own=1, seed=5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GENERIC_CASES))
+def test_forward_shapes(hl, name):
+    cfg = GENERIC_CASES[name]
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev)
+    qs = None if cfg["Lq"] <= 300 else sorted(set(range(0, 80)) | set(range(cfg["Lq"] - 40, cfg["Lq"])))
+    check_forward(host, cfg, out, idx, lse, queries=qs)
+
+
+def test_values_one_give_output_one(hl):
+    cfg = _case(B=1, Hq=8, Hkv=2, d=128, Lq=700, Lkv=700, S=64, K=4)
+    host, dev = make_device_inputs(cfg)
+    dev["v"] = torch.ones_like(dev["v"])
+    out, idx, lse = _run(hl, cfg, dev)
+    assert np.all(out[:, :, 64:] == 1.0)   # every query past the first chunk fuses >= 1 member
+
+
+@pytest.mark.parametrize("Lkv,K", [(8209, 32), (4096, 16), (100, 8), (64, 4)])
+def test_decode_small(hl, Lkv, K):
+    cfg = config("decode_128k", B=2, Lkv=Lkv, K=K)
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev, entry="decode")
+    check_forward(host, cfg, out, idx, lse)
+    # same inputs through the shape-generic forward (query at position Lkv - 1)
+    o2, i2, l2 = _run(hl, cfg, dev, entry="forward")
+    np.testing.assert_array_equal(idx, i2)
+    assert_close("decode vs forward", out, o2, "abs", 8e-3)
+
+
+def test_decode_is_last_prefill_row(hl):
+    cfg = _case(B=1, Hq=8, Hkv=2, d=128, Lq=1000, Lkv=1000, S=64, K=8, lmk="iid", seed=9)
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev)
+    qd = dev["q"][:, :, -1:].contiguous()
+    o2, i2, l2 = hl.hils_decode(qd, dev["k"], dev["v"], dev["lmk"], None, chunk_size=64, top_k=8)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx[:, :, -1:], i2.cpu().numpy())
+    assert_close("decode vs last row", to_np(o2), out[:, :, -1:], "abs", 8e-3)
+    assert_close("decode lse vs last row", l2.cpu().numpy(), lse[:, :, -1:], "abs", 1e-4)
+
+
+def test_decode_128k(hl):
+    cfg = config("decode_128k")
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev, entry="decode")
+    for b in range(cfg["B"]):
+        for g in range(cfg["Hkv"]):
+            assert host["needle_pos"][b, g] in idx[b, g, 0], (b, g)
+    check_forward(host, cfg, out, idx, lse)
+
+
+def test_decode_4m(hl):
+    cfg = config("decode_4m")
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev, entry="decode")
+    for g in range(cfg["Hkv"]):
+        assert host["needle_pos"][0, g] in idx[0, g, 0], g
+    check_forward(host, cfg, out, idx, lse)
+    del dev
+    torch.cuda.empty_cache()
+
+
+def test_prefill_8k_sampled(hl):
+    cfg = config("prefill_8k")
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev)
+    rng = np.random.default_rng(0)
+    qs = sorted(set(range(0, 130)) | set(rng.choice(cfg["Lq"], 120, replace=False).tolist())
+                | set(range(cfg["Lq"] - 10, cfg["Lq"])))
+    check_forward(host, cfg, out, idx, lse, queries=qs)
+    # every query with at least K candidates selected exactly K chunks
+    own = np.arange(cfg["Lq"]) // cfg["S"]
+    nsel = (idx[0] >= 0).sum(-1)
+    np.testing.assert_array_equal(nsel, np.minimum(own, cfg["K"])[None, :].repeat(cfg["Hkv"], 0))
