@@ -9,6 +9,14 @@
 
 #include "hils.h"
 #include "hils_kernels.h"
+#include "hils_profile.h"
+
+namespace hils {
+ProfileSlot& profile_slot() {
+  static thread_local ProfileSlot slot;
+  return slot;
+}
+}  // namespace hils
 
 namespace {
 
@@ -213,5 +221,23 @@ const char* hils_status_string(hils_status s) {
 }
 
 const char* hils_last_error(void) { return g_last_error.c_str(); }
+
+hils_status hils_profile_kernel(int32_t kernel, void* const* starts, void* const* stops, int32_t n) {
+  hils::ProfileSlot& ps = hils::profile_slot();
+  if (n == 0) {
+    ps = hils::ProfileSlot();
+    return HILS_OK;
+  }
+  if (kernel < 1 || kernel >= hils::kKernelIdEnd || n < 0 || !starts || !stops)
+    return fail(HILS_ERR_INVALID_ARG, "bad profiling request");
+  ps.kernel = kernel;
+  ps.starts = reinterpret_cast<hipEvent_t const*>(starts);
+  ps.stops = reinterpret_cast<hipEvent_t const*>(stops);
+  ps.n = n;
+  ps.next = 0;
+  return HILS_OK;
+}
+
+int32_t hils_profile_count(void) { return hils::profile_slot().next; }
 
 }  // extern "C"

@@ -177,28 +177,43 @@ __device__ __forceinline__ uint64_t wave_rank_sort64(uint64_t key, uint64_t* buf
   return out;
 }
 
-// Top-K (K <= 64) of R keys per lane.  Returns, in lane l < K, the l-th largest
-// key (0 where fewer than l+1 valid keys exist); lanes >= K hold the following
-// keys in order.  `buf` is 64 uint64 of LDS private to the calling wave.
+// Top 64 of the union of two lists sorted descending (one key per lane, keys
+// unique apart from 0): max(a_i, b_{63-i}) is a bitonic sequence holding
+// exactly the 64 largest keys of both, which a rank sort then orders.
+__device__ __forceinline__ uint64_t wave_merge_sorted(uint64_t a, uint64_t b, uint64_t* buf) {
+  const int lane = lane_id();
+  buf[lane] = b;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t br = buf[kWave - 1 - lane];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return wave_rank_sort64(a > br ? a : br, buf);
+}
+
+// Top-K (K <= 64) of R keys per lane (keys unique apart from 0 = empty).
+// Returns, in lane l < K, the l-th largest key (0 where fewer than l+1 valid
+// keys exist); lanes >= K hold the following keys in order.  `buf` is 64
+// uint64 of LDS private to the calling wave.
 //
-// tau = K-th largest of the lane maxima: the K lanes owning the largest maxima
-// each hold a key >= tau, so the top K keys are all >= tau.  When at most 64
-// keys qualify (always when K * R <= 64, and nearly always otherwise) they are
-// compacted and rank-sorted; otherwise all 64R keys go through a bitonic sort.
+// K * R <= 64: tau = K-th largest of the lane maxima.  The K lanes owning the
+// largest maxima hold every key >= tau (at most K * R <= 64 of them), and the
+// top K are among them, so one compaction and one rank sort finish the job.
+// Otherwise the R columns are merged into a running sorted list; a column
+// whose maximum does not beat the current K-th key is skipped.
 template <int R>
 __device__ __forceinline__ uint64_t wave_topk(uint64_t (&keys)[R], int K, uint64_t* buf) {
   const int lane = lane_id();
-  uint64_t lm = keys[0];
+  if (R == 1) return wave_rank_sort64(keys[0], buf);
+  if (K * R <= kWave) {
+    uint64_t lm = keys[0];
 #pragma unroll
-  for (int r = 1; r < R; ++r) lm = keys[r] > lm ? keys[r] : lm;
-  if (R == 1) return wave_rank_sort64(lm, buf);
-  uint64_t srt = wave_rank_sort64(lm, buf);
-  uint64_t tau = shfl_u64(srt, K - 1);
-  if (tau == 0) tau = 1;
-  int cnt = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[r] >= tau));
-  if (cnt <= kWave) {
+    for (int r = 1; r < R; ++r) lm = keys[r] > lm ? keys[r] : lm;
+    uint64_t srt = wave_rank_sort64(lm, buf);
+    uint64_t tau = shfl_u64(srt, K - 1);
+    if (tau == 0) tau = 1;
     int base = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -213,8 +228,22 @@ __device__ __forceinline__ uint64_t wave_topk(uint64_t (&keys)[R], int K, uint64
     uint64_t key = lane < base ? buf[lane] : 0ull;
     return wave_rank_sort64(key, buf);
   }
-  wave_sort_desc<R>(keys);
-  return keys[0];
+  uint64_t run = wave_rank_sort64(keys[0], buf);
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    const uint64_t kth = shfl_u64(run, K - 1);
+    if (wave_max_u64(keys[r]) > kth) run = wave_merge_sorted(run, wave_rank_sort64(keys[r], buf), buf);
+  }
+  return run;
+}
+
+// Merge a list sorted descending (lanes >= K hold 0) into the running sorted
+// top list `run`, unless its head cannot beat the current K-th key.
+__device__ __forceinline__ uint64_t wave_merge_into(uint64_t run, uint64_t list, int K,
+                                                    uint64_t* buf) {
+  const uint64_t kth = shfl_u64(run, K - 1);
+  const uint64_t head = shfl_u64(list, 0);
+  return head > kth ? wave_merge_sorted(run, list, buf) : run;
 }
 
 // ---------------------------------------------------------------- block reductions

@@ -5,7 +5,7 @@
 // "Sparse training", GQA-shared selection §4 "Architecture", per-chunk softmax
 // and score-weighted fusion §3 "Hierarchical softmax".
 //
-// Three launches on the caller's stream:
+// Four launches on the caller's stream:
 //  1. score_select  grid (nsplit, B*Hkv): each workgroup streams a contiguous
 //     range of landmark rows (16 lanes x 16 B per 256 B row, coalesced), forms
 //     the group score scale*<mean_h q_h, lmk_c> + bias_c (the group mean is
@@ -15,10 +15,14 @@
 //  3. attend        grid (K+1, B*Hkv): one workgroup per selected chunk (and
 //     one for the own chunk) reads the chunk's 16 KB of K and 16 KB of V once
 //     for all G heads, computes the chunk softmax and o_c, and writes
-//     (s_c, o_c); the last workgroup of each (b, kv head) fuses the partials
-//     with a log-sum-exp over the retrieval scores.
+//     (s_c, o_c).
+//  4. fuse          grid (B*Hkv): log-sum-exp over the retrieval scores of the
+//     K+1 partials.  (A separate launch: on this multi-XCD part a device-scope
+//     fence per workgroup -- needed for a last-workgroup reduction -- writes
+//     back and invalidates L2 and costs far more than one more launch.)
 #include "hils_common.h"
 #include "hils_kernels.h"
+#include "hils_profile.h"
 
 namespace hils {
 
@@ -33,7 +37,6 @@ constexpr int kPartStride = kD + 4;   // o[128], s, pad  (floats)
 struct DecodeWs {
   uint64_t* lists;   // [B*Hkv][nsplit][K]
   float* parts;      // [B*Hkv][K+1][G][kPartStride]
-  unsigned* counters;  // [B*Hkv]
 };
 
 __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
@@ -51,14 +54,13 @@ template <int R>
 __global__ void __launch_bounds__(kThreads)
 decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ lmk,
                     const float* __restrict__ bias, int ncand, int cps, int nsplit,
-                    uint64_t* __restrict__ lists, unsigned* __restrict__ counters) {
+                    uint64_t* __restrict__ lists) {
   __shared__ uint64_t buf[4][kWave];
   __shared__ uint64_t wl[4][kWave];
   const int split = blockIdx.x, bkv = blockIdx.y;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int sub = lane & 15, grp = lane >> 4;
-  if (split == 0 && tid == 0) counters[bkv] = 0u;
 
   // this lane's 8 dims of the mean query
   float qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -108,8 +110,8 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   wl[w][lane] = lane < g.K ? top : 0ull;
   __syncthreads();
   if (w == 0) {
-    uint64_t four[4] = {wl[0][lane], wl[1][lane], wl[2][lane], wl[3][lane]};
-    uint64_t t = wave_topk<4>(four, g.K, buf[0]);
+    uint64_t t = wl[0][lane];
+    for (int x = 1; x < 4; ++x) t = wave_merge_into(t, wl[x][lane], g.K, buf[0]);
     if (lane < g.K) lists[((size_t)bkv * nsplit + split) * g.K + lane] = t;
   }
 }
@@ -117,7 +119,6 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
 // ----------------------------------------------------------------------------
 // 2. merge the nsplit local lists of one (b, kv head); write ascending ids.
 // ----------------------------------------------------------------------------
-constexpr int kMergeR = 15;   // + the running list = 16 keys per lane
 __global__ void __launch_bounds__(kThreads)
 decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
              int32_t* __restrict__ sel_idx) {
@@ -125,24 +126,17 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
   __shared__ uint64_t wl[4][kWave];
   const int bkv = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int n = nsplit * g.K;
-  const uint64_t* src = lists + (size_t)bkv * n;
+  const uint64_t* src = lists + (size_t)bkv * nsplit * g.K;
   uint64_t run = 0;
-  for (int base = w * kWave * kMergeR; base < n; base += 4 * kWave * kMergeR) {
-    uint64_t keys[kMergeR + 1];
-#pragma unroll
-    for (int r = 0; r < kMergeR; ++r) {
-      const int e = base + r * kWave + lane;
-      keys[r] = e < n ? src[e] : 0ull;
-    }
-    keys[kMergeR] = run;
-    run = wave_topk<kMergeR + 1>(keys, g.K, buf[w]);
+  for (int j = w; j < nsplit; j += 4) {   // each local list is sorted descending
+    const uint64_t key = lane < g.K ? src[(size_t)j * g.K + lane] : 0ull;
+    run = wave_merge_into(run, key, g.K, buf[w]);
   }
   wl[w][lane] = lane < g.K ? run : 0ull;
   __syncthreads();
   if (w == 0) {
-    uint64_t four[4] = {wl[0][lane], wl[1][lane], wl[2][lane], wl[3][lane]};
-    uint64_t top = wave_topk<4>(four, g.K, buf[0]);
+    uint64_t top = wl[0][lane];
+    for (int x = 1; x < 4; ++x) top = wave_merge_into(top, wl[x][lane], g.K, buf[0]);
     uint64_t asc = (lane < g.K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
     asc = wave_rank_sort64(asc, buf[0]);
     if (lane < g.K) sel_idx[(size_t)bkv * g.K + lane] = asc ? (int)(0xffffffffull - (asc - 1)) : -1;
@@ -156,13 +150,11 @@ __global__ void __launch_bounds__(kThreads)
 decode_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
               const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
-              float* __restrict__ parts, unsigned* __restrict__ counters,
-              uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+              float* __restrict__ parts) {
   __shared__ float qs[kMaxGd][kD];
   __shared__ float lg[kMaxGd][kS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
   __shared__ float sc[kMaxGd];
-  __shared__ int is_last;
   const int slot = blockIdx.x, bkv = blockIdx.y;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -256,28 +248,34 @@ decode_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __rest
     for (int h = tid; h < G; h += kThreads) part[(size_t)h * kPartStride + kD] = -INFINITY;
   }
 
-  // last workgroup of this (b, kv head) fuses the K+1 partials
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(&counters[bkv], 1u) == (unsigned)(nslot - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+}
+
+// ----------------------------------------------------------------------------
+// 4. fusion: log-sum-exp over the retrieval scores of the K+1 partials.
+// grid (B*Hkv); thread -> dims (2*dp, 2*dp+1) of heads hg, hg+4, ...
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+decode_fuse(Geometry g, const float* __restrict__ parts, uint16_t* __restrict__ out,
+            float* __restrict__ lse_out) {
+  const int bkv = blockIdx.x;
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int G = g.G, nslot = g.K + 1;
   const float* pb = parts + (size_t)bkv * nslot * G * kPartStride;
-  const int dp = tid & 63, hg = tid >> 6;
+  const int dp = threadIdx.x & 63, hg = threadIdx.x >> 6;
   for (int h = hg; h < G; h += 4) {
     float m = -INFINITY;
-    for (int s = 0; s < nslot; ++s) m = fmaxf(m, __builtin_nontemporal_load(pb + ((size_t)s * G + h) * kPartStride + kD));
+    for (int s = 0; s < nslot; ++s) m = fmaxf(m, pb[((size_t)s * G + h) * kPartStride + kD]);
     float z = 0.f, o0 = 0.f, o1 = 0.f;
     if (m != -INFINITY) {
       for (int s = 0; s < nslot; ++s) {
         const float* ph = pb + ((size_t)s * G + h) * kPartStride;
-        const float sv = __builtin_nontemporal_load(ph + kD);
+        const float sv = ph[kD];
         if (sv == -INFINITY) continue;
         const float e = __expf(sv - m);
+        const float2 o = *reinterpret_cast<const float2*>(ph + 2 * dp);
         z += e;
-        o0 += e * __builtin_nontemporal_load(ph + 2 * dp);
-        o1 += e * __builtin_nontemporal_load(ph + 2 * dp + 1);
+        o0 += e * o.x;
+        o1 += e * o.y;
       }
     }
     const size_t orow = (size_t)(b * g.Hq + kvh * G + h) * kD;
@@ -286,7 +284,6 @@ decode_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __rest
     reinterpret_cast<uint32_t*>(out + orow)[dp] = pk;
     if (dp == 0 && lse_out) lse_out[b * g.Hq + kvh * G + h] = z > 0.f ? m + __logf(z) : -INFINITY;
   }
-  if (tid == 0) counters[bkv] = 0u;
 }
 
 struct DecodePlan {
@@ -316,8 +313,6 @@ DecodeWs carve(const Geometry& g, const DecodePlan& p, void* ws) {
   d.lists = reinterpret_cast<uint64_t*>(c + off);
   off += ((size_t)g.B * g.Hkv * p.nsplit * g.K * 8 + 255) & ~(size_t)255;
   d.parts = reinterpret_cast<float*>(c + off);
-  off += ((size_t)g.B * g.Hkv * (g.K + 1) * g.G * kPartStride * 4 + 255) & ~(size_t)255;
-  d.counters = reinterpret_cast<unsigned*>(c + off);
   return d;
 }
 
@@ -332,7 +327,6 @@ size_t decode_fast_ws(const Geometry& g) {
   DecodePlan p = plan(g);
   size_t off = ((size_t)g.B * g.Hkv * p.nsplit * g.K * 8 + 255) & ~(size_t)255;
   off += ((size_t)g.B * g.Hkv * (g.K + 1) * g.G * kPartStride * 4 + 255) & ~(size_t)255;
-  off += (size_t)g.B * g.Hkv * 4;
   return off;
 }
 
@@ -345,16 +339,23 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, c
   const uint16_t* Q = (const uint16_t*)q;
   const uint16_t* Lm = (const uint16_t*)lmk;
   dim3 g1(p.nsplit, bkv);
+  prof_begin(kDecodeScore, st);
   switch (p.R) {
-    case 1: hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
-    case 2: hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
-    case 4: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
-    default: hipLaunchKernelGGL(decode_score_select<8>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists, d.counters); break;
+    case 1: hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
+    case 2: hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
+    case 4: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
+    default: hipLaunchKernelGGL(decode_score_select<8>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
   }
+  prof_end(kDecodeScore, st);
+  prof_begin(kDecodeMerge, st);
   hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kThreads), 0, st, g, p.nsplit, d.lists, sel_idx);
+  prof_end(kDecodeMerge, st);
+  prof_begin(kDecodeAttend, st);
   hipLaunchKernelGGL(decode_attend, dim3(g.K + 1, bkv), dim3(kThreads), 0, st, g, Q,
-                     (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts,
-                     d.counters, (uint16_t*)out, lse);
+                     (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
+  prof_end(kDecodeAttend, st);
+  hipLaunchKernelGGL(decode_fuse, dim3(bkv), dim3(kThreads), 0, st, g, d.parts, (uint16_t*)out,
+                     lse);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 // (no gradient to unselected chunks).
 #include "hils_common.h"
 #include "hils_kernels.h"
+#include "hils_profile.h"
 
 namespace hils {
 
@@ -62,11 +63,11 @@ generic_select_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
     uint64_t pair[2] = {run, key};
     run = wave_topk<2>(pair, g.K, scratch[w]);
   }
-  lists[w][lane] = run;
+  lists[w][lane] = lane < g.K ? run : 0ull;
   __syncthreads();
   if (w == 0) {
-    uint64_t four[4] = {lists[0][lane], lists[1][lane], lists[2][lane], lists[3][lane]};
-    uint64_t top = wave_topk<4>(four, g.K, scratch[0]);
+    uint64_t top = lists[0][lane];
+    for (int x = 1; x < 4; ++x) top = wave_merge_into(top, lists[x][lane], g.K, scratch[0]);
     // ascending chunk ids: sort descending on the complemented id
     uint64_t asc = (lane < g.K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
     asc = wave_sort64_desc(asc);
@@ -420,10 +421,14 @@ hipError_t launch_generic_forward_t(const Geometry& g, const void* q, const void
                                     const void* lmk, const float* bias, void* out, int32_t* sel_idx,
                                     float* lse, hipStream_t st) {
   dim3 grid(g.Lq, g.B * g.Hkv);
+  prof_begin(kGenericSelect, st);
   hipLaunchKernelGGL(generic_select_kernel<T>, grid, dim3(kThreads), 0, st, g, (const T*)q,
                      (const T*)lmk, bias, sel_idx);
+  prof_end(kGenericSelect, st);
+  prof_begin(kGenericAttend, st);
   hipLaunchKernelGGL(generic_attend_kernel<T>, grid, dim3(kThreads), 0, st, g, (const T*)q,
                      (const T*)k, (const T*)v, (const T*)lmk, bias, sel_idx, (T*)out, lse);
+  prof_end(kGenericAttend, st);
   return hipGetLastError();
 }
 
@@ -444,18 +449,22 @@ hipError_t launch_generic_backward_t(const Geometry& g, const void* q, const voi
                                      const int32_t* sel_idx, void* dq, void* dk, void* dv,
                                      void* dlmk, float* dbias, void* ws, hipStream_t st) {
   float4* stats = (float4*)ws;
+  prof_begin(kGenericBwdRows, st);
   hipLaunchKernelGGL(generic_bwd_rows_kernel<T>, dim3(g.Lq, g.B * g.Hkv), dim3(kThreads), 0, st, g,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)lmk, bias, (const T*)dout,
                      sel_idx, (T*)dq, stats);
+  prof_end(kGenericBwdRows, st);
   const int nck = (g.Lkv + g.S - 1) / g.S;
   const int gx = nck > g.NCcap ? nck : g.NCcap;
   if (gx > 0) {
     const size_t sm = (size_t)2 * g.S * g.d * sizeof(float);
     hipFuncSetAttribute((const void*)generic_bwd_chunks_kernel<T>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    prof_begin(kGenericBwdChunks, st);
     hipLaunchKernelGGL(generic_bwd_chunks_kernel<T>, dim3(gx, g.B * g.Hkv), dim3(kThreads), sm, st,
                        g, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, sel_idx, stats,
                        (T*)dk, (T*)dv, (T*)dlmk, dbias);
+    prof_end(kGenericBwdChunks, st);
   }
   return hipGetLastError();
 }

@@ -21,7 +21,12 @@ HILS_F32, HILS_BF16 = 0, 1
 HILS_OP_FORWARD, HILS_OP_DECODE, HILS_OP_BACKWARD = 0, 1, 2
 
 EXPORTS = ("hils_workspace_size", "hils_forward", "hils_decode", "hils_backward",
-           "hils_status_string", "hils_last_error")
+           "hils_profile_kernel", "hils_profile_count", "hils_status_string", "hils_last_error")
+
+KERNEL_IDS = {"generic_select": 1, "generic_attend": 2, "generic_bwd_rows": 3,
+              "generic_bwd_chunks": 4, "decode_score": 5, "decode_merge": 6, "decode_attend": 7,
+              "prefill_select": 8, "prefill_attend": 9, "prefill_bwd_rows": 10,
+              "prefill_bwd_chunks": 11}
 
 
 class HilsParams(ctypes.Structure):
@@ -66,6 +71,10 @@ def load_library(path=None):
     lib.hils_backward.restype = ctypes.c_int
     lib.hils_status_string.argtypes = [ctypes.c_int]
     lib.hils_status_string.restype = ctypes.c_char_p
+    lib.hils_profile_kernel.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
+    lib.hils_profile_kernel.restype = ctypes.c_int
+    lib.hils_profile_count.argtypes = []
+    lib.hils_profile_count.restype = i32
     lib.hils_last_error.argtypes = []
     lib.hils_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -178,6 +187,23 @@ def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size
                            _ptr(dv), _ptr(dlmk), _ptr(dbias), _ptr(ws), nbytes, _stream(stream))
     _check(st)
     return dq, dk, dv, dlmk, dbias
+
+
+def hils_profile_kernel(kernel, starts, stops):
+    """Arm per-launch event recording for a kernel family (names in KERNEL_IDS).
+
+    ``starts``/``stops``: equal-length lists of raw hipEvent_t handles (ints)."""
+    lib = load_library()
+    n = len(starts)
+    arr = ctypes.c_void_p * max(n, 1)
+    a, b = arr(*starts), arr(*stops)
+    kid = KERNEL_IDS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check(lib.hils_profile_kernel(kid, a, b, n))
+    return (a, b)   # keep the arrays alive while armed
+
+
+def hils_profile_count():
+    return int(load_library().hils_profile_count())
 
 
 def default_scale(d):

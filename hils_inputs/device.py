@@ -71,3 +71,33 @@ def make_device_inputs(cfg, device="cuda", host=None):
         else:
             dev[name] = to_device(x, dt, device)
     return host, dev
+
+
+def make_decode_inputs_on_device(cfg, device="cuda"):
+    """Decode workload with every large tensor generated on the device.
+
+    q (small) and the needle rows are computed on the host; the landmark table,
+    K and V are filled in place by the counter generator.  Same values as
+    make_host_inputs(cfg) for the same seed."""
+    from .configs import _draw, _store, _needle_landmarks
+    assert cfg["lmk"] in ("iid", "needle") and cfg["dtype"] == "bf16"
+    B, Hq, Hkv, d, Lkv, S = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["Lkv"], cfg["S"]
+    NC = Lkv // S
+    q = _store(cfg, _draw(cfg, "q", (B, Hq, cfg["Lq"], d)))
+    dev = {"q": to_device(q, "bf16", device), "bias": None}
+    lmk = torch.empty((B, Hkv, NC, d), dtype=torch.bfloat16, device=device)
+    fill_normal(lmk, cfg["seed"], "lmk")
+    if cfg["lmk"] == "needle":
+        rows = np.zeros((B, Hkv, max(NC, 1), d), dtype=np.float32)
+        rows, pos = _needle_landmarks(cfg, q, rows)
+        for b in range(B):
+            for g in range(Hkv):
+                if NC > 0 and (Lkv - 1) // S > 0:
+                    c = int(pos[b, g])
+                    lmk[b, g, c] = to_device(rows[b, g, c], "bf16", device)
+    dev["lmk"] = lmk
+    for name in ("k", "v"):
+        t = torch.empty((B, Hkv, Lkv, d), dtype=torch.bfloat16, device=device)
+        fill_normal(t, cfg["seed"], name)
+        dev[name] = t
+    return dev

@@ -124,6 +124,35 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* k, co
                           void* dq, void* dk, void* dv, void* dlmk, float* dlmk_bias,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* Kernel families, for hils_profile_kernel. */
+typedef enum {
+  HILS_KERNEL_GENERIC_SELECT = 1,
+  HILS_KERNEL_GENERIC_ATTEND = 2,
+  HILS_KERNEL_GENERIC_BWD_ROWS = 3,
+  HILS_KERNEL_GENERIC_BWD_CHUNKS = 4,
+  HILS_KERNEL_DECODE_SCORE = 5,
+  HILS_KERNEL_DECODE_MERGE = 6,
+  HILS_KERNEL_DECODE_ATTEND = 7,
+  HILS_KERNEL_PREFILL_SELECT = 8,
+  HILS_KERNEL_PREFILL_ATTEND = 9,
+  HILS_KERNEL_PREFILL_BWD_ROWS = 10,
+  HILS_KERNEL_PREFILL_BWD_CHUNKS = 11
+} hils_kernel_id;
+
+/* Profiling hook (measurement only; not needed for computation).  Until `n`
+ * launches of kernel family `kernel` (a hils_kernel_id) have been made by
+ * library calls on the calling thread, launch i is bracketed by
+ * hipEventRecord(starts[i]) and hipEventRecord(stops[i]) on its stream.  The
+ * caller owns the n + n events (hipEvent_t, created with timing enabled) and
+ * reads them with hipEventElapsedTime.  n = 0 disarms.  Thread-local state:
+ * the only state the library keeps.  Returns HILS_ERR_INVALID_ARG for an
+ * unknown kernel id, a negative n, or null arrays with n > 0. */
+hils_status hils_profile_kernel(int32_t kernel, void* const* starts, void* const* stops,
+                                int32_t n);
+
+/* Number of launches recorded since hils_profile_kernel armed the hook. */
+int32_t hils_profile_count(void);
+
 /* Static description of a status code. */
 const char* hils_status_string(hils_status s);
 

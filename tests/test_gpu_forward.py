@@ -53,6 +53,16 @@ GENERIC_CASES = {
     "f32_mha_k_exceeds": _case(B=1, Hq=3, Hkv=3, d=48, Lq=90, Lkv=90, S=8, K=20, dtype="f32"),
     "bf16_d128_s64_k64": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1100, Lkv=1100, S=64, K=64,
                                keep_own=1, seed=5),
+    # MFMA prefill path (bf16, d=128, S=64, causal, L % 64 == 0, G in {1,2,4}, K <= 32)
+    "mfma_g4_k16": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=16,
+                         lmk="chunk_mean", seed=6),
+    "mfma_g2_k8_bias": _case(B=2, Hq=4, Hkv=2, d=128, Lq=2048, Lkv=2048, S=64, K=8, bias=0.3,
+                             seed=7),
+    "mfma_g1_k32": _case(B=1, Hq=2, Hkv=2, d=128, Lq=4096, Lkv=4096, S=64, K=32, seed=8),
+    "mfma_g4_no_own": _case(B=1, Hq=4, Hkv=1, d=128, Lq=1024, Lkv=1024, S=64, K=4, keep_own=0,
+                            lmk="chunk_mean", seed=10),
+    "mfma_g4_nc256_sortpath": _case(B=1, Hq=4, Hkv=1, d=128, Lq=16384, Lkv=16384, S=64, K=32,
+                                    lmk="chunk_mean", seed=12),
 }
 
 
@@ -61,12 +71,18 @@ def test_forward_shapes(hl, name):
     cfg = GENERIC_CASES[name]
     host, dev = make_device_inputs(cfg)
     out, idx, lse = _run(hl, cfg, dev)
-    qs = None if cfg["Lq"] <= 300 else sorted(set(range(0, 80)) | set(range(cfg["Lq"] - 40, cfg["Lq"])))
+    if cfg["Lq"] <= 300:
+        qs = None
+    else:
+        rng = np.random.default_rng(1)
+        qs = sorted(set(range(0, 80)) | set(range(cfg["Lq"] - 40, cfg["Lq"]))
+                    | set(rng.choice(cfg["Lq"], 60, replace=False).tolist()))
     check_forward(host, cfg, out, idx, lse, queries=qs)
 
 
-def test_values_one_give_output_one(hl):
-    cfg = _case(B=1, Hq=8, Hkv=2, d=128, Lq=700, Lkv=700, S=64, K=4)
+@pytest.mark.parametrize("L", [700, 1024])
+def test_values_one_give_output_one(hl, L):
+    cfg = _case(B=1, Hq=8, Hkv=2, d=128, Lq=L, Lkv=L, S=64, K=4)
     host, dev = make_device_inputs(cfg)
     dev["v"] = torch.ones_like(dev["v"])
     out, idx, lse = _run(hl, cfg, dev)
