@@ -51,7 +51,6 @@ constexpr int kMaxT = kW / 4;    // 16-row tiles per chunk at most
 constexpr int kMaxKf = 32;       // top-K bound on this path
 constexpr int kMaxNC = 256;      // chunks bound on this path (L <= 16384)
 constexpr int kQStride = 136;    // bf16 per staged Q row (272 B: 2-way bank spread)
-constexpr int kPStride = 68;     // bf16 per P row (136 B: conflict-free 8-B reads)
 constexpr int kFragsPerChunk = 16;   // V fragments per chunk: 8 column blocks x 2 key steps
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
@@ -73,8 +72,11 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+// two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ----------------------------------------------------------------------------
@@ -147,7 +149,9 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   __shared__ uint64_t buf[4][kWave];
   __shared__ uint64_t buf2[4][kWave];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
-  const int win = blockIdx.x, bkv = blockIdx.y;
+  const int nbkv = g.B * g.Hkv;            // (b, kv head) fastest: one head per XCD
+  const int bkv = blockIdx.x % nbkv;
+  const int win = (g.Lq / kSelWin - 1) - blockIdx.x / nbkv;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int i0 = win * kSelWin;
@@ -258,7 +262,7 @@ __device__ __forceinline__ void load_chunk_frags(const uint16_t* Kc, const uint1
 struct AttendSmem {
   float acc[kRows * kAccStride];                 // fp32 output rows (row = qi*4 + h)
   uint16_t qs[kRows * kQStride];                 // window Q, row = qi*4 + h; reused for output
-  uint16_t pb[kTB * 16 * kPStride];              // unnormalised P of the current tile batch
+  uint4 pf[kTB][2][kWave];                       // unnormalised P, in A-operand fragment order
   float smax[kTB][4][16];
   float ssum[kTB][4][16];
   float wts[kW * kMaxKf * kG];                   // (query, slot, head): score, then weight
@@ -268,7 +272,7 @@ struct AttendSmem {
   uint16_t ulist[kMaxNC];
   float lseown[kRows];
   float wown[kRows];
-  int tq[4][kW];
+  float wsl[4][kW][kG];                          // per wave: fusion weight of (slot, head)
   int wcount[4];
 };
 
@@ -277,14 +281,14 @@ struct AttendSmem {
 // r16/4, query slot r16%4); slot n of the chunk is query list[n].  vis_own >= 0
 // marks the own chunk: key kk of query qi is visible when kk <= qi + vis_own.
 __device__ __forceinline__ void phase_a(AttendSmem& sm, const ChunkFrags& f, int w, int tbase,
-                                        int ntl, const int* list, int nlist, float scale,
-                                        int vis_own, float (&s)[kTB][4]) {
+                                        int ntl, int lq, int nlist, float scale, int vis_own,
+                                        float (&s)[kTB][4]) {
   const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int tl = 0; tl < kTB; ++tl) {
     if (tl >= ntl) break;
     const int slot = (tbase + tl) * 4 + (r16 & 3);
-    const int qi = list[slot < nlist ? slot : 0];
+    const int qi = __shfl(lq, slot < nlist ? slot : 0, kWave);
     const uint16_t* qr = sm.qs + (qi * kG + (r16 >> 2)) * kQStride + g4 * 8;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -325,7 +329,8 @@ __device__ __forceinline__ void phase_b(AttendSmem& sm, int w, int ntl, float (&
     z += __shfl_xor(z, 16, kWave);
     z += __shfl_xor(z, 32, kWave);
     if (lane < 16) sm.ssum[tl][w][r16] = z;
-    *reinterpret_cast<uint2*>(sm.pb + (tl * 16 + r16) * kPStride + w * 16 + g4 * 4) =
+    // keys 16w + 4*g4 + i are elements 4*(w&1) + i of this lane's fragment for k-step w>>1
+    reinterpret_cast<uint2*>(&sm.pf[tl][w >> 1][lane])[w & 1] =
         make_uint2(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]));
     s[tl][0] = m;
   }
@@ -339,12 +344,7 @@ __device__ __forceinline__ void phase_c(const AttendSmem& sm, const ChunkFrags& 
   const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
   bf16x8 pa[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint16_t* pr = sm.pb + (tl * 16 + r16) * kPStride + ks * 32 + g4 * 4;
-    const uint2 lo = *reinterpret_cast<const uint2*>(pr);
-    const uint2 hi = *reinterpret_cast<const uint2*>(pr + 16);
-    pa[ks] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-  }
+  for (int ks = 0; ks < 2; ++ks) pa[ks] = as_bf16x8(sm.pf[tl][ks][lane]);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -358,14 +358,26 @@ __device__ __forceinline__ void phase_c(const AttendSmem& sm, const ChunkFrags& 
   for (int i = 0; i < 4; ++i) zi[i] = __shfl(inv, g4 * 4 + i, kWave);
 }
 
-// acc[row of (query qi, head g4)][this wave's columns] += wgt * O   (no other
-// wave writes these columns, so a plain read-modify-write is race free)
-__device__ __forceinline__ void acc_update(AttendSmem& sm, int w, int qi, int i,
-                                           const f32x4 (&o)[2], float wgt) {
+// acc[row of (query of slot i, head lane/16)][this wave's 32 columns] +=
+// wgt[i] * O[.][i] for the nv valid slots of a tile.  No other wave writes these
+// columns and the slots of a tile hold distinct queries, so all reads are issued
+// before any write.
+__device__ __forceinline__ void acc_update_tile(AttendSmem& sm, int w, const int (&qi)[4], int nv,
+                                                const f32x4 (&o)[2], const float (&wgt)[4]) {
   const int lane = lane_id();
-  float* a = sm.acc + (qi * kG + (lane >> 4)) * kAccStride + 32 * w + (lane & 15);
-  a[0] += wgt * o[0][i];
-  a[16] += wgt * o[1][i];
+  float* a[4];
+  float x0[4], x1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = sm.acc + (qi[i] * kG + (lane >> 4)) * kAccStride + 32 * w + (lane & 15);
+    if (i < nv) { x0[i] = a[i][0]; x1[i] = a[i][16]; }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nv) {
+      a[i][0] = x0[i] + wgt[i] * o[0][i];
+      a[i][16] = x1[i] + wgt[i] * o[1][i];
+    }
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -375,7 +387,12 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
                uint16_t* __restrict__ out, float* __restrict__ lse_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   AttendSmem& sm = *reinterpret_cast<AttendSmem*>(smem_raw);
-  const int win = blockIdx.x, bkv = blockIdx.y;
+  // Workgroups are dispatched round-robin over the XCDs: with (b, kv head)
+  // varying fastest, each XCD's L2 keeps serving the K/V of the same heads.
+  // Windows run last-to-first (the late ones have the largest unions).
+  const int nbkv = g.B * g.Hkv;
+  const int bkv = blockIdx.x % nbkv;
+  const int win = (g.Lq / kW - 1) - blockIdx.x / nbkv;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -460,15 +477,12 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
 
   float s[kTB][4];
   ChunkFrags fr;
-  int* mylist = sm.tq[w];
 
   // ---- own chunk, pass 1: row statistics -> lse_own (tile t = queries 4t..4t+3)
   if (g.keep_own) {
     load_chunk_frags(Kg + (size_t)own * kS * kD, Vfg + (size_t)own * kFragsPerChunk * kWave * 8, w, fr);
-    if (lane < kW) mylist[lane] = lane;
-    wave_sync_lds();
     for (int tb = 0; tb < kMaxT; tb += kTB) {
-      phase_a(sm, fr, w, tb, kTB, mylist, kW, scale, i0 - own * kS, s);
+      phase_a(sm, fr, w, tb, kTB, lane, kW, scale, i0 - own * kS, s);
       __syncthreads();
       phase_b(sm, w, kTB, s);
       __syncthreads();
@@ -505,7 +519,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   // ---- own chunk, pass 2: P V weighted by w_own
   if (g.keep_own) {
     for (int tb = 0; tb < kMaxT; tb += kTB) {
-      phase_a(sm, fr, w, tb, kTB, mylist, kW, scale, i0 - own * kS, s);
+      phase_a(sm, fr, w, tb, kTB, lane, kW, scale, i0 - own * kS, s);
       __syncthreads();
       phase_b(sm, w, kTB, s);
       __syncthreads();
@@ -514,11 +528,14 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
         f32x4 o[2];
         float zi[4];
         phase_c(sm, fr, tl, o, zi);
+        int qi[4];
+        float wg[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int qi = (tb + tl) * 4 + i;
-          acc_update(sm, w, qi, i, o, sm.wown[qi * kG + g4] * zi[i]);
+          qi[i] = (tb + tl) * 4 + i;
+          wg[i] = sm.wown[qi[i] * kG + g4] * zi[i];
         }
+        acc_update_tile(sm, w, qi, 4, o, wg);
       }
       __syncthreads();
     }
@@ -533,10 +550,23 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     const uint32_t qmk = sm.qmask[c];
     const int p = __popc(qmk);
     const int ntiles = (p + 3) >> 2;
+    // slot n (n < p) of this chunk is the n-th selecting query: lane n holds it
+    // in lq and its four fusion weights in wsl[w][n][*]
+    int lq;
     {
       const bool bit = lane < kW && ((qmk >> (lane & 31)) & 1u);
       const uint64_t m = __ballot(bit);
-      if (bit) mylist[mask_rank(m)] = lane;
+      const int pos = mask_rank(m);
+      // lane n takes the query of the n-th set bit (inverse of the rank map, via LDS)
+      if (bit) sm.wsl[w][pos][0] = __int_as_float(lane);
+      wave_sync_lds();
+      lq = lane < p ? __float_as_int(sm.wsl[w][lane][0]) : 0;
+      wave_sync_lds();
+      if (lane < p) {
+        const int ks = sm.slotmap[lq * kMaxNC + c];
+        const float4 wv = *reinterpret_cast<const float4*>(&sm.wts[(lq * K + ks) * kG]);
+        *reinterpret_cast<float4*>(&sm.wsl[w][lane][0]) = wv;
+      }
     }
     ChunkFrags nx;
     const bool more = u + 1 < nunion;
@@ -547,7 +577,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int tb = 0; tb < ntiles; tb += kTB) {
       const int ntl = min(kTB, ntiles - tb);
       __syncthreads();   // previous batch's P, maxima and sums are consumed
-      phase_a(sm, fr, w, tb, ntl, mylist, p, scale, -1, s);
+      phase_a(sm, fr, w, tb, ntl, lq, p, scale, -1, s);
       __syncthreads();
       phase_b(sm, w, ntl, s);
       __syncthreads();
@@ -555,14 +585,17 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
         f32x4 o[2];
         float zi[4];
         phase_c(sm, fr, tl, o, zi);
+        const int s0 = (tb + tl) * 4;
+        const int nv = min(4, p - s0);
+        int qi[4];
+        float wg[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int slot = (tb + tl) * 4 + i;
-          if (slot >= p) break;
-          const int qi = mylist[slot];
-          const int ks = sm.slotmap[qi * kMaxNC + c];
-          acc_update(sm, w, qi, i, o, sm.wts[(qi * K + ks) * kG + g4] * zi[i]);
+          const int sl = i < nv ? s0 + i : s0;
+          qi[i] = __builtin_amdgcn_readlane(lq, sl);
+          wg[i] = sm.wsl[w][sl][g4] * zi[i];
         }
+        acc_update_tile(sm, w, qi, nv, o, wg);
       }
     }
     if (more) fr = nx;
@@ -601,7 +634,7 @@ hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, 
   const uint16_t* Lm = (const uint16_t*)lmk;
   uint16_t* vfrag = (uint16_t*)ws;
   const int R = g.NC <= 64 ? 1 : g.NC <= 128 ? 2 : 4;
-  dim3 gsel(g.Lq / kSelWin, g.B * g.Hkv);
+  dim3 gsel((g.Lq / kSelWin) * g.B * g.Hkv);
   prof_begin(kPrefillSelect, st);
   switch (R) {
     case 1: hipLaunchKernelGGL(prefill_select<1>, gsel, dim3(kThreads), 0, st, g, Q, (const uint16_t*)v, Lm, bias, sel_idx, vfrag); break;
@@ -613,7 +646,7 @@ hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, 
   // dynamic LDS above 64 KB must be enabled for the kernel (per device; cheap)
   hipFuncSetAttribute((const void*)prefill_attend, hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)sizeof(AttendSmem));
-  hipLaunchKernelGGL(prefill_attend, dim3(g.Lq / kW, g.B * g.Hkv), dim3(kThreads), sizeof(AttendSmem), st, g, Q,
+  hipLaunchKernelGGL(prefill_attend, dim3((g.Lq / kW) * g.B * g.Hkv), dim3(kThreads), sizeof(AttendSmem), st, g, Q,
                      (const uint16_t*)k, vfrag, Lm, bias, sel_idx, (uint16_t*)out, lse);
   prof_end(kPrefillAttend, st);
   return hipGetLastError();
