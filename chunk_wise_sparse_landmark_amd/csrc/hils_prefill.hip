@@ -4,31 +4,30 @@
 // Method: Hierarchical Sparse Attention Done Right (arXiv 2607.02980v1, summary
 // page): landmark scores §3 "Linear surrogate for chunk mass", top-K routing §3
 // "Sparse training", GQA-shared selection §4 "Architecture", per-chunk softmax
-// and fusion by the retrieval scores §3 "Hierarchical softmax".  The page's own
-// kernel batches M adjacent queries over the union of their chunks so that a
-// loaded chunk feeds an (M x G, d) x (d, S) product (§4 "Kernel design"); here
-// the idea is rebuilt for 64-wide waves and 16x16x32 bf16 MFMA:
+// and fusion by the retrieval scores §3 "Hierarchical softmax"; the attention
+// kernel follows the page's kernel design (§4 "Kernel design": M adjacent
+// queries x G heads as one (M x G, d) x (d, S) product over the union of their
+// chunks, M x G >= 16), rebuilt for 64-wide waves and 16x16x32 bf16 MFMA.
 //
-//  1. prefill_select  grid (L/64, B*Hkv), one workgroup per chunk-aligned
-//     64-query window.  Group scores sum_h q_h . lmk_c are one MFMA chain (the
-//     G heads extend the reduction), then each query's top-K is found without
-//     sorting: tau = K-th largest lane maximum, keys >= tau are compacted in
-//     chunk order and a rank count keeps K, which come out in ascending id.
-//     The same workgroup also rewrites its chunk of V in MFMA B-operand order
-//     (16 B per lane per fragment), so the attention kernel loads V fully
-//     coalesced and never transposes it.
-//  2. prefill_attend  grid (L/32, B*Hkv).  A 32-query window (128 rows) walks
-//     the union of its queries' selected chunks.  For each chunk only the
-//     queries that selected it are gathered, four per 16-row tile (rows ordered
-//     head-major, so in the MFMA result the register index is the query slot
-//     and the lane group is the head).  The four waves split the work of a
-//     chunk by keys for S^T = K Q^T (16 keys each; row max and sum go through
-//     LDS) and by output columns for O = P V (32 columns each), so the fp32
-//     accumulators of all 128 rows live in registers, each wave owning its 32
-//     columns: no LDS accumulation, no atomics, a fixed summation order.
-//     Retrieval scores of the window's rows against its union come from one
-//     MFMA pass; the own chunk is attended first, so every fusion weight is
-//     final before the retrieved chunks are added.
+//  1. prefill_select  one workgroup per chunk-aligned 64-query window.  Group
+//     scores sum_h q_h . lmk_c are one MFMA chain (the G heads extend the
+//     reduction), then each query's top-K is found without sorting: tau = K-th
+//     largest lane maximum, keys >= tau are compacted in chunk order and a rank
+//     count keeps K, which come out in ascending id.  The same workgroup also
+//     rewrites its chunk of K and V in MFMA operand-fragment order (16 B per
+//     lane per fragment), so the attention kernel stages a chunk with plain
+//     coalesced copies and reads conflict-free 16-B fragments from LDS.
+//  2. prefill_attend  one workgroup per 64-query window = 16 query blocks of
+//     M = 4 queries x G = 4 heads = 16 rows.  Each wave owns four blocks and
+//     keeps their fp32 output tiles in MFMA accumulators across all chunks.
+//     For every chunk of the window's union it computes S^T = K Q^T, the chunk
+//     softmax, and O += (w/Z) P V, where w is the row's fusion weight (0 for a
+//     row whose query did not select the chunk) and Z the chunk's softmax sum;
+//     a block none of whose queries selected the chunk is skipped.  Retrieval
+//     scores of the window's rows against its union come from one MFMA pass and
+//     the own chunk is attended first, so every fusion weight is final before
+//     any chunk is accumulated.  Chunk fragments are double-buffered in LDS:
+//     one barrier per chunk.
 #include "hils_common.h"
 #include "hils_kernels.h"
 #include "hils_profile.h"
@@ -38,20 +37,21 @@ namespace hils {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kD = 128;
 constexpr int kS = 64;
 constexpr int kG = 4;            // query heads per KV group on this path
 constexpr int kThreads = 256;
-constexpr int kSelWin = 64;      // queries per selection window (one chunk)
-constexpr int kW = 32;           // queries per attention window
-constexpr int kRows = kW * kG;   // 128 rows
-constexpr int kMaxT = kW / 4;    // 16-row tiles per chunk at most
+constexpr int kWin = 64;         // queries per window (one chunk), both kernels
+constexpr int kBlocks = kWin / 4;          // 16 query blocks of 4 queries
+constexpr int kBlocksPerWave = kBlocks / 4;
 constexpr int kMaxKf = 32;       // top-K bound on this path
 constexpr int kMaxNC = 256;      // chunks bound on this path (L <= 16384)
-constexpr int kQStride = 136;    // bf16 per staged Q row (272 B: 2-way bank spread)
-constexpr int kFragsPerChunk = 16;   // V fragments per chunk: 8 column blocks x 2 key steps
+constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
+constexpr int kChunkFrags = 32;            // 16 K + 16 V fragments per chunk
+constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
@@ -72,7 +72,6 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 // two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
@@ -135,32 +134,39 @@ __device__ void select_ascending(uint64_t (&keys)[R], int K, uint64_t* buf, uint
 }
 
 // ----------------------------------------------------------------------------
-// 1. selection (+ V of this window's chunk in B-operand fragment order)
-//    Vf[bkv][chunk][db 0..7][ks 0..1][lane 0..63][8]: lane l, element j holds
-//    V[32ks + 16(j/4) + 4(l/16) + j%4][16db + l%16].
+// 1. selection (+ this window's chunk of K and V in operand-fragment order)
+//    KVf[bkv][chunk] = 16 K fragments then 16 V fragments, 64 lanes x 16 B each:
+//    K fragment f = mt*4 + ks, lane l, element j: K[16mt + l%16][32ks + 8(l/16) + j]
+//      (A operand of S^T = K Q^T for keys 16mt.., k-step ks);
+//    V fragment f = db*2 + ks, lane l, element j:
+//      V[32ks + 16(j/4) + 4(l/16) + j%4][16db + l%16]
+//      (B operand of O = P V for columns 16db.., keys 32ks.., in the key order
+//      in which P leaves the S^T accumulators).
 // ----------------------------------------------------------------------------
 template <int R>
 __global__ void __launch_bounds__(kThreads)
-prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ v,
-               const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
-               int32_t* __restrict__ sel_idx, uint16_t* __restrict__ vf) {
+prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+               const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
+               const float* __restrict__ bias, int32_t* __restrict__ sel_idx,
+               uint16_t* __restrict__ kvf) {
   constexpr int NCP = R * kWave;
-  __shared__ float gs[kSelWin][NCP + 1];
+  __shared__ float gs[kWin][NCP + 1];
   __shared__ uint64_t buf[4][kWave];
   __shared__ uint64_t buf2[4][kWave];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
   const int nbkv = g.B * g.Hkv;            // (b, kv head) fastest: one head per XCD
   const int bkv = blockIdx.x % nbkv;
-  const int win = (g.Lq / kSelWin - 1) - blockIdx.x / nbkv;
+  const int win = (g.Lq / kWin - 1) - blockIdx.x / nbkv;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int i0 = win * kSelWin;
+  const int i0 = win * kWin;
   const int ncand = min(i0 / kS, g.NC);
   const int r16 = lane & 15, g4 = lane >> 4;
 
   // V of chunk `win` -> LDS (coalesced), later rewritten in fragment order
-  const uint16_t* Vc = v + ((size_t)bkv * g.Lkv + (size_t)win * kS) * kD;
-#pragma unroll
+  const size_t row0 = (size_t)bkv * g.Lkv + (size_t)win * kS;
+  const uint16_t* Vc = v + row0 * kD;
+  const uint16_t* Kc = k + row0 * kD;
   for (int x = tid; x < kS * kD / 8; x += kThreads)
     reinterpret_cast<uint4*>(vs)[x] = reinterpret_cast<const uint4*>(Vc)[x];
 
@@ -177,7 +183,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const float sc = g.scale / (float)kG;
   const int ntile = (ncand + 15) / 16;
   for (int nt0 = 0; nt0 < ntile; nt0 += 8) {
-    bf16x8 bv[8][4];   // all loads of up to 8 column tiles in flight together
+    bf16x8 bv[8][4];   // the loads of up to 8 column tiles in flight together
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int c = (nt0 + x) * 16 + r16;
@@ -200,12 +206,19 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       for (int i = 0; i < 4; ++i) gs[w * 16 + g4 * 4 + i][c] = acc[i] * sc + bc;
     }
   }
+
+  // K fragments of this chunk: straight 16-B copies
+  uint16_t* kdst = kvf + ((size_t)bkv * g.NC + win) * kChunkElems;
+  for (int f = tid; f < 16 * kWave; f += kThreads) {
+    const int fl = f % kWave, ks = (f / kWave) % 4, mt = f / (4 * kWave);
+    reinterpret_cast<uint4*>(kdst)[f] = *reinterpret_cast<const uint4*>(
+        Kc + (size_t)(16 * mt + fl % 16) * kD + 32 * ks + 8 * (fl / 16));
+  }
   __syncthreads();
 
-  // V fragments of this chunk (1024 x 16 B, four per thread)
-  uint16_t* vdst = vf + ((size_t)bkv * g.NC + win) * kFragsPerChunk * kWave * 8;
-#pragma unroll
-  for (int f = tid; f < kFragsPerChunk * kWave; f += kThreads) {
+  // V fragments of this chunk
+  uint16_t* vdst = kdst + 16 * kFrag;
+  for (int f = tid; f < 16 * kWave; f += kThreads) {
     const int fl = f % kWave, ks = (f / kWave) % 2, db = f / (2 * kWave);
     uint32_t wd[4];
 #pragma unroll
@@ -238,200 +251,155 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
 // ----------------------------------------------------------------------------
 // 2. attention
 // ----------------------------------------------------------------------------
-constexpr int kTB = 4;          // tiles per batch (P, row max and row sums in LDS)
-constexpr int kAccStride = 144; // floats per accumulator row (576 B: head rows on other banks)
-
-struct ChunkFrags {
-  bf16x8 k[4];        // A operand: keys 16w + lane%16, k-step ks
-  bf16x8 v[2][2];     // B operand: column block 2w + nb, key step ks
-};
-
-__device__ __forceinline__ void load_chunk_frags(const uint16_t* Kc, const uint16_t* Vfc, int w,
-                                                 ChunkFrags& f) {
-  const int lane = lane_id();
-  const uint16_t* kr = Kc + (size_t)(w * 16 + (lane & 15)) * kD + (lane >> 4) * 8;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) f.k[ks] = ld8(kr + ks * 32);
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      f.v[nb][ks] = ld8(Vfc + ((size_t)((2 * w + nb) * 2 + ks) * kWave + lane) * 8);
-}
-
 struct AttendSmem {
-  float acc[kRows * kAccStride];                 // fp32 output rows (row = qi*4 + h)
-  uint16_t qs[kRows * kQStride];                 // window Q, row = qi*4 + h; reused for output
-  uint4 pf[kTB][2][kWave];                       // unnormalised P, in A-operand fragment order
-  float smax[kTB][4][16];
-  float ssum[kTB][4][16];
-  float wts[kW * kMaxKf * kG];                   // (query, slot, head): score, then weight
-  int sel[kW * kMaxKf];
-  uint8_t slotmap[kW * kMaxNC];                  // (query, chunk) -> slot, 0xff if not selected
-  uint32_t qmask[kMaxNC];
+  uint4 kv[2][kChunkFrags * kWave];      // double-buffered chunk fragments (2 x 32 KB)
+  float wts[kWin * kMaxKf * kG];          // (query, slot, head): score, then weight
+  int sel[kWin * kMaxKf];
+  uint8_t slotmap[kWin * kMaxNC];         // (query, chunk) -> slot, 0xff if not selected
+  uint64_t qmask[kMaxNC];                 // chunk -> window queries that selected it
   uint16_t ulist[kMaxNC];
-  float lseown[kRows];
-  float wown[kRows];
-  float wsl[4][kW][kG];                          // per wave: fusion weight of (slot, head)
+  float lseown[kWin * kG];
+  float wown[kWin * kG];
   int wcount[4];
 };
 
-// Phase A for tiles tbase .. tbase+ntl-1 (ntl <= kTB) of one chunk: S^T for this
-// wave's 16 keys and the wave-partial row max.  Row r16 of a tile = (head
-// r16/4, query slot r16%4); slot n of the chunk is query list[n].  vis_own >= 0
-// marks the own chunk: key kk of query qi is visible when kk <= qi + vis_own.
-__device__ __forceinline__ void phase_a(AttendSmem& sm, const ChunkFrags& f, int w, int tbase,
-                                        int ntl, int lq, int nlist, float scale, int vis_own,
-                                        float (&s)[kTB][4]) {
-  const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+// Start copying one chunk's 32 KB of fragments into an LDS buffer with direct
+// global->LDS loads (16 B per lane; lane i of a wave lands at the wave's LDS
+// base + 16 i).  Completion: s_waitcnt vmcnt(0), then a barrier.
+__device__ __forceinline__ void stage_async(const uint16_t* src, uint4* dst) {
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  const int wbase = (threadIdx.x / kWave) * kWave;
 #pragma unroll
-  for (int tl = 0; tl < kTB; ++tl) {
-    if (tl >= ntl) break;
-    const int slot = (tbase + tl) * 4 + (r16 & 3);
-    const int qi = __shfl(lq, slot < nlist ? slot : 0, kWave);
-    const uint16_t* qr = sm.qs + (qi * kG + (r16 >> 2)) * kQStride + g4 * 8;
+  for (int x = 0; x < 8; ++x)
+    __builtin_amdgcn_global_load_lds((const void*)(s + x * kThreads + threadIdx.x),
+                                     (__attribute__((address_space(3))) void*)(dst + x * kThreads + wbase),
+                                     16, 0, 0);
+}
+__device__ __forceinline__ void stage_wait() { __builtin_amdgcn_s_waitcnt(0); }
+
+struct ChunkRegs {
+  bf16x8 k[16];   // K fragments (mt*4 + ks)
+  bf16x8 v[16];   // V fragments (db*2 + ks)
+};
+__device__ __forceinline__ void load_chunk_regs(const uint4* kvb, ChunkRegs& cr) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int f = 0; f < 16; ++f) cr.k[f] = as_bf16x8(kvb[f * kWave + lane]);
+#pragma unroll
+  for (int f = 0; f < 16; ++f) cr.v[f] = as_bf16x8(kvb[(16 + f) * kWave + lane]);
+}
+
+// One query block against one chunk (fragments in registers).  Row r16 of the
+// block = (query 4*blk + r16/4, head r16%4).  kMasked: keys >= vis are hidden
+// (own chunk).  kStatsOnly: return the row max (in log2 units) and sum;
+// otherwise accumulate (rw / rowsum) * P V into o (rw = the row's fusion
+// weight; 0 removes the row).  sc2 = scale * log2(e): exponentials are exp2 of
+// one fused multiply-add per logit.
+template <bool kMasked, bool kStatsOnly>
+__device__ __forceinline__ void block_chunk(const ChunkRegs& cr, const bf16x8 (&qf)[4], float sc2,
+                                            int vis, float rw, f32x4 (&o)[8], float& m_out,
+                                            float& z_out) {
+  const int lane = lane_id();
+  const int g4 = lane >> 4;
+  f32x4 s[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 qb = as_bf16x8(*reinterpret_cast<const uint4*>(qr + ks * 32));
-      acc = mfma(f.k[ks], qb, acc);
-    }
-    float mx = -INFINITY;
+    for (int ks = 0; ks < 4; ++ks) acc = mfma(cr.k[mt * 4 + ks], qf[ks], acc);
+    s[mt] = acc;
+  }
+  if (kMasked) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (mt * 16 + g4 * 4 + i >= vis) s[mt][i] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+  for (int mt = 1; mt < 4; ++mt)
+    mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float mb = mx * sc2;
+  float z = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kk = w * 16 + g4 * 4 + i;
-      const bool vis = vis_own < 0 || kk <= qi + vis_own;
-      const float x = vis ? acc[i] * scale : -INFINITY;
-      s[tl][i] = x;
-      mx = fmaxf(mx, x);
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -mb));
+      s[mt][i] = e;
+      z += e;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    if (lane < 16) sm.smax[tl][w][r16] = mx;
+  z += __shfl_xor(z, 16, kWave);
+  z += __shfl_xor(z, 32, kWave);
+  if (kStatsOnly) {
+    m_out = mb;
+    z_out = z;
+    return;
   }
-}
-
-// Phase B: row max over the four waves, exponentials, P (bf16) and partial
-// sums; s[tl][0] keeps the row max of row r16.
-__device__ __forceinline__ void phase_b(AttendSmem& sm, int w, int ntl, float (&s)[kTB][4]) {
-  const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int tl = 0; tl < kTB; ++tl) {
-    if (tl >= ntl) break;
-    const float m = fmaxf(fmaxf(sm.smax[tl][0][r16], sm.smax[tl][1][r16]),
-                          fmaxf(sm.smax[tl][2][r16], sm.smax[tl][3][r16]));
-    float e[4], z = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      e[i] = __expf(s[tl][i] - m);
-      z += e[i];
-    }
-    z += __shfl_xor(z, 16, kWave);
-    z += __shfl_xor(z, 32, kWave);
-    if (lane < 16) sm.ssum[tl][w][r16] = z;
-    // keys 16w + 4*g4 + i are elements 4*(w&1) + i of this lane's fragment for k-step w>>1
-    reinterpret_cast<uint2*>(&sm.pf[tl][w >> 1][lane])[w & 1] =
-        make_uint2(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]));
-    s[tl][0] = m;
-  }
-}
-
-// Phase C for tile tl of the batch: O = P V for this wave's 32 columns; lane
-// holds O[row 4*g4 + i][column 32w + 16nb + lane%16] in o[nb][i], and 1/rowsum
-// of those rows in zi[i].
-__device__ __forceinline__ void phase_c(const AttendSmem& sm, const ChunkFrags& f, int tl,
-                                        f32x4 (&o)[2], float (&zi)[4]) {
-  const int lane = lane_id(), r16 = lane & 15, g4 = lane >> 4;
+  const float f = rw / z;
+  // P as the A operand of O += P V: k-slot (g4, j) <-> key 32ks + 16(j/4) + 4g4 + j%4
   bf16x8 pa[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) pa[ks] = as_bf16x8(sm.pf[tl][ks][lane]);
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) acc = mfma(pa[ks], f.v[nb][ks], acc);
-    o[nb] = acc;
-  }
-  const float z = sm.ssum[tl][0][r16] + sm.ssum[tl][1][r16] + sm.ssum[tl][2][r16] + sm.ssum[tl][3][r16];
-  const float inv = 1.f / z;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) zi[i] = __shfl(inv, g4 * 4 + i, kWave);
-}
-
-// acc[row of (query of slot i, head lane/16)][this wave's 32 columns] +=
-// wgt[i] * O[.][i] for the nv valid slots of a tile.  No other wave writes these
-// columns and the slots of a tile hold distinct queries, so all reads are issued
-// before any write.
-__device__ __forceinline__ void acc_update_tile(AttendSmem& sm, int w, const int (&qi)[4], int nv,
-                                                const f32x4 (&o)[2], const float (&wgt)[4]) {
-  const int lane = lane_id();
-  float* a[4];
-  float x0[4], x1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = sm.acc + (qi[i] * kG + (lane >> 4)) * kAccStride + 32 * w + (lane & 15);
-    if (i < nv) { x0[i] = a[i][0]; x1[i] = a[i][16]; }
+  for (int ks = 0; ks < 2; ++ks) {
+    uint32_t w4[4];
+    w4[0] = pack_bf16x2(s[2 * ks][0] * f, s[2 * ks][1] * f);
+    w4[1] = pack_bf16x2(s[2 * ks][2] * f, s[2 * ks][3] * f);
+    w4[2] = pack_bf16x2(s[2 * ks + 1][0] * f, s[2 * ks + 1][1] * f);
+    w4[3] = pack_bf16x2(s[2 * ks + 1][2] * f, s[2 * ks + 1][3] * f);
+    __builtin_memcpy(&pa[ks], w4, 16);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i < nv) {
-      a[i][0] = x0[i] + wgt[i] * o[0][i];
-      a[i][16] = x1[i] + wgt[i] * o[1][i];
-    }
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) o[db] = mfma(pa[ks], cr.v[db * 2 + ks], o[db]);
 }
 
 __global__ void __launch_bounds__(kThreads)
-prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-               const uint16_t* __restrict__ vf, const uint16_t* __restrict__ lmk,
-               const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
-               uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kvf,
+               const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
+               const int32_t* __restrict__ sel_idx, uint16_t* __restrict__ out,
+               float* __restrict__ lse_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   AttendSmem& sm = *reinterpret_cast<AttendSmem*>(smem_raw);
-  // Workgroups are dispatched round-robin over the XCDs: with (b, kv head)
-  // varying fastest, each XCD's L2 keeps serving the K/V of the same heads.
-  // Windows run last-to-first (the late ones have the largest unions).
+  // (b, kv head) fastest over the workgroup id: consecutive workgroups go to
+  // different XCDs, so each XCD's L2 keeps serving the same heads.  Windows run
+  // last to first (late windows have the largest unions).
   const int nbkv = g.B * g.Hkv;
   const int bkv = blockIdx.x % nbkv;
-  const int win = (g.Lq / kW - 1) - blockIdx.x / nbkv;
+  const int win = (g.Lq / kWin - 1) - blockIdx.x / nbkv;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int K = g.K;
-  const int i0 = win * kW;
-  const int own = i0 / kS;
+  const int i0 = win * kWin;
+  const int own = win;                    // the window is exactly chunk `win`
   const int ncand = min(own, g.NC);
-  const uint16_t* Kg = k + (size_t)bkv * g.Lkv * kD;
-  const uint16_t* Vfg = vf + (size_t)bkv * g.NC * kFragsPerChunk * kWave * 8;
+  const uint16_t* KVg = kvf + (size_t)bkv * g.NC * kChunkElems;
   const uint16_t* Lg = lmk + (size_t)bkv * g.NCcap * kD;
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   const float scale = g.scale;
 
-  // ---- setup: window Q in LDS, selections, chunk -> query masks, union list
-  for (int x = tid; x < kRows * 16; x += kThreads) {
-    const int row = x >> 4, seg = x & 15;
-    const int qi = row >> 2, h = row & 3;
-    const uint4 u = *reinterpret_cast<const uint4*>(
-        q + ((size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + qi) * kD + seg * 8);
-    *reinterpret_cast<uint4*>(sm.qs + row * kQStride + seg * 8) = u;
-  }
-  for (int x = tid; x < kRows * kAccStride; x += kThreads) sm.acc[x] = 0.f;
-  for (int x = tid; x < kW * K; x += kThreads)
+  // ---- setup: selections, chunk -> query masks, union list
+  for (int x = tid; x < kWin * K; x += kThreads)
     sm.sel[x] = sel_idx[((size_t)bkv * g.Lq + i0 + x / K) * K + x % K];
-  for (int x = tid; x < kW * kMaxNC / 4; x += kThreads)
+  for (int x = tid; x < kWin * kMaxNC / 4; x += kThreads)
     reinterpret_cast<uint32_t*>(sm.slotmap)[x] = 0xffffffffu;
-  for (int c = tid; c < kMaxNC; c += kThreads) sm.qmask[c] = 0u;
+  for (int c = tid; c < kMaxNC; c += kThreads) sm.qmask[c] = 0ull;
   __syncthreads();
-  for (int x = tid; x < kW * K; x += kThreads) {
+  for (int x = tid; x < kWin * K; x += kThreads) {
     const int c = sm.sel[x];
     if (c >= 0) {
-      atomicOr(&sm.qmask[c], 1u << (x / K));
+      atomicOr((unsigned long long*)&sm.qmask[c], 1ull << (x / K));
       sm.slotmap[(x / K) * kMaxNC + c] = (uint8_t)(x % K);
     }
   }
   __syncthreads();
   {
     const int c = tid;
-    const bool f = c < ncand && sm.qmask[c] != 0u;
+    const bool f = c < ncand && sm.qmask[c] != 0ull;
     const uint64_t m = __ballot(f);
     if (lane == 0) sm.wcount[w] = __popcll(m);
     __syncthreads();
@@ -441,213 +409,173 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   }
   const int nunion = sm.wcount[0] + sm.wcount[1] + sm.wcount[2] + sm.wcount[3];
 
+  // Q fragments of this wave's four blocks (B operand of S^T, also the A operand
+  // of the retrieval scores): row r16 = (query 4*blk + r16/4, head r16%4)
+  bf16x8 qf[kBlocksPerWave][4];
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j) {
+    const int blk = w * kBlocksPerWave + j;
+    const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
+    const uint16_t* qr = q + ((size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + qi) * kD + g4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[j][ks] = ld8(qr + ks * 32);
+  }
+
+  // first staged chunk: the own chunk if kept, else the first of the union
+  const int first = g.keep_own ? own : (nunion > 0 ? sm.ulist[0] : -1);
+  if (first >= 0) stage_async(KVg + (size_t)first * kChunkElems, sm.kv[0]);
+
   // ---- retrieval scores of (row, selected chunk) by MFMA: rows x union columns
-  {
-    bf16x8 aq[2][4];
+  for (int nt = 0; nt * 16 < nunion; ++nt) {
+    const int u = nt * 16 + r16;
+    const int c = sm.ulist[u < nunion ? u : 0];
+    bf16x8 bl[4];
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const int row = (2 * w + m2) * 16 + r16;
+    for (int ks = 0; ks < 4; ++ks) bl[ks] = ld8(Lg + (size_t)c * kD + g4 * 8 + ks * 32);
+    const float bc = bb ? bb[c] : 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        aq[m2][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sm.qs + row * kQStride + g4 * 8 + ks * 32));
-    }
-    for (int nt = 0; nt * 16 < nunion; ++nt) {
-      const int u = nt * 16 + r16;
-      const int c = sm.ulist[u < nunion ? u : 0];
-      bf16x8 bl[4];
+    for (int j = 0; j < kBlocksPerWave; ++j) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bl[ks] = ld8(Lg + (size_t)c * kD + g4 * 8 + ks * 32);
-      const float bc = bb ? bb[c] : 0.f;
+      for (int ks = 0; ks < 4; ++ks) acc = mfma(qf[j][ks], bl[ks], acc);
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma(aq[m2][ks], bl[ks], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = (2 * w + m2) * 16 + g4 * 4 + i;
-          const int qi = row >> 2, h = row & 3;
-          const int slot = u < nunion ? sm.slotmap[qi * kMaxNC + c] : 0xff;
-          if (slot != 0xff) sm.wts[(qi * K + slot) * kG + h] = scale * acc[i] + bc;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int rr = g4 * 4 + i;                 // block row: query rr/4, head rr%4
+        const int qi = (w * kBlocksPerWave + j) * 4 + (rr >> 2), h = rr & 3;
+        const int slot = u < nunion ? sm.slotmap[qi * kMaxNC + c] : 0xff;
+        if (slot != 0xff) sm.wts[(qi * K + slot) * kG + h] = scale * acc[i] + bc;
       }
+    }
+  }
+  stage_wait();
+  __syncthreads();
+
+  f32x4 o[kBlocksPerWave][8];
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- own chunk, pass 1: lse of the visible tokens (key kk visible to query
+  //      qi when kk <= qi, as the window is the chunk)
+  const float sc2 = scale * 1.4426950408889634f;   // scale * log2(e)
+  ChunkRegs cr;
+  if (g.keep_own) {
+    load_chunk_regs(sm.kv[0], cr);
+#pragma unroll
+    for (int j = 0; j < kBlocksPerWave; ++j) {
+      const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2);
+      float m2, z;
+      f32x4 unused[8];
+      block_chunk<true, true>(cr, qf[j], sc2, qi + 1, 0.f, unused, m2, z);
+      // natural-log lse of the visible tokens: (m2 + log2 z) * ln 2
+      if (lane < 16) sm.lseown[qi * kG + (r16 & 3)] = (m2 + __log2f(z)) * 0.6931471805599453f;
     }
   }
   __syncthreads();
-
-  float s[kTB][4];
-  ChunkFrags fr;
-
-  // ---- own chunk, pass 1: row statistics -> lse_own (tile t = queries 4t..4t+3)
-  if (g.keep_own) {
-    load_chunk_frags(Kg + (size_t)own * kS * kD, Vfg + (size_t)own * kFragsPerChunk * kWave * 8, w, fr);
-    for (int tb = 0; tb < kMaxT; tb += kTB) {
-      phase_a(sm, fr, w, tb, kTB, lane, kW, scale, i0 - own * kS, s);
-      __syncthreads();
-      phase_b(sm, w, kTB, s);
-      __syncthreads();
-      if (w == 0) {
-#pragma unroll
-        for (int tl = 0; tl < kTB; ++tl) {
-          const float z = sm.ssum[tl][0][r16] + sm.ssum[tl][1][r16] + sm.ssum[tl][2][r16] + sm.ssum[tl][3][r16];
-          if (lane < 16) {
-            const int qi = (tb + tl) * 4 + (r16 & 3), h = r16 >> 2;
-            sm.lseown[qi * kG + h] = s[tl][0] + __logf(z);
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
   // ---- fusion weights: LSE over the retrieval scores and the own chunk's lse
-  if (tid < kRows) {
-    const int qi = tid >> 2, h = tid & 3;
-    float m = g.keep_own ? sm.lseown[tid] : -INFINITY;
+  {
+    const int qi = tid >> 2, h = tid & 3;     // 256 threads = 64 queries x 4 heads
+    const float lo = g.keep_own ? sm.lseown[tid] : -INFINITY;
+    float m = lo;
     for (int slot = 0; slot < K; ++slot)
       if (sm.sel[qi * K + slot] >= 0) m = fmaxf(m, sm.wts[(qi * K + slot) * kG + h]);
-    float z = g.keep_own ? __expf(sm.lseown[tid] - m) : 0.f;
+    float z = g.keep_own ? __expf(lo - m) : 0.f;
     for (int slot = 0; slot < K; ++slot)
       if (sm.sel[qi * K + slot] >= 0) z += __expf(sm.wts[(qi * K + slot) * kG + h] - m);
     const float LSE = z > 0.f ? m + __logf(z) : -INFINITY;
     for (int slot = 0; slot < K; ++slot)
       if (sm.sel[qi * K + slot] >= 0)
         sm.wts[(qi * K + slot) * kG + h] = __expf(sm.wts[(qi * K + slot) * kG + h] - LSE);
-    sm.wown[tid] = (g.keep_own && z > 0.f) ? __expf(sm.lseown[tid] - LSE) : 0.f;
+    sm.wown[tid] = (g.keep_own && z > 0.f) ? __expf(lo - LSE) : 0.f;
     if (lse_out) lse_out[(size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + qi] = LSE;
   }
   __syncthreads();
-  // ---- own chunk, pass 2: P V weighted by w_own
-  if (g.keep_own) {
-    for (int tb = 0; tb < kMaxT; tb += kTB) {
-      phase_a(sm, fr, w, tb, kTB, lane, kW, scale, i0 - own * kS, s);
-      __syncthreads();
-      phase_b(sm, w, kTB, s);
-      __syncthreads();
+
+  // ---- chunk loop: step 0 is the own chunk (if kept), then the union.  The
+  //      next chunk is loaded into registers while this one is computed.
+  const int nsteps = nunion + (g.keep_own ? 1 : 0);
+  for (int stp = 0; stp < nsteps; ++stp) {
+    const int cur = stp & 1;
+    const bool is_own = g.keep_own && stp == 0;
+    const int uidx = stp - (g.keep_own ? 1 : 0);
+    const int c = is_own ? own : sm.ulist[uidx];
+    const bool more = stp + 1 < nsteps;
+    if (more) stage_async(KVg + (size_t)sm.ulist[uidx + 1] * kChunkElems, sm.kv[cur ^ 1]);
+    const uint64_t qmk = is_own ? ~0ull : sm.qmask[c];
+    load_chunk_regs(sm.kv[cur], cr);
 #pragma unroll
-      for (int tl = 0; tl < kTB; ++tl) {
-        f32x4 o[2];
-        float zi[4];
-        phase_c(sm, fr, tl, o, zi);
-        int qi[4];
-        float wg[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qi[i] = (tb + tl) * 4 + i;
-          wg[i] = sm.wown[qi[i] * kG + g4] * zi[i];
-        }
-        acc_update_tile(sm, w, qi, 4, o, wg);
+    for (int j = 0; j < kBlocksPerWave; ++j) {
+      const int blk = w * kBlocksPerWave + j;
+      if (((qmk >> (blk * 4)) & 0xfull) == 0) continue;      // no query of the block selected c
+      const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
+      float rw;
+      if (is_own) {
+        rw = sm.wown[qi * kG + h];
+      } else {
+        const int slot = sm.slotmap[qi * kMaxNC + c];
+        rw = slot != 0xff ? sm.wts[(qi * K + slot) * kG + h] : 0.f;
       }
-      __syncthreads();
+      float m, z;
+      if (is_own) block_chunk<true, false>(cr, qf[j], sc2, qi + 1, rw, o[j], m, z);
+      else block_chunk<false, false>(cr, qf[j], sc2, kS, rw, o[j], m, z);
     }
+    stage_wait();
+    __syncthreads();
   }
 
-  // ---- retrieved chunks, all waves in step over the union
-  if (nunion > 0)
-    load_chunk_frags(Kg + (size_t)sm.ulist[0] * kS * kD,
-                     Vfg + (size_t)sm.ulist[0] * kFragsPerChunk * kWave * 8, w, fr);
-  for (int u = 0; u < nunion; ++u) {
-    const int c = sm.ulist[u];
-    const uint32_t qmk = sm.qmask[c];
-    const int p = __popc(qmk);
-    const int ntiles = (p + 3) >> 2;
-    // slot n (n < p) of this chunk is the n-th selecting query: lane n holds it
-    // in lq and its four fusion weights in wsl[w][n][*]
-    int lq;
-    {
-      const bool bit = lane < kW && ((qmk >> (lane & 31)) & 1u);
-      const uint64_t m = __ballot(bit);
-      const int pos = mask_rank(m);
-      // lane n takes the query of the n-th set bit (inverse of the rank map, via LDS)
-      if (bit) sm.wsl[w][pos][0] = __int_as_float(lane);
-      wave_sync_lds();
-      lq = lane < p ? __float_as_int(sm.wsl[w][lane][0]) : 0;
-      wave_sync_lds();
-      if (lane < p) {
-        const int ks = sm.slotmap[lq * kMaxNC + c];
-        const float4 wv = *reinterpret_cast<const float4*>(&sm.wts[(lq * K + ks) * kG]);
-        *reinterpret_cast<float4*>(&sm.wsl[w][lane][0]) = wv;
-      }
-    }
-    ChunkFrags nx;
-    const bool more = u + 1 < nunion;
-    if (more) {   // prefetch the next chunk's fragments before this chunk's MFMA work
-      const int cn = sm.ulist[u + 1];
-      load_chunk_frags(Kg + (size_t)cn * kS * kD, Vfg + (size_t)cn * kFragsPerChunk * kWave * 8, w, nx);
-    }
-    for (int tb = 0; tb < ntiles; tb += kTB) {
-      const int ntl = min(kTB, ntiles - tb);
-      __syncthreads();   // previous batch's P, maxima and sums are consumed
-      phase_a(sm, fr, w, tb, ntl, lq, p, scale, -1, s);
-      __syncthreads();
-      phase_b(sm, w, ntl, s);
-      __syncthreads();
-      for (int tl = 0; tl < ntl; ++tl) {
-        f32x4 o[2];
-        float zi[4];
-        phase_c(sm, fr, tl, o, zi);
-        const int s0 = (tb + tl) * 4;
-        const int nv = min(4, p - s0);
-        int qi[4];
-        float wg[4];
+  // ---- output: lane holds O[row 4*g4 + i][16*db + r16] of each block;
+  //      row 4*g4 + i = (query 4*blk + g4, head i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sl = i < nv ? s0 + i : s0;
-          qi[i] = __builtin_amdgcn_readlane(lq, sl);
-          wg[i] = sm.wsl[w][sl][g4] * zi[i];
-        }
-        acc_update_tile(sm, w, qi, nv, o, wg);
-      }
+  for (int j = 0; j < kBlocksPerWave; ++j) {
+    const int qi = (w * kBlocksPerWave + j) * 4 + g4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t* orow = out + ((size_t)(b * g.Hq + kvh * kG + i) * g.Lq + i0 + qi) * kD + r16;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) orow[16 * db] = f32_to_bf16(o[j][db][i]);
     }
-    if (more) fr = nx;
   }
-  __syncthreads();
+}
 
-  // ---- output rows (bf16), 16 B per thread
-  for (int x = tid; x < kRows * 16; x += kThreads) {
-    const int row = x >> 4, seg = x & 15;
-    const int qi = row >> 2, h = row & 3;
-    const float* a = sm.acc + row * kAccStride + seg * 8;
-    uint4 pk;
-    pk.x = pack_bf16x2(a[0], a[1]);
-    pk.y = pack_bf16x2(a[2], a[3]);
-    pk.z = pack_bf16x2(a[4], a[5]);
-    pk.w = pack_bf16x2(a[6], a[7]);
-    *reinterpret_cast<uint4*>(out + ((size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + qi) * kD + seg * 8) = pk;
-  }
+template <int R>
+void launch_select(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const uint16_t* lmk, const float* bias, int32_t* sel_idx, uint16_t* kvf,
+                   hipStream_t st) {
+  hipLaunchKernelGGL(prefill_select<R>, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kThreads), 0, st,
+                     g, q, k, v, lmk, bias, sel_idx, kvf);
 }
 
 }  // namespace
 
 bool prefill_fast_supported(const Geometry& g, int bf16) {
-  return bf16 && g.d == kD && g.S == kS && g.causal && g.Lq == g.Lkv && g.Lq % kSelWin == 0 &&
+  return bf16 && g.d == kD && g.S == kS && g.causal && g.Lq == g.Lkv && g.Lq % kWin == 0 &&
          g.G == kG && g.K <= kMaxKf && g.NC <= kMaxNC && g.Lq > 0;
 }
 
 size_t prefill_fast_ws(const Geometry& g) {
-  return (size_t)g.B * g.Hkv * g.NC * kFragsPerChunk * kWave * 16;
+  return (size_t)g.B * g.Hkv * g.NC * kChunkElems * sizeof(uint16_t);
 }
 
 hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, const void* v,
                                const void* lmk, const float* bias, void* out, int32_t* sel_idx,
                                float* lse, void* ws, hipStream_t st) {
   const uint16_t* Q = (const uint16_t*)q;
+  const uint16_t* Kp = (const uint16_t*)k;
+  const uint16_t* Vp = (const uint16_t*)v;
   const uint16_t* Lm = (const uint16_t*)lmk;
-  uint16_t* vfrag = (uint16_t*)ws;
-  const int R = g.NC <= 64 ? 1 : g.NC <= 128 ? 2 : 4;
-  dim3 gsel((g.Lq / kSelWin) * g.B * g.Hkv);
+  uint16_t* kvf = (uint16_t*)ws;
   prof_begin(kPrefillSelect, st);
-  switch (R) {
-    case 1: hipLaunchKernelGGL(prefill_select<1>, gsel, dim3(kThreads), 0, st, g, Q, (const uint16_t*)v, Lm, bias, sel_idx, vfrag); break;
-    case 2: hipLaunchKernelGGL(prefill_select<2>, gsel, dim3(kThreads), 0, st, g, Q, (const uint16_t*)v, Lm, bias, sel_idx, vfrag); break;
-    default: hipLaunchKernelGGL(prefill_select<4>, gsel, dim3(kThreads), 0, st, g, Q, (const uint16_t*)v, Lm, bias, sel_idx, vfrag); break;
-  }
+  if (g.NC <= 64) launch_select<1>(g, Q, Kp, Vp, Lm, bias, sel_idx, kvf, st);
+  else if (g.NC <= 128) launch_select<2>(g, Q, Kp, Vp, Lm, bias, sel_idx, kvf, st);
+  else launch_select<4>(g, Q, Kp, Vp, Lm, bias, sel_idx, kvf, st);
   prof_end(kPrefillSelect, st);
-  prof_begin(kPrefillAttend, st);
   // dynamic LDS above 64 KB must be enabled for the kernel (per device; cheap)
   hipFuncSetAttribute((const void*)prefill_attend, hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)sizeof(AttendSmem));
-  hipLaunchKernelGGL(prefill_attend, dim3((g.Lq / kW) * g.B * g.Hkv), dim3(kThreads), sizeof(AttendSmem), st, g, Q,
-                     (const uint16_t*)k, vfrag, Lm, bias, sel_idx, (uint16_t*)out, lse);
+  prof_begin(kPrefillAttend, st);
+  hipLaunchKernelGGL(prefill_attend, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kThreads),
+                     sizeof(AttendSmem), st, g, Q, kvf, Lm, bias, sel_idx, (uint16_t*)out, lse);
   prof_end(kPrefillAttend, st);
   return hipGetLastError();
 }

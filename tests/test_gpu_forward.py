@@ -86,7 +86,10 @@ def test_values_one_give_output_one(hl, L):
     host, dev = make_device_inputs(cfg)
     dev["v"] = torch.ones_like(dev["v"])
     out, idx, lse = _run(hl, cfg, dev)
-    assert np.all(out[:, :, 64:] == 1.0)   # every query past the first chunk fuses >= 1 member
+    # The fusion weights sum to one, so V = 1 gives O = 1 up to rounding: P enters
+    # the P.V product in bf16 (relative error <= 2^-9 summed over all terms) and
+    # O is rounded to bf16 (2^-8 below 1).  A dropped chunk of weight > 0.6% fails.
+    assert np.abs(out - 1.0).max() <= 2.0 ** -9 + 2.0 ** -8 + 1e-6
 
 
 @pytest.mark.parametrize("Lkv,K", [(8209, 32), (4096, 16), (100, 8), (64, 4)])
