@@ -20,7 +20,10 @@ HIP events the library records around each launch of the dominant kernel on
 its own stream (hils_profile_kernel).
 """
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import math
 import os
@@ -33,6 +36,20 @@ sys.path.insert(0, ROOT)
 METRIC = "HiLS decode KV GB/s @128K-4M ctx + prefill TFLOP/s @8K; % of roofline"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "chunk_wise_sparse_landmark_amd", "csrc")
+# source files whose text fixes each timed kernel's machine code
+KERNEL_SOURCES = {
+    "prefill_attend": ["hils_prefill.hip", "hils_common.h"],
+    "prefill_select": ["hils_prefill.hip", "hils_common.h"],
+    "decode_attend": ["hils_decode.hip", "hils_common.h"],
+    "decode_score": ["hils_decode.hip", "hils_common.h"],
+    "generic_attend": ["hils_generic.hip", "hils_common.h"],
+    "generic_bwd_chunks": ["hils_generic.hip", "hils_common.h"],
+    "prefill_bwd_chunks": ["hils_prefill_bwd.hip", "hils_common.h"],
+    "prefill_bwd_rows": ["hils_prefill_bwd.hip", "hils_common.h"],
+}
+COPY_MIB = 1024   # size of the plain copy that calibrates the HBM byte counters
 
 
 # --------------------------------------------------------------------------- HIP events
@@ -100,6 +117,121 @@ def decode_bytes(cfg):
     kv = B * Hkv * int(nsel[-1] * cfg["S"] + nown[-1]) * d * 2 * 2
     small = 2 * B * Hq * d * 2 + B * Hkv * K * 4 + B * Hq * 4
     return float(lmk + kv + small), float(lmk), float(kv)
+
+
+# --------------------------------------------------------------------------- HBM traffic
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        path = os.path.join(CSRC, f)
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(PROFILES, "%s_%s_traffic.txt" % (kernel, workload))
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or the kernel's sources changed since it was taken."""
+    path = traffic_file(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    for ln in open(path):
+        if ln.startswith("{"):
+            rec = json.loads(ln)
+            if rec.get("source_hash") == source_hash(kernel):
+                return rec["traffic_bytes_per_launch"]
+    return None
+
+
+def _counter_means(run_dir):
+    """{kernel name: {counter: mean over dispatches}} from a rocprofv3 --pmc csv run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under " + run_dir)
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            d = acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], [])
+            d.append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def _find(means, key):
+    hits = [k for k in means if key in k]
+    if not hits:
+        raise SystemExit("kernel %r not in counter output (have: %s)" % (key, list(means)[:8]))
+    return hits[0]
+
+
+def summarize_traffic(kernel, workload, fetch_dir, write_dir, commands):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of `kernel`, each scaled by what
+    the same counter reads for the plain COPY_MIB copy in the same run."""
+    fm, wm = _counter_means(fetch_dir), _counter_means(write_dir)
+    copy_bytes = COPY_MIB * 2 ** 20
+    ck_f, ck_w = _find(fm, "copy_u4"), _find(wm, "copy_u4")
+    f_fetch = copy_bytes / (fm[ck_f]["FETCH_SIZE"] * 1024.0)
+    f_write = copy_bytes / (wm[ck_w]["WRITE_SIZE"] * 1024.0)
+    kf, kw = _find(fm, kernel), _find(wm, kernel)
+    fetch_b = fm[kf]["FETCH_SIZE"] * 1024.0 * f_fetch
+    write_b = wm[kw]["WRITE_SIZE"] * 1024.0 * f_write
+    rec = dict(kernel=kernel, workload=workload, source_hash=source_hash(kernel),
+               fetch_kib_per_dispatch=fm[kf]["FETCH_SIZE"], write_kib_per_dispatch=wm[kw]["WRITE_SIZE"],
+               copy_bytes=copy_bytes, copy_fetch_kib=fm[ck_f]["FETCH_SIZE"],
+               copy_write_kib=wm[ck_w]["WRITE_SIZE"], fetch_scale=f_fetch, write_scale=f_write,
+               fetch_bytes_per_launch=fetch_b, write_bytes_per_launch=write_b,
+               traffic_bytes_per_launch=fetch_b + write_b)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(kernel, workload), "w") as f:
+        f.write("HBM traffic of %s on %s (rocprofv3 --pmc, one counter per run)\n" % (kernel, workload))
+        for c in commands:
+            f.write("command: %s\n" % c)
+        f.write("copy calibration: copy_u4 of %d MiB (reads and writes exactly that much); "
+                "scale = copy bytes / counter bytes\n" % COPY_MIB)
+        f.write("%-28s %14s %14s\n" % ("dispatch mean", "FETCH_SIZE KiB", "WRITE_SIZE KiB"))
+        f.write("%-28s %14.1f %14.1f\n" % (kernel, rec["fetch_kib_per_dispatch"],
+                                             rec["write_kib_per_dispatch"]))
+        f.write("%-28s %14.1f %14.1f\n" % ("copy (%d MiB)" % COPY_MIB, rec["copy_fetch_kib"],
+                                             rec["copy_write_kib"]))
+        f.write("scaled bytes per launch: fetch %.4g, write %.4g, total %.4g\n"
+                % (fetch_b, write_b, fetch_b + write_b))
+        f.write(json.dumps(rec) + "\n")
+    return rec
+
+
+def summarize_stats(run_dir, out_name, command):
+    """Short text copy of a rocprofv3 --kernel-trace --stats run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under " + run_dir)
+    rows = list(csv.DictReader(open(files[0])))
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, out_name), "w") as f:
+        f.write("rocprofv3 kernel statistics\ncommand: %s\n" % command)
+        f.write("%-44s %6s %12s %12s %12s %12s %7s\n" % ("kernel", "calls", "total_us", "avg_us",
+                                                         "min_us", "max_us", "pct"))
+        for r in rows:
+            f.write("%-44s %6s %12.1f %12.2f %12.2f %12.2f %7.2f\n" % (
+                r["Name"][:44], r["Calls"], float(r["TotalDurationNs"]) / 1e3,
+                float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                float(r["Percentage"])))
+
+
+def copy_calibration():
+    """One plain device copy of COPY_MIB MiB (its counters scale FETCH_SIZE/WRITE_SIZE)."""
+    import torch
+    from hils_inputs.device import device_copy
+    src = torch.empty(COPY_MIB * 2 ** 20, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    device_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 # --------------------------------------------------------------------------- runners
@@ -174,7 +306,8 @@ def run_prefill(hl, cfg, steps, warmup, ev):
     res = dict(value=flops / (ms * 1e-3) / 1e12, unit="TFLOP/s", ms_per_step=ms,
                roofline=dict(bound="mfma", kernel=kern, kernel_ms=kms, launches=n,
                              achieved=attn_flops / (kms * 1e-3) / 1e12, peak=PEAK_BF16_TFLOPS,
-                             unit="TFLOP/s", traffic=None,
+                             unit="TFLOP/s",
+                             traffic=recorded_traffic(kern, cfg.get("name", "")),
                              per_launch_flops=attn_flops))
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_BF16_TFLOPS
     del dev
@@ -210,7 +343,8 @@ def run_decode(hl, cfg, steps, warmup, ev, nsets):
     res = dict(value=total / (ms * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms, bytes_per_step=total,
                roofline=dict(bound="hbm", kernel=kern, kernel_ms=kms, launches=n,
                              achieved=kbytes / (kms * 1e-3) / 1e9, peak=PEAK_HBM_GBS, unit="GB/s",
-                             traffic=None, per_launch_bytes=kbytes))
+                             traffic=recorded_traffic(kern, cfg.get("name", "")),
+                             per_launch_bytes=kbytes))
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBS
     res["frac_of_hbm_peak"] = res["value"] / PEAK_HBM_GBS
     del sets, outs
@@ -277,7 +411,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", default=None, help="run one workload: prefill_8k, decode_128k, "
                                                      "decode_4m, train_8k, prefill_32k")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain %d MiB device copy (HBM counter calibration)" % COPY_MIB)
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/<kernel>_<workload>_traffic.txt from two --pmc runs")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("RUN_DIR", "OUT_NAME"),
+                    help="write profiles/OUT_NAME from a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--command", action="append", default=[],
+                    help="the profiling command(s) a summary records")
     args = ap.parse_args()
+    if args.traffic_summary:
+        k, w, fd, wd = args.traffic_summary
+        print(json.dumps(summarize_traffic(k, w, fd, wd, args.command)))
+        return
+    if args.stats_summary:
+        summarize_stats(args.stats_summary[0], args.stats_summary[1], " ; ".join(args.command))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
@@ -343,6 +492,8 @@ def main():
                 "data": "synthetic", "config": {"workload": r["workload"]},
                 "roofline": r.get("roofline")}
     line["extra"] = extra
+    if args.calibrate_copy:
+        copy_calibration()
     if not args.no_cpu and main_name is not None:
         log("cpu baseline: oracle on a sample (~%.0f s)" % args.cpu_seconds)
         line["cpu_baseline"] = cpu_baseline(config(main_name), args.cpu_seconds)

@@ -41,7 +41,7 @@ CONFIGS = {
 
 
 def config(name, **overrides):
-    cfg = dict(CONFIGS[name])
+    cfg = dict(CONFIGS[name], name=name)
     cfg.update(overrides)
     if "Lq" not in overrides and cfg["Lq"] != 1 and "Lkv" in overrides:
         cfg["Lq"] = cfg["Lkv"]

@@ -27,6 +27,9 @@ def _fill_lib():
             ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
             ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         _lib.hils_inputs_fill_normal.restype = ctypes.c_int
+        _lib.hils_inputs_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                          ctypes.c_void_p]
+        _lib.hils_inputs_copy.restype = ctypes.c_int
     return _lib
 
 
@@ -49,6 +52,18 @@ def fill_normal(t, seed, tid_name, offset=0, scale=1.0):
     if rc != 0:
         raise RuntimeError("device fill failed")
     return t
+
+
+def device_copy(dst, src):
+    """dst[:] = src[:] for contiguous device tensors of equal byte size (plain copy kernel)."""
+    assert dst.is_contiguous() and src.is_contiguous()
+    nb = src.numel() * src.element_size()
+    assert nb == dst.numel() * dst.element_size()
+    st = torch.cuda.current_stream().cuda_stream
+    if _fill_lib().hils_inputs_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                    nb, ctypes.c_void_p(st)) != 0:
+        raise RuntimeError("device copy failed")
+    return dst
 
 
 def make_device_inputs(cfg, device="cuda", host=None):

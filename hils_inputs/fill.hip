@@ -75,3 +75,21 @@ extern "C" int hils_inputs_fill_normal(void* dst, uint64_t n, uint64_t seed, uin
                        inv_sd, scale, scaled);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
+
+// Plain device copy of whole 16-byte words (grid-stride).  Its HBM byte counters
+// are the calibration for the per-kernel traffic figures: it reads and writes
+// exactly 16 * n bytes.
+__global__ void copy_u4(const uint4* __restrict__ src, uint4* __restrict__ dst, uint64_t n) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
+}
+
+extern "C" int hils_inputs_copy(void* dst, const void* src, uint64_t bytes, void* stream) {
+  if (bytes % 16 != 0 || ((uintptr_t)dst | (uintptr_t)src) % 16 != 0) return 1;
+  const uint64_t n = bytes / 16;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(copy_u4, dim3(4096), dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
+                     (uint4*)dst, n);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
