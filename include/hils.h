@@ -40,7 +40,8 @@
  * patterns); arithmetic is fp32. HILS_F32: all of them fp32.
  *
  * Ownership and concurrency: every pointer is a device pointer owned by the
- * caller.  The library allocates nothing and keeps no mutable global state;
+ * caller.  The library allocates nothing and shares no mutable state between
+ * threads (the last-error message and the profiling hook are per calling thread);
  * scratch memory is the caller's `ws` buffer of at least
  * hils_workspace_size() bytes (256-byte aligned).  Work is enqueued on
  * `stream` (a hipStream_t; NULL = the default stream) and never synchronised;
