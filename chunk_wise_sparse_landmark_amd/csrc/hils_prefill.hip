@@ -277,38 +277,49 @@ __device__ __forceinline__ void stage_async(const uint16_t* src, uint4* dst) {
 }
 __device__ __forceinline__ void stage_wait() { __builtin_amdgcn_s_waitcnt(0); }
 
-struct ChunkRegs {
-  bf16x8 k[16];   // K fragments (mt*4 + ks)
-  bf16x8 v[16];   // V fragments (db*2 + ks)
-};
-__device__ __forceinline__ void load_chunk_regs(const uint4* kvb, ChunkRegs& cr) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int f = 0; f < 16; ++f) cr.k[f] = as_bf16x8(kvb[f * kWave + lane]);
-#pragma unroll
-  for (int f = 0; f < 16; ++f) cr.v[f] = as_bf16x8(kvb[(16 + f) * kWave + lane]);
+// max(a, b) in one v_med3_f32 (no NaN quieting of the MFMA outputs needed:
+// the inputs are finite logits or -inf)
+__device__ __forceinline__ float fmax2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+}
+// reductions over the four lanes l, l^16, l^32, l^48 (one MFMA row) with the
+// lane-swap VALU instructions instead of LDS permutes
+__device__ __forceinline__ float rowgroup_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmax2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto c = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmax2(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto c = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// One query block against one chunk (fragments in registers).  Row r16 of the
-// block = (query 4*blk + r16/4, head r16%4).  kMasked: keys >= vis are hidden
-// (own chunk).  kStatsOnly: return the row max (in log2 units) and sum;
-// otherwise accumulate (rw / rowsum) * P V into o (rw = the row's fusion
-// weight; 0 removes the row).  sc2 = scale * log2(e): exponentials are exp2 of
-// one fused multiply-add per logit.
-template <bool kMasked, bool kStatsOnly>
-__device__ __forceinline__ void block_chunk(const ChunkRegs& cr, const bf16x8 (&qf)[4], float sc2,
-                                            int vis, float rw, f32x4 (&o)[8], float& m_out,
-                                            float& z_out) {
-  const int lane = lane_id();
-  const int g4 = lane >> 4;
-  f32x4 s[4];
+// S^T = K Q^T of one block: 64 keys x 16 rows; lane l holds keys
+// 16mt + 4(l/16) + i of row l%16.
+__device__ __forceinline__ void block_scores(const bf16x8 (&kf)[16], const bf16x8 (&qf)[4],
+                                             f32x4 (&s)[4]) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma(cr.k[mt * 4 + ks], qf[ks], acc);
+    for (int ks = 0; ks < 4; ++ks) acc = mfma(kf[mt * 4 + ks], qf[ks], acc);
     s[mt] = acc;
   }
+}
+
+// Chunk softmax of one block in place: s <- exp2(sc2*s - m); returns the row
+// max m (log2 units) and the row sum z.  kMasked hides keys >= vis.
+template <bool kMasked>
+__device__ __forceinline__ void block_softmax(f32x4 (&s)[4], float sc2, int vis, float& m_out,
+                                              float& z_out) {
+  const int g4 = lane_id() >> 4;
   if (kMasked) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -316,12 +327,11 @@ __device__ __forceinline__ void block_chunk(const ChunkRegs& cr, const bf16x8 (&
       for (int i = 0; i < 4; ++i)
         if (mt * 16 + g4 * 4 + i >= vis) s[mt][i] = -INFINITY;
   }
-  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+  float mx = fmax2(fmax2(s[0][0], s[0][1]), fmax2(s[0][2], s[0][3]));
 #pragma unroll
   for (int mt = 1; mt < 4; ++mt)
-    mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = fmax2(mx, fmax2(fmax2(s[mt][0], s[mt][1]), fmax2(s[mt][2], s[mt][3])));
+  mx = rowgroup_max(mx);
   const float mb = mx * sc2;
   float z = 0.f;
 #pragma unroll
@@ -332,16 +342,13 @@ __device__ __forceinline__ void block_chunk(const ChunkRegs& cr, const bf16x8 (&
       s[mt][i] = e;
       z += e;
     }
-  z += __shfl_xor(z, 16, kWave);
-  z += __shfl_xor(z, 32, kWave);
-  if (kStatsOnly) {
-    m_out = mb;
-    z_out = z;
-    return;
-  }
-  const float f = rw / z;
-  // P as the A operand of O += P V: k-slot (g4, j) <-> key 32ks + 16(j/4) + 4g4 + j%4
-  bf16x8 pa[2];
+  m_out = mb;
+  z_out = rowgroup_sum(z);
+}
+
+// P (scaled by f) as the A operand of O += P V: k-slot (g4, j) <-> key
+// 32ks + 16(j/4) + 4g4 + j%4, which is how S^T left the keys in the lane.
+__device__ __forceinline__ void pack_p(const f32x4 (&s)[4], float f, bf16x8 (&pa)[2]) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     uint32_t w4[4];
@@ -351,10 +358,52 @@ __device__ __forceinline__ void block_chunk(const ChunkRegs& cr, const bf16x8 (&
     w4[3] = pack_bf16x2(s[2 * ks + 1][2] * f, s[2 * ks + 1][3] * f);
     __builtin_memcpy(&pa[ks], w4, 16);
   }
+}
+
+__device__ __forceinline__ void load_frags(const uint4* src, bf16x8 (&f)[16]) {
+  const int lane = lane_id();
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int x = 0; x < 16; ++x) f[x] = as_bf16x8(src[x * kWave + lane]);
+}
+
+// One staged chunk against the wave's four query blocks, in phases so the
+// MFMA work of one block overlaps the softmax of another: S^T of every active
+// block, then the softmaxes, then O += (rw / z) P V.  `act` has bit j set when
+// block j takes part (uniform over the wave); rw[j] is this lane's row weight.
+template <bool kMasked>
+__device__ __forceinline__ void chunk_step(const uint4* kvb, const bf16x8 (&qf)[kBlocksPerWave][4],
+                                           float sc2, unsigned act, const int (&vis)[kBlocksPerWave],
+                                           const float (&rw)[kBlocksPerWave],
+                                           f32x4 (&o)[kBlocksPerWave][8]) {
+  f32x4 s[kBlocksPerWave][4];
+  {
+    bf16x8 kf[16];
+    load_frags(kvb, kf);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) o[db] = mfma(pa[ks], cr.v[db * 2 + ks], o[db]);
+    for (int j = 0; j < kBlocksPerWave; ++j)
+      if (act & (1u << j)) block_scores(kf, qf[j], s[j]);
+  }
+  bf16x8 pa[kBlocksPerWave][2];
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j) {
+    if (act & (1u << j)) {
+      float m, z;
+      block_softmax<kMasked>(s[j], sc2, vis[j], m, z);
+      pack_p(s[j], rw[j] * __builtin_amdgcn_rcpf(z), pa[j]);
+    }
+  }
+  // keep the V fragment loads after the softmax (register pressure)
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 vf[16];
+  load_frags(kvb + 16 * kWave, vf);
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j)
+    if (act & (1u << j)) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) o[j][db] = mfma(pa[j][ks], vf[db * 2 + ks], o[j][db]);
+    }
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -459,15 +508,16 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   // ---- own chunk, pass 1: lse of the visible tokens (key kk visible to query
   //      qi when kk <= qi, as the window is the chunk)
   const float sc2 = scale * 1.4426950408889634f;   // scale * log2(e)
-  ChunkRegs cr;
   if (g.keep_own) {
-    load_chunk_regs(sm.kv[0], cr);
+    bf16x8 kf[16];
+    load_frags(sm.kv[0], kf);
 #pragma unroll
     for (int j = 0; j < kBlocksPerWave; ++j) {
       const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2);
+      f32x4 st[4];
       float m2, z;
-      f32x4 unused[8];
-      block_chunk<true, true>(cr, qf[j], sc2, qi + 1, 0.f, unused, m2, z);
+      block_scores(kf, qf[j], st);
+      block_softmax<true>(st, sc2, qi + 1, m2, z);
       // natural-log lse of the visible tokens: (m2 + log2 z) * ln 2
       if (lane < 16) sm.lseown[qi * kG + (r16 & 3)] = (m2 + __log2f(z)) * 0.6931471805599453f;
     }
@@ -492,34 +542,41 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   }
   __syncthreads();
 
-  // ---- chunk loop: step 0 is the own chunk (if kept), then the union.  The
-  //      next chunk is loaded into registers while this one is computed.
-  const int nsteps = nunion + (g.keep_own ? 1 : 0);
-  for (int stp = 0; stp < nsteps; ++stp) {
-    const int cur = stp & 1;
-    const bool is_own = g.keep_own && stp == 0;
-    const int uidx = stp - (g.keep_own ? 1 : 0);
-    const int c = is_own ? own : sm.ulist[uidx];
-    const bool more = stp + 1 < nsteps;
-    if (more) stage_async(KVg + (size_t)sm.ulist[uidx + 1] * kChunkElems, sm.kv[cur ^ 1]);
-    const uint64_t qmk = is_own ? ~0ull : sm.qmask[c];
-    load_chunk_regs(sm.kv[cur], cr);
+  // ---- the own chunk (staged in buffer 0), then the union; the next chunk is
+  //      copied into the other buffer while one is computed
+  int cur = 0;
+  if (g.keep_own) {
+    if (nunion > 0) stage_async(KVg + (size_t)sm.ulist[0] * kChunkElems, sm.kv[1]);
+    int vis[kBlocksPerWave];
+    float rw[kBlocksPerWave];
+#pragma unroll
+    for (int j = 0; j < kBlocksPerWave; ++j) {
+      const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2);
+      vis[j] = qi + 1;                       // key kk of the chunk visible when kk <= qi
+      rw[j] = sm.wown[qi * kG + (r16 & 3)];
+    }
+    chunk_step<true>(sm.kv[0], qf, sc2, (1u << kBlocksPerWave) - 1, vis, rw, o);
+    stage_wait();
+    __syncthreads();
+    cur = 1;
+  }
+  for (int u = 0; u < nunion; ++u, cur ^= 1) {
+    const int c = sm.ulist[u];
+    if (u + 1 < nunion) stage_async(KVg + (size_t)sm.ulist[u + 1] * kChunkElems, sm.kv[cur ^ 1]);
+    const uint64_t qmk = sm.qmask[c];
+    unsigned act = 0;
+    int vis[kBlocksPerWave];
+    float rw[kBlocksPerWave];
 #pragma unroll
     for (int j = 0; j < kBlocksPerWave; ++j) {
       const int blk = w * kBlocksPerWave + j;
-      if (((qmk >> (blk * 4)) & 0xfull) == 0) continue;      // no query of the block selected c
-      const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
-      float rw;
-      if (is_own) {
-        rw = sm.wown[qi * kG + h];
-      } else {
-        const int slot = sm.slotmap[qi * kMaxNC + c];
-        rw = slot != 0xff ? sm.wts[(qi * K + slot) * kG + h] : 0.f;
-      }
-      float m, z;
-      if (is_own) block_chunk<true, false>(cr, qf[j], sc2, qi + 1, rw, o[j], m, z);
-      else block_chunk<false, false>(cr, qf[j], sc2, kS, rw, o[j], m, z);
+      if ((qmk >> (blk * 4)) & 0xfull) act |= 1u << j;    // some query of the block selected c
+      const int qi = blk * 4 + (r16 >> 2);
+      const int slot = sm.slotmap[qi * kMaxNC + c];
+      vis[j] = kS;
+      rw[j] = slot != 0xff ? sm.wts[(qi * K + slot) * kG + (r16 & 3)] : 0.f;
     }
+    chunk_step<false>(sm.kv[cur], qf, sc2, act, vis, rw, o);
     stage_wait();
     __syncthreads();
   }
