@@ -43,10 +43,12 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kD = 128;
 constexpr int kS = 64;
 constexpr int kG = 4;            // query heads per KV group on this path
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;            // prefill_select
+constexpr int kAttWaves = 8;             // prefill_attend: two waves per SIMD
+constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kWin = 64;         // queries per window (one chunk), both kernels
 constexpr int kBlocks = kWin / 4;          // 16 query blocks of 4 queries
-constexpr int kBlocksPerWave = kBlocks / 4;
+constexpr int kBlocksPerWave = kBlocks / kAttWaves;
 constexpr int kMaxKf = 32;       // top-K bound on this path
 constexpr int kMaxNC = 256;      // chunks bound on this path (L <= 16384)
 constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
@@ -260,7 +262,7 @@ struct AttendSmem {
   uint16_t ulist[kMaxNC];
   float lseown[kWin * kG];
   float wown[kWin * kG];
-  int wcount[4];
+  int wcount[kAttWaves];
 };
 
 // Start copying one chunk's 32 KB of fragments into an LDS buffer with direct
@@ -270,9 +272,9 @@ __device__ __forceinline__ void stage_async(const uint16_t* src, uint4* dst) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
   const int wbase = (threadIdx.x / kWave) * kWave;
 #pragma unroll
-  for (int x = 0; x < 8; ++x)
-    __builtin_amdgcn_global_load_lds((const void*)(s + x * kThreads + threadIdx.x),
-                                     (__attribute__((address_space(3))) void*)(dst + x * kThreads + wbase),
+  for (int x = 0; x < kChunkFrags * kWave / kAttThreads; ++x)
+    __builtin_amdgcn_global_load_lds((const void*)(s + x * kAttThreads + threadIdx.x),
+                                     (__attribute__((address_space(3))) void*)(dst + x * kAttThreads + wbase),
                                      16, 0, 0);
 }
 __device__ __forceinline__ void stage_wait() { __builtin_amdgcn_s_waitcnt(0); }
@@ -406,7 +408,7 @@ __device__ __forceinline__ void chunk_step(const uint4* kvb, const bf16x8 (&qf)[
     }
 }
 
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kAttThreads)
 prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kvf,
                const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
                const int32_t* __restrict__ sel_idx, uint16_t* __restrict__ out,
@@ -432,13 +434,13 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const float scale = g.scale;
 
   // ---- setup: selections, chunk -> query masks, union list
-  for (int x = tid; x < kWin * K; x += kThreads)
+  for (int x = tid; x < kWin * K; x += kAttThreads)
     sm.sel[x] = sel_idx[((size_t)bkv * g.Lq + i0 + x / K) * K + x % K];
-  for (int x = tid; x < kWin * kMaxNC / 4; x += kThreads)
+  for (int x = tid; x < kWin * kMaxNC / 4; x += kAttThreads)
     reinterpret_cast<uint32_t*>(sm.slotmap)[x] = 0xffffffffu;
-  for (int c = tid; c < kMaxNC; c += kThreads) sm.qmask[c] = 0ull;
+  for (int c = tid; c < kMaxNC; c += kAttThreads) sm.qmask[c] = 0ull;
   __syncthreads();
-  for (int x = tid; x < kWin * K; x += kThreads) {
+  for (int x = tid; x < kWin * K; x += kAttThreads) {
     const int c = sm.sel[x];
     if (c >= 0) {
       atomicOr((unsigned long long*)&sm.qmask[c], 1ull << (x / K));
@@ -456,7 +458,8 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int x = 0; x < w; ++x) off += sm.wcount[x];
     if (f) sm.ulist[off + mask_rank(m)] = (uint16_t)c;
   }
-  const int nunion = sm.wcount[0] + sm.wcount[1] + sm.wcount[2] + sm.wcount[3];
+  int nunion = 0;
+  for (int x = 0; x < kAttWaves; ++x) nunion += sm.wcount[x];
 
   // Q fragments of this wave's four blocks (B operand of S^T, also the A operand
   // of the retrieval scores): row r16 = (query 4*blk + r16/4, head r16%4)
@@ -524,8 +527,8 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   }
   __syncthreads();
   // ---- fusion weights: LSE over the retrieval scores and the own chunk's lse
-  {
-    const int qi = tid >> 2, h = tid & 3;     // 256 threads = 64 queries x 4 heads
+  if (tid < kWin * kG) {
+    const int qi = tid >> 2, h = tid & 3;     // 64 queries x 4 heads
     const float lo = g.keep_own ? sm.lseown[tid] : -INFINITY;
     float m = lo;
     for (int slot = 0; slot < K; ++slot)
@@ -631,7 +634,7 @@ hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, 
   hipFuncSetAttribute((const void*)prefill_attend, hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)sizeof(AttendSmem));
   prof_begin(kPrefillAttend, st);
-  hipLaunchKernelGGL(prefill_attend, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kThreads),
+  hipLaunchKernelGGL(prefill_attend, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kAttThreads),
                      sizeof(AttendSmem), st, g, Q, kvf, Lm, bias, sel_idx, (uint16_t*)out, lse);
   prof_end(kPrefillAttend, st);
   return hipGetLastError();
