@@ -109,7 +109,8 @@ size_t ws_bytes_for(const hils_params* p, int op) {
     case HILS_OP_DECODE:
       return hils::decode_fast_supported(g, bf16) ? round256(hils::decode_fast_ws(g)) : 0;
     case HILS_OP_BACKWARD:
-      return round256(hils::generic_backward_ws(g));
+      return hils::prefill_bwd_fast_supported(g, bf16) ? round256(hils::prefill_bwd_fast_ws(g))
+                                                       : round256(hils::generic_backward_ws(g));
     default:
       return 0;
   }
@@ -203,6 +204,11 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* k, co
   hils::Geometry g = geometry(p, HILS_OP_BACKWARD);
   const int bf16 = p->dtype == HILS_BF16;
   hipGetLastError();
+  if (hils::prefill_bwd_fast_supported(g, bf16))
+    return launch_status(hils::launch_prefill_bwd_fast(g, q, k, v, lmk, lmk_bias, out, dout, sel_idx,
+                                                       lse, dq, dk, dv, dlmk, dlmk_bias, ws,
+                                                       reinterpret_cast<hipStream_t>(stream)),
+                         "backward launch");
   return launch_status(hils::launch_generic_backward(g, bf16, q, k, v, lmk, lmk_bias, dout, sel_idx,
                                                      dq, dk, dv, dlmk, dlmk_bias, ws,
                                                      reinterpret_cast<hipStream_t>(stream)),

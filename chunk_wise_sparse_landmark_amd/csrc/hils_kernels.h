@@ -32,4 +32,13 @@ hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, 
                                const void* lmk, const float* bias, void* out, int32_t* sel_idx,
                                float* lse, void* ws, hipStream_t st);
 
+// MFMA prefill backward (same shapes as the MFMA forward)
+bool prefill_bwd_fast_supported(const Geometry& g, int bf16);
+size_t prefill_bwd_fast_ws(const Geometry& g);
+hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void* k, const void* v,
+                                   const void* lmk, const float* bias, const void* out,
+                                   const void* dout, const int32_t* sel_idx, const float* lse,
+                                   void* dq, void* dk, void* dv, void* dlmk, float* dbias,
+                                   void* ws, hipStream_t st);
+
 }  // namespace hils

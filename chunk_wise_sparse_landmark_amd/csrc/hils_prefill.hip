@@ -28,17 +28,13 @@
 //     the own chunk is attended first, so every fusion weight is final before
 //     any chunk is accumulated.  Chunk fragments are double-buffered in LDS:
 //     one barrier per chunk.
-#include "hils_common.h"
+#include "hils_mfma.h"
 #include "hils_kernels.h"
 #include "hils_profile.h"
 
 namespace hils {
 
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kD = 128;
 constexpr int kS = 64;
@@ -54,31 +50,6 @@ constexpr int kMaxNC = 256;      // chunks bound on this path (L <= 16384)
 constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
 constexpr int kChunkFrags = 32;            // 16 K + 16 V fragments per chunk
 constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
-
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, 16);
-  return r;
-}
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, 16);
-  return r;
-}
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-// two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // ----------------------------------------------------------------------------
 // Top-K of R keys per lane (candidate c = r*64 + lane), written as ascending
@@ -278,30 +249,6 @@ __device__ __forceinline__ void stage_async(const uint16_t* src, uint4* dst) {
                                      16, 0, 0);
 }
 __device__ __forceinline__ void stage_wait() { __builtin_amdgcn_s_waitcnt(0); }
-
-// max(a, b) in one v_med3_f32 (no NaN quieting of the MFMA outputs needed:
-// the inputs are finite logits or -inf)
-__device__ __forceinline__ float fmax2(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
-}
-// reductions over the four lanes l, l^16, l^32, l^48 (one MFMA row) with the
-// lane-swap VALU instructions instead of LDS permutes
-__device__ __forceinline__ float rowgroup_max(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmax2(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t v = __float_as_uint(x);
-  const auto c = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return fmax2(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float rowgroup_sum(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t v = __float_as_uint(x);
-  const auto c = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
 
 // S^T = K Q^T of one block: 64 keys x 16 rows; lane l holds keys
 // 16mt + 4(l/16) + i of row l%16.

@@ -1,0 +1,765 @@
+// MFMA backward of the prefill path: bf16, head_dim 128, chunk 64, GQA group
+// of 4, causal, seq_q == seq_kv (the shapes the MFMA forward covers).
+//
+// Method: Hierarchical Sparse Attention Done Right (arXiv 2607.02980v1, summary
+// page), §3 "Hierarchical softmax" (gradients of the LM loss reach the chunk
+// retrieval scores through the fusion weights) and §9 (unselected chunks get no
+// gradient).  With the selection fixed, for a query row with fusion weights w_c
+// (w_c = exp(s_c - LSE), s_own = lse_own) and chunk softmaxes p:
+//   D   = <dO, O>,  u_j = <dO, v_j>,  D_c = sum_j p_j u_j
+//   retrieved chunk: dl_j = w_c p_j (u_j - D_c),  ds_c = w_c (D_c - D)
+//   own chunk:       dl_j = w_own p_j (u_j - D)
+//   dq = scale (sum_j dl_j k_j + sum_c ds_c lmk_c),  dk_j += scale dl_j q,
+//   dv_j += w p_j dO,  dlmk_c += scale ds_c q,  dbias_c += ds_c.
+//
+// Three launches:
+//  1. prefill_bwd_prep    per (b, kv head, 64-query window): the window's
+//     chunk of K and V in operand-fragment order, q and dO with the four heads
+//     interleaved per dimension, D per row, and the (query, chunk) -> slot map
+//     with per-window query masks.
+//  2. prefill_bwd_rows    per window (like the forward's attention kernel):
+//     for every chunk of the window's union, S^T = K Q^T and U^T = V dO^T by
+//     MFMA, the chunk softmax, D_c, dl, and dQ += dL K in MFMA accumulators;
+//     each (row, slot)'s (w, log2 lse_c, D_c) goes to a table; after the loop
+//     dq gains scale * sum ds_c lmk_c.
+//  3. prefill_bwd_chunks  per (b, kv head, chunk): gathers the queries that
+//     selected the chunk (and the chunk's own window) in tiles of 8 queries x
+//     4 heads = 32 rows, recomputes S = Q K^T and U = dO V^T for the wave's 16
+//     keys, turns them into w p and dl with the row table (no reductions), and
+//     accumulates dV += (w P)^T dO and dK += dL^T Q by MFMA over the rows, plus
+//     dlmk and dbias.  Each chunk is owned by one workgroup: no atomics.
+#include "hils_mfma.h"
+#include "hils_kernels.h"
+#include "hils_profile.h"
+
+namespace hils {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kS = 64;
+constexpr int kG = 4;
+constexpr int kWin = 64;
+constexpr int kMaxKb = 32;
+constexpr int kMaxNCb = 256;
+constexpr int kMaxL = kMaxNCb * kS;
+constexpr int kFragE = kWave * 8;                  // bf16 per fragment
+constexpr int kBwdFrags = 48;                      // K (A), V (A), K (B, P order)
+constexpr int kBwdChunkElems = kBwdFrags * kFragE; // 48 KB per chunk
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = kRowWaves * kWave;
+constexpr int kRowBlocks = kWin / 4 / kRowWaves;   // query blocks per wave
+constexpr int kPrepThreads = 256;
+constexpr int kChunkThreads = 256;
+
+struct BwdWs {
+  uint16_t* frags;   // [bkv][NC][48 fragments][64 lanes][8]
+  uint16_t* qi;      // [bkv][L][d][4 heads]
+  uint16_t* doi;     // [bkv][L][d][4 heads]
+  float* Drow;       // [B][Hq][L]
+  float4* stats;     // [B][Hq][L][K+1]: (w, log2 lse_c, D_c (own: D), 0)
+  uint64_t* qm;      // [bkv][NW][NC]: window queries that selected chunk c
+  uint8_t* slot;     // [bkv][L][NC]: slot of chunk c in query i's selection, 0xff if none
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdWs carve(const Geometry& g, void* base, size_t* total) {
+  const size_t nbkv = (size_t)g.B * g.Hkv, L = g.Lq, NW = L / kWin;
+  size_t off = 0;
+  char* c = reinterpret_cast<char*>(base);
+  BwdWs w;
+  w.frags = reinterpret_cast<uint16_t*>(c + off);
+  off += align256(nbkv * g.NC * kBwdChunkElems * 2);
+  w.qi = reinterpret_cast<uint16_t*>(c + off);
+  off += align256(nbkv * L * kD * kG * 2);
+  w.doi = reinterpret_cast<uint16_t*>(c + off);
+  off += align256(nbkv * L * kD * kG * 2);
+  w.Drow = reinterpret_cast<float*>(c + off);
+  off += align256((size_t)g.B * g.Hq * L * 4);
+  w.stats = reinterpret_cast<float4*>(c + off);
+  off += align256((size_t)g.B * g.Hq * L * (g.K + 1) * 16);
+  w.qm = reinterpret_cast<uint64_t*>(c + off);
+  off += align256(nbkv * NW * g.NC * 8);
+  w.slot = reinterpret_cast<uint8_t*>(c + off);
+  off += align256(nbkv * L * g.NC);
+  if (total) *total = off;
+  return w;
+}
+
+// ----------------------------------------------------------------------------
+// 1. prep
+//    fragment f, lane l, element j:
+//      f <  16 (mt*4+ks):   K[16mt + l%16][32ks + 8(l/16) + j]   A of S^T = K Q^T
+//      f <  32 (16+mt*4+ks): V, same                              A of U^T = V dO^T
+//      f <  48 (32+db*2+ks): K[32ks + 16(j/4) + 4(l/16) + j%4][16db + l%16]
+//                            B of dQ = dL K, keys in the order dL leaves S^T
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(kPrepThreads)
+prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                 const uint16_t* __restrict__ v, const uint16_t* __restrict__ out,
+                 const uint16_t* __restrict__ dout, const int32_t* __restrict__ sel_idx,
+                 BwdWs ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks_[kS * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_[kS * kD];
+  __shared__ uint64_t qmask[kMaxNCb];
+  __shared__ uint8_t slots[kWin * kMaxNCb];
+  const int nbkv = g.B * g.Hkv;
+  const int bkv = blockIdx.x % nbkv, win = blockIdx.x / nbkv;
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int tid = threadIdx.x;
+  const int L = g.Lq, NW = L / kWin;
+  const size_t row0 = (size_t)bkv * L + (size_t)win * kS;
+  for (int x = tid; x < kS * kD / 8; x += kPrepThreads) {
+    reinterpret_cast<uint4*>(ks_)[x] = reinterpret_cast<const uint4*>(k + row0 * kD)[x];
+    reinterpret_cast<uint4*>(vs_)[x] = reinterpret_cast<const uint4*>(v + row0 * kD)[x];
+  }
+  for (int c = tid; c < kMaxNCb; c += kPrepThreads) qmask[c] = 0ull;
+  for (int x = tid; x < kWin * kMaxNCb / 4; x += kPrepThreads)
+    reinterpret_cast<uint32_t*>(slots)[x] = 0xffffffffu;
+  __syncthreads();
+
+  uint16_t* fd = ws.frags + ((size_t)bkv * g.NC + win) * kBwdChunkElems;
+  for (int e = tid; e < kBwdFrags * kWave; e += kPrepThreads) {
+    const int f = e / kWave, l = e % kWave;
+    uint4 val;
+    if (f < 32) {
+      const uint16_t* src = f < 16 ? ks_ : vs_;
+      const int mt = (f % 16) / 4, kk = f % 4;
+      val = *reinterpret_cast<const uint4*>(src + (16 * mt + l % 16) * kD + 32 * kk + 8 * (l / 16));
+    } else {
+      const int db = (f - 32) / 2, kk = (f - 32) % 2;
+      uint32_t wd[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        uint32_t h2[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int j = jj * 2 + x;
+          const int key = 32 * kk + 16 * (j / 4) + 4 * (l / 16) + (j % 4);
+          h2[x] = ks_[key * kD + 16 * db + (l % 16)];
+        }
+        wd[jj] = h2[0] | (h2[1] << 16);
+      }
+      val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    reinterpret_cast<uint4*>(fd)[e] = val;
+  }
+
+  // q and dO with the heads interleaved: xi[bkv][i][d][h]
+  for (int e = tid; e < 2 * kWin * (kD / 8); e += kPrepThreads) {
+    const int which = e / (kWin * (kD / 8)), r = e % (kWin * (kD / 8));
+    const int qq = r / (kD / 8), dg = r % (kD / 8);
+    const int i = win * kWin + qq;
+    const uint16_t* src = which ? dout : q;
+    uint16_t* dst = (which ? ws.doi : ws.qi) + (((size_t)bkv * L + i) * kD + dg * 8) * kG;
+    uint16_t hv[kG][8];
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+      const uint4 u = *reinterpret_cast<const uint4*>(
+          src + ((size_t)(b * g.Hq + kvh * kG + h) * L + i) * kD + dg * 8);
+      __builtin_memcpy(hv[h], &u, 16);
+    }
+    uint32_t o[16];
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      o[2 * dd] = hv[0][dd] | ((uint32_t)hv[1][dd] << 16);
+      o[2 * dd + 1] = hv[2][dd] | ((uint32_t)hv[3][dd] << 16);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      reinterpret_cast<uint4*>(dst)[x] = make_uint4(o[4 * x], o[4 * x + 1], o[4 * x + 2], o[4 * x + 3]);
+  }
+
+  // D = <dO, O> per (query, head)
+  {
+    const int qq = tid >> 2, h = tid & 3;
+    const size_t row = (size_t)(b * g.Hq + kvh * kG + h) * L + win * kWin + qq;
+    const uint4* po = reinterpret_cast<const uint4*>(out + row * kD);
+    const uint4* pd = reinterpret_cast<const uint4*>(dout + row * kD);
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < kD / 8; ++x) {
+      const uint4 a = po[x], c = pd[x];
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += __uint_as_float(aw[e] << 16) * __uint_as_float(cw[e] << 16);
+        acc += __uint_as_float(aw[e] & 0xffff0000u) * __uint_as_float(cw[e] & 0xffff0000u);
+      }
+    }
+    ws.Drow[row] = acc;
+  }
+
+  // selection masks and slots of this window's queries
+  for (int x = tid; x < kWin * g.K; x += kPrepThreads) {
+    const int qq = x / g.K, s = x % g.K;
+    const int c = sel_idx[((size_t)bkv * L + win * kWin + qq) * g.K + s];
+    if (c >= 0) {
+      atomicOr((unsigned long long*)&qmask[c], 1ull << qq);
+      slots[qq * kMaxNCb + c] = (uint8_t)s;
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < g.NC; c += kPrepThreads)
+    ws.qm[((size_t)bkv * NW + win) * g.NC + c] = qmask[c];
+  for (int x = tid; x < kWin * g.NC; x += kPrepThreads) {
+    const int qq = x / g.NC, c = x % g.NC;
+    ws.slot[((size_t)bkv * L + win * kWin + qq) * g.NC + c] = slots[qq * kMaxNCb + c];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 2. rows: dq and the per-(row, slot) table
+// ----------------------------------------------------------------------------
+struct RowsSmem {
+  uint4 kv[2][kBwdFrags * kWave];     // 2 x 48 KB of chunk fragments
+  float wts[kWin * kMaxKb * kG];      // (query, slot, head): weight, then ds
+  uint8_t slotmap[kWin * kMaxNCb];    // (query, chunk) -> slot
+  int sel[kWin * kMaxKb];
+  uint64_t qmask[kMaxNCb];
+  uint16_t ulist[kMaxNCb];
+  float Dr[kWin * kG];
+  float LSE2[kWin * kG];              // forward LSE in log2 units
+  int wcount[kRowWaves];
+};
+
+__device__ __forceinline__ void stage48(const uint16_t* src, uint4* dst) {
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  const int wbase = (threadIdx.x / kWave) * kWave;
+#pragma unroll
+  for (int x = 0; x < kBwdFrags * kWave / kRowThreads; ++x)
+    __builtin_amdgcn_global_load_lds((const void*)(s + x * kRowThreads + threadIdx.x),
+                                     (__attribute__((address_space(3))) void*)(dst + x * kRowThreads + wbase),
+                                     16, 0, 0);
+}
+
+__device__ __forceinline__ void stage_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ void load16(const uint4* src, bf16x8 (&f)[16]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int x = 0; x < 16; ++x) f[x] = as_bf16x8(src[x * kWave + lane]);
+}
+
+// X^T = F Y^T for one block: F fragments (A, 64 keys) against the block's B
+// fragments; lane l gets keys 16mt + 4(l/16) + i of row l%16.
+__device__ __forceinline__ void keys_by_rows(const bf16x8 (&f)[16], const bf16x8 (&y)[4],
+                                             f32x4 (&x)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma(f[mt * 4 + ks], y[ks], acc);
+    x[mt] = acc;
+  }
+}
+
+// dl (scaled values as bf16) in the A layout of dQ = dL K: k-slot (g4, j) <->
+// key 32ks + 16(j/4) + 4g4 + j%4.
+__device__ __forceinline__ void pack_keys(const f32x4 (&x)[4], bf16x8 (&pa)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    uint32_t w4[4];
+    w4[0] = pack_bf16x2(x[2 * ks][0], x[2 * ks][1]);
+    w4[1] = pack_bf16x2(x[2 * ks][2], x[2 * ks][3]);
+    w4[2] = pack_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1]);
+    w4[3] = pack_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3]);
+    __builtin_memcpy(&pa[ks], w4, 16);
+  }
+}
+
+// One block against one staged chunk.  kOwn: keys >= vis hidden, D_c := D and
+// the weight is the own chunk's (computed here from its lse).  Returns the row's
+// (w, log2 lse_c, D_c) in lanes l < 16 (and in all lanes of the row group).
+template <bool kOwn>
+__device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)[4],
+                                            const bf16x8 (&df)[4], float sc2, int vis, float w_in,
+                                            float Drow, float lse2_row, f32x4 (&dq)[8]) {
+  const int g4 = lane_id() >> 4;
+  f32x4 s[4], u[4];
+  // one fragment set in registers at a time (the barriers keep the compiler
+  // from hoisting the next set's loads)
+  {
+    bf16x8 f[16];
+    load16(kvb, f);
+    keys_by_rows(f, qf, s);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    bf16x8 f[16];
+    load16(kvb + 16 * kWave, f);
+    keys_by_rows(f, df, u);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (kOwn) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (mt * 16 + g4 * 4 + i >= vis) s[mt][i] = -INFINITY;
+  }
+  float mx = fmax2(fmax2(s[0][0], s[0][1]), fmax2(s[0][2], s[0][3]));
+#pragma unroll
+  for (int mt = 1; mt < 4; ++mt)
+    mx = fmax2(mx, fmax2(fmax2(s[mt][0], s[mt][1]), fmax2(s[mt][2], s[mt][3])));
+  mx = rowgroup_max(mx);
+  const float mb = mx * sc2;
+  float z = 0.f, y = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -mb));
+      s[mt][i] = e;
+      z += e;
+      y = __builtin_fmaf(e, u[mt][i], y);
+    }
+  z = rowgroup_sum(z);
+  y = rowgroup_sum(y);
+  const float rz = __builtin_amdgcn_rcpf(z);
+  const float lse2 = mb + __log2f(z);
+  const float Dc = y * rz;                               // sum_j p_j u_j
+  const float w = kOwn ? __builtin_amdgcn_exp2f(lse2 - lse2_row) : w_in;
+  const float ref = kOwn ? Drow : Dc;
+  const float f = w * rz;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[mt][i] = f * s[mt][i] * (u[mt][i] - ref);   // dl
+  bf16x8 pa[2];
+  pack_keys(s, pa);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 kb[16];
+  load16(kvb + 32 * kWave, kb);
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(pa[ks], kb[db * 2 + ks], dq[db]);
+  return make_float4(w, lse2, kOwn ? Drow : Dc, 0.f);
+}
+
+__global__ void __launch_bounds__(kRowThreads)
+prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
+                 const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
+                 const int32_t* __restrict__ sel_idx, const float* __restrict__ lse,
+                 BwdWs ws, uint16_t* __restrict__ dq_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
+  const int nbkv = g.B * g.Hkv;
+  const int bkv = blockIdx.x % nbkv;
+  const int win = (g.Lq / kWin - 1) - blockIdx.x / nbkv;
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int K = g.K, L = g.Lq;
+  const int i0 = win * kWin, own = win;
+  const int ncand = min(own, g.NC);
+  const uint16_t* Fg = ws.frags + (size_t)bkv * g.NC * kBwdChunkElems;
+  const uint16_t* Lg = lmk + (size_t)bkv * g.NCcap * kD;
+  const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
+  const float scale = g.scale;
+  const float sc2 = scale * 1.4426950408889634f;
+
+  // ---- selection tables and the window's chunk union
+  for (int x = tid; x < kWin * K; x += kRowThreads)
+    sm.sel[x] = sel_idx[((size_t)bkv * L + i0 + x / K) * K + x % K];
+  for (int x = tid; x < kWin * kMaxNCb / 4; x += kRowThreads)
+    reinterpret_cast<uint32_t*>(sm.slotmap)[x] = 0xffffffffu;
+  for (int c = tid; c < kMaxNCb; c += kRowThreads) sm.qmask[c] = 0ull;
+  if (tid < kWin * kG) {
+    const int qq = tid >> 2, h = tid & 3;
+    const size_t row = (size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qq;
+    sm.Dr[tid] = ws.Drow[row];
+    sm.LSE2[tid] = lse[row] * 1.4426950408889634f;
+  }
+  __syncthreads();
+  for (int x = tid; x < kWin * K; x += kRowThreads) {
+    const int c = sm.sel[x];
+    if (c >= 0) {
+      atomicOr((unsigned long long*)&sm.qmask[c], 1ull << (x / K));
+      sm.slotmap[(x / K) * kMaxNCb + c] = (uint8_t)(x % K);
+    }
+  }
+  __syncthreads();
+  {
+    const int c = tid;
+    const bool f = c < ncand && sm.qmask[c] != 0ull;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) sm.wcount[w] = __popcll(m);
+    __syncthreads();
+    int off = 0;
+    for (int x = 0; x < w; ++x) off += sm.wcount[x];
+    if (f) sm.ulist[off + mask_rank(m)] = (uint16_t)c;
+  }
+  int nunion = 0;
+  for (int x = 0; x < kRowWaves; ++x) nunion += sm.wcount[x];
+
+  // B fragments of q and dO of this wave's blocks: row r16 = (query 4*blk + r16/4, head r16%4)
+  bf16x8 qf[kRowBlocks][4], df[kRowBlocks][4];
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) {
+    const int blk = w * kRowBlocks + j;
+    const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
+    const size_t row = ((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * kD + g4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[j][ks] = ld8(q + row + ks * 32);
+      df[j][ks] = ld8(dout + row + ks * 32);
+    }
+  }
+
+  const int first = g.keep_own ? own : (nunion > 0 ? sm.ulist[0] : -1);
+  if (first >= 0) stage48(Fg + (size_t)first * kBwdChunkElems, sm.kv[0]);
+
+  // ---- fusion weights of (row, selected chunk): exp(scale q.lmk + bias - LSE)
+  for (int nt = 0; nt * 16 < nunion; ++nt) {
+    const int uu = nt * 16 + r16;
+    const int c = sm.ulist[uu < nunion ? uu : 0];
+    bf16x8 bl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bl[ks] = ld8(Lg + (size_t)c * kD + g4 * 8 + ks * 32);
+    const float bc = bb ? bb[c] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kRowBlocks; ++j) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma(qf[j][ks], bl[ks], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = g4 * 4 + i;
+        const int qi = (w * kRowBlocks + j) * 4 + (rr >> 2), h = rr & 3;
+        const int slot = uu < nunion ? sm.slotmap[qi * kMaxNCb + c] : 0xff;
+        if (slot != 0xff)
+          sm.wts[(qi * K + slot) * kG + h] = __builtin_amdgcn_exp2f(
+              (scale * acc[i] + bc) * 1.4426950408889634f - sm.LSE2[qi * kG + h]);
+      }
+    }
+  }
+  stage_wait_all();
+  __syncthreads();
+
+  f32x4 dq[kRowBlocks][8];
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) dq[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const size_t srow_stride = (size_t)(K + 1);
+  int cur = 0;
+  if (g.keep_own) {
+    if (nunion > 0) stage48(Fg + (size_t)sm.ulist[0] * kBwdChunkElems, sm.kv[1]);
+#pragma unroll
+    for (int j = 0; j < kRowBlocks; ++j) {
+      const int qi = (w * kRowBlocks + j) * 4 + (r16 >> 2), h = r16 & 3;
+      const float4 st = block_bwd<true>(sm.kv[0], qf[j], df[j], sc2, qi + 1, 0.f,
+                                        sm.Dr[qi * kG + h], sm.LSE2[qi * kG + h], dq[j]);
+      if (lane < 16)
+        ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * srow_stride + K] = st;
+    }
+    stage_wait_all();
+    __syncthreads();
+    cur = 1;
+  }
+  for (int uidx = 0; uidx < nunion; ++uidx, cur ^= 1) {
+    const int c = sm.ulist[uidx];
+    if (uidx + 1 < nunion) stage48(Fg + (size_t)sm.ulist[uidx + 1] * kBwdChunkElems, sm.kv[cur ^ 1]);
+    const uint64_t qmk = sm.qmask[c];
+#pragma unroll
+    for (int j = 0; j < kRowBlocks; ++j) {
+      const int blk = w * kRowBlocks + j;
+      if (((qmk >> (blk * 4)) & 0xfull) == 0) continue;
+      const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
+      const int slot = sm.slotmap[qi * kMaxNCb + c];
+      const float wv = slot != 0xff ? sm.wts[(qi * K + slot) * kG + h] : 0.f;
+      const float Dr = sm.Dr[qi * kG + h];
+      const float4 st = block_bwd<false>(sm.kv[cur], qf[j], df[j], sc2, kS, wv, Dr, 0.f, dq[j]);
+      if (lane < 16 && slot != 0xff) {
+        ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * srow_stride + slot] = st;
+        sm.wts[(qi * K + slot) * kG + h] = wv * (st.z - Dr);          // ds_c
+      }
+    }
+    stage_wait_all();
+    __syncthreads();
+  }
+
+  // ---- dq += sum_c ds_c lmk_c, then scale; lane holds dQ[row 4*g4 + i][16*db + r16],
+  //      row 4*g4 + i = (query 4*blk + g4, head i)
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) {
+    const int qi = (w * kRowBlocks + j) * 4 + g4;
+    for (int s = 0; s < K; ++s) {
+      const int c = sm.sel[qi * K + s];
+      if (c < 0) continue;
+      float lv[8];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) lv[db] = bf16_to_f32(Lg[(size_t)c * kD + 16 * db + r16]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ds = sm.wts[(qi * K + s) * kG + i];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) dq[j][db][i] = __builtin_fmaf(ds, lv[db], dq[j][db][i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t* orow = dq_out + ((size_t)(b * g.Hq + kvh * kG + i) * L + i0 + qi) * kD + r16;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) orow[16 * db] = f32_to_bf16(scale * dq[j][db][i]);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 3. chunks: dk, dv, dlmk, dbias
+// ----------------------------------------------------------------------------
+struct ChunkAcc {
+  f32x4 dv[8], dk[8];
+  float dl[8];     // dlmk partial (wave 0): column 16db + l%16, rows of group l/16
+  float dbias;
+};
+
+// One tile of 8 queries x 4 heads (rows (mt, qq, h), query = qs[4 mt + qq]).
+// kOwn: the chunk is the queries' own chunk (slot K, causal mask, no ds).
+template <bool kOwn>
+__device__ __forceinline__ void chunk_tile(const Geometry& g, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ dout, const BwdWs& ws,
+                                           int b, int kvh, int bkv, int c, int w,
+                                           const int (&qa)[2], const int (&qb)[2],
+                                           const bool (&vb)[2], const bf16x8 (&kB)[4],
+                                           const bf16x8 (&vB)[4], float sc2, ChunkAcc& acc) {
+  const int lane = lane_id();
+  const int L = g.Lq;
+  const int ha = lane & 3;
+  // S = Q K^T and U = dO V^T for this wave's 16 keys: A rows = (qq = (l%16)/4, h = l%4)
+  f32x4 s[2], u[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const size_t row = ((size_t)(b * g.Hq + kvh * kG + ha) * L + qa[mt]) * kD + 8 * (lane >> 4);
+    f32x4 as = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      as = mfma(ld8(q + row + 32 * ks), kB[ks], as);
+      au = mfma(ld8(dout + row + 32 * ks), vB[ks], au);
+    }
+    s[mt] = as;
+    u[mt] = au;
+  }
+  // rows of the D layout: (mt, qq = l/16, h = i), key 16w + l%16
+  const int key = c * kS + 16 * w + (lane & 15);
+  float wp[2][4], dl[2][4], ds[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int qs = qb[mt];
+    int slot = g.K;
+    if (!kOwn) slot = ws.slot[((size_t)bkv * L + qs) * g.NC + c];
+    const bool valid = vb[mt] && slot != 0xff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t row = (size_t)(b * g.Hq + kvh * kG + i) * L + qs;
+      float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (valid) st = ws.stats[row * (g.K + 1) + (valid ? slot : 0)];
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -st.y));
+      if (kOwn && key > qs) p = 0.f;
+      wp[mt][i] = st.x * p;
+      dl[mt][i] = wp[mt][i] * (u[mt][i] - st.z);
+      ds[mt][i] = 0.f;
+      if (!kOwn && valid && w == 0) ds[mt][i] = st.x * (st.z - ws.Drow[row]);
+    }
+  }
+  float a8[8], d8[8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a8[4 * mt + i] = wp[mt][i];
+      d8[4 * mt + i] = dl[mt][i];
+    }
+  const bf16x8 Awp = pack_bf16x8(a8), Adl = pack_bf16x8(d8);
+  // B operands: rows k = 8(l/16) + j <-> (mt = j/4, qq = l/16, h = j%4), column 16db + l%16
+  const uint16_t* qr0 = ws.qi + ((size_t)bkv * L + qb[0]) * kD * kG;
+  const uint16_t* qr1 = ws.qi + ((size_t)bkv * L + qb[1]) * kD * kG;
+  const uint16_t* dr0 = ws.doi + ((size_t)bkv * L + qb[0]) * kD * kG;
+  const uint16_t* dr1 = ws.doi + ((size_t)bkv * L + qb[1]) * kD * kG;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int col = 16 * db + (lane & 15);
+    const uint2 q0 = *reinterpret_cast<const uint2*>(qr0 + col * kG);
+    const uint2 q1 = *reinterpret_cast<const uint2*>(qr1 + col * kG);
+    const uint2 d0 = *reinterpret_cast<const uint2*>(dr0 + col * kG);
+    const uint2 d1 = *reinterpret_cast<const uint2*>(dr1 + col * kG);
+    const bf16x8 Bq = as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y));
+    const bf16x8 Bd = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
+    acc.dv[db] = mfma(Awp, Bd, acc.dv[db]);
+    acc.dk[db] = mfma(Adl, Bq, acc.dk[db]);
+    if (!kOwn && w == 0) {
+      const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
+      float t = acc.dl[db];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int mt = e / 2;
+        t = __builtin_fmaf(ds[mt][(e % 2) * 2], __uint_as_float(qw[e] << 16), t);
+        t = __builtin_fmaf(ds[mt][(e % 2) * 2 + 1], __uint_as_float(qw[e] & 0xffff0000u), t);
+      }
+      acc.dl[db] = t;
+    }
+  }
+  if (!kOwn && w == 0 && (lane & 15) == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc.dbias += ds[mt][i];
+  }
+}
+
+__global__ void __launch_bounds__(kChunkThreads)
+prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, BwdWs ws,
+                   uint16_t* __restrict__ dk_out, uint16_t* __restrict__ dv_out,
+                   uint16_t* __restrict__ dlmk_out, float* __restrict__ dbias_out) {
+  __shared__ uint16_t qlist[kMaxL];
+  __shared__ int scan[kChunkThreads];
+  const int nbkv = g.B * g.Hkv;
+  const int bkv = blockIdx.x % nbkv, c = blockIdx.x / nbkv;   // early chunks (most queries) first
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int L = g.Lq, NW = L / kWin;
+  const float scale = g.scale, sc2 = scale * 1.4426950408889634f;
+  if (c >= g.NC) {   // landmark rows past the complete chunks get zero gradient
+    if (tid < kD) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + tid] = 0;
+    if (tid == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = 0.f;
+    return;
+  }
+
+  // ---- the queries (of later windows) that selected chunk c, in query order
+  const int nwin = NW - c - 1;
+  uint64_t m = 0;
+  if (tid < nwin) m = ws.qm[((size_t)bkv * NW + c + 1 + tid) * g.NC + c];
+  const int cnt = __popcll(m);
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kChunkThreads; off <<= 1) {
+    const int t = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += t;
+    __syncthreads();
+  }
+  const int n = scan[kChunkThreads - 1];
+  {
+    int pos = scan[tid] - cnt;
+    uint64_t mm = m;
+    while (mm) {
+      const int bit = __ffsll((long long)mm) - 1;
+      mm &= mm - 1;
+      qlist[pos++] = (uint16_t)((c + 1 + tid) * kWin + bit);
+    }
+  }
+  __syncthreads();
+
+  // this wave's 16 keys of the chunk as B fragments of S = Q K^T and U = dO V^T
+  bf16x8 kB[4], vB[4];
+  {
+    const size_t row = ((size_t)bkv * L + c * kS + 16 * w + (lane & 15)) * kD + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kB[ks] = ld8(k + row + 32 * ks);
+      vB[ks] = ld8(v + row + 32 * ks);
+    }
+  }
+  ChunkAcc acc;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    acc.dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.dl[db] = 0.f;
+  }
+  acc.dbias = 0.f;
+
+  // own window: queries c*64 .. c*64+63, eight tiles
+  if (g.keep_own) {
+    for (int t = 0; t < kWin / 8; ++t) {
+      int qa[2], qb[2];
+      bool vb[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        qa[mt] = c * kWin + t * 8 + 4 * mt + ((lane & 15) >> 2);
+        qb[mt] = c * kWin + t * 8 + 4 * mt + (lane >> 4);
+        vb[mt] = true;
+      }
+      chunk_tile<true>(g, q, dout, ws, b, kvh, bkv, c, w, qa, qb, vb, kB, vB, sc2, acc);
+    }
+  }
+  for (int t0 = 0; t0 < n; t0 += 8) {
+    int qa[2], qb[2];
+    bool vb[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int ea = t0 + 4 * mt + ((lane & 15) >> 2), eb = t0 + 4 * mt + (lane >> 4);
+      qa[mt] = qlist[ea < n ? ea : t0];
+      qb[mt] = qlist[eb < n ? eb : t0];
+      vb[mt] = eb < n;
+    }
+    chunk_tile<false>(g, q, dout, ws, b, kvh, bkv, c, w, qa, qb, vb, kB, vB, sc2, acc);
+  }
+
+  // ---- outputs: lane holds dX[key 16w + 4(l/16) + i][16db + l%16]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t row = ((size_t)bkv * L + c * kS + 16 * w + 4 * (lane >> 4) + i) * kD + (lane & 15);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      dv_out[row + 16 * db] = f32_to_bf16(acc.dv[db][i]);
+      dk_out[row + 16 * db] = f32_to_bf16(scale * acc.dk[db][i]);
+    }
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const float t = rowgroup_sum(acc.dl[db]);
+      if (lane < 16) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + 16 * db + lane] = f32_to_bf16(scale * t);
+    }
+    const float tb = rowgroup_sum(acc.dbias);
+    if (lane == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = tb;
+  }
+}
+
+}  // namespace
+
+bool prefill_bwd_fast_supported(const Geometry& g, int bf16) {
+  return bf16 && g.d == kD && g.S == kS && g.G == kG && g.causal && g.Lq == g.Lkv &&
+         g.Lq % kWin == 0 && g.K <= kMaxKb && g.NC <= kMaxNCb && g.NC >= 1;
+}
+
+size_t prefill_bwd_fast_ws(const Geometry& g) {
+  size_t total = 0;
+  carve(g, nullptr, &total);
+  return total;
+}
+
+hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void* k, const void* v,
+                                   const void* lmk, const float* bias, const void* out,
+                                   const void* dout, const int32_t* sel_idx, const float* lse,
+                                   void* dq, void* dk, void* dv, void* dlmk, float* dbias,
+                                   void* wsp, hipStream_t st) {
+  BwdWs ws = carve(g, wsp, nullptr);
+  const int nbkv = g.B * g.Hkv, NW = g.Lq / kWin;
+  const uint16_t* Q = (const uint16_t*)q;
+  const uint16_t* DO = (const uint16_t*)dout;
+  hipLaunchKernelGGL(prefill_bwd_prep, dim3(nbkv * NW), dim3(kPrepThreads), 0, st, g, Q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)out, DO, sel_idx, ws);
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_bwd_rows,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(RowsSmem));
+  if (e != hipSuccess) return e;
+  prof_begin(kPrefillBwdRows, st);
+  hipLaunchKernelGGL(prefill_bwd_rows, dim3(nbkv * NW), dim3(kRowThreads), sizeof(RowsSmem), st, g,
+                     Q, DO, (const uint16_t*)lmk, bias, sel_idx, lse, ws, (uint16_t*)dq);
+  prof_end(kPrefillBwdRows, st);
+  prof_begin(kPrefillBwdChunks, st);
+  hipLaunchKernelGGL(prefill_bwd_chunks, dim3(nbkv * g.NCcap), dim3(kChunkThreads), 0, st, g, Q,
+                     (const uint16_t*)k, (const uint16_t*)v, DO, ws, (uint16_t*)dk, (uint16_t*)dv,
+                     (uint16_t*)dlmk, dbias);
+  prof_end(kPrefillBwdChunks, st);
+  return hipGetLastError();
+}
+
+}  // namespace hils

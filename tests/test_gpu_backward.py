@@ -46,8 +46,44 @@ def test_tiny_f32_backward(hl):
     dict(B=2, Hq=6, Hkv=2, d=64, Lq=150, Lkv=150, S=16, K=4, dtype="bf16", lmk="iid", bias=0.5),
     dict(B=1, Hq=2, Hkv=1, d=32, Lq=70, Lkv=70, S=8, K=3, dtype="f32", lmk="iid", keep_own=0),
     dict(B=1, Hq=2, Hkv=2, d=64, Lq=45, Lkv=131, S=16, K=2, dtype="f32", lmk="iid", causal=0),
+    # MFMA backward path (bf16, d = 128, S = 64, G = 4, causal, L % 64 == 0, K <= 32)
+    dict(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=8, dtype="bf16", lmk="chunk_mean",
+         bias=0.3),
+    dict(B=2, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="iid",
+         keep_own=0),
+    dict(B=1, Hq=4, Hkv=1, d=128, Lq=1536, Lkv=1536, S=64, K=32, dtype="bf16", lmk="chunk_mean"),
 ])
 def test_backward_shapes(hl, over):
     cfg = dict(config("tiny_f32"), seed=31, dout=True)
     cfg.update(over)
     _grad_case(hl, cfg)
+
+
+def test_train_8k_sampled(hl):
+    """Full training shape through the product path.  dq is checked on sampled
+    query rows; dk, dv of the last two chunks and dlmk, dbias of the second-to-
+    last one are complete once every query of the last two windows is included
+    (no earlier query can reach those chunks)."""
+    cfg = config("train_8k")
+    host, dev = make_device_inputs(cfg)
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=True)
+    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
+    dq, dk, dv, dl, db = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out,
+                                          dev["dout"], idx, lse, need_dbias=True, **kw)
+    torch.cuda.synchronize()
+    L, S = cfg["Lq"], cfg["S"]
+    rng = np.random.default_rng(3)
+    qs = np.array(sorted(set(rng.choice(L - 2 * S, 24, replace=False).tolist())
+                         | set(range(L - 2 * S, L))))
+    gi = idx.cpu().numpy().astype(np.int64)[:, :, qs]
+    rdq, rdk, rdv, rdl, rdb = ref_backward(host["q"], host["k"], host["v"], host["lmk"], None,
+                                           host["dout"], forced_idx=gi, queries=qs, **kw)
+    assert_close("dq rows", to_np(dq)[:, :, qs], rdq[:, :, qs], "norm", 2e-2)
+    tail = slice(L - 2 * S, L)
+    assert_close("dk tail", to_np(dk)[:, :, tail], rdk[:, :, tail], "norm", 2e-2)
+    assert_close("dv tail", to_np(dv)[:, :, tail], rdv[:, :, tail], "norm", 2e-2)
+    c = L // S - 2
+    assert_close("dlmk", to_np(dl)[:, :, c], rdl[:, :, c], "norm", 2e-2)
+    assert_close("dbias", to_np(db)[:, :, c], rdb[:, :, c], "norm", 2e-2)
+    # rows past the complete chunks and chunks no query reaches get zero
+    assert np.all(to_np(dl)[:, :, L // S - 1] == 0)
