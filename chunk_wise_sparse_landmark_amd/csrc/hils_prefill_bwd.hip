@@ -51,15 +51,30 @@ constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowBlocks = kWin / 4 / kRowWaves;   // query blocks per wave
 constexpr int kPrepThreads = 256;
 constexpr int kChunkThreads = 256;
+constexpr int kTilesPerItem = 32;                  // 256 (query, chunk) pairs per work item
+constexpr int kPartFloats = 2 * kS * kD + kD + 4;  // dV, dK, dlmk, dbias (+pad)
+
+// Upper bound of the work items of one (b, kv head): a query selects at most K
+// chunks, so the retrieved tiles number at most L*K/8 plus one partial tile per
+// chunk; each chunk adds its own-window tiles and at most one short item.
+int max_items_of(const Geometry& g) {
+  const long tiles = (long)g.Lq * g.K / 8 + g.NC + (long)g.NC * (kWin / 8);
+  return (int)(tiles / kTilesPerItem + 2 * g.NC + 1);
+}
 
 struct BwdWs {
   uint16_t* frags;   // [bkv][NC][48 fragments][64 lanes][8]
   uint16_t* qi;      // [bkv][L][d][4 heads]
   uint16_t* doi;     // [bkv][L][d][4 heads]
   float* Drow;       // [B][Hq][L]
-  float4* stats;     // [B][Hq][L][K+1]: (w, log2 lse_c, D_c (own: D), 0)
+  float4* stats;     // [B][Hq][L][K+1]: (w, log2 lse_c, D_c (own: D), ds_c (own: 0))
   uint64_t* qm;      // [bkv][NW][NC]: window queries that selected chunk c
   uint8_t* slot;     // [bkv][L][NC]: slot of chunk c in query i's selection, 0xff if none
+  int4* items;       // [bkv][max_items]: (chunk, first tile, end tile, partial slot or -1)
+  int* nitems;       // [bkv]
+  int2* chunkseg;    // [bkv][NC]: (first partial slot, number of items)
+  float* part;       // [bkv * max_items][kPartFloats]: partial dV, dK, dlmk, dbias
+  int max_items;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -83,6 +98,15 @@ BwdWs carve(const Geometry& g, void* base, size_t* total) {
   off += align256(nbkv * NW * g.NC * 8);
   w.slot = reinterpret_cast<uint8_t*>(c + off);
   off += align256(nbkv * L * g.NC);
+  w.max_items = max_items_of(g);
+  w.items = reinterpret_cast<int4*>(c + off);
+  off += align256(nbkv * w.max_items * 16);
+  w.nitems = reinterpret_cast<int*>(c + off);
+  off += align256(nbkv * 4);
+  w.chunkseg = reinterpret_cast<int2*>(c + off);
+  off += align256(nbkv * g.NC * 8);
+  w.part = reinterpret_cast<float*>(c + off);
+  off += align256(nbkv * (size_t)w.max_items * kPartFloats * 4);
   if (total) *total = off;
   return w;
 }
@@ -473,10 +497,11 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
       const int slot = sm.slotmap[qi * kMaxNCb + c];
       const float wv = slot != 0xff ? sm.wts[(qi * K + slot) * kG + h] : 0.f;
       const float Dr = sm.Dr[qi * kG + h];
-      const float4 st = block_bwd<false>(sm.kv[cur], qf[j], df[j], sc2, kS, wv, Dr, 0.f, dq[j]);
+      float4 st = block_bwd<false>(sm.kv[cur], qf[j], df[j], sc2, kS, wv, Dr, 0.f, dq[j]);
+      st.w = wv * (st.z - Dr);                                         // ds_c
       if (lane < 16 && slot != 0xff) {
         ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * srow_stride + slot] = st;
-        sm.wts[(qi * K + slot) * kG + h] = wv * (st.z - Dr);          // ds_c
+        sm.wts[(qi * K + slot) * kG + h] = st.w;
       }
     }
     stage_wait_all();
@@ -513,102 +538,106 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
 // ----------------------------------------------------------------------------
 // 3. chunks: dk, dv, dlmk, dbias
 // ----------------------------------------------------------------------------
-struct ChunkAcc {
-  f32x4 dv[8], dk[8];
-  float dl[8];     // dlmk partial (wave 0): column 16db + l%16, rows of group l/16
-  float dbias;
+// (tile staging helpers and the chunk kernel follow the planner)
+
+// ---- work items: each chunk's tiles (own window first, then the retrieving
+//      queries in query order, 8 per tile) cut into items of kTilesPerItem.
+//      One workgroup per (b, kv head).
+__global__ void __launch_bounds__(kChunkThreads)
+prefill_bwd_plan(Geometry g, BwdWs ws) {
+  __shared__ int scan[kChunkThreads];
+  const int bkv = blockIdx.x, tid = threadIdx.x;
+  const int NW = g.Lq / kWin;
+  int nseg = 0, tiles = 0;
+  if (tid < g.NC) {
+    int n = 0;
+    for (int wdw = tid + 1; wdw < NW; ++wdw) n += __popcll(ws.qm[((size_t)bkv * NW + wdw) * g.NC + tid]);
+    tiles = (n + 7) / 8 + (g.keep_own ? kWin / 8 : 0);
+    nseg = max(1, (tiles + kTilesPerItem - 1) / kTilesPerItem);
+  }
+  scan[tid] = nseg;
+  __syncthreads();
+  for (int off = 1; off < kChunkThreads; off <<= 1) {
+    const int t = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += t;
+    __syncthreads();
+  }
+  if (tid < g.NC) {
+    const int base = scan[tid] - nseg;
+    for (int sgi = 0; sgi < nseg; ++sgi) {
+      const int t0 = sgi * kTilesPerItem, t1 = min(tiles, t0 + kTilesPerItem);
+      ws.items[(size_t)bkv * ws.max_items + base + sgi] =
+          make_int4(tid, t0, t1, nseg > 1 ? base + sgi : -1);
+    }
+    ws.chunkseg[(size_t)bkv * g.NC + tid] = make_int2(base, nseg);
+  }
+  if (tid == 0) ws.nitems[bkv] = scan[kChunkThreads - 1];
+}
+
+// One tile of 8 queries x 4 heads = 32 rows, staged in LDS by the four waves
+// with direct global->LDS loads:
+//   qa, da  [8 fragments][64 lanes] x 16 B: A operands of S = Q K^T, U = dO V^T;
+//           fragment mt*4+ks, lane l: row (query 4mt + (l%16)/4, head l%4),
+//           dims 32ks + 8(l/16) .. +7
+//   qi, di  [8 queries][128 dims][4 heads] bf16: rows of the B operands
+//   st      [32 rows] (w, log2 lse_c, D_c, ds_c), row r = (query r/4, head r%4)
+struct TileBuf {
+  uint4 qa[8 * kWave];
+  uint4 da[8 * kWave];
+  uint4 qi[8 * kD * kG / 8];
+  uint4 di[8 * kD * kG / 8];
+  float4 st[32];
+};
+struct ChunkSmem {
+  TileBuf tb[2];
+  uint16_t eq[kTilesPerItem * 8];   // tile entries: query
+  uint8_t es[kTilesPerItem * 8];    // slot (K = own chunk), 0xff = padding
+  int scan[kChunkThreads];
 };
 
-// One tile of 8 queries x 4 heads (rows (mt, qq, h), query = qs[4 mt + qq]).
-// kOwn: the chunk is the queries' own chunk (slot K, causal mask, no ds).
-template <bool kOwn>
-__device__ __forceinline__ void chunk_tile(const Geometry& g, const uint16_t* __restrict__ q,
+__device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)ldst_wave_base,
+                                   16, 0, 0);
+}
+
+// wave w stages its share of tile t into buffer tb
+__device__ __forceinline__ void stage_tile(const Geometry& g, const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ dout, const BwdWs& ws,
-                                           int b, int kvh, int bkv, int c, int w,
-                                           const int (&qa)[2], const int (&qb)[2],
-                                           const bool (&vb)[2], const bf16x8 (&kB)[4],
-                                           const bf16x8 (&vB)[4], float sc2, ChunkAcc& acc) {
-  const int lane = lane_id();
+                                           int b, int kvh, int bkv, const uint16_t* eq,
+                                           const uint8_t* es, int t, TileBuf& tb) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
   const int L = g.Lq;
-  const int ha = lane & 3;
-  // S = Q K^T and U = dO V^T for this wave's 16 keys: A rows = (qq = (l%16)/4, h = l%4)
-  f32x4 s[2], u[2];
+  const int e0 = t * 8;
+  if (w < 2) {   // A fragments of q (wave 0) or dO (wave 1)
+    const uint16_t* src = w == 0 ? q : dout;
+    uint4* dst = w == 0 ? tb.qa : tb.da;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const size_t row = ((size_t)(b * g.Hq + kvh * kG + ha) * L + qa[mt]) * kD + 8 * (lane >> 4);
-    f32x4 as = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      as = mfma(ld8(q + row + 32 * ks), kB[ks], as);
-      au = mfma(ld8(dout + row + 32 * ks), vB[ks], au);
+    for (int f = 0; f < 8; ++f) {
+      const int mt = f / 4, ks = f % 4;
+      const int e = e0 + 4 * mt + ((lane & 15) >> 2);
+      const int qq = eq[es[e] != 0xff ? e : e0];
+      const uint16_t* p = src + ((size_t)(b * g.Hq + kvh * kG + (lane & 3)) * L + qq) * kD +
+                          32 * ks + 8 * (lane >> 4);
+      lds_load16(p, dst + f * kWave);
     }
-    s[mt] = as;
-    u[mt] = au;
-  }
-  // rows of the D layout: (mt, qq = l/16, h = i), key 16w + l%16
-  const int key = c * kS + 16 * w + (lane & 15);
-  float wp[2][4], dl[2][4], ds[2][4];
+  } else {       // head-interleaved rows of q (wave 2) or dO (wave 3), 1 KB per query
+    const uint16_t* src = w == 2 ? ws.qi : ws.doi;
+    uint4* dst = w == 2 ? tb.qi : tb.di;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int qs = qb[mt];
-    int slot = g.K;
-    if (!kOwn) slot = ws.slot[((size_t)bkv * L + qs) * g.NC + c];
-    const bool valid = vb[mt] && slot != 0xff;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t row = (size_t)(b * g.Hq + kvh * kG + i) * L + qs;
-      float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (valid) st = ws.stats[row * (g.K + 1) + (valid ? slot : 0)];
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -st.y));
-      if (kOwn && key > qs) p = 0.f;
-      wp[mt][i] = st.x * p;
-      dl[mt][i] = wp[mt][i] * (u[mt][i] - st.z);
-      ds[mt][i] = 0.f;
-      if (!kOwn && valid && w == 0) ds[mt][i] = st.x * (st.z - ws.Drow[row]);
+    for (int e = 0; e < 8; ++e) {
+      const int ee = e0 + e;
+      const int qq = eq[es[ee] != 0xff ? ee : e0];
+      lds_load16(src + ((size_t)bkv * L + qq) * kD * kG + lane * 8, dst + e * kWave);
     }
-  }
-  float a8[8], d8[8];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a8[4 * mt + i] = wp[mt][i];
-      d8[4 * mt + i] = dl[mt][i];
+    if (w == 2 && lane < 32) {   // the row table: row r = (query r/4, head r%4)
+      const int ee = e0 + (lane >> 2);
+      const int sl = es[ee];
+      const int qq = eq[sl != 0xff ? ee : e0];
+      const int slot = sl != 0xff ? sl : es[e0];
+      const float4* p = ws.stats + ((size_t)(b * g.Hq + kvh * kG + (lane & 3)) * L + qq) * (g.K + 1) + slot;
+      lds_load16(p, tb.st);
     }
-  const bf16x8 Awp = pack_bf16x8(a8), Adl = pack_bf16x8(d8);
-  // B operands: rows k = 8(l/16) + j <-> (mt = j/4, qq = l/16, h = j%4), column 16db + l%16
-  const uint16_t* qr0 = ws.qi + ((size_t)bkv * L + qb[0]) * kD * kG;
-  const uint16_t* qr1 = ws.qi + ((size_t)bkv * L + qb[1]) * kD * kG;
-  const uint16_t* dr0 = ws.doi + ((size_t)bkv * L + qb[0]) * kD * kG;
-  const uint16_t* dr1 = ws.doi + ((size_t)bkv * L + qb[1]) * kD * kG;
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const int col = 16 * db + (lane & 15);
-    const uint2 q0 = *reinterpret_cast<const uint2*>(qr0 + col * kG);
-    const uint2 q1 = *reinterpret_cast<const uint2*>(qr1 + col * kG);
-    const uint2 d0 = *reinterpret_cast<const uint2*>(dr0 + col * kG);
-    const uint2 d1 = *reinterpret_cast<const uint2*>(dr1 + col * kG);
-    const bf16x8 Bq = as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y));
-    const bf16x8 Bd = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
-    acc.dv[db] = mfma(Awp, Bd, acc.dv[db]);
-    acc.dk[db] = mfma(Adl, Bq, acc.dk[db]);
-    if (!kOwn && w == 0) {
-      const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
-      float t = acc.dl[db];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int mt = e / 2;
-        t = __builtin_fmaf(ds[mt][(e % 2) * 2], __uint_as_float(qw[e] << 16), t);
-        t = __builtin_fmaf(ds[mt][(e % 2) * 2 + 1], __uint_as_float(qw[e] & 0xffff0000u), t);
-      }
-      acc.dl[db] = t;
-    }
-  }
-  if (!kOwn && w == 0 && (lane & 15) == 0) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc.dbias += ds[mt][i];
   }
 }
 
@@ -617,41 +646,58 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, BwdWs ws,
                    uint16_t* __restrict__ dk_out, uint16_t* __restrict__ dv_out,
                    uint16_t* __restrict__ dlmk_out, float* __restrict__ dbias_out) {
-  __shared__ uint16_t qlist[kMaxL];
-  __shared__ int scan[kChunkThreads];
+  __shared__ ChunkSmem sm;
   const int nbkv = g.B * g.Hkv;
-  const int bkv = blockIdx.x % nbkv, c = blockIdx.x / nbkv;   // early chunks (most queries) first
+  const int bkv = blockIdx.x % nbkv, item = blockIdx.x / nbkv;
+  if (item >= ws.nitems[bkv]) return;
+  const int4 it = ws.items[(size_t)bkv * ws.max_items + item];
+  const int c = it.x, t0 = it.y, t1 = it.z, part = it.w;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = g.Lq, NW = L / kWin;
   const float scale = g.scale, sc2 = scale * 1.4426950408889634f;
-  if (c >= g.NC) {   // landmark rows past the complete chunks get zero gradient
-    if (tid < kD) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + tid] = 0;
-    if (tid == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = 0.f;
-    return;
-  }
+  const int own_tiles = g.keep_own ? kWin / 8 : 0;
+  const int ntile = t1 - t0;
 
-  // ---- the queries (of later windows) that selected chunk c, in query order
+  // ---- tile entries of this item: own-window queries (slot K), then the
+  //      retrieving queries of later windows in query order
+  for (int e = tid; e < kTilesPerItem * 8; e += kChunkThreads) sm.es[e] = 0xff;
+  __syncthreads();
+  for (int e = tid; e < ntile * 8; e += kChunkThreads) {
+    const int t = t0 + e / 8;
+    if (t < own_tiles) {
+      sm.eq[e] = (uint16_t)(c * kWin + t * 8 + e % 8);
+      sm.es[e] = (uint8_t)g.K;
+    }
+  }
+  const int r0 = 8 * max(0, t0 - own_tiles), r1 = 8 * max(0, t1 - own_tiles);
+  const int rbase = 8 * max(0, own_tiles - t0);   // entry index of the first retrieved query
   const int nwin = NW - c - 1;
   uint64_t m = 0;
-  if (tid < nwin) m = ws.qm[((size_t)bkv * NW + c + 1 + tid) * g.NC + c];
+  if (tid < nwin && r1 > r0) m = ws.qm[((size_t)bkv * NW + c + 1 + tid) * g.NC + c];
   const int cnt = __popcll(m);
-  scan[tid] = cnt;
+  sm.scan[tid] = cnt;
   __syncthreads();
   for (int off = 1; off < kChunkThreads; off <<= 1) {
-    const int t = tid >= off ? scan[tid - off] : 0;
+    const int tt = tid >= off ? sm.scan[tid - off] : 0;
     __syncthreads();
-    scan[tid] += t;
+    sm.scan[tid] += tt;
     __syncthreads();
   }
-  const int n = scan[kChunkThreads - 1];
   {
-    int pos = scan[tid] - cnt;
-    uint64_t mm = m;
-    while (mm) {
-      const int bit = __ffsll((long long)mm) - 1;
-      mm &= mm - 1;
-      qlist[pos++] = (uint16_t)((c + 1 + tid) * kWin + bit);
+    int pos = sm.scan[tid] - cnt;
+    if (pos < r1 && pos + cnt > r0) {
+      uint64_t mm = m;
+      while (mm) {
+        const int bit = __ffsll((long long)mm) - 1;
+        mm &= mm - 1;
+        if (pos >= r0 && pos < r1) {
+          const int qq = (c + 1 + tid) * kWin + bit;
+          sm.eq[rbase + pos - r0] = (uint16_t)qq;
+          sm.es[rbase + pos - r0] = ws.slot[((size_t)bkv * L + qq) * g.NC + c];
+        }
+        ++pos;
+      }
     }
   }
   __syncthreads();
@@ -666,60 +712,165 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
       vB[ks] = ld8(v + row + 32 * ks);
     }
   }
-  ChunkAcc acc;
+  f32x4 dv[8], dk[8];
+  float dlm[8];
+  float dbt = 0.f;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    acc.dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc.dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc.dl[db] = 0.f;
+    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dlm[db] = 0.f;
   }
-  acc.dbias = 0.f;
+  const int key = c * kS + 16 * w + (lane & 15);
 
-  // own window: queries c*64 .. c*64+63, eight tiles
-  if (g.keep_own) {
-    for (int t = 0; t < kWin / 8; ++t) {
-      int qa[2], qb[2];
-      bool vb[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        qa[mt] = c * kWin + t * 8 + 4 * mt + ((lane & 15) >> 2);
-        qb[mt] = c * kWin + t * 8 + 4 * mt + (lane >> 4);
-        vb[mt] = true;
-      }
-      chunk_tile<true>(g, q, dout, ws, b, kvh, bkv, c, w, qa, qb, vb, kB, vB, sc2, acc);
-    }
-  }
-  for (int t0 = 0; t0 < n; t0 += 8) {
-    int qa[2], qb[2];
-    bool vb[2];
+  if (ntile > 0) stage_tile(g, q, dout, ws, b, kvh, bkv, sm.eq, sm.es, 0, sm.tb[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const TileBuf& tb = sm.tb[t & 1];
+    if (t + 1 < ntile) stage_tile(g, q, dout, ws, b, kvh, bkv, sm.eq, sm.es, t + 1, sm.tb[(t + 1) & 1]);
+    // S and U for this wave's keys; D layout rows (mt, qq = l/16, h = i), key l%16
+    f32x4 s[2], u[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int ea = t0 + 4 * mt + ((lane & 15) >> 2), eb = t0 + 4 * mt + (lane >> 4);
-      qa[mt] = qlist[ea < n ? ea : t0];
-      qb[mt] = qlist[eb < n ? eb : t0];
-      vb[mt] = eb < n;
+      f32x4 as = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        as = mfma(as_bf16x8(tb.qa[(mt * 4 + ks) * kWave + lane]), kB[ks], as);
+        au = mfma(as_bf16x8(tb.da[(mt * 4 + ks) * kWave + lane]), vB[ks], au);
+      }
+      s[mt] = as;
+      u[mt] = au;
     }
-    chunk_tile<false>(g, q, dout, ws, b, kvh, bkv, c, w, qa, qb, vb, kB, vB, sc2, acc);
+    float a8[8], d8[8], ds[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int e = t * 8 + 4 * mt + (lane >> 4);
+      const int sl = sm.es[e];
+      const bool valid = sl != 0xff;
+      const bool own = sl == g.K;
+      const int qq = sm.eq[valid ? e : t * 8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 st = tb.st[(4 * mt + (lane >> 4)) * 4 + i];
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -st.y));
+        if (!valid || (own && key > qq)) p = 0.f;
+        const float wp = st.x * p;
+        a8[4 * mt + i] = wp;
+        d8[4 * mt + i] = wp * (u[mt][i] - st.z);
+        ds[mt][i] = (valid && !own) ? st.w : 0.f;
+      }
+    }
+    const bf16x8 Awp = pack_bf16x8(a8), Adl = pack_bf16x8(d8);
+    const uint16_t* qi0 = reinterpret_cast<const uint16_t*>(tb.qi) + (lane >> 4) * kD * kG;
+    const uint16_t* qi1 = qi0 + 4 * kD * kG;
+    const uint16_t* di0 = reinterpret_cast<const uint16_t*>(tb.di) + (lane >> 4) * kD * kG;
+    const uint16_t* di1 = di0 + 4 * kD * kG;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int col = (16 * db + (lane & 15)) * kG;
+      const uint2 q0 = *reinterpret_cast<const uint2*>(qi0 + col);
+      const uint2 q1 = *reinterpret_cast<const uint2*>(qi1 + col);
+      const uint2 d0 = *reinterpret_cast<const uint2*>(di0 + col);
+      const uint2 d1 = *reinterpret_cast<const uint2*>(di1 + col);
+      dv[db] = mfma(Awp, as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dv[db]);
+      dk[db] = mfma(Adl, as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dk[db]);
+      if (w == 0) {
+        const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
+        float tacc = dlm[db];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2], __uint_as_float(qw[e] << 16), tacc);
+          tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2 + 1], __uint_as_float(qw[e] & 0xffff0000u), tacc);
+        }
+        dlm[db] = tacc;
+      }
+    }
+    if (w == 0 && (lane & 15) == 0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dbt += ds[mt][i];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // ---- outputs: lane holds dX[key 16w + 4(l/16) + i][16db + l%16]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const size_t row = ((size_t)bkv * L + c * kS + 16 * w + 4 * (lane >> 4) + i) * kD + (lane & 15);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      dv_out[row + 16 * db] = f32_to_bf16(acc.dv[db][i]);
-      dk_out[row + 16 * db] = f32_to_bf16(scale * acc.dk[db][i]);
-    }
-  }
   if (w == 0) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const float t = rowgroup_sum(acc.dl[db]);
-      if (lane < 16) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + 16 * db + lane] = f32_to_bf16(scale * t);
+    for (int db = 0; db < 8; ++db) dlm[db] = rowgroup_sum(dlm[db]);
+    dbt = rowgroup_sum(dbt);
+  }
+  if (part < 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t row = ((size_t)bkv * L + c * kS + 16 * w + 4 * (lane >> 4) + i) * kD + (lane & 15);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        dv_out[row + 16 * db] = f32_to_bf16(dv[db][i]);
+        dk_out[row + 16 * db] = f32_to_bf16(scale * dk[db][i]);
+      }
     }
-    const float tb = rowgroup_sum(acc.dbias);
-    if (lane == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = tb;
+    if (w == 0) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        if (lane < 16) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + 16 * db + lane] = f32_to_bf16(scale * dlm[db]);
+      if (lane == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = dbt;
+    }
+  } else {
+    float* pp = ws.part + ((size_t)bkv * ws.max_items + part) * kPartFloats;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 16 * w + 4 * (lane >> 4) + i;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        pp[kr * kD + 16 * db + (lane & 15)] = dv[db][i];
+        pp[kS * kD + kr * kD + 16 * db + (lane & 15)] = dk[db][i];
+      }
+    }
+    if (w == 0) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        if (lane < 16) pp[2 * kS * kD + 16 * db + lane] = dlm[db];
+      if (lane == 0) pp[2 * kS * kD + kD] = dbt;
+    }
+  }
+}
+
+// ---- sums the partial items of chunks split over several workgroups, in item
+//      order; zeroes the landmark rows past the complete chunks.
+__global__ void __launch_bounds__(kChunkThreads)
+prefill_bwd_reduce(Geometry g, BwdWs ws, uint16_t* __restrict__ dk_out,
+                   uint16_t* __restrict__ dv_out, uint16_t* __restrict__ dlmk_out,
+                   float* __restrict__ dbias_out) {
+  const int nbkv = g.B * g.Hkv;
+  const int bkv = blockIdx.x % nbkv, c = blockIdx.x / nbkv;
+  const int tid = threadIdx.x;
+  const float scale = g.scale;
+  if (c >= g.NC) {
+    if (tid < kD) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + tid] = 0;
+    if (tid == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = 0.f;
+    return;
+  }
+  const int2 cs = ws.chunkseg[(size_t)bkv * g.NC + c];
+  if (cs.y <= 1) return;
+  const float* pb = ws.part + ((size_t)bkv * ws.max_items + cs.x) * kPartFloats;
+  const size_t row0 = ((size_t)bkv * g.Lq + c * kS) * kD;
+  for (int x = tid; x < kS * kD; x += kChunkThreads) {
+    float sv = 0.f, sk = 0.f;
+    for (int sgi = 0; sgi < cs.y; ++sgi) {
+      sv += pb[(size_t)sgi * kPartFloats + x];
+      sk += pb[(size_t)sgi * kPartFloats + kS * kD + x];
+    }
+    dv_out[row0 + x] = f32_to_bf16(sv);
+    dk_out[row0 + x] = f32_to_bf16(scale * sk);
+  }
+  if (tid <= kD) {
+    float sl = 0.f;
+    for (int sgi = 0; sgi < cs.y; ++sgi) sl += pb[(size_t)sgi * kPartFloats + 2 * kS * kD + tid];
+    if (tid < kD) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + tid] = f32_to_bf16(scale * sl);
+    else if (dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = sl;
   }
 }
 
@@ -754,11 +905,14 @@ hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void*
   hipLaunchKernelGGL(prefill_bwd_rows, dim3(nbkv * NW), dim3(kRowThreads), sizeof(RowsSmem), st, g,
                      Q, DO, (const uint16_t*)lmk, bias, sel_idx, lse, ws, (uint16_t*)dq);
   prof_end(kPrefillBwdRows, st);
+  hipLaunchKernelGGL(prefill_bwd_plan, dim3(nbkv), dim3(kChunkThreads), 0, st, g, ws);
   prof_begin(kPrefillBwdChunks, st);
-  hipLaunchKernelGGL(prefill_bwd_chunks, dim3(nbkv * g.NCcap), dim3(kChunkThreads), 0, st, g, Q,
-                     (const uint16_t*)k, (const uint16_t*)v, DO, ws, (uint16_t*)dk, (uint16_t*)dv,
-                     (uint16_t*)dlmk, dbias);
+  hipLaunchKernelGGL(prefill_bwd_chunks, dim3(nbkv * ws.max_items), dim3(kChunkThreads), 0, st, g,
+                     Q, (const uint16_t*)k, (const uint16_t*)v, DO, ws, (uint16_t*)dk,
+                     (uint16_t*)dv, (uint16_t*)dlmk, dbias);
   prof_end(kPrefillBwdChunks, st);
+  hipLaunchKernelGGL(prefill_bwd_reduce, dim3(nbkv * g.NCcap), dim3(kChunkThreads), 0, st, g, ws,
+                     (uint16_t*)dk, (uint16_t*)dv, (uint16_t*)dlmk, dbias);
   return hipGetLastError();
 }
 
