@@ -51,8 +51,8 @@ constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowBlocks = kWin / 4 / kRowWaves;   // query blocks per wave
 constexpr int kPrepThreads = 256;
 constexpr int kChunkThreads = 256;
-constexpr int kTilesPerItem = 32;                  // 256 (query, chunk) pairs per work item
-constexpr int kPartFloats = 2 * kS * kD + kD + 4;  // dV, dK, dlmk, dbias (+pad)
+constexpr int kTilesPerItem = 64;                  // 512 (query, chunk) pairs per work item
+constexpr int kPartFloats = 2 * kS * kD + kD + 4;  // dV, dK, dlmk, dbias (+pad to 16 B)
 
 // Upper bound of the work items of one (b, kv head): a query selects at most K
 // chunks, so the retrieved tiles number at most L*K/8 plus one partial tile per
@@ -551,6 +551,7 @@ prefill_bwd_plan(Geometry g, BwdWs ws) {
   int nseg = 0, tiles = 0;
   if (tid < g.NC) {
     int n = 0;
+#pragma unroll 8
     for (int wdw = tid + 1; wdw < NW; ++wdw) n += __popcll(ws.qm[((size_t)bkv * NW + wdw) * g.NC + tid]);
     tiles = (n + 7) / 8 + (g.keep_own ? kWin / 8 : 0);
     nseg = max(1, (tiles + kTilesPerItem - 1) / kTilesPerItem);
@@ -857,14 +858,20 @@ prefill_bwd_reduce(Geometry g, BwdWs ws, uint16_t* __restrict__ dk_out,
   if (cs.y <= 1) return;
   const float* pb = ws.part + ((size_t)bkv * ws.max_items + cs.x) * kPartFloats;
   const size_t row0 = ((size_t)bkv * g.Lq + c * kS) * kD;
-  for (int x = tid; x < kS * kD; x += kChunkThreads) {
-    float sv = 0.f, sk = 0.f;
+  for (int x = tid * 4; x < kS * kD; x += kChunkThreads * 4) {
+    float4 sv = make_float4(0.f, 0.f, 0.f, 0.f), sk = sv;
     for (int sgi = 0; sgi < cs.y; ++sgi) {
-      sv += pb[(size_t)sgi * kPartFloats + x];
-      sk += pb[(size_t)sgi * kPartFloats + kS * kD + x];
+      const float4 a = *reinterpret_cast<const float4*>(pb + (size_t)sgi * kPartFloats + x);
+      const float4 bq = *reinterpret_cast<const float4*>(pb + (size_t)sgi * kPartFloats + kS * kD + x);
+      sv.x += a.x; sv.y += a.y; sv.z += a.z; sv.w += a.w;
+      sk.x += bq.x; sk.y += bq.y; sk.z += bq.z; sk.w += bq.w;
     }
-    dv_out[row0 + x] = f32_to_bf16(sv);
-    dk_out[row0 + x] = f32_to_bf16(scale * sk);
+    const uint2 ov = make_uint2((uint32_t)f32_to_bf16(sv.x) | ((uint32_t)f32_to_bf16(sv.y) << 16),
+                                (uint32_t)f32_to_bf16(sv.z) | ((uint32_t)f32_to_bf16(sv.w) << 16));
+    const uint2 ok = make_uint2((uint32_t)f32_to_bf16(scale * sk.x) | ((uint32_t)f32_to_bf16(scale * sk.y) << 16),
+                                (uint32_t)f32_to_bf16(scale * sk.z) | ((uint32_t)f32_to_bf16(scale * sk.w) << 16));
+    *reinterpret_cast<uint2*>(dv_out + row0 + x) = ov;
+    *reinterpret_cast<uint2*>(dk_out + row0 + x) = ok;
   }
   if (tid <= kD) {
     float sl = 0.f;
