@@ -12,14 +12,16 @@
 //     linear in q), and keeps its local top-K as composite keys.
 //  2. merge         grid (B*Hkv): top-K of the nsplit local lists; writes the
 //     ascending chunk ids.
-//  3. attend        grid (K+1, B*Hkv): one workgroup per selected chunk (and
-//     one for the own chunk) reads the chunk's 16 KB of K and 16 KB of V once
-//     for all G heads, computes the chunk softmax and o_c, and writes
-//     (s_c, o_c).
-//  4. fuse          grid (B*Hkv): log-sum-exp over the retrieval scores of the
-//     K+1 partials.  (A separate launch: on this multi-XCD part a device-scope
-//     fence per workgroup -- needed for a last-workgroup reduction -- writes
-//     back and invalidates L2 and costs far more than one more launch.)
+//  3. attend        grid (nsplit', B*Hkv): each workgroup walks a few of the
+//     K+1 fusion slots (selected chunks and the own chunk), reading each
+//     chunk's 16 KB of K and 16 KB of V once for all G heads with the next
+//     chunk's loads in flight, and folds the chunk outputs into a running
+//     (max score, weight sum, weighted output) per head.
+//  4. fuse          one wave per (b, q head): log-sum-exp merge of the
+//     nsplit' partials.  (A separate launch: on this multi-XCD part a
+//     device-scope fence per workgroup -- needed for a last-workgroup
+//     reduction -- writes back and invalidates L2 and costs far more than one
+//     more launch.)
 #include "hils_common.h"
 #include "hils_kernels.h"
 #include "hils_profile.h"
@@ -32,11 +34,10 @@ constexpr int kD = 128;
 constexpr int kS = 64;
 constexpr int kThreads = 256;
 constexpr int kMaxGd = 16;            // heads per KV group on this path
-constexpr int kPartStride = kD + 4;   // o[128], s, pad  (floats)
 
 struct DecodeWs {
   uint64_t* lists;   // [B*Hkv][nsplit][K]
-  float* parts;      // [B*Hkv][K+1][G][kPartStride]
+  float* parts;      // [B*Hkv][asplit <= K+1][G][kPartStride]: (O, M, Z) per head
 };
 
 __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
@@ -144,10 +145,40 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
 }
 
 // ----------------------------------------------------------------------------
-// 3. per-chunk attention for the G heads + last-block fusion.
+// 3. chunk attention with online fusion.  grid (nsplit, B*Hkv): workgroup
+//    `split` walks fusion slots [split*apc, split*apc + apc) of its (b, kv
+//    head) -- slot < K is the slot-th selected chunk, slot K the own chunk --
+//    reading each chunk's 16 KB of K and 16 KB of V once for all G heads, with
+//    the next chunk's loads in flight while one is computed.  Per head it keeps
+//    (M, Z, O) = (max s, sum e^{s-M}, sum e^{s-M} o_c) over its chunks, s the
+//    retrieval score (own chunk: its exact lse), and writes them as a partial.
 // ----------------------------------------------------------------------------
+constexpr int kPartStride = kD + 4;   // O[128], M, Z, pad  (floats)
+
+struct ChunkLoads {
+  uint4 k[4];   // key tid/4, dims 32*(tid%4) .. +31
+  uint4 v[4];   // V rows, 16 B per thread per step, coalesced
+};
+
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ Kc,
+                                           const uint16_t* __restrict__ Vc, int n,
+                                           ChunkLoads& L) {
+  const int tid = threadIdx.x;
+  const int j = tid >> 2, qd = tid & 3;
+#pragma unroll
+  for (int p4 = 0; p4 < 4; ++p4)
+    L.k[p4] = j < n ? *reinterpret_cast<const uint4*>(Kc + (size_t)j * kD + qd * 32 + p4 * 8)
+                    : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int idx = x * kThreads + tid;          // uint4 index within the chunk's V
+    const int row = idx / (kD / 8);
+    L.v[x] = row < n ? reinterpret_cast<const uint4*>(Vc)[idx] : make_uint4(0, 0, 0, 0);
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
-decode_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
               const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
               float* __restrict__ parts) {
@@ -155,139 +186,189 @@ decode_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __rest
   __shared__ float lg[kMaxGd][kS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
   __shared__ float sc[kMaxGd];
-  const int slot = blockIdx.x, bkv = blockIdx.y;
+  __shared__ int ca[8], cn[8], cc[8];
+  const int split = blockIdx.x, bkv = blockIdx.y;
+  const int nsplit = gridDim.x;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int G = g.G;
-  const int nslot = g.K + 1;
-
-  // which tokens: a selected chunk, or the own chunk's visible tokens
   const int t = g.Lkv - 1;
-  int a = 0, n = 0, c = -1;
-  if (slot < g.K) {
-    c = sel_idx[(size_t)bkv * g.K + slot];
-    if (c >= 0) { a = c * kS; n = kS; }
-  } else if (g.keep_own) {
-    a = (t / kS) * kS;
-    n = t - a + 1;
-  }
-  float* part = parts + ((size_t)bkv * nslot + slot) * G * kPartStride;
 
-  if (n > 0) {
-    for (int x = tid; x < G * kD; x += kThreads)
-      qs[x / kD][x % kD] = bf16_to_f32(q[(size_t)(b * g.Hq + kvh * G) * kD + x]);
-    const uint16_t* Kc = k + ((size_t)bkv * g.Lkv + a) * kD;
-    const uint16_t* Vc = v + ((size_t)bkv * g.Lkv + a) * kD;
-    // stage V (16 B per thread per step); rows >= n are zero
-    for (int x = tid; x < kS * kD / 8; x += kThreads) {
-      const int row = x / (kD / 8);
-      uint4 u = row < n ? reinterpret_cast<const uint4*>(Vc)[x] : make_uint4(0, 0, 0, 0);
-      reinterpret_cast<uint4*>(vs)[x] = u;
+  // token ranges of this workgroup's slots
+  if (tid < apc) {
+    const int slot = split * apc + tid;
+    int a = 0, n = 0, c = -1;
+    if (slot < g.K) {
+      c = sel_idx[(size_t)bkv * g.K + slot];
+      if (c >= 0) { a = c * kS; n = kS; }
+    } else if (slot == g.K && g.keep_own) {
+      a = (t / kS) * kS;
+      n = t - a + 1;
     }
-    // K: thread -> (key j = tid/4, quarter = tid%4 -> 32 dims)
-    const int j = tid >> 2, qd = tid & 3;
-    float kx[32];
-    if (j < n) {
+    ca[tid] = a; cn[tid] = n; cc[tid] = c;
+  }
+  for (int x = tid; x < G * kD; x += kThreads)
+    qs[x / kD][x % kD] = bf16_to_f32(q[(size_t)(b * g.Hq + kvh * G) * kD + x]);
+  __syncthreads();
+
+  const uint16_t* Kb = k + (size_t)bkv * g.Lkv * kD;
+  const uint16_t* Vb = v + (size_t)bkv * g.Lkv * kD;
+  const int dp = tid & 63, hg = tid >> 6;      // PV: dims 2dp, 2dp+1 of heads hg, hg+4, ...
+  float M[4], Z[4], O0[4], O1[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) { M[x] = -INFINITY; Z[x] = 0.f; O0[x] = 0.f; O1[x] = 0.f; }
+
+  ChunkLoads cur, nxt;
+  int first = 0;
+  while (first < apc && cn[first] == 0) ++first;
+  if (first < apc) load_chunk(Kb + (size_t)ca[first] * kD, Vb + (size_t)ca[first] * kD, cn[first], cur);
+  for (int s = first; s < apc; ) {
+    int nx = s + 1;
+    while (nx < apc && cn[nx] == 0) ++nx;
+    if (nx < apc) load_chunk(Kb + (size_t)ca[nx] * kD, Vb + (size_t)ca[nx] * kD, cn[nx], nxt);
+    const int n = cn[s], c = cc[s];
+    // V of this chunk -> LDS
+#pragma unroll
+    for (int x = 0; x < 4; ++x) reinterpret_cast<uint4*>(vs)[x * kThreads + tid] = cur.v[x];
+    // logits: thread -> key j, 32 dims
+    {
+      const int j = tid >> 2, qd = tid & 3;
+      float kx[32];
 #pragma unroll
       for (int p4 = 0; p4 < 4; ++p4) {
-        float x[8];
-        load_bf16x8(Kc + (size_t)j * kD + qd * 32 + p4 * 8, x);
+        const uint32_t u[4] = {cur.k[p4].x, cur.k[p4].y, cur.k[p4].z, cur.k[p4].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[p4 * 8 + e] = x[e];
+        for (int e = 0; e < 4; ++e) {
+          kx[p4 * 8 + 2 * e] = __uint_as_float(u[e] << 16);
+          kx[p4 * 8 + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
       }
-    } else {
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) kx[e] = 0.f;
+        for (int e = 0; e < 32; ++e) d = __builtin_fmaf(qs[h][qd * 32 + e], kx[e], d);
+        d += __shfl_xor(d, 1, kWave);
+        d += __shfl_xor(d, 2, kWave);
+        if (qd == 0) lg[h][j] = j < n ? g.scale * d : -INFINITY;
+      }
     }
     __syncthreads();
-    for (int h = 0; h < G; ++h) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) s += qs[h][qd * 32 + e] * kx[e];
-      s += __shfl_xor(s, 1, kWave);
-      s += __shfl_xor(s, 2, kWave);
-      if (qd == 0) lg[h][j] = j < n ? g.scale * s : -INFINITY;
-    }
-    __syncthreads();
-    // softmax per head (wave w takes heads w, w+4, ...), and the retrieval score
+    // chunk softmax per head (wave w: heads w, w+4, ...) and the fusion score
     for (int h = w; h < G; h += 4) {
       const float l = lg[h][lane];
       const float m = wave_max(l);
       const float e = __expf(l - m);
       const float z = wave_sum(e);
       lg[h][lane] = e / z;
-      float s;
-      if (slot < g.K) {
+      float sv;
+      if (c >= 0) {
         const uint16_t* lr = lmk + ((size_t)bkv * g.NCcap + c) * kD;
-        float part_s = qs[h][2 * lane] * bf16_to_f32(lr[2 * lane]) +
-                       qs[h][2 * lane + 1] * bf16_to_f32(lr[2 * lane + 1]);
-        s = g.scale * wave_sum(part_s) + (bias ? bias[(size_t)bkv * g.NCcap + c] : 0.f);
+        const float ps = qs[h][2 * lane] * bf16_to_f32(lr[2 * lane]) +
+                         qs[h][2 * lane + 1] * bf16_to_f32(lr[2 * lane + 1]);
+        sv = g.scale * wave_sum(ps) + (bias ? bias[(size_t)bkv * g.NCcap + c] : 0.f);
       } else {
-        s = m + __logf(z);   // own chunk: its exact log-sum-exp
+        sv = m + __logf(z);   // own chunk: its exact log-sum-exp
       }
-      if (lane == 0) sc[h] = s;
+      if (lane == 0) sc[h] = sv;
     }
     __syncthreads();
-    // o_c = P V : thread -> dims (2*dp, 2*dp+1) of heads hg, hg+4, ...
-    const int dp = tid & 63, hg = tid >> 6;
-    for (int h = hg; h < G; h += 4) {
+    // o_c = P V, folded into the running (M, Z, O) of each head
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int h = hg + 4 * x;
+      if (h >= G) break;
       float o0 = 0.f, o1 = 0.f;
 #pragma unroll 8
       for (int jj = 0; jj < kS; ++jj) {
         const uint32_t pr = reinterpret_cast<const uint32_t*>(vs)[jj * (kD / 2) + dp];
         const float pj = lg[h][jj];
-        o0 += pj * __uint_as_float(pr << 16);
-        o1 += pj * __uint_as_float(pr & 0xffff0000u);
+        o0 = __builtin_fmaf(pj, __uint_as_float(pr << 16), o0);
+        o1 = __builtin_fmaf(pj, __uint_as_float(pr & 0xffff0000u), o1);
       }
-      float* ph = part + (size_t)h * kPartStride;
-      ph[2 * dp] = o0;
-      ph[2 * dp + 1] = o1;
-      if (dp == 0) ph[kD] = sc[h];
+      const float sv = sc[h];
+      const float mn = fmaxf(M[x], sv);
+      const float fo = __expf(M[x] - mn), fn = __expf(sv - mn);
+      Z[x] = Z[x] * fo + fn;
+      O0[x] = O0[x] * fo + fn * o0;
+      O1[x] = O1[x] * fo + fn * o1;
+      M[x] = mn;
     }
-  } else {
-    for (int h = tid; h < G; h += kThreads) part[(size_t)h * kPartStride + kD] = -INFINITY;
+    __syncthreads();
+    cur = nxt;
+    s = nx;
   }
-
+  float* part = parts + ((size_t)bkv * nsplit + split) * G * kPartStride;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int h = hg + 4 * x;
+    if (h >= G) break;
+    float* ph = part + (size_t)h * kPartStride;
+    reinterpret_cast<float2*>(ph)[dp] = make_float2(O0[x], O1[x]);
+    if (dp == 0) { ph[kD] = M[x]; ph[kD + 1] = Z[x]; }
+  }
 }
 
 // ----------------------------------------------------------------------------
-// 4. fusion: log-sum-exp over the retrieval scores of the K+1 partials.
-// grid (B*Hkv); thread -> dims (2*dp, 2*dp+1) of heads hg, hg+4, ...
+// 4. merge of the nsplit partials of each (b, q head): one wave per row, lane
+//    -> dims 2l, 2l+1.  O = sum_s e^{M_s - M} O_s / sum_s e^{M_s - M} Z_s.
 // ----------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads)
-decode_fuse(Geometry g, const float* __restrict__ parts, uint16_t* __restrict__ out,
+decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* __restrict__ out,
             float* __restrict__ lse_out) {
-  const int bkv = blockIdx.x;
-  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
-  const int G = g.G, nslot = g.K + 1;
-  const float* pb = parts + (size_t)bkv * nslot * G * kPartStride;
-  const int dp = threadIdx.x & 63, hg = threadIdx.x >> 6;
-  for (int h = hg; h < G; h += 4) {
-    float m = -INFINITY;
-    for (int s = 0; s < nslot; ++s) m = fmaxf(m, pb[((size_t)s * G + h) * kPartStride + kD]);
-    float z = 0.f, o0 = 0.f, o1 = 0.f;
-    if (m != -INFINITY) {
-      for (int s = 0; s < nslot; ++s) {
-        const float* ph = pb + ((size_t)s * G + h) * kPartStride;
-        const float sv = ph[kD];
-        if (sv == -INFINITY) continue;
-        const float e = __expf(sv - m);
-        const float2 o = *reinterpret_cast<const float2*>(ph + 2 * dp);
-        z += e;
-        o0 += e * o.x;
-        o1 += e * o.y;
+  const int row = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;   // b * Hq + hq
+  const int lane = lane_id();
+  if (row >= g.B * g.Hq) return;
+  const int b = row / g.Hq, hq = row % g.Hq;
+  const int kvh = hq / g.G, h = hq % g.G;
+  const int bkv = b * g.Hkv + kvh;
+  const float* pb = parts + (size_t)bkv * nsplit * g.G * kPartStride + (size_t)h * kPartStride;
+  const size_t sstride = (size_t)g.G * kPartStride;
+  float m = -INFINITY;
+  for (int s0 = 0; s0 < nsplit; s0 += kWave) {
+    const int sidx = s0 + lane;
+    const float ms = sidx < nsplit ? pb[sidx * sstride + kD] : -INFINITY;
+    m = fmaxf(m, wave_max(ms));
+  }
+  float z = 0.f, o0 = 0.f, o1 = 0.f;
+  if (m != -INFINITY) {
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {
+      float2 ov[4];
+      float ms[4], zs[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float* ps = pb + (s + x) * sstride;
+        ov[x] = reinterpret_cast<const float2*>(ps)[lane];
+        ms[x] = ps[kD];
+        zs[x] = ps[kD + 1];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float f = ms[x] == -INFINITY ? 0.f : __expf(ms[x] - m);
+        z += f * zs[x];
+        o0 += f * ov[x].x;
+        o1 += f * ov[x].y;
       }
     }
-    const size_t orow = (size_t)(b * g.Hq + kvh * G + h) * kD;
-    const float inv = z > 0.f ? 1.f / z : 0.f;
-    const uint32_t pk = (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
-    reinterpret_cast<uint32_t*>(out + orow)[dp] = pk;
-    if (dp == 0 && lse_out) lse_out[b * g.Hq + kvh * G + h] = z > 0.f ? m + __logf(z) : -INFINITY;
+    for (; s < nsplit; ++s) {
+      const float* ps = pb + s * sstride;
+      const float2 ov = reinterpret_cast<const float2*>(ps)[lane];
+      const float ms = ps[kD];
+      const float f = ms == -INFINITY ? 0.f : __expf(ms - m);
+      z += f * ps[kD + 1];
+      o0 += f * ov.x;
+      o1 += f * ov.y;
+    }
   }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  const uint32_t pk = (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
+  reinterpret_cast<uint32_t*>(out + (size_t)row * kD)[lane] = pk;
+  if (lane == 0 && lse_out) lse_out[row] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
 struct DecodePlan {
   int ncand, R, cps, nsplit;
+  int apc, asplit;      // attention: fusion slots per workgroup, workgroups per (b, kv head)
 };
 
 DecodePlan plan(const Geometry& g) {
@@ -303,6 +384,10 @@ DecodePlan plan(const Geometry& g) {
   p.R = R;
   p.cps = 256 * R;
   p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
+  // attention: about 1024 workgroups, at most 8 chunks each
+  const int nslot = g.K + 1;
+  p.apc = min(8, max(1, (nslot * bkv + 1023) / 1024));
+  p.asplit = (nslot + p.apc - 1) / p.apc;
   return p;
 }
 
@@ -351,11 +436,11 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, c
   hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kThreads), 0, st, g, p.nsplit, d.lists, sel_idx);
   prof_end(kDecodeMerge, st);
   prof_begin(kDecodeAttend, st);
-  hipLaunchKernelGGL(decode_attend, dim3(g.K + 1, bkv), dim3(kThreads), 0, st, g, Q,
+  hipLaunchKernelGGL(decode_attend, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc, Q,
                      (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
   prof_end(kDecodeAttend, st);
-  hipLaunchKernelGGL(decode_fuse, dim3(bkv), dim3(kThreads), 0, st, g, d.parts, (uint16_t*)out,
-                     lse);
+  hipLaunchKernelGGL(decode_fuse, dim3((g.B * g.Hq + kThreads / kWave - 1) / (kThreads / kWave)),
+                     dim3(kThreads), 0, st, g, p.asplit, d.parts, (uint16_t*)out, lse);
   return hipGetLastError();
 }
 
