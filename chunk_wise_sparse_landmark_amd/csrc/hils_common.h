@@ -177,6 +177,36 @@ __device__ __forceinline__ uint64_t wave_rank_sort64(uint64_t key, uint64_t* buf
 // Top 64 of the union of two lists sorted descending (one key per lane, keys
 // unique apart from 0): max(a_i, b_{63-i}) is a bitonic sequence holding
 // exactly the 64 largest keys of both, which a rank sort then orders.
+// Value held by lane l ^ J (J a power of two), for 64-bit keys: the lane-swap
+// VALU instructions for J = 32, 16, LDS permutes below.
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
+  const int lane = lane_id();
+  uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+  if (J == 32 || J == 16) {
+    const auto a = J == 32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                           : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = J == 32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                           : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const bool up = (lane & J) != 0;
+    lo = up ? a[0] : a[1];
+    hi = up ? b[0] : b[1];
+  } else {
+    lo = __shfl_xor(lo, J, kWave);
+    hi = __shfl_xor(hi, J, kWave);
+  }
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <int J>
+__device__ __forceinline__ uint64_t bitonic_step_desc(uint64_t c) {
+  const uint64_t o = lane_xor_u64<J>(c);
+  const bool lower = (lane_id() & J) == 0;
+  const uint64_t mx = o > c ? o : c, mn = o > c ? c : o;
+  return lower ? mx : mn;
+}
+// Top 64 of two wave-wide lists sorted descending, sorted descending: the
+// elementwise max of a and reversed b is bitonic and holds the top 64; six
+// compare-exchange stages sort it.  (`buf`: 64 keys of LDS for the reversal.)
 __device__ __forceinline__ uint64_t wave_merge_sorted(uint64_t a, uint64_t b, uint64_t* buf) {
   const int lane = lane_id();
   buf[lane] = b;
@@ -187,7 +217,14 @@ __device__ __forceinline__ uint64_t wave_merge_sorted(uint64_t a, uint64_t b, ui
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  return wave_rank_sort64(a > br ? a : br, buf);
+  uint64_t c = a > br ? a : br;
+  c = bitonic_step_desc<32>(c);
+  c = bitonic_step_desc<16>(c);
+  c = bitonic_step_desc<8>(c);
+  c = bitonic_step_desc<4>(c);
+  c = bitonic_step_desc<2>(c);
+  c = bitonic_step_desc<1>(c);
+  return c;
 }
 
 // Top-K (K <= 64) of R keys per lane (keys unique apart from 0 = empty).

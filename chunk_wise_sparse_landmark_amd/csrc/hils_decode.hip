@@ -12,10 +12,10 @@
 //     linear in q), and keeps its local top-K as composite keys.
 //  2. merge         grid (B*Hkv): top-K of the nsplit local lists; writes the
 //     ascending chunk ids.
-//  3. attend        grid (nsplit', B*Hkv): each workgroup walks a few of the
-//     K+1 fusion slots (selected chunks and the own chunk), reading each
-//     chunk's 16 KB of K and 16 KB of V once for all G heads with the next
-//     chunk's loads in flight, and folds the chunk outputs into a running
+//  3. attend        grid (nsplit', B*Hkv): each workgroup walks one or a few
+//     of the K+1 fusion slots (selected chunks and the own chunk), reading
+//     each chunk's 16 KB of K and 16 KB of V once for all G heads with the
+//     next chunk's loads in flight, and folds the chunk outputs into a running
 //     (max score, weight sum, weighted output) per head.
 //  4. fuse          one wave per (b, q head): log-sum-exp merge of the
 //     nsplit' partials.  (A separate launch: on this multi-XCD part a
@@ -120,24 +120,34 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
 // ----------------------------------------------------------------------------
 // 2. merge the nsplit local lists of one (b, kv head); write ascending ids.
 // ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads)
+constexpr int kMergeWaves = 8;
+__global__ void __launch_bounds__(kMergeWaves * kWave)
 decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
              int32_t* __restrict__ sel_idx) {
-  __shared__ uint64_t buf[4][kWave];
-  __shared__ uint64_t wl[4][kWave];
+  __shared__ uint64_t buf[kMergeWaves][kWave];
+  __shared__ uint64_t wl[kMergeWaves][kWave];
   const int bkv = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const uint64_t* src = lists + (size_t)bkv * nsplit * g.K;
+  // each wave merges every 8th local list (each is sorted descending) ...
   uint64_t run = 0;
-  for (int j = w; j < nsplit; j += 4) {   // each local list is sorted descending
+  for (int j = w; j < nsplit; j += kMergeWaves) {
     const uint64_t key = lane < g.K ? src[(size_t)j * g.K + lane] : 0ull;
     run = wave_merge_into(run, key, g.K, buf[w]);
   }
   wl[w][lane] = lane < g.K ? run : 0ull;
   __syncthreads();
+  // ... then the wave lists are merged pairwise in a tree
+  for (int half = kMergeWaves / 2; half >= 1; half >>= 1) {
+    if (w < half) {
+      const uint64_t mine = wl[w][lane], other = wl[w + half][lane];
+      const uint64_t mg = wave_merge_into(mine, other, g.K, buf[w]);
+      wl[w][lane] = lane < g.K ? mg : 0ull;
+    }
+    __syncthreads();
+  }
   if (w == 0) {
-    uint64_t top = wl[0][lane];
-    for (int x = 1; x < 4; ++x) top = wave_merge_into(top, wl[x][lane], g.K, buf[0]);
+    const uint64_t top = wl[0][lane];
     uint64_t asc = (lane < g.K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
     asc = wave_rank_sort64(asc, buf[0]);
     if (lane < g.K) sel_idx[(size_t)bkv * g.K + lane] = asc ? (int)(0xffffffffull - (asc - 1)) : -1;
@@ -309,61 +319,56 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
 }
 
 // ----------------------------------------------------------------------------
-// 4. merge of the nsplit partials of each (b, q head): one wave per row, lane
-//    -> dims 2l, 2l+1.  O = sum_s e^{M_s - M} O_s / sum_s e^{M_s - M} Z_s.
+// 4. merge of the nsplit partials of each (b, q head): one workgroup per row;
+//    wave w takes splits w, w+4, ...; lane -> dims 2l, 2l+1.
+//    O = sum_s e^{M_s - M} O_s / sum_s e^{M_s - M} Z_s,  LSE = M + log(...).
 // ----------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads)
 decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* __restrict__ out,
             float* __restrict__ lse_out) {
-  const int row = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;   // b * Hq + hq
-  const int lane = lane_id();
-  if (row >= g.B * g.Hq) return;
+  __shared__ float red[4][2 * kWave + 2];
+  const int row = blockIdx.x;                  // b * Hq + hq
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int b = row / g.Hq, hq = row % g.Hq;
   const int kvh = hq / g.G, h = hq % g.G;
   const int bkv = b * g.Hkv + kvh;
-  const float* pb = parts + (size_t)bkv * nsplit * g.G * kPartStride + (size_t)h * kPartStride;
   const size_t sstride = (size_t)g.G * kPartStride;
+  const float* pb = parts + (size_t)bkv * nsplit * sstride + (size_t)h * kPartStride;
   float m = -INFINITY;
   for (int s0 = 0; s0 < nsplit; s0 += kWave) {
-    const int sidx = s0 + lane;
-    const float ms = sidx < nsplit ? pb[sidx * sstride + kD] : -INFINITY;
-    m = fmaxf(m, wave_max(ms));
+    const int si = s0 + lane;
+    m = fmaxf(m, wave_max(si < nsplit ? pb[si * sstride + kD] : -INFINITY));
   }
   float z = 0.f, o0 = 0.f, o1 = 0.f;
   if (m != -INFINITY) {
-    int s = 0;
-    for (; s + 4 <= nsplit; s += 4) {
-      float2 ov[4];
-      float ms[4], zs[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float* ps = pb + (s + x) * sstride;
-        ov[x] = reinterpret_cast<const float2*>(ps)[lane];
-        ms[x] = ps[kD];
-        zs[x] = ps[kD + 1];
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float f = ms[x] == -INFINITY ? 0.f : __expf(ms[x] - m);
-        z += f * zs[x];
-        o0 += f * ov[x].x;
-        o1 += f * ov[x].y;
-      }
-    }
-    for (; s < nsplit; ++s) {
+#pragma unroll 4
+    for (int s = w; s < nsplit; s += 4) {
       const float* ps = pb + s * sstride;
       const float2 ov = reinterpret_cast<const float2*>(ps)[lane];
       const float ms = ps[kD];
       const float f = ms == -INFINITY ? 0.f : __expf(ms - m);
-      z += f * ps[kD + 1];
-      o0 += f * ov.x;
-      o1 += f * ov.y;
+      z = __builtin_fmaf(f, ps[kD + 1], z);
+      o0 = __builtin_fmaf(f, ov.x, o0);
+      o1 = __builtin_fmaf(f, ov.y, o1);
     }
   }
-  const float inv = z > 0.f ? 1.f / z : 0.f;
-  const uint32_t pk = (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
-  reinterpret_cast<uint32_t*>(out + (size_t)row * kD)[lane] = pk;
-  if (lane == 0 && lse_out) lse_out[row] = z > 0.f ? m + __logf(z) : -INFINITY;
+  red[w][2 * lane] = o0;
+  red[w][2 * lane + 1] = o1;
+  if (lane == 0) red[w][2 * kWave] = z;
+  __syncthreads();
+  if (w == 0) {
+    float zt = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      zt += red[x][2 * kWave];
+      a0 += red[x][2 * lane];
+      a1 += red[x][2 * lane + 1];
+    }
+    const float inv = zt > 0.f ? 1.f / zt : 0.f;
+    const uint32_t pk = (uint32_t)f32_to_bf16(a0 * inv) | ((uint32_t)f32_to_bf16(a1 * inv) << 16);
+    reinterpret_cast<uint32_t*>(out + (size_t)row * kD)[lane] = pk;
+    if (lane == 0 && lse_out) lse_out[row] = zt > 0.f ? m + __logf(zt) : -INFINITY;
+  }
 }
 
 struct DecodePlan {
@@ -384,9 +389,10 @@ DecodePlan plan(const Geometry& g) {
   p.R = R;
   p.cps = 256 * R;
   p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
-  // attention: about 1024 workgroups, at most 8 chunks each
+  // attention: one fusion slot per workgroup (latency hidden by parallelism)
+  // unless that gives fewer than 256 workgroups; then up to 8 per workgroup
   const int nslot = g.K + 1;
-  p.apc = min(8, max(1, (nslot * bkv + 1023) / 1024));
+  p.apc = min(8, max(1, 256 / max(1, nslot * bkv)));
   p.asplit = (nslot + p.apc - 1) / p.apc;
   return p;
 }
@@ -433,14 +439,15 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, c
   }
   prof_end(kDecodeScore, st);
   prof_begin(kDecodeMerge, st);
-  hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kThreads), 0, st, g, p.nsplit, d.lists, sel_idx);
+  hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kMergeWaves * kWave), 0, st, g, p.nsplit, d.lists,
+                     sel_idx);
   prof_end(kDecodeMerge, st);
   prof_begin(kDecodeAttend, st);
   hipLaunchKernelGGL(decode_attend, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc, Q,
                      (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
   prof_end(kDecodeAttend, st);
-  hipLaunchKernelGGL(decode_fuse, dim3((g.B * g.Hq + kThreads / kWave - 1) / (kThreads / kWave)),
-                     dim3(kThreads), 0, st, g, p.asplit, d.parts, (uint16_t*)out, lse);
+  hipLaunchKernelGGL(decode_fuse, dim3(g.B * g.Hq), dim3(kThreads), 0, st, g, p.asplit, d.parts,
+                     (uint16_t*)out, lse);
   return hipGetLastError();
 }
 
