@@ -79,29 +79,35 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   const int c1 = min(c0 + cps, ncand);
   const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
-  uint64_t keys[R];
+  // every row load of the wave's R blocks in flight before any arithmetic
+  uint4 raw[R][16];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int base = c0 + (r * 4 + w) * kWave;   // this wave's block of 64
-    uint4 raw[16];
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int c = base + grp * 16 + it;
-      raw[it] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
-                       : make_uint4(0, 0, 0, 0);
+      raw[r][it] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
+                          : make_uint4(0, 0, 0, 0);
     }
+  }
+  uint64_t keys[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int base = c0 + (r * 4 + w) * kWave;
     float mine = 0.f;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-      const uint4 u = raw[it];
+      const uint4 u = raw[r][it];
       float s = qb[0] * __uint_as_float(u.x << 16) + qb[1] * __uint_as_float(u.x & 0xffff0000u)
               + qb[2] * __uint_as_float(u.y << 16) + qb[3] * __uint_as_float(u.y & 0xffff0000u)
               + qb[4] * __uint_as_float(u.z << 16) + qb[5] * __uint_as_float(u.z & 0xffff0000u)
               + qb[6] * __uint_as_float(u.w << 16) + qb[7] * __uint_as_float(u.w & 0xffff0000u);
-      s += __shfl_xor(s, 8, kWave);
-      s += __shfl_xor(s, 4, kWave);
-      s += __shfl_xor(s, 2, kWave);
-      s += __shfl_xor(s, 1, kWave);
+      // sum over the 16 lanes of the row: rotations within a 16-lane DPP row
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x128, 0xf, 0xf, false));
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x124, 0xf, 0xf, false));
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x122, 0xf, 0xf, false));
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x121, 0xf, 0xf, false));
       if (it == sub) mine = s;
     }
     const int c = base + lane;   // = base + grp*16 + sub
@@ -168,12 +174,17 @@ constexpr int kPartStride = kD + 4;   // O[128], M, Z, pad  (floats)
 struct ChunkLoads {
   uint4 k[4];   // key tid/4, dims 32*(tid%4) .. +31
   uint4 v[4];   // V rows, 16 B per thread per step, coalesced
+  uint32_t lm;  // landmark dims 2*(tid%64), +1 (selected chunks)
+  float bias;
 };
 
 __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ Kc,
                                            const uint16_t* __restrict__ Vc, int n,
-                                           ChunkLoads& L) {
+                                           const uint16_t* __restrict__ lrow,
+                                           const float* __restrict__ brow, ChunkLoads& L) {
   const int tid = threadIdx.x;
+  L.lm = lrow ? reinterpret_cast<const uint32_t*>(lrow)[tid & 63] : 0u;
+  L.bias = brow ? *brow : 0.f;
   const int j = tid >> 2, qd = tid & 3;
 #pragma unroll
   for (int p4 = 0; p4 < 4; ++p4)
@@ -228,14 +239,24 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
 #pragma unroll
   for (int x = 0; x < 4; ++x) { M[x] = -INFINITY; Z[x] = 0.f; O0[x] = 0.f; O1[x] = 0.f; }
 
+  const uint16_t* Lb = lmk + (size_t)bkv * g.NCcap * kD;
+  const float* Bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   ChunkLoads cur, nxt;
   int first = 0;
   while (first < apc && cn[first] == 0) ++first;
-  if (first < apc) load_chunk(Kb + (size_t)ca[first] * kD, Vb + (size_t)ca[first] * kD, cn[first], cur);
+  if (first < apc) {
+    const int c0 = cc[first];
+    load_chunk(Kb + (size_t)ca[first] * kD, Vb + (size_t)ca[first] * kD, cn[first],
+               c0 >= 0 ? Lb + (size_t)c0 * kD : nullptr, (c0 >= 0 && Bb) ? Bb + c0 : nullptr, cur);
+  }
   for (int s = first; s < apc; ) {
     int nx = s + 1;
     while (nx < apc && cn[nx] == 0) ++nx;
-    if (nx < apc) load_chunk(Kb + (size_t)ca[nx] * kD, Vb + (size_t)ca[nx] * kD, cn[nx], nxt);
+    if (nx < apc) {
+      const int c1 = cc[nx];
+      load_chunk(Kb + (size_t)ca[nx] * kD, Vb + (size_t)ca[nx] * kD, cn[nx],
+                 c1 >= 0 ? Lb + (size_t)c1 * kD : nullptr, (c1 >= 0 && Bb) ? Bb + c1 : nullptr, nxt);
+    }
     const int n = cn[s], c = cc[s];
     // V of this chunk -> LDS
 #pragma unroll
@@ -272,10 +293,9 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
       lg[h][lane] = e / z;
       float sv;
       if (c >= 0) {
-        const uint16_t* lr = lmk + ((size_t)bkv * g.NCcap + c) * kD;
-        const float ps = qs[h][2 * lane] * bf16_to_f32(lr[2 * lane]) +
-                         qs[h][2 * lane + 1] * bf16_to_f32(lr[2 * lane + 1]);
-        sv = g.scale * wave_sum(ps) + (bias ? bias[(size_t)bkv * g.NCcap + c] : 0.f);
+        const float ps = qs[h][2 * lane] * __uint_as_float(cur.lm << 16) +
+                         qs[h][2 * lane + 1] * __uint_as_float(cur.lm & 0xffff0000u);
+        sv = g.scale * wave_sum(ps) + cur.bias;
       } else {
         sv = m + __logf(z);   // own chunk: its exact log-sum-exp
       }
@@ -385,7 +405,7 @@ DecodePlan plan(const Geometry& g) {
   int want_splits = max(1, 1024 / max(1, bkv));
   int per = (p.ncand + want_splits - 1) / want_splits;
   int R = 1;
-  while (R < 8 && R * 256 < per) R <<= 1;
+  while (R < 4 && R * 256 < per) R <<= 1;
   p.R = R;
   p.cps = 256 * R;
   p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
@@ -434,8 +454,7 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, c
   switch (p.R) {
     case 1: hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
     case 2: hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
-    case 4: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
-    default: hipLaunchKernelGGL(decode_score_select<8>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
+    default: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
   }
   prof_end(kDecodeScore, st);
   prof_begin(kDecodeMerge, st);
