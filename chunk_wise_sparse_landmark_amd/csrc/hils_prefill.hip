@@ -239,7 +239,7 @@ struct AttendSmem {
 // Start copying one chunk's 32 KB of fragments into an LDS buffer with direct
 // global->LDS loads (16 B per lane; lane i of a wave lands at the wave's LDS
 // base + 16 i).  Completion: s_waitcnt vmcnt(0), then a barrier.
-__device__ __forceinline__ void stage_async(const uint16_t* src, uint4* dst) {
+__device__ __forceinline__ void stage_async(const uint16_t* __restrict__ src, uint4* __restrict__ dst) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
   const int wbase = (threadIdx.x / kWave) * kWave;
 #pragma unroll
@@ -309,7 +309,7 @@ __device__ __forceinline__ void pack_p(const f32x4 (&s)[4], float f, bf16x8 (&pa
   }
 }
 
-__device__ __forceinline__ void load_frags(const uint4* src, bf16x8 (&f)[16]) {
+__device__ __forceinline__ void load_frags(const uint4* __restrict__ src, bf16x8 (&f)[16]) {
   const int lane = lane_id();
 #pragma unroll
   for (int x = 0; x < 16; ++x) f[x] = as_bf16x8(src[x * kWave + lane]);
@@ -320,10 +320,15 @@ __device__ __forceinline__ void load_frags(const uint4* src, bf16x8 (&f)[16]) {
 // block, then the softmaxes, then O += (rw / z) P V.  `act` has bit j set when
 // block j takes part (uniform over the wave); rw[j] is this lane's row weight.
 template <bool kMasked>
-__device__ __forceinline__ void chunk_step(const uint4* kvb, const bf16x8 (&qf)[kBlocksPerWave][4],
+__device__ __forceinline__ void chunk_step(const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
+                                           const uint16_t* __restrict__ nsrc,
+                                           const bf16x8 (&qf)[kBlocksPerWave][4],
                                            float sc2, unsigned act, const int (&vis)[kBlocksPerWave],
                                            const float (&rw)[kBlocksPerWave],
                                            f32x4 (&o)[kBlocksPerWave][8]) {
+  // the next chunk's direct global->LDS copy into the other buffer (disjoint
+  // from kvb: both are restrict, so the reads below need not wait for it)
+  if (nsrc) stage_async(nsrc, nxt);
   f32x4 s[kBlocksPerWave][4];
   {
     bf16x8 kf[16];
@@ -496,7 +501,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   //      copied into the other buffer while one is computed
   int cur = 0;
   if (g.keep_own) {
-    if (nunion > 0) stage_async(KVg + (size_t)sm.ulist[0] * kChunkElems, sm.kv[1]);
+    const uint16_t* nsrc = nunion > 0 ? KVg + (size_t)sm.ulist[0] * kChunkElems : nullptr;
     int vis[kBlocksPerWave];
     float rw[kBlocksPerWave];
 #pragma unroll
@@ -505,14 +510,14 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       vis[j] = qi + 1;                       // key kk of the chunk visible when kk <= qi
       rw[j] = sm.wown[qi * kG + (r16 & 3)];
     }
-    chunk_step<true>(sm.kv[0], qf, sc2, (1u << kBlocksPerWave) - 1, vis, rw, o);
+    chunk_step<true>(sm.kv[0], sm.kv[1], nsrc, qf, sc2, (1u << kBlocksPerWave) - 1, vis, rw, o);
     stage_wait();
     __syncthreads();
     cur = 1;
   }
   for (int u = 0; u < nunion; ++u, cur ^= 1) {
     const int c = sm.ulist[u];
-    if (u + 1 < nunion) stage_async(KVg + (size_t)sm.ulist[u + 1] * kChunkElems, sm.kv[cur ^ 1]);
+    const uint16_t* nsrc = u + 1 < nunion ? KVg + (size_t)sm.ulist[u + 1] * kChunkElems : nullptr;
     const uint64_t qmk = sm.qmask[c];
     unsigned act = 0;
     int vis[kBlocksPerWave];
@@ -526,7 +531,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       vis[j] = kS;
       rw[j] = slot != 0xff ? sm.wts[(qi * K + slot) * kG + (r16 & 3)] : 0.f;
     }
-    chunk_step<false>(sm.kv[cur], qf, sc2, act, vis, rw, o);
+    chunk_step<false>(sm.kv[cur], sm.kv[cur ^ 1], nsrc, qf, sc2, act, vis, rw, o);
     stage_wait();
     __syncthreads();
   }
