@@ -27,6 +27,14 @@ template <> struct Elem<uint16_t> {
   __device__ static __forceinline__ void st(uint16_t* p, float x) { *p = f32_to_bf16(x); }
 };
 
+// Workgroup barrier for LDS data only: this wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it leaves outstanding global loads,
+// stores and global->LDS copies in flight (their waits are the caller's).  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------- wave primitives
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
