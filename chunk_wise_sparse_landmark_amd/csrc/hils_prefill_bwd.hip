@@ -642,6 +642,82 @@ __device__ __forceinline__ void stage_tile(const Geometry& g, const uint16_t* __
   }
 }
 
+// One tile: start copying the next tile into `nxt`, then accumulate this one.
+// `tb` and `nxt` are restrict (distinct buffers), so the LDS reads of this
+// tile need not wait for the copy.
+__device__ __forceinline__ void chunk_tile_step(
+    const Geometry& g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
+    const BwdWs& ws, int b, int kvh, int bkv, int w, int lane, int key, float sc2, int t,
+    bool more, const TileBuf* __restrict__ tbp, TileBuf* __restrict__ nxt,
+    const uint16_t* __restrict__ eq, const uint8_t* __restrict__ es, const bf16x8 (&kB)[4],
+    const bf16x8 (&vB)[4], f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[8], float& dbt) {
+  const TileBuf& tb = *tbp;
+  if (more) stage_tile(g, q, dout, ws, b, kvh, bkv, eq, es, t + 1, *nxt);
+  // S and U for this wave's keys; D layout rows (mt, qq = l/16, h = i), key l%16
+  f32x4 s[2], u[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    f32x4 as = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      as = mfma(as_bf16x8(tb.qa[(mt * 4 + ks) * kWave + lane]), kB[ks], as);
+      au = mfma(as_bf16x8(tb.da[(mt * 4 + ks) * kWave + lane]), vB[ks], au);
+    }
+    s[mt] = as;
+    u[mt] = au;
+  }
+  float a8[8], d8[8], ds[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int e = t * 8 + 4 * mt + (lane >> 4);
+    const int sl = es[e];
+    const bool valid = sl != 0xff;
+    const bool own = sl == g.K;
+    const int qq = eq[valid ? e : t * 8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 st = tb.st[(4 * mt + (lane >> 4)) * 4 + i];
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -st.y));
+      if (!valid || (own && key > qq)) p = 0.f;
+      const float wp = st.x * p;
+      a8[4 * mt + i] = wp;
+      d8[4 * mt + i] = wp * (u[mt][i] - st.z);
+      ds[mt][i] = (valid && !own) ? st.w : 0.f;
+    }
+  }
+  const bf16x8 Awp = pack_bf16x8(a8), Adl = pack_bf16x8(d8);
+  const uint16_t* qi0 = reinterpret_cast<const uint16_t*>(tb.qi) + (lane >> 4) * kD * kG;
+  const uint16_t* qi1 = qi0 + 4 * kD * kG;
+  const uint16_t* di0 = reinterpret_cast<const uint16_t*>(tb.di) + (lane >> 4) * kD * kG;
+  const uint16_t* di1 = di0 + 4 * kD * kG;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int col = (16 * db + (lane & 15)) * kG;
+    const uint2 q0 = *reinterpret_cast<const uint2*>(qi0 + col);
+    const uint2 q1 = *reinterpret_cast<const uint2*>(qi1 + col);
+    const uint2 d0 = *reinterpret_cast<const uint2*>(di0 + col);
+    const uint2 d1 = *reinterpret_cast<const uint2*>(di1 + col);
+    dv[db] = mfma(Awp, as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dv[db]);
+    dk[db] = mfma(Adl, as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dk[db]);
+    if (w == 0) {
+      const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
+      float tacc = dlm[db];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2], __uint_as_float(qw[e] << 16), tacc);
+        tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2 + 1], __uint_as_float(qw[e] & 0xffff0000u), tacc);
+      }
+      dlm[db] = tacc;
+    }
+  }
+  if (w == 0 && (lane & 15) == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dbt += ds[mt][i];
+  }
+}
+
 __global__ void __launch_bounds__(kChunkThreads)
 prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, BwdWs ws,
@@ -728,71 +804,8 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < ntile; ++t) {
-    const TileBuf& tb = sm.tb[t & 1];
-    if (t + 1 < ntile) stage_tile(g, q, dout, ws, b, kvh, bkv, sm.eq, sm.es, t + 1, sm.tb[(t + 1) & 1]);
-    // S and U for this wave's keys; D layout rows (mt, qq = l/16, h = i), key l%16
-    f32x4 s[2], u[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 as = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        as = mfma(as_bf16x8(tb.qa[(mt * 4 + ks) * kWave + lane]), kB[ks], as);
-        au = mfma(as_bf16x8(tb.da[(mt * 4 + ks) * kWave + lane]), vB[ks], au);
-      }
-      s[mt] = as;
-      u[mt] = au;
-    }
-    float a8[8], d8[8], ds[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int e = t * 8 + 4 * mt + (lane >> 4);
-      const int sl = sm.es[e];
-      const bool valid = sl != 0xff;
-      const bool own = sl == g.K;
-      const int qq = sm.eq[valid ? e : t * 8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 st = tb.st[(4 * mt + (lane >> 4)) * 4 + i];
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -st.y));
-        if (!valid || (own && key > qq)) p = 0.f;
-        const float wp = st.x * p;
-        a8[4 * mt + i] = wp;
-        d8[4 * mt + i] = wp * (u[mt][i] - st.z);
-        ds[mt][i] = (valid && !own) ? st.w : 0.f;
-      }
-    }
-    const bf16x8 Awp = pack_bf16x8(a8), Adl = pack_bf16x8(d8);
-    const uint16_t* qi0 = reinterpret_cast<const uint16_t*>(tb.qi) + (lane >> 4) * kD * kG;
-    const uint16_t* qi1 = qi0 + 4 * kD * kG;
-    const uint16_t* di0 = reinterpret_cast<const uint16_t*>(tb.di) + (lane >> 4) * kD * kG;
-    const uint16_t* di1 = di0 + 4 * kD * kG;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int col = (16 * db + (lane & 15)) * kG;
-      const uint2 q0 = *reinterpret_cast<const uint2*>(qi0 + col);
-      const uint2 q1 = *reinterpret_cast<const uint2*>(qi1 + col);
-      const uint2 d0 = *reinterpret_cast<const uint2*>(di0 + col);
-      const uint2 d1 = *reinterpret_cast<const uint2*>(di1 + col);
-      dv[db] = mfma(Awp, as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dv[db]);
-      dk[db] = mfma(Adl, as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dk[db]);
-      if (w == 0) {
-        const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
-        float tacc = dlm[db];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2], __uint_as_float(qw[e] << 16), tacc);
-          tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2 + 1], __uint_as_float(qw[e] & 0xffff0000u), tacc);
-        }
-        dlm[db] = tacc;
-      }
-    }
-    if (w == 0 && (lane & 15) == 0) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dbt += ds[mt][i];
-    }
+    chunk_tile_step(g, q, dout, ws, b, kvh, bkv, w, lane, key, sc2, t, t + 1 < ntile,
+                    &sm.tb[t & 1], &sm.tb[(t + 1) & 1], sm.eq, sm.es, kB, vB, dv, dk, dlm, dbt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
