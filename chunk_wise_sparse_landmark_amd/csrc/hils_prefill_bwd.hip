@@ -248,7 +248,7 @@ struct RowsSmem {
   int wcount[kRowWaves];
 };
 
-__device__ __forceinline__ void stage48(const uint16_t* src, uint4* dst) {
+__device__ __forceinline__ void stage48(const uint16_t* __restrict__ src, uint4* __restrict__ dst) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
   const int wbase = (threadIdx.x / kWave) * kWave;
 #pragma unroll
@@ -260,7 +260,7 @@ __device__ __forceinline__ void stage48(const uint16_t* src, uint4* dst) {
 
 __device__ __forceinline__ void stage_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-__device__ __forceinline__ void load16(const uint4* src, bf16x8 (&f)[16]) {
+__device__ __forceinline__ void load16(const uint4* __restrict__ src, bf16x8 (&f)[16]) {
   const int lane = lane_id();
 #pragma unroll
   for (int x = 0; x < 16; ++x) f[x] = as_bf16x8(src[x * kWave + lane]);
@@ -361,6 +361,54 @@ __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(pa[ks], kb[db * 2 + ks], dq[db]);
   return make_float4(w, lse2, kOwn ? Drow : Dc, 0.f);
+}
+
+// The own-chunk step and a union-chunk step of the rows pass.  Each first
+// starts the next chunk's copy into `nxt`; the chunk buffers and LDS tables are
+// restrict so the reads of `kvb` need not wait for that copy.
+__device__ __forceinline__ void rows_own_step(
+    const Geometry& g, const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
+    const uint16_t* __restrict__ nsrc, const float* __restrict__ Dr,
+    const float* __restrict__ LSE2, const bf16x8 (&qf)[kRowBlocks][4],
+    const bf16x8 (&df)[kRowBlocks][4], float sc2, const BwdWs& ws, int b, int kvh, int i0,
+    int w, f32x4 (&dq)[kRowBlocks][8]) {
+  const int lane = lane_id(), r16 = lane & 15;
+  const int K = g.K, L = g.Lq;
+  if (nsrc) stage48(nsrc, nxt);
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) {
+    const int qi = (w * kRowBlocks + j) * 4 + (r16 >> 2), h = r16 & 3;
+    const float4 st = block_bwd<true>(kvb, qf[j], df[j], sc2, qi + 1, 0.f, Dr[qi * kG + h],
+                                      LSE2[qi * kG + h], dq[j]);
+    if (lane < 16)
+      ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * (size_t)(K + 1) + K] = st;
+  }
+}
+
+__device__ __forceinline__ void rows_union_step(
+    const Geometry& g, const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
+    const uint16_t* __restrict__ nsrc, const uint8_t* __restrict__ slotmap,
+    float* __restrict__ wts, const float* __restrict__ Dr, uint64_t qmk, int c,
+    const bf16x8 (&qf)[kRowBlocks][4], const bf16x8 (&df)[kRowBlocks][4], float sc2,
+    const BwdWs& ws, int b, int kvh, int i0, int w, f32x4 (&dq)[kRowBlocks][8]) {
+  const int lane = lane_id(), r16 = lane & 15;
+  const int K = g.K, L = g.Lq;
+  if (nsrc) stage48(nsrc, nxt);
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) {
+    const int blk = w * kRowBlocks + j;
+    if (((qmk >> (blk * 4)) & 0xfull) == 0) continue;
+    const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
+    const int slot = slotmap[qi * kMaxNCb + c];
+    const float wv = slot != 0xff ? wts[(qi * K + slot) * kG + h] : 0.f;
+    const float dr = Dr[qi * kG + h];
+    float4 st = block_bwd<false>(kvb, qf[j], df[j], sc2, kS, wv, dr, 0.f, dq[j]);
+    st.w = wv * (st.z - dr);                                         // ds_c
+    if (lane < 16 && slot != 0xff) {
+      ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * (size_t)(K + 1) + slot] = st;
+      wts[(qi * K + slot) * kG + h] = st.w;
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kRowThreads)
@@ -469,41 +517,20 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
 #pragma unroll
     for (int db = 0; db < 8; ++db) dq[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const size_t srow_stride = (size_t)(K + 1);
   int cur = 0;
   if (g.keep_own) {
-    if (nunion > 0) stage48(Fg + (size_t)sm.ulist[0] * kBwdChunkElems, sm.kv[1]);
-#pragma unroll
-    for (int j = 0; j < kRowBlocks; ++j) {
-      const int qi = (w * kRowBlocks + j) * 4 + (r16 >> 2), h = r16 & 3;
-      const float4 st = block_bwd<true>(sm.kv[0], qf[j], df[j], sc2, qi + 1, 0.f,
-                                        sm.Dr[qi * kG + h], sm.LSE2[qi * kG + h], dq[j]);
-      if (lane < 16)
-        ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * srow_stride + K] = st;
-    }
+    rows_own_step(g, sm.kv[0], sm.kv[1],
+                  nunion > 0 ? Fg + (size_t)sm.ulist[0] * kBwdChunkElems : nullptr, sm.Dr, sm.LSE2,
+                  qf, df, sc2, ws, b, kvh, i0, w, dq);
     stage_wait_all();
     __syncthreads();
     cur = 1;
   }
   for (int uidx = 0; uidx < nunion; ++uidx, cur ^= 1) {
     const int c = sm.ulist[uidx];
-    if (uidx + 1 < nunion) stage48(Fg + (size_t)sm.ulist[uidx + 1] * kBwdChunkElems, sm.kv[cur ^ 1]);
-    const uint64_t qmk = sm.qmask[c];
-#pragma unroll
-    for (int j = 0; j < kRowBlocks; ++j) {
-      const int blk = w * kRowBlocks + j;
-      if (((qmk >> (blk * 4)) & 0xfull) == 0) continue;
-      const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
-      const int slot = sm.slotmap[qi * kMaxNCb + c];
-      const float wv = slot != 0xff ? sm.wts[(qi * K + slot) * kG + h] : 0.f;
-      const float Dr = sm.Dr[qi * kG + h];
-      float4 st = block_bwd<false>(sm.kv[cur], qf[j], df[j], sc2, kS, wv, Dr, 0.f, dq[j]);
-      st.w = wv * (st.z - Dr);                                         // ds_c
-      if (lane < 16 && slot != 0xff) {
-        ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * srow_stride + slot] = st;
-        sm.wts[(qi * K + slot) * kG + h] = st.w;
-      }
-    }
+    rows_union_step(g, sm.kv[cur], sm.kv[cur ^ 1],
+                    uidx + 1 < nunion ? Fg + (size_t)sm.ulist[uidx + 1] * kBwdChunkElems : nullptr,
+                    sm.slotmap, sm.wts, sm.Dr, sm.qmask[c], c, qf, df, sc2, ws, b, kvh, i0, w, dq);
     stage_wait_all();
     __syncthreads();
   }
