@@ -52,58 +52,41 @@ constexpr int kChunkFrags = 32;            // 16 K + 16 V fragments per chunk
 constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
 
 // ----------------------------------------------------------------------------
-// Top-K of R keys per lane (candidate c = r*64 + lane), written as ascending
-// chunk ids (-1 padded) to dst[0..K).  Keys are unique apart from 0 (empty).
-// K * R <= 64: order-preserving compaction + rank count, no sort.
+// Top-K of R composite keys per lane (candidate c = r*64 + lane, key 0 =
+// empty), written as ascending chunk ids (-1 padded) to dst[0..K).  The K-th
+// largest key is found bit by bit from the top with wave ballots (count of
+// keys >= prefix); keys are unique, so exactly the keys >= it are selected.
+// With chunk ids below 256 the low word of every key is 0xffffff00 | ~id, so
+// only the 32 score bits and the 8 id bits are searched.
 // ----------------------------------------------------------------------------
 template <int R>
-__device__ void select_ascending(uint64_t (&keys)[R], int K, uint64_t* buf, uint64_t* buf2,
-                                 int32_t* dst) {
+__device__ __forceinline__ void select_ascending(const uint64_t (&keys)[R], int K, int32_t* dst) {
   const int lane = lane_id();
-  if (K * R > kWave) {
-    const uint64_t top = wave_topk<R>(keys, K, buf);
-    const uint64_t asc = (lane < K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
-    const uint64_t srt = wave_rank_sort64(asc, buf);
-    if (lane < K) dst[lane] = srt ? (int)(0xffffffffull - (srt - 1)) : -1;
-    return;
-  }
-  uint64_t lm = keys[0];
+  uint64_t p = 0;
+  for (int bit = 63; bit >= 32; --bit) {
+    const uint64_t t = p | (1ull << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int r = 1; r < R; ++r) lm = keys[r] > lm ? keys[r] : lm;
-  buf[lane] = lm;
-  wave_sync_lds();
-  int rank = 0;
-  const ulonglong2* b2 = reinterpret_cast<const ulonglong2*>(buf);
-#pragma unroll
-  for (int j = 0; j < kWave / 2; ++j) {
-    const ulonglong2 kk = b2[j];
-    rank += (kk.x > lm) + (kk.y > lm);
+    for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[r] >= t));
+    if (cnt >= K) p = t;
   }
-  const uint64_t hit = __ballot(rank == K - 1 && lm != 0);
-  uint64_t tau = 1;
-  if (hit) tau = shfl_u64(lm, __ffsll((long long)hit) - 1);
+  p |= 0xffffff00ull;
+  for (int bit = 7; bit >= 0; --bit) {
+    const uint64_t t = p | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[r] >= t));
+    if (cnt >= K) p = t;
+  }
   int base = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const bool pred = keys[r] >= tau;
+    const bool pred = keys[r] != 0ull && keys[r] >= p;
     const uint64_t m = __ballot(pred);
-    if (pred) buf2[base + mask_rank(m)] = keys[r];
+    if (pred) dst[base + mask_rank(m)] = r * kWave + lane;
     base += __popcll(m);
   }
-  wave_sync_lds();
-  const uint64_t key = lane < base ? buf2[lane] : 0ull;
-  int rank2 = 0;
-  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(buf2);
-  for (int j = 0; j < (base + 1) / 2; ++j) {
-    const ulonglong2 kk = c2[j];
-    rank2 += (kk.x > key) + ((2 * j + 1 < base) && (kk.y > key));
-  }
-  const uint64_t sel_key = (key != 0 && rank2 < K) ? key : 0ull;
-  wave_sync_lds();
-  const uint64_t m = __ballot(sel_key != 0);
-  const int nsel = __popcll(m);
-  if (sel_key != 0) dst[mask_rank(m)] = key_index(sel_key);
-  if (lane >= nsel && lane < K) dst[lane] = -1;
+  for (int x = base + lane; x < K; x += kWave) dst[x] = -1;
 }
 
 // ----------------------------------------------------------------------------
@@ -124,8 +107,6 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
                uint16_t* __restrict__ kvf) {
   constexpr int NCP = R * kWave;
   __shared__ float gs[kWin][NCP + 1];
-  __shared__ uint64_t buf[4][kWave];
-  __shared__ uint64_t buf2[4][kWave];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
   const int nbkv = g.B * g.Hkv;            // (b, kv head) fastest: one head per XCD
   const int bkv = blockIdx.x % nbkv;
@@ -216,8 +197,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       const int c = r * kWave + lane;
       keys[r] = c < ncand ? make_key(gs[qrow][c], c) : 0ull;
     }
-    select_ascending<R>(keys, g.K, buf[w], buf2[w],
-                        sel_idx + ((size_t)bkv * g.Lq + i0 + qrow) * g.K);
+    select_ascending<R>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + qrow) * g.K);
   }
 }
 
