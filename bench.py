@@ -363,12 +363,15 @@ def run_train(hl, cfg, steps, warmup, ev):
         hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out, dev["dout"], idx,
                          lse, **kw)
 
-    kern = "prefill_bwd_chunks" if launched(hl, ev, "prefill_bwd_chunks", lambda: step(0)) else "generic_bwd_chunks"
-    ms, kms, n = timed(step, steps, warmup, ev, kern, hl)
+    mfma = launched(hl, ev, "prefill_bwd_rows", lambda: step(0))
+    kernels = ["prefill_bwd_rows", "prefill_bwd_chunks"] if mfma else ["generic_bwd_rows", "generic_bwd_chunks"]
+    ms, kms0, n0 = timed(step, steps, warmup, ev, kernels[0], hl)
+    _, kms1, n1 = timed(step, steps, 1, ev, kernels[1], hl)
     flops = forward_flops(cfg) + backward_flops(cfg)
     res = dict(value=flops / (ms * 1e-3) / 1e12, unit="TFLOP/s", ms_per_step=ms,
                frac_of_bf16_peak=flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-               dominant_kernel=dict(kernel=kern, kernel_ms=kms, launches=n))
+               backward_kernels={kernels[0]: dict(kernel_ms=kms0, launches=n0),
+                                 kernels[1]: dict(kernel_ms=kms1, launches=n1)})
     del dev
     torch.cuda.empty_cache()
     return res
