@@ -126,7 +126,7 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
 // ----------------------------------------------------------------------------
 // 2. merge the nsplit local lists of one (b, kv head); write ascending ids.
 // ----------------------------------------------------------------------------
-constexpr int kMergeWaves = 8;
+constexpr int kMergeWaves = 16;
 __global__ void __launch_bounds__(kMergeWaves * kWave)
 decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
              int32_t* __restrict__ sel_idx) {
@@ -135,7 +135,7 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
   const int bkv = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const uint64_t* src = lists + (size_t)bkv * nsplit * g.K;
-  // each wave merges every 8th local list (each is sorted descending) ...
+  // each wave merges every 16th local list (each is sorted descending) ...
   uint64_t run = 0;
   for (int j = w; j < nsplit; j += kMergeWaves) {
     const uint64_t key = lane < g.K ? src[(size_t)j * g.K + lane] : 0ull;
@@ -155,7 +155,7 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
   if (w == 0) {
     const uint64_t top = wl[0][lane];
     uint64_t asc = (lane < g.K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
-    asc = wave_rank_sort64(asc, buf[0]);
+    asc = wave_sort64_desc(asc);
     if (lane < g.K) sel_idx[(size_t)bkv * g.K + lane] = asc ? (int)(0xffffffffull - (asc - 1)) : -1;
   }
 }
