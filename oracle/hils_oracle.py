@@ -41,7 +41,13 @@ design notes of the repository):
 * with keep_own_chunk the visible tokens of the own chunk are attended exactly
   and enter the fusion with score = their exact LogSumExp (the one-chunk case
   of the chunk-aligned local window); fusion weights are per head;
-* an empty fusion set gives O = 0 and LSE = -inf.
+* an empty fusion set gives O = 0 and LSE = -inf;
+* landmark formation (the step before scoring): the chunk's landmark query lq_c
+  induces p = softmax_j(scale <lq_c, k_j>) over its S keys; the landmark key is
+  sum_j p_j k_j and the bias the entropy -sum_j p_j log p_j.  This is the
+  first-order Taylor expansion of the chunk's LogSumExp at lq_c, so the score
+  equals the exact chunk mass for q = lq_c [HSADR §3 "Linear surrogate for
+  chunk mass"; the entropy limits log S / 0 are the page's].
 
 Parity pins (what ties this oracle to something other than itself) live in
 tests/test_oracle_pins.py: dense attention (S = 1, all chunks), exact chunk mass
@@ -292,3 +298,66 @@ def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
                 for c, val in r["dbias"]:
                     dbias[b, g, c] += val
     return dq, dk, dv, dlmk, dbias
+
+
+# ----------------------------------------------------------------------------
+# landmark formation  [HSADR §3 "Linear surrogate for chunk mass": the learned
+# landmark query induces a distribution over the chunk's keys; the weighted key
+# sum is the summary and an entropy term is the bias]
+# ----------------------------------------------------------------------------
+def _chunk_distribution(lq_c, k_blk, sc):
+    l = sc * (k_blk @ lq_c)
+    return np.exp(l - _logsumexp(l))
+
+
+def landmark_formation(lq, k, *, chunk_size, scale=None):
+    """Landmark key and entropy bias of every complete chunk.
+
+    lq: [B, Hkv, NCcap, d] landmark queries (rows c < NC are used); k: [B, Hkv,
+    Lkv, d].  For chunk c: p = softmax_j(scale * <lq_c, k_j>) over its S keys,
+    lmk_c = sum_j p_j k_j and bias_c = -sum_j p_j log p_j.  Rows c >= NC are 0.
+    """
+    B, Hkv, Lkv, d = k.shape
+    S = int(chunk_size)
+    NC = Lkv // S
+    sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    lmk = np.zeros(lq.shape)
+    bias = np.zeros(lq.shape[:3])
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(NC):
+                kb = _f64(k[b, g, c * S:(c + 1) * S])
+                p = _chunk_distribution(_f64(lq[b, g, c]), kb, sc)
+                lmk[b, g, c] = p @ kb
+                nz = p > 0
+                bias[b, g, c] = -float(np.sum(p[nz] * np.log(p[nz])))
+    return lmk, bias
+
+
+def landmark_formation_backward(lq, k, dlmk, dbias, *, chunk_size, scale=None):
+    """Gradients of sum(<dlmk, lmk>) + sum(dbias * bias) for lq and k.
+
+    With l_j = scale <lq, k_j>, p = softmax(l): dp_j = <dlmk, k_j> - dbias (log p_j
+    + 1); dl_j = p_j (dp_j - sum_i p_i dp_i); dlq = scale sum_j dl_j k_j and
+    dk_j = scale dl_j lq + p_j dlmk.  Keys of an incomplete tail chunk get 0.
+    """
+    B, Hkv, Lkv, d = k.shape
+    S = int(chunk_size)
+    NC = Lkv // S
+    sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    dlq = np.zeros(lq.shape)
+    dk = np.zeros(k.shape)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(NC):
+                kb = _f64(k[b, g, c * S:(c + 1) * S])
+                q = _f64(lq[b, g, c])
+                p = _chunk_distribution(q, kb, sc)
+                dm = _f64(dlmk[b, g, c])
+                db = 0.0 if dbias is None else float(dbias[b, g, c])
+                logp = np.log(np.maximum(p, 1e-300))
+                dp = kb @ dm - db * (logp + 1.0)
+                dl = p * (dp - float(p @ dp))
+                dlq[b, g, c] = sc * (dl @ kb)
+                dk[b, g, c * S:(c + 1) * S] = sc * np.outer(dl, q) + np.outer(p, dm)
+    return dlq, dk

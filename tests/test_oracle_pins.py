@@ -12,7 +12,10 @@
   permutation inside a chunk and a constant bias shift change nothing; GQA with
   identical heads equals one head;
 * central finite differences for every gradient, the dense-attention gradients
-  from torch autograd, and the zero-sum of the fusion-score gradients.
+  from torch autograd, and the zero-sum of the fusion-score gradients;
+* landmark formation: the surrogate score equals the exact chunk LogSumExp (and
+  its gradient) at the landmark query, uniform and one-hot limits (bias log S and
+  0), the entropy against scipy, and finite differences of its backward.
 """
 import heapq
 import json
@@ -25,7 +28,10 @@ import pytest
 import scipy.special
 import torch
 
-from oracle.hils_oracle import ref_forward, ref_decode, ref_backward
+import scipy.stats
+
+from oracle.hils_oracle import (ref_forward, ref_decode, ref_backward, landmark_formation,
+                                landmark_formation_backward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_example.json")
 
@@ -373,3 +379,88 @@ def test_fusion_score_gradients_sum_to_zero():
                                      keep_own_chunk=False)
     assert abs(dbias.sum()) < 1e-12
     assert np.count_nonzero(dbias) == K
+
+
+# --------------------------------------------------------------------------- landmark formation
+def _lm_inputs(rng, B=1, Hkv=2, L=192, d=16, S=32):
+    k = rng.standard_normal((B, Hkv, L, d))
+    lq = rng.standard_normal((B, Hkv, L // S + 1, d))   # one spare row past the chunks
+    return lq, k
+
+
+def test_landmark_surrogate_exact_at_its_query():
+    """s(q) = scale <q, lmk_c> + bias_c is the first-order Taylor expansion of the
+    chunk's LogSumExp at q = lq_c: value and gradient agree there."""
+    rng = np.random.default_rng(41)
+    lq, k = _lm_inputs(rng)
+    S, d = 32, k.shape[-1]
+    sc = 1.0 / math.sqrt(d)
+    lmk, bias = landmark_formation(lq, k, chunk_size=S)
+    for g in range(2):
+        for c in range(k.shape[2] // S):
+            kb = k[0, g, c * S:(c + 1) * S]
+            q = lq[0, g, c]
+            exact = scipy.special.logsumexp(sc * kb @ q)
+            assert abs(sc * q @ lmk[0, g, c] + bias[0, g, c] - exact) < 1e-12
+            # d/dq logsumexp(sc k q) at q = lq_c equals sc * lmk_c
+            eps = 1e-6
+            grad = np.array([(scipy.special.logsumexp(sc * kb @ (q + eps * e)) -
+                              scipy.special.logsumexp(sc * kb @ (q - eps * e))) / (2 * eps)
+                             for e in np.eye(d)])
+            assert np.abs(grad - sc * lmk[0, g, c]).max() < 1e-7
+    assert np.all(lmk[0, :, -1] == 0) and np.all(bias[0, :, -1] == 0)
+
+
+def test_landmark_uniform_and_one_hot_limits():
+    rng = np.random.default_rng(42)
+    S, d = 64, 8
+    k = rng.standard_normal((1, 1, S, d))
+    lmk, bias = landmark_formation(np.zeros((1, 1, 1, d)), k, chunk_size=S)
+    assert abs(bias[0, 0, 0] - math.log(S)) < 1e-12               # uniform: log S
+    assert np.abs(lmk[0, 0, 0] - k[0, 0].mean(axis=0)).max() < 1e-12
+    k2 = 0.01 * rng.standard_normal((1, 1, S, d))
+    k2[0, 0, 5] = 0.0
+    k2[0, 0, 5, 0] = 1.0
+    lq = np.zeros((1, 1, 1, d))
+    lq[0, 0, 0, 0] = 400.0 * math.sqrt(d)                           # key 5 dominates
+    lmk, bias = landmark_formation(lq, k2, chunk_size=S)
+    assert bias[0, 0, 0] < 1e-6                                     # one-hot: 0
+    assert np.abs(lmk[0, 0, 0] - k2[0, 0, 5]).max() < 1e-6
+
+
+def test_landmark_entropy_matches_scipy():
+    rng = np.random.default_rng(43)
+    lq, k = _lm_inputs(rng, d=32)
+    S = 32
+    sc = 1.0 / math.sqrt(32)
+    lmk, bias = landmark_formation(lq, k, chunk_size=S)
+    for g in range(2):
+        for c in range(k.shape[2] // S):
+            kb = k[0, g, c * S:(c + 1) * S]
+            p = scipy.special.softmax(sc * kb @ lq[0, g, c])
+            assert abs(bias[0, g, c] - scipy.stats.entropy(p)) < 1e-12
+            assert np.abs(lmk[0, g, c] - p @ kb).max() < 1e-12
+
+
+def test_landmark_backward_finite_differences():
+    rng = np.random.default_rng(44)
+    lq, k = _lm_inputs(rng, L=100, d=8, S=32)   # tail keys 96..99 belong to no chunk
+    S = 32
+    R = rng.standard_normal(lq.shape)
+    r = rng.standard_normal(lq.shape[:3])
+
+    def loss(lq_, k_):
+        lm, bi = landmark_formation(lq_, k_, chunk_size=S)
+        return float((R * lm).sum() + (r * bi).sum())
+
+    dlq, dk = landmark_formation_backward(lq, k, R, r, chunk_size=S)
+    eps = 1e-6
+    for idx in [(0, 0, 0, 1), (0, 1, 2, 5), (0, 1, 1, 0)]:
+        e = np.zeros_like(lq)
+        e[idx] = eps
+        assert abs((loss(lq + e, k) - loss(lq - e, k)) / (2 * eps) - dlq[idx]) < 1e-6
+    for idx in [(0, 0, 3, 2), (0, 1, 40, 7), (0, 0, 95, 0), (0, 1, 97, 3)]:
+        e = np.zeros_like(k)
+        e[idx] = eps
+        assert abs((loss(lq, k + e) - loss(lq, k - e)) / (2 * eps) - dk[idx]) < 1e-6
+    assert np.all(dk[:, :, 96:] == 0) and np.all(dlq[:, :, -1] == 0)
