@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "hils.h"
@@ -160,6 +161,40 @@ hils_status forward_like(int op, const hils_params* p, const void* q, const void
       "forward launch");
 }
 
+// Checks of the landmark-formation entry points: only the fields they use.  A
+// pointer is required when the buffer it names is not empty.
+struct Buf {
+  const void* ptr;
+  bool required;
+};
+
+hils_status check_landmarks(const hils_params* p, std::initializer_list<Buf> bufs) {
+  if (!p) return fail(HILS_ERR_INVALID_ARG, "params is null");
+  if (p->batch < 0 || p->heads_kv < 0 || p->head_dim < 0 || p->seq_kv < 0 || p->num_landmarks < 0)
+    return fail(HILS_ERR_INVALID_ARG, "negative size");
+  if (p->dtype != HILS_F32 && p->dtype != HILS_BF16)
+    return fail(HILS_ERR_INVALID_ARG, "dtype %d is not HILS_F32 or HILS_BF16", p->dtype);
+  if (p->chunk_size < 1) return fail(HILS_ERR_INVALID_ARG, "chunk_size must be >= 1");
+  if (p->head_dim < 1) return fail(HILS_ERR_INVALID_ARG, "head_dim must be >= 1");
+  if (!std::isfinite(p->scale)) return fail(HILS_ERR_INVALID_ARG, "scale is not finite");
+  if (p->num_landmarks < p->seq_kv / p->chunk_size)
+    return fail(HILS_ERR_INVALID_ARG, "num_landmarks (%d) < seq_kv / chunk_size (%d)",
+                p->num_landmarks, p->seq_kv / p->chunk_size);
+  if (!hils::landmarks_supported(geometry(p, HILS_OP_FORWARD)))
+    return fail(HILS_ERR_UNSUPPORTED,
+                "landmark formation needs chunk_size, head_dim <= 256 and their product <= 16384");
+  for (const Buf& b : bufs) {
+    if (b.required && !b.ptr) return fail(HILS_ERR_INVALID_ARG, "a required pointer is null");
+    if (b.ptr && !aligned16(b.ptr))
+      return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
+  }
+  return HILS_OK;
+}
+
+bool landmarks_empty(const hils_params* p) {
+  return p->batch == 0 || p->heads_kv == 0 || (p->seq_kv == 0 && p->num_landmarks == 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,6 +248,37 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* k, co
                                                      dq, dk, dv, dlmk, dlmk_bias, ws,
                                                      reinterpret_cast<hipStream_t>(stream)),
                        "backward launch");
+}
+
+hils_status hils_landmarks(const hils_params* p, const void* lq, const void* k, void* lmk,
+                           float* lmk_bias, void* stream) {
+  hils_status s = check_landmarks(p, {});
+  if (s != HILS_OK || landmarks_empty(p)) return s;
+  const bool full = p->seq_kv >= p->chunk_size;
+  s = check_landmarks(p, {{lq, full}, {k, full}, {lmk, p->num_landmarks > 0}, {lmk_bias, false}});
+  if (s != HILS_OK) return s;
+  hipGetLastError();
+  return launch_status(hils::launch_landmarks(geometry(p, HILS_OP_FORWARD), p->dtype == HILS_BF16,
+                                              lq, k, lmk, lmk_bias,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                       "landmark launch");
+}
+
+hils_status hils_landmarks_backward(const hils_params* p, const void* lq, const void* k,
+                                    const void* dlmk, const float* dlmk_bias, void* dlq, void* dk,
+                                    void* stream) {
+  hils_status s = check_landmarks(p, {});
+  if (s != HILS_OK || landmarks_empty(p)) return s;
+  const bool full = p->seq_kv >= p->chunk_size;
+  s = check_landmarks(p, {{lq, full}, {k, p->seq_kv > 0}, {dlmk, full}, {dlmk_bias, false},
+                          {dlq, p->num_landmarks > 0}, {dk, p->seq_kv > 0}});
+  if (s != HILS_OK) return s;
+  hipGetLastError();
+  return launch_status(
+      hils::launch_landmarks_backward(geometry(p, HILS_OP_FORWARD), p->dtype == HILS_BF16, lq, k,
+                                      dlmk, dlmk_bias, dlq, dk,
+                                      reinterpret_cast<hipStream_t>(stream)),
+      "landmark backward launch");
 }
 
 const char* hils_status_string(hils_status s) {

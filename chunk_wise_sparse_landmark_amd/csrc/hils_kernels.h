@@ -41,4 +41,12 @@ hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void*
                                    void* dq, void* dk, void* dv, void* dlmk, float* dbias,
                                    void* ws, hipStream_t st);
 
+// landmark formation (weighted key sum + entropy bias per chunk) and its backward
+bool landmarks_supported(const Geometry& g);
+hipError_t launch_landmarks(const Geometry& g, int bf16, const void* lq, const void* k, void* lmk,
+                            float* bias, hipStream_t st);
+hipError_t launch_landmarks_backward(const Geometry& g, int bf16, const void* lq, const void* k,
+                                     const void* dlmk, const float* dbias, void* dlq, void* dk,
+                                     hipStream_t st);
+
 }  // namespace hils

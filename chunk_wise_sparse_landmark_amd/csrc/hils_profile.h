@@ -8,7 +8,8 @@ enum KernelId {
   kGenericSelect = 1, kGenericAttend = 2, kGenericBwdRows = 3, kGenericBwdChunks = 4,
   kDecodeScore = 5, kDecodeMerge = 6, kDecodeAttend = 7,
   kPrefillSelect = 8, kPrefillAttend = 9, kPrefillBwdRows = 10, kPrefillBwdChunks = 11,
-  kKernelIdEnd = 12
+  kLandmarks = 12, kLandmarksBwd = 13,
+  kKernelIdEnd = 14
 };
 
 struct ProfileSlot {

@@ -21,12 +21,12 @@ HILS_F32, HILS_BF16 = 0, 1
 HILS_OP_FORWARD, HILS_OP_DECODE, HILS_OP_BACKWARD = 0, 1, 2
 
 EXPORTS = ("hils_workspace_size", "hils_forward", "hils_decode", "hils_backward",
-           "hils_profile_kernel", "hils_profile_count", "hils_status_string", "hils_last_error")
+           "hils_landmarks", "hils_landmarks_backward", "hils_profile_kernel", "hils_profile_count", "hils_status_string", "hils_last_error")
 
 KERNEL_IDS = {"generic_select": 1, "generic_attend": 2, "generic_bwd_rows": 3,
               "generic_bwd_chunks": 4, "decode_score": 5, "decode_merge": 6, "decode_attend": 7,
               "prefill_select": 8, "prefill_attend": 9, "prefill_bwd_rows": 10,
-              "prefill_bwd_chunks": 11}
+              "prefill_bwd_chunks": 11, "landmarks": 12, "landmarks_bwd": 13}
 
 
 class HilsParams(ctypes.Structure):
@@ -69,6 +69,10 @@ def load_library(path=None):
     lib.hils_decode.restype = ctypes.c_int
     lib.hils_backward.argtypes = [P] + [vp] * 14 + [vp, sz, vp]
     lib.hils_backward.restype = ctypes.c_int
+    lib.hils_landmarks.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.hils_landmarks.restype = ctypes.c_int
+    lib.hils_landmarks_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.hils_landmarks_backward.restype = ctypes.c_int
     lib.hils_status_string.argtypes = [ctypes.c_int]
     lib.hils_status_string.restype = ctypes.c_char_p
     lib.hils_profile_kernel.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
@@ -187,6 +191,41 @@ def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size
                            _ptr(dv), _ptr(dlmk), _ptr(dbias), _ptr(ws), nbytes, _stream(stream))
     _check(st)
     return dq, dk, dv, dlmk, dbias
+
+
+def _landmark_params(lq, k, chunk_size, scale):
+    for name, t in (("lq", lq), ("k", k)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if lq.dtype != k.dtype:
+        raise TypeError("lq and k must share a dtype")
+    B, Hkv, Lkv, d = k.shape
+    return make_params(batch=B, heads_q=Hkv, heads_kv=Hkv, head_dim=d, seq_q=0, seq_kv=Lkv,
+                       chunk_size=chunk_size, top_k=1, num_landmarks=lq.shape[2], scale=scale,
+                       dtype=_dtype_code(k))
+
+
+def hils_landmarks(lq, k, *, chunk_size, scale=0.0, need_bias=True, stream=None):
+    """Landmark keys [B,Hkv,NCcap,d] and entropy biases (fp32 [B,Hkv,NCcap], or None)
+    from landmark queries lq [B,Hkv,NCcap,d] and keys k [B,Hkv,Lkv,d]."""
+    p = _landmark_params(lq, k, chunk_size, scale)
+    lmk = torch.empty_like(lq)
+    bias = torch.empty(lq.shape[:3], dtype=torch.float32, device=lq.device) if need_bias else None
+    _check(load_library().hils_landmarks(ctypes.byref(p), _ptr(lq), _ptr(k), _ptr(lmk), _ptr(bias),
+                                         _stream(stream)))
+    return lmk, bias
+
+
+def hils_landmarks_backward(lq, k, dlmk, dbias=None, *, chunk_size, scale=0.0, stream=None):
+    """Gradients (dlq, dk) of the landmark formation; dk is its own contribution."""
+    p = _landmark_params(lq, k, chunk_size, scale)
+    if not dlmk.is_contiguous() or dlmk.dtype != lq.dtype or dlmk.shape != lq.shape:
+        raise ValueError("dlmk must be contiguous with lq's shape and dtype")
+    dlq, dk = torch.empty_like(lq), torch.empty_like(k)
+    _check(load_library().hils_landmarks_backward(ctypes.byref(p), _ptr(lq), _ptr(k), _ptr(dlmk),
+                                                  _ptr(dbias), _ptr(dlq), _ptr(dk),
+                                                  _stream(stream)))
+    return dlq, dk
 
 
 def hils_profile_kernel(kernel, starts, stops):

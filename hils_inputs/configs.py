@@ -198,6 +198,22 @@ def make_host_inputs(cfg, lazy_kv=None):
     return out
 
 
+def make_landmark_inputs(cfg, lq_scale=1.0, num_landmarks=None, grads=False):
+    """Inputs of landmark formation: landmark queries lq [B, Hkv, NCcap, d] drawn
+    N(0, lq_scale^2) (a query-like vector per chunk; a larger scale gives sharper
+    in-chunk distributions), the keys k of the workload (the same draw as the
+    attention inputs), and with ``grads`` the incoming gradients dlmk (N(0, 1))
+    and dbias (N(0, 1), fp32).  NCcap defaults to the number of complete chunks."""
+    B, Hkv, d, Lkv, S = cfg["B"], cfg["Hkv"], cfg["d"], cfg["Lkv"], cfg["S"]
+    ncap = Lkv // S if num_landmarks is None else int(num_landmarks)
+    out = {"k": _store(cfg, _draw(cfg, "k", (B, Hkv, Lkv, d))),
+           "lq": _store(cfg, _draw(cfg, "lq", (B, Hkv, ncap, d), scale=lq_scale))}
+    if grads:
+        out["dlmk"] = _store(cfg, _draw(cfg, "dlmk", (B, Hkv, ncap, d)))
+        out["dbias"] = _draw(cfg, "dbias", (B, Hkv, ncap))
+    return out
+
+
 def make_inputs(name_or_cfg, **overrides):
     cfg = config(name_or_cfg, **overrides) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
     return make_host_inputs(cfg)

@@ -125,6 +125,39 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* k, co
                           void* dq, void* dk, void* dv, void* dlmk, float* dlmk_bias,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* Landmark formation [HSADR §3 "Linear surrogate for chunk mass"]: for every
+ * complete chunk c < seq_kv / chunk_size of each (batch, kv head), the landmark
+ * query lq_c induces p = softmax_j(scale * <lq_c, k_j>) over the chunk's keys
+ * j in [c*S, c*S + S); the landmark key is lmk_c = sum_j p_j k_j and the bias is
+ * the entropy of p, -sum_j p_j log p_j (with these, the retrieval score equals
+ * the chunk's exact LogSumExp at q = lq_c and is its first-order expansion
+ * around it).
+ *   lq, lmk       [batch, heads_kv, num_landmarks, head_dim]   dtype of p
+ *   k             [batch, heads_kv, seq_kv, head_dim]          dtype of p
+ *   lmk_bias      [batch, heads_kv, num_landmarks]             fp32, nullable
+ * Rows c >= seq_kv / chunk_size of lmk and lmk_bias are written as 0; lq's rows
+ * there are not read.  Fields used: dtype, batch, heads_kv, head_dim, seq_kv,
+ * chunk_size, num_landmarks, scale (heads_q, seq_q, top_k, causal and
+ * keep_own_chunk are ignored).  Errors: a null pointer to a non-empty buffer, a negative size,
+ * num_landmarks < seq_kv / chunk_size or a base pointer not 16-byte aligned give
+ * HILS_ERR_INVALID_ARG; chunk_size or head_dim above 256, or
+ * chunk_size * head_dim above 16384, give HILS_ERR_UNSUPPORTED.  No workspace. */
+hils_status hils_landmarks(const hils_params* p, const void* lq, const void* k, void* lmk,
+                           float* lmk_bias, void* stream);
+
+/* Gradient of hils_landmarks: given dlmk (dtype of p) and dlmk_bias (fp32,
+ * nullable = zero), writes (overwrites) dlq [batch, heads_kv, num_landmarks,
+ * head_dim] and dk [batch, heads_kv, seq_kv, head_dim]:
+ *   dp_j = <dlmk_c, k_j> - dbias_c (log p_j + 1),
+ *   dl_j = p_j (dp_j - sum_i p_i dp_i),
+ *   dlq_c = scale sum_j dl_j k_j,   dk_j = scale dl_j lq_c + p_j dlmk_c.
+ * Rows of dlq past the complete chunks and keys of a trailing partial chunk
+ * get 0.  dk is this step's contribution only: a caller that also has the
+ * attention's dk adds the two.  Same fields and errors as hils_landmarks. */
+hils_status hils_landmarks_backward(const hils_params* p, const void* lq, const void* k,
+                                    const void* dlmk, const float* dlmk_bias, void* dlq, void* dk,
+                                    void* stream);
+
 /* Kernel families, for hils_profile_kernel. */
 typedef enum {
   HILS_KERNEL_GENERIC_SELECT = 1,
@@ -137,7 +170,9 @@ typedef enum {
   HILS_KERNEL_PREFILL_SELECT = 8,
   HILS_KERNEL_PREFILL_ATTEND = 9,
   HILS_KERNEL_PREFILL_BWD_ROWS = 10,
-  HILS_KERNEL_PREFILL_BWD_CHUNKS = 11
+  HILS_KERNEL_PREFILL_BWD_CHUNKS = 11,
+  HILS_KERNEL_LANDMARKS = 12,
+  HILS_KERNEL_LANDMARKS_BWD = 13
 } hils_kernel_id;
 
 /* Profiling hook (measurement only; not needed for computation).  Until `n`

@@ -132,3 +132,52 @@ def test_status_strings():
     lib = H.load_library()
     for s in range(5):
         assert lib.hils_status_string(s).decode().startswith("HILS_")
+
+
+def _lmk_call(p, lq=FAKE, k=FAKE, lmk=FAKE, bias=None):
+    return H.load_library().hils_landmarks(ctypes.byref(p), lq, k, lmk, bias, None)
+
+
+def _lmk_bwd_call(p, lq=FAKE, k=FAKE, dlmk=FAKE, dbias=None, dlq=FAKE, dk=FAKE):
+    return H.load_library().hils_landmarks_backward(ctypes.byref(p), lq, k, dlmk, dbias, dlq, dk,
+                                                    None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk_size=0), H.HILS_ERR_INVALID_ARG),
+    (dict(num_landmarks=3), H.HILS_ERR_INVALID_ARG),        # < seq_kv / S
+    (dict(seq_kv=-64), H.HILS_ERR_INVALID_ARG),
+    (dict(dtype=9), H.HILS_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), H.HILS_ERR_INVALID_ARG),
+    (dict(head_dim=512), H.HILS_ERR_UNSUPPORTED),
+    (dict(chunk_size=128, head_dim=256), H.HILS_ERR_UNSUPPORTED),   # S * d > 16384
+])
+def test_landmarks_reject(kw, status):
+    assert _lmk_call(_p(**kw)) == status
+    assert _err()
+    assert _lmk_bwd_call(_p(**kw)) == status
+
+
+def test_landmarks_ignore_attention_only_fields():
+    """top_k, causal, keep_own_chunk, seq_q and heads_q take no part in landmark
+    formation: values that the attention entry points reject pass its checks
+    (the call then fails only on the pointer it is given)."""
+    p = _p(top_k=0, causal=5, keep_own_chunk=7, seq_q=-1, heads_q=3)
+    assert _lmk_call(p, lq=None) == H.HILS_ERR_INVALID_ARG
+    assert "null" in _err()
+
+
+def test_landmarks_pointer_checks():
+    assert _lmk_call(_p(), k=None) == H.HILS_ERR_INVALID_ARG
+    assert _lmk_call(_p(), lmk=MIS) == H.HILS_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    assert _lmk_call(_p(), bias=MIS) == H.HILS_ERR_INVALID_ARG
+    assert _lmk_bwd_call(_p(), dk=None) == H.HILS_ERR_INVALID_ARG
+    assert _lmk_bwd_call(_p(), dbias=MIS) == H.HILS_ERR_INVALID_ARG
+
+
+def test_landmarks_empty_is_a_no_op():
+    assert _lmk_call(_p(batch=0), lq=None, k=None, lmk=None) == H.HILS_OK
+    assert _lmk_call(_p(heads_kv=0, heads_q=0), lq=None, k=None, lmk=None) == H.HILS_OK
+    assert _lmk_call(_p(seq_kv=0, num_landmarks=0), lq=None, k=None, lmk=None) == H.HILS_OK
+    assert _lmk_bwd_call(_p(batch=0), lq=None, k=None, dlmk=None, dlq=None, dk=None) == H.HILS_OK
