@@ -13,7 +13,9 @@ Extra workloads in the same JSON line (`extra`): batch-16 decode over a 128K
 cache and batch-1 decode over a 4M cache (algorithmic HBM GB/s: landmarks of
 all candidates + K/V of the selected and own tokens + q, out, idx, lse; inputs
 rotate over several independent sets so the 256 MB last-level cache cannot hold
-them), and the training step (forward + backward, TFLOP/s).
+them), the training step (forward + backward, TFLOP/s), and landmark formation
+with its backward over the training batch's keys (algorithmic HBM GB/s, 16
+rotating input sets).
 
 Every input is resident in HBM before timing.  Per-kernel durations come from
 HIP events the library records around each launch of the dominant kernel on
@@ -48,7 +50,11 @@ KERNEL_SOURCES = {
     "generic_bwd_chunks": ["hils_generic.hip", "hils_common.h"],
     "prefill_bwd_chunks": ["hils_prefill_bwd.hip", "hils_common.h"],
     "prefill_bwd_rows": ["hils_prefill_bwd.hip", "hils_common.h"],
+    "landmarks": ["hils_landmarks.hip", "hils_common.h"],
+    "landmarks_bwd": ["hils_landmarks.hip", "hils_common.h"],
 }
+# kernel family -> substring of its kernel symbols (default: the family name)
+KERNEL_SYMBOLS = {"landmarks": "landmark_forward", "landmarks_bwd": "landmark_backward"}
 COPY_MIB = 1024   # size of the plain copy that calibrates the HBM byte counters
 
 
@@ -175,7 +181,8 @@ def summarize_traffic(kernel, workload, fetch_dir, write_dir, commands):
     ck_f, ck_w = _find(fm, "copy_u4"), _find(wm, "copy_u4")
     f_fetch = copy_bytes / (fm[ck_f]["FETCH_SIZE"] * 1024.0)
     f_write = copy_bytes / (wm[ck_w]["WRITE_SIZE"] * 1024.0)
-    kf, kw = _find(fm, kernel), _find(wm, kernel)
+    sym = KERNEL_SYMBOLS.get(kernel, kernel)
+    kf, kw = _find(fm, sym), _find(wm, sym)
     fetch_b = fm[kf]["FETCH_SIZE"] * 1024.0 * f_fetch
     write_b = wm[kw]["WRITE_SIZE"] * 1024.0 * f_write
     rec = dict(kernel=kernel, workload=workload, source_hash=source_hash(kernel),
@@ -259,6 +266,50 @@ def timed(step, steps, warmup, ev, kernel, hl):
     kms = [ev.elapsed_ms(starts[i], stops[i]) for i in range(n)]
     ev.destroy(starts + stops + [t0, t1])
     return total / steps, (sum(kms) / len(kms) if kms else float("nan")), n
+
+
+_SLEEP_CYCLES_PER_MS = None
+
+
+def _hold(ms, ev):
+    """Keep the stream busy for about `ms` (torch's bounded spin kernel), so that
+    work enqueued meanwhile by the host runs back to back afterwards."""
+    import torch
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        t0, t1 = ev.create(1)[0], ev.create(1)[0]
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        ev.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        torch.cuda._sleep(1000)
+        ev.rt.hipEventRecord(ctypes.c_void_p(t0), st)
+        torch.cuda._sleep(1000000)
+        ev.rt.hipEventRecord(ctypes.c_void_p(t1), st)
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1000000 / max(ev.elapsed_ms(t0, t1), 1e-3)
+        ev.destroy([t0, t1])
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
+def timed_batch(fn, n, ev, host_us=60.0):
+    """Mean ms per call of `fn(i)`, i < n, between one pair of HIP events.  The
+    calls are enqueued while the stream is held busy (host_us per call), so the
+    GPU runs them back to back and the mean is their device time, not the
+    host's launch rate."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    t0, t1 = ev.create(1)[0], ev.create(1)[0]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ev.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    _hold(n * host_us * 1e-3 + 2.0, ev)
+    ev.rt.hipEventRecord(ctypes.c_void_p(t0), st)
+    for i in range(n):
+        fn(i)
+    ev.rt.hipEventRecord(ctypes.c_void_p(t1), st)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(t0, t1) / n
+    ev.destroy([t0, t1])
+    return ms, n
 
 
 def launched(hl, ev, kernel, fn):
@@ -377,6 +428,70 @@ def run_train(hl, cfg, steps, warmup, ev):
     return res
 
 
+def landmark_bytes(cfg):
+    """Algorithmic HBM bytes of landmark formation (forward, backward) over every
+    complete chunk: the forward reads lq and the keys and writes lmk (bf16) and
+    bias (fp32); the backward reads lq, keys, dlmk, dbias and writes dlq, dk."""
+    B, Hkv, d, S = cfg["B"], cfg["Hkv"], cfg["d"], cfg["S"]
+    nc = B * Hkv * (cfg["Lkv"] // S)
+    e = 2 if cfg["dtype"] == "bf16" else 4
+    keys, rows = nc * S * d * e, nc * d * e
+    return keys + 2 * rows + nc * 4, 2 * keys + 3 * rows + nc * 4
+
+
+def run_landmarks(hl, cfg, steps, warmup, ev, nsets):
+    """Landmark formation forward + backward over the keys of one training batch;
+    inputs rotate over `nsets` independent sets so the last-level cache cannot
+    hold them between steps."""
+    import torch
+    from hils_inputs.device import fill_normal
+    B, Hkv, d, NC = cfg["B"], cfg["Hkv"], cfg["d"], cfg["Lkv"] // cfg["S"]
+    sets = []
+    for r in range(nsets):
+        seed = cfg["seed"] + 1000 * r
+        e = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        sets.append(dict(lq=fill_normal(e(B, Hkv, NC, d), seed, "lq"),
+                         k=fill_normal(e(B, Hkv, cfg["Lkv"], d), seed, "k"),
+                         dlmk=fill_normal(e(B, Hkv, NC, d), seed, "dlmk"),
+                         dbias=fill_normal(torch.empty((B, Hkv, NC), device="cuda"), seed, "dbias")))
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = sets[i % nsets]
+        hl.hils_landmarks(s["lq"], s["k"], chunk_size=cfg["S"])
+        hl.hils_landmarks_backward(s["lq"], s["k"], s["dlmk"], s["dbias"], chunk_size=cfg["S"])
+
+    def fwd(i):
+        s = sets[i % nsets]
+        hl.hils_landmarks(s["lq"], s["k"], chunk_size=cfg["S"])
+
+    def bwd(i):
+        s = sets[i % nsets]
+        hl.hils_landmarks_backward(s["lq"], s["k"], s["dlmk"], s["dbias"], chunk_size=cfg["S"])
+
+    fb, bb = landmark_bytes(cfg)
+    for i in range(warmup):
+        step(i)
+    # these kernels last a few microseconds, less than the host needs to launch
+    # them: steps and kernels are timed over back-to-back launches enqueued
+    # behind a hold (an event pair around each launch would add its own latency)
+    ms, _ = timed_batch(step, steps, ev, host_us=120.0)
+    kms, n = timed_batch(bwd, steps, ev)
+    fms, fn = timed_batch(fwd, steps, ev)
+    res = dict(value=(fb + bb) / (ms * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms,
+               bytes_per_step=fb + bb,
+               forward_kernel=dict(kernel_ms=fms, launches=fn, per_launch_bytes=fb,
+                                   achieved=fb / (fms * 1e-3) / 1e9),
+               roofline=dict(bound="hbm", kernel="landmarks_bwd", kernel_ms=kms, launches=n,
+                             achieved=bb / (kms * 1e-3) / 1e9, peak=PEAK_HBM_GBS, unit="GB/s",
+                             traffic=recorded_traffic("landmarks_bwd", cfg.get("name", "")),
+                             per_launch_bytes=bb))
+    res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBS
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 # --------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(cfg, seconds):
     """The CPU oracle, as it stands, on a bounded sample of the workload's queries."""
@@ -413,7 +528,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", default=None, help="run one workload: prefill_8k, decode_128k, "
-                                                     "decode_4m, train_8k, prefill_32k")
+                                                     "decode_4m, train_8k, landmarks_8k, prefill_32k")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain %d MiB device copy (HBM counter calibration)" % COPY_MIB)
     ap.add_argument("--traffic-summary", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
@@ -468,12 +583,17 @@ def main():
                 "roofline": r["roofline"]}
     todo = []
     if not args.no_extra and args.only is None:
-        todo = ["decode_128k", "decode_4m", "train_8k"]
-    elif args.only in ("decode_128k", "decode_4m", "train_8k"):
+        todo = ["decode_128k", "decode_4m", "train_8k", "landmarks_8k"]
+    elif args.only in ("decode_128k", "decode_4m", "train_8k", "landmarks_8k"):
         todo = [args.only]
     for name in todo:
-        cfg = config(name)
-        if name.startswith("decode"):
+        cfg = dict(config("train_8k"), name=name) if name == "landmarks_8k" else config(name)
+        if name == "landmarks_8k":
+            steps, warm = max(args.steps * 5, 50), max(args.warmup, 5)
+            log("%s: 16 sets, %d warmup + %d timed steps" % (name, warm, steps))
+            r = run_landmarks(hl, cfg, steps, warm, ev, 16)
+            log("%s: %.1f us/step, %.0f GB/s" % (name, r["ms_per_step"] * 1e3, r["value"]))
+        elif name.startswith("decode"):
             steps, warm = max(args.steps * 10, 100), max(args.warmup, 10)
             nsets = 4 if name == "decode_128k" else 3
             log("%s: %d sets, %d warmup + %d timed steps" % (name, nsets, warm, steps))

@@ -12,10 +12,17 @@
 //   dl_j = p_j (dp_j - sum_i p_i dp_i),  dlq = scale sum_j dl_j k_j,
 //   dk_j = scale dl_j lq_c + p_j dlmk_c.
 //
-// One workgroup per (b, kv head, chunk): the chunk's S x d keys are staged in
-// LDS as fp32 (row stride d + 1: conflict-free column and row reads), one thread
-// per key forms its logit, block reductions give the softmax, and one thread per
-// dimension forms the weighted sums.  HBM-bound (each key is read once).
+// HBM-bound: each key is read once (and its gradient written once).  Two paths:
+//  * bf16, d = 128, S = 64: one wave per chunk, the chunk's keys held in
+//    registers.  Lane (r = lane / 16, t = lane % 16) holds dims [8t, 8t + 8) of
+//    keys r + 4i (i < 16), so every load and dk store instruction covers 1 KB of
+//    contiguous rows.  Per-key dot products are reduced over the 16 lanes of a
+//    row group by a butterfly that leaves lane (r, t) with key r + 4t: softmax
+//    and entropy are then plain wave reductions (one key per lane).  Weighted key
+//    sums broadcast p within the row group and reduce over the four groups.
+//  * otherwise one workgroup per chunk: keys staged in LDS as fp32 (row stride
+//    d + 1: conflict-free column and row reads), one thread per key for the
+//    logits, block reductions, one thread per dimension for the weighted sums.
 #include "hils_common.h"
 #include "hils_kernels.h"
 #include "hils_profile.h"
@@ -152,13 +159,197 @@ landmark_backward_kernel(Geometry g, const T* __restrict__ lq, const T* __restri
   }
 }
 
+// ------------------------------------------------------------ bf16, d = 128, S = 64
+constexpr int kFastD = 128, kFastS = 64, kFastWaves = 4;
+
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// v[i] = <a, lane's 8 dims of key r + 4i>
+__device__ __forceinline__ void partial_dots(const uint4 (&kr)[16], const float* a, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float kf[8];
+    unpack8(kr[i], kf);
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc = __builtin_fmaf(a[x], kf[x], acc);
+    v[i] = acc;
+  }
+}
+
+// Sum of v[i] over the 16 lanes of the row group, returned to lane t for i = t.
+// At the step with mask h the lane keeps the half of its values whose index bit
+// matches its own lane bit and adds the partner's copy of that half.
+__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int t) {
+#pragma unroll
+  for (int h = 8; h >= 1; h >>= 1) {
+    const bool up = (t & h) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      float a = v[i], b = v[i + h];
+      asm("" : "+v"(a), "+v"(b));   // keep the selects on registers (no indexed array access)
+      v[i] = (up ? b : a) + __shfl_xor(up ? a : b, h, kWave);
+    }
+  }
+  return v[0];
+}
+
+// acc[x] (lane's 8 dims, partial over its row group's keys) summed over the four
+// row groups; lane (r, t) receives dims 8t + 2r and 8t + 2r + 1.
+__device__ __forceinline__ float2 reduce_groups(float (&acc)[8], int lane) {
+#pragma unroll
+  for (int h = 32; h >= 16; h >>= 1) {
+    const bool up = (lane & h) != 0;
+    const int np = h == 32 ? 2 : 1;        // pairs kept after this step
+#pragma unroll
+    for (int pr = 0; pr < np; ++pr) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float lo = acc[2 * pr + e], hi = acc[2 * (pr + np) + e];
+        asm("" : "+v"(lo), "+v"(hi));
+        acc[2 * pr + e] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, h, kWave);
+      }
+    }
+  }
+  return make_float2(acc[0], acc[1]);
+}
+
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ k, size_t row0, int r, int t,
+                                           uint4 (&kr)[16]) {
+  const uint4* kc = reinterpret_cast<const uint4*>(k + row0 * kFastD);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) kr[i] = kc[(r + 4 * i) * (kFastD / 8) + t];
+}
+
+// sum_j w_j k_j over the chunk, w_j of key j = r + 4t held by lane (r, t)
+__device__ __forceinline__ float2 weighted_keys(const uint4 (&kr)[16], float w, int lane) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float wi = __shfl(w, (lane & 48) | i, kWave);
+    float kf[8];
+    unpack8(kr[i], kf);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[x] = __builtin_fmaf(wi, kf[x], acc[x]);
+  }
+  return reduce_groups(acc, lane);
+}
+
+__global__ void __launch_bounds__(kFastWaves * kWave)
+landmark_forward_fast(Geometry g, int nx, const uint16_t* __restrict__ lq,
+                      const uint16_t* __restrict__ k, uint16_t* __restrict__ lmk,
+                      float* __restrict__ bias) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = blockIdx.x * kFastWaves + threadIdx.x / kWave, bkv = blockIdx.y;
+  if (c >= nx) return;
+  const int r = lane >> 4, t = lane & 15;
+  const size_t row = (size_t)bkv * g.NCcap + c;
+  uint32_t* orow = reinterpret_cast<uint32_t*>(lmk + row * kFastD);
+  if (c >= g.NC) {
+    orow[lane] = 0u;
+    if (lane == 0 && bias) bias[row] = 0.f;
+    return;
+  }
+  uint4 kr[16];
+  load_chunk(k, (size_t)bkv * g.Lkv + (size_t)c * kFastS, r, t, kr);
+  float qf[8];
+  unpack8(reinterpret_cast<const uint4*>(lq + row * kFastD)[t], qf);
+  float v[16];
+  partial_dots(kr, qf, v);
+  const float l = g.scale * reduce_scatter16(v, t);      // key r + 4t
+  const float m = wave_max(l);
+  const float e = expf(l - m);
+  const float z = wave_sum(e);
+  const float p = e / z;
+  const float pl = wave_sum(p * l);
+  const float2 o = weighted_keys(kr, p, lane);
+  orow[4 * t + r] = pack2(o.x, o.y);
+  if (lane == 0 && bias) bias[row] = m + logf(z) - pl;
+}
+
+__global__ void __launch_bounds__(kFastWaves * kWave)
+landmark_backward_fast(Geometry g, int nx, const uint16_t* __restrict__ lq,
+                       const uint16_t* __restrict__ k, const uint16_t* __restrict__ dlmk,
+                       const float* __restrict__ dbias, uint16_t* __restrict__ dlq,
+                       uint16_t* __restrict__ dk) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = blockIdx.x * kFastWaves + threadIdx.x / kWave, bkv = blockIdx.y;
+  if (c >= nx) return;
+  const int r = lane >> 4, t = lane & 15;
+  const size_t row = (size_t)bkv * g.NCcap + c;
+  if (c >= g.NC) {
+    if (c < g.NCcap) reinterpret_cast<uint32_t*>(dlq + row * kFastD)[lane] = 0u;
+    if (c == g.NC) {
+      const size_t t0 = (size_t)g.NC * kFastS;
+      uint32_t* tail = reinterpret_cast<uint32_t*>(dk + ((size_t)bkv * g.Lkv + t0) * kFastD);
+      for (size_t e = lane; e < ((size_t)g.Lkv - t0) * (kFastD / 2); e += kWave) tail[e] = 0u;
+    }
+    return;
+  }
+  const size_t krow0 = (size_t)bkv * g.Lkv + (size_t)c * kFastS;
+  uint4 kr[16];
+  load_chunk(k, krow0, r, t, kr);
+  float qf[8], df[8];
+  unpack8(reinterpret_cast<const uint4*>(lq + row * kFastD)[t], qf);
+  unpack8(reinterpret_cast<const uint4*>(dlmk + row * kFastD)[t], df);
+  const float db = dbias ? dbias[row] : 0.f;
+  float v[16];
+  partial_dots(kr, qf, v);
+  const float l = g.scale * reduce_scatter16(v, t);      // key r + 4t
+  const float m = wave_max(l);
+  const float e = expf(l - m);
+  const float z = wave_sum(e);
+  const float p = e / z;
+  const float logp = l - m - logf(z);
+  partial_dots(kr, df, v);
+  const float dp = reduce_scatter16(v, t) - db * (logp + 1.f);
+  const float pdp = wave_sum(p * dp);
+  const float dl = p * (dp - pdp);
+  const float2 o = weighted_keys(kr, dl, lane);
+  reinterpret_cast<uint32_t*>(dlq + row * kFastD)[4 * t + r] = pack2(g.scale * o.x, g.scale * o.y);
+  uint4* dkc = reinterpret_cast<uint4*>(dk + krow0 * kFastD);
+  const float sdl = g.scale * dl;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = __shfl(sdl, (lane & 48) | i, kWave);
+    const float b = __shfl(p, (lane & 48) | i, kWave);
+    float y[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) y[x] = __builtin_fmaf(a, qf[x], b * df[x]);
+    dkc[(r + 4 * i) * (kFastD / 8) + t] =
+        make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
+  }
+}
+
+bool fast_shape(const Geometry& g, int bf16) { return bf16 && g.d == kFastD && g.S == kFastS; }
+
+// chunks each launch covers: every landmark row, and the chunk slot of a
+// partial tail (backward: its keys' gradients are zeroed)
+int fwd_chunks(const Geometry& g) { return g.NCcap > g.NC ? g.NCcap : g.NC; }
+int bwd_chunks(const Geometry& g) {
+  int nx = fwd_chunks(g);
+  if ((size_t)g.NC * g.S < (size_t)g.Lkv && nx < g.NC + 1) nx = g.NC + 1;
+  return nx;
+}
+
 size_t fwd_lds(const Geometry& g) { return ((size_t)g.S * (g.d + 1) + g.d + 2 * g.S + 8) * 4; }
 size_t bwd_lds(const Geometry& g) { return fwd_lds(g) + ((size_t)g.d + g.S + 8) * 4; }
 
 template <typename T>
 hipError_t launch_fwd(const Geometry& g, const void* lq, const void* k, void* lmk, float* bias,
                       hipStream_t st) {
-  const int nx = g.NCcap > g.NC ? g.NCcap : g.NC;
+  const int nx = fwd_chunks(g);
   if (nx == 0) return hipSuccess;
   const size_t sm = fwd_lds(g);
   hipError_t e = hipFuncSetAttribute((const void*)landmark_forward_kernel<T>,
@@ -174,9 +365,7 @@ hipError_t launch_fwd(const Geometry& g, const void* lq, const void* k, void* lm
 template <typename T>
 hipError_t launch_bwd(const Geometry& g, const void* lq, const void* k, const void* dlmk,
                       const float* dbias, void* dlq, void* dk, hipStream_t st) {
-  const bool tail = (size_t)g.NC * g.S < (size_t)g.Lkv;
-  int nx = g.NCcap > g.NC ? g.NCcap : g.NC;
-  if (tail && nx < g.NC + 1) nx = g.NC + 1;
+  const int nx = bwd_chunks(g);
   if (nx == 0) return hipSuccess;
   const size_t sm = bwd_lds(g);
   hipError_t e = hipFuncSetAttribute((const void*)landmark_backward_kernel<T>,
@@ -197,6 +386,16 @@ bool landmarks_supported(const Geometry& g) {
 
 hipError_t launch_landmarks(const Geometry& g, int bf16, const void* lq, const void* k, void* lmk,
                             float* bias, hipStream_t st) {
+  if (fast_shape(g, bf16)) {
+    const int nx = fwd_chunks(g);
+    if (nx == 0) return hipSuccess;
+    prof_begin(kLandmarks, st);
+    hipLaunchKernelGGL(landmark_forward_fast, dim3((nx + kFastWaves - 1) / kFastWaves, g.B * g.Hkv),
+                       dim3(kFastWaves * kWave), 0, st, g, nx, (const uint16_t*)lq,
+                       (const uint16_t*)k, (uint16_t*)lmk, bias);
+    prof_end(kLandmarks, st);
+    return hipGetLastError();
+  }
   return bf16 ? launch_fwd<uint16_t>(g, lq, k, lmk, bias, st)
               : launch_fwd<float>(g, lq, k, lmk, bias, st);
 }
@@ -204,6 +403,17 @@ hipError_t launch_landmarks(const Geometry& g, int bf16, const void* lq, const v
 hipError_t launch_landmarks_backward(const Geometry& g, int bf16, const void* lq, const void* k,
                                      const void* dlmk, const float* dbias, void* dlq, void* dk,
                                      hipStream_t st) {
+  if (fast_shape(g, bf16)) {
+    const int nx = bwd_chunks(g);
+    if (nx == 0) return hipSuccess;
+    prof_begin(kLandmarksBwd, st);
+    hipLaunchKernelGGL(landmark_backward_fast, dim3((nx + kFastWaves - 1) / kFastWaves, g.B * g.Hkv),
+                       dim3(kFastWaves * kWave), 0, st, g, nx, (const uint16_t*)lq,
+                       (const uint16_t*)k, (const uint16_t*)dlmk, dbias, (uint16_t*)dlq,
+                       (uint16_t*)dk);
+    prof_end(kLandmarksBwd, st);
+    return hipGetLastError();
+  }
   return bf16 ? launch_bwd<uint16_t>(g, lq, k, dlmk, dbias, dlq, dk, st)
               : launch_bwd<float>(g, lq, k, dlmk, dbias, dlq, dk, st);
 }

@@ -67,6 +67,8 @@ def test_train_8k_full(hl):
     (dict(Lkv=1024, S=256, d=64, dtype="f32"), 1.0, None),   # S * d at the 16384 bound
     (dict(Lkv=256, S=64, d=256, dtype="bf16"), 1.0, 5),      # d at its 256 bound
     (dict(Lkv=640, S=64, d=128, dtype="bf16"), 8.0, None),   # sharp in-chunk distributions
+    (dict(B=2, Hkv=3, Lkv=700, S=64, d=128, dtype="bf16"), 1.0, 13),  # wave path, ragged
+    (dict(Lkv=50, S=64, d=128, dtype="bf16"), 2.0, 3),       # wave path, no complete chunk
     (dict(Lkv=333, S=48, d=96, dtype="f32"), 3.0, 9),
     (dict(Lkv=40, S=64, d=64, dtype="f32"), 1.0, 2),         # no complete chunk
 ])
