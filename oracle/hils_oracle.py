@@ -38,9 +38,14 @@ design notes of the repository):
   o_i = floor(t_i / S) is never a candidate (its landmark would summarise
   future tokens); candidates are chunks c < o_i. Non-causal mode: all complete
   chunks are candidates and the trailing partial chunk (if any) is "own";
-* with keep_own_chunk the visible tokens of the own chunk are attended exactly
-  and enter the fusion with score = their exact LogSumExp (the one-chunk case
-  of the chunk-aligned local window); fusion weights are per head;
+* chunk-aligned local window of w chunk slots (w = local_chunks; keep_own_chunk
+  is w = 1): the own slot (the query's own chunk, its visible tokens only; in
+  non-causal mode the trailing partial chunk) and the w - 1 complete chunks
+  before it.  Each window chunk is attended exactly and enters the fusion as
+  its own member with score = its exact LogSumExp [HSADR §2 Preliminary: the
+  window is chunk-aligned and never overlaps retrieved chunks; §5 and §6: the
+  measured models keep top-K retrieval plus a 512-token window].  Candidates
+  are the complete chunks before the window; fusion weights are per head;
 * an empty fusion set gives O = 0 and LSE = -inf;
 * landmark formation (the step before scoring): the chunk's landmark query lq_c
   induces p = softmax_j(scale <lq_c, k_j>) over its S keys; the landmark key is
@@ -52,8 +57,10 @@ design notes of the repository):
 Parity pins (what ties this oracle to something other than itself) live in
 tests/test_oracle_pins.py: dense attention (S = 1, all chunks), exact chunk mass
 = restricted softmax, top-1, weights summing to one, a hand-derived worked
-example, decode = last prefill row, ties, invariances, and central finite
-differences for every gradient.
+example, decode = last prefill row, ties, invariances, central finite
+differences for every gradient, and for the local window: dense attention when
+it covers every key, restricted softmax under exact-mass scores, and a
+token-level second formulation.
 """
 import math
 import numpy as np
@@ -62,18 +69,36 @@ import numpy as np
 # ----------------------------------------------------------------------------
 # positions and candidate sets  [HSADR §2 Preliminary; §3 "Sparse training"]
 # ----------------------------------------------------------------------------
-def query_layout(i, Lq, Lkv, S, causal):
-    """Return (candidate chunk ids, own-chunk token range [a, b)) for query i."""
+def query_layout(i, Lq, Lkv, S, causal, local_chunks=1):
+    """Return (candidate chunk ids, local-window members) for query i.
+
+    The own slot o holds the query (causal: floor(t_i / S)); in non-causal mode it
+    is the trailing partial chunk, slot NC.  The local window is the slots
+    o - w + 1 .. o (w = local_chunks, clipped at 0): the own slot's visible tokens
+    and the complete chunks before it.  Candidates are the complete chunks before
+    the window, so window and retrieval never overlap.  Members are
+    (slot, (a, b)) token ranges, own slot first; empty ranges are dropped.
+    """
     NC = Lkv // S
+    w = int(local_chunks)
     if causal:
         t = Lkv - Lq + i
         own = t // S
-        cand = np.arange(0, min(own, NC))
         own_rng = (own * S, t + 1)
     else:
-        cand = np.arange(0, NC)
+        own = NC
         own_rng = (NC * S, Lkv)
-    return cand, own_rng
+    first_local = own - max(w - 1, 0)
+    cand = np.arange(0, max(0, min(first_local, NC)))
+    window = []
+    for j in range(w):
+        c = own - j
+        if c < 0:
+            break
+        a, b = own_rng if j == 0 else (c * S, c * S + S)
+        if b > a:
+            window.append((c, (a, b)))
+    return cand, window
 
 
 def select_chunks(gbar, cand, K):
@@ -111,18 +136,20 @@ def _chunk_attention(q, k_blk, v_blk, scale):
 # one query of one KV group: forward and (optionally) backward
 # ----------------------------------------------------------------------------
 def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale,
-               forced=None, dout=None):
+               forced=None, dout=None, local_chunks=None):
     """Forward (and backward if ``dout``) of query i for the G heads of one KV group.
 
     qg: [G, d] query rows of the group; k, v: [Lkv, d] (indexable) this group's
     cache; lmk: [NCcap, d]; bias: [NCcap] or None; forced: chunk ids to use
-    instead of the selection (ascending), or None.
+    instead of the selection (ascending), or None; local_chunks: width w of the
+    local window in chunk slots (default: 1 if keep_own else 0).
     Returns a dict with idx, out [G, d], lse [G], scores, and for backward dq
     [G, d] and the lists of contributions to dk, dv (per token range), dlmk and
     dbias (per chunk).
     """
     G, d = qg.shape
-    cand, (oa, ob) = query_layout(i, Lq, Lkv, S, causal)
+    w_loc = (1 if keep_own else 0) if local_chunks is None else int(local_chunks)
+    cand, window = query_layout(i, Lq, Lkv, S, causal, w_loc)
 
     # retrieval scores of every candidate, per head  [HSADR §3 "Linear surrogate"]
     if len(cand):
@@ -142,8 +169,7 @@ def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale
 
     # members of the fusion set: (kind, chunk id, token range)
     members = [("ret", int(c), (int(c) * S, int(c) * S + S)) for c in sel]
-    if keep_own and ob > oa:
-        members.append(("own", -1, (oa, ob)))
+    members += [("loc", int(c), rng) for c, rng in window]
 
     out = np.zeros((G, d))
     lse = np.full(G, -math.inf)
@@ -166,7 +192,7 @@ def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale
                 else:                                       # forced chunk outside C_i
                     s_c = scale * float(q @ lmk[c]) + (0.0 if bias is None else float(bias[c]))
             else:
-                s_c = lse_c                                  # exact mass of the own chunk
+                s_c = lse_c                                  # exact mass of a window chunk
             parts.append((kind, c, a, b, kb, vb, p, o_c, s_c))
         # fusion by a softmax over the retrieval scores  [HSADR §3 "Hierarchical softmax"]
         s_vec = np.array([pt[8] for pt in parts])
@@ -194,7 +220,7 @@ def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale
                 res["dlmk"].append((c, scale * ds * q))
                 res["dbias"].append((c, ds))
             else:
-                dl = wc * p * (u - D)                        # s_own = lse_own adds ds_own*p
+                dl = wc * p * (u - D)                        # s_c = lse_c adds ds_c * p
             dq = dq + scale * (dl @ kb)
             res["dkv"].append((a, b, scale * np.outer(dl, q), np.outer(wc * p, g)))
         res["dq"][h] = dq
@@ -210,13 +236,15 @@ def _f64(x):
 
 def ref_forward(q, k, v, lmk, bias=None, *, chunk_size, top_k, causal=True,
                 keep_own_chunk=True, scale=None, queries=None, heads_kv=None,
-                batches=None, forced_idx=None):
+                batches=None, forced_idx=None, local_chunks=None):
     """HiLS forward. q [B,Hq,Lq,d]; k, v [B,Hkv,Lkv,d]; lmk [B,Hkv,NCcap,d]; bias [B,Hkv,NCcap].
 
     Returns out [B,Hq,nq,d], idx [B,Hkv,nq,K] (int64, -1 padded), lse [B,Hq,nq]
     for the query positions ``queries`` (default: all).  ``forced_idx``
     ([B,Hkv,nq,K], -1 padded) replaces the selection.  k and v may be lazy
     indexable objects; only the rows of the used chunks are read.
+    ``local_chunks`` (default 1 if keep_own_chunk else 0) is the width of the
+    chunk-aligned local window in chunk slots.
     """
     B, Hq, Lq, d = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
@@ -241,7 +269,8 @@ def ref_forward(q, k, v, lmk, bias=None, *, chunk_size, top_k, causal=True,
                     forced = f[f >= 0]
                 r = hils_query(_f64(q[b, g * G:(g + 1) * G, i]), kg, vg, lg, bg, int(i),
                                Lq=Lq, Lkv=Lkv, S=S, K=K, causal=bool(causal),
-                               keep_own=bool(keep_own_chunk), scale=sc, forced=forced)
+                               keep_own=bool(keep_own_chunk), scale=sc, forced=forced,
+                               local_chunks=local_chunks)
                 idx[b, g, n] = r["idx"]
                 out[b, g * G:(g + 1) * G, n] = r["out"]
                 lse[b, g * G:(g + 1) * G, n] = r["lse"]
@@ -257,7 +286,8 @@ def ref_decode(q, k, v, lmk, bias=None, **kw):
 
 
 def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
-                 keep_own_chunk=True, scale=None, forced_idx=None, queries=None):
+                 keep_own_chunk=True, scale=None, forced_idx=None, queries=None,
+                 local_chunks=None):
     """Gradients of sum(<dout, out>) for every input, selection held fixed.
 
     Returns dq [B,Hq,Lq,d] (rows outside ``queries`` are zero), dk, dv
@@ -288,7 +318,8 @@ def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
                 r = hils_query(_f64(q[b, g * G:(g + 1) * G, i]), kg, vg, lg, bg, int(i),
                                Lq=Lq, Lkv=Lkv, S=S, K=K, causal=bool(causal),
                                keep_own=bool(keep_own_chunk), scale=sc, forced=forced,
-                               dout=_f64(dout[b, g * G:(g + 1) * G, i]))
+                               dout=_f64(dout[b, g * G:(g + 1) * G, i]),
+                               local_chunks=local_chunks)
                 dq[b, g * G:(g + 1) * G, i] = r["dq"]
                 for a, e, dkp, dvp in r["dkv"]:
                     dk[b, g, a:e] += dkp

@@ -13,6 +13,11 @@
   identical heads equals one head;
 * central finite differences for every gradient, the dense-attention gradients
   from torch autograd, and the zero-sum of the fusion-score gradients;
+* chunk-aligned local window (local_chunks = w): a window covering every key is
+  dense attention (and dense gradients); with exact-mass scores it is the
+  softmax restricted to the retrieved and window tokens; a token-level second
+  formulation (window tokens weighted by their own logits); no overlap of
+  window and retrieval; decode = last prefill row; finite differences;
 * landmark formation: the surrogate score equals the exact chunk LogSumExp (and
   its gradient) at the landmark query, uniform and one-hot limits (bias log S and
   0), the entropy against scipy, and finite differences of its backward.
@@ -338,14 +343,14 @@ def _loss(params, R, kw):
     return float(np.sum(out * R)), idx
 
 
-@pytest.mark.parametrize("keep_own", [True, False])
-def test_finite_differences(keep_own):
-    rng = np.random.default_rng(14 + keep_own)
+@pytest.mark.parametrize("local", [1, 0, 3])
+def test_finite_differences(local):
+    rng = np.random.default_rng(14 + local)
     B, Hq, Hkv, d, S, L, K = 1, 4, 2, 6, 4, 28, 2
     q, k, v = _rand(rng, B, Hq, L, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
     lmk, bias = _rand(rng, B, Hkv, L // S, d), _rand(rng, B, Hkv, L // S)
     R = _rand(rng, B, Hq, L, d)
-    kw = dict(chunk_size=S, top_k=K, causal=True, keep_own_chunk=keep_own)
+    kw = dict(chunk_size=S, top_k=K, causal=True, local_chunks=local)
     grads = ref_backward(q, k, v, lmk, bias, R, **kw)
     params = [q, k, v, lmk, bias]
     _, idx0 = _loss(params, R, kw)
@@ -379,6 +384,126 @@ def test_fusion_score_gradients_sum_to_zero():
                                      keep_own_chunk=False)
     assert abs(dbias.sum()) < 1e-12
     assert np.count_nonzero(dbias) == K
+
+
+# --------------------------------------------------------------------------- local window
+@pytest.mark.parametrize("causal,Lq", [(True, 29), (True, 6), (False, 5)])
+def test_window_covering_every_key_is_dense(causal, Lq):
+    """A local window wider than the cache leaves no candidates: every visible
+    token is attended exactly, i.e. textbook dense attention (and its gradients)."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, d, S, Lkv = 1, 4, 2, 8, 4, 29
+    q, k, v = _rand(rng, B, Hq, Lq, d), _rand(rng, B, Hkv, Lkv, d), _rand(rng, B, Hkv, Lkv, d)
+    lmk, bias = _rand(rng, B, Hkv, Lkv // S, d), _rand(rng, B, Hkv, Lkv // S)
+    kw = dict(chunk_size=S, top_k=3, causal=causal, local_chunks=Lkv // S + 1)
+    out, idx, lse = ref_forward(q, k, v, lmk, bias, **kw)
+    assert (idx == -1).all()
+    if causal:
+        mask = np.arange(Lkv)[None, :] <= (Lkv - Lq + np.arange(Lq))[:, None]
+    else:
+        mask = np.ones((Lq, Lkv), dtype=bool)
+    ro, rl = _dense_torch(q, k, v, 1 / math.sqrt(d), mask)
+    np.testing.assert_allclose(out, ro, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, atol=1e-12)
+    dout = _rand(rng, B, Hq, Lq, d)
+    dq, dk, dv, dlmk, dbias = ref_backward(q, k, v, lmk, bias, dout, **kw)
+    G = Hq // Hkv
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1),
+        attn_mask=torch.tensor(mask))
+    (o * torch.tensor(dout)).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-11)
+    assert not dlmk.any() and not dbias.any()
+
+
+def test_window_exact_mass_is_restricted_softmax():
+    """Exact-mass scores with a three-chunk window: naive block-sparse attention
+    over the top-K chunks before the window plus every window token."""
+    rng = np.random.default_rng(22)
+    B, H, d, S, NC, K, w = 2, 2, 8, 4, 11, 3, 3
+    Lkv = NC * S + 1                                   # own chunk: 2 visible tokens
+    q, k, v = _rand(rng, B, H, 1, d), _rand(rng, B, H, Lkv, d), _rand(rng, B, H, Lkv, d)
+    lmk = _rand(rng, B, H, NC, d)
+    scale = 1 / math.sqrt(d)
+    logits = scale * np.einsum("bhd,bhtd->bht", q[:, :, 0], k)
+    mass = scipy.special.logsumexp(logits[:, :, :NC * S].reshape(B, H, NC, S), axis=-1)
+    bias = mass - scale * np.einsum("bhd,bhcd->bhc", q[:, :, 0], lmk)
+    out, idx, lse = ref_decode(q, k, v, lmk, bias, chunk_size=S, top_k=K, local_chunks=w)
+    own = (Lkv - 1) // S
+    first_local = own - (w - 1)
+    for b in range(B):
+        for h in range(H):
+            best = sorted(np.argsort(-mass[b, h, :first_local], kind="stable")[:K].tolist())
+            assert idx[b, h, 0].tolist() == best
+            mask = np.zeros((1, Lkv), dtype=bool)
+            for c in best:
+                mask[0, c * S:(c + 1) * S] = True
+            mask[0, first_local * S:Lkv] = True
+            ro, rl = _dense_torch(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                  scale, mask)
+            np.testing.assert_allclose(out[b, h, 0], ro[0, 0, 0], atol=1e-12)
+            np.testing.assert_allclose(lse[b, h, 0], rl[0, 0, 0], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_token_weight_formulation(causal):
+    """Token-level second formulation: a retrieved chunk's tokens get
+    softmax(scores + window logits)[c] * softmax(chunk logits); a window token j gets
+    exp(l_j - LSE) directly, LSE over the retrieval scores and the window logits."""
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, d, S, L, K, w = 1, 4, 2, 8, 4, 43, 3, 3
+    Lq = L if causal else 6
+    q, k, v = _rand(rng, B, Hq, Lq, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    NC = L // S
+    lmk, bias = _rand(rng, B, Hkv, NC, d), 0.3 * _rand(rng, B, Hkv, NC)
+    out, idx, lse = ref_forward(q, k, v, lmk, bias, chunk_size=S, top_k=K, causal=causal,
+                                local_chunks=w)
+    scale = 1 / math.sqrt(d)
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        logits = scale * q[0, h] @ k[0, g].T
+        lscore = scale * q[0, h] @ lmk[0, g].T + bias[0, g][None, :]
+        for i in range(Lq):
+            t = i if causal else L - 1
+            own = t // S if causal else NC
+            lo = max(own - (w - 1), 0) * S                 # first window token
+            win = np.arange(lo, t + 1)
+            sel = [int(c) for c in idx[0, g, i] if c >= 0]
+            ncand = max(0, min(own - (w - 1), NC))
+            assert len(sel) == min(K, ncand) and all(c < ncand for c in sel)
+            ent = [lscore[i, c] for c in sel] + list(logits[i, win])
+            LSE = scipy.special.logsumexp(ent)
+            a = np.zeros(L)
+            for c in sel:
+                toks = np.arange(c * S, c * S + S)
+                a[toks] += math.exp(lscore[i, c] - LSE) * scipy.special.softmax(logits[i, toks])
+            a[win] += np.exp(logits[i, win] - LSE)
+            assert abs(a.sum() - 1) < 1e-12
+            np.testing.assert_allclose(out[0, h, i], a @ v[0, g], atol=1e-12)
+            np.testing.assert_allclose(lse[0, h, i], LSE, atol=1e-12)
+
+
+def test_window_decode_is_last_prefill_row():
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, d, S, L, K = 2, 4, 2, 8, 4, 53, 3
+    q, k, v = _rand(rng, B, Hq, L, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    lmk, bias = _rand(rng, B, Hkv, L // S, d), _rand(rng, B, Hkv, L // S)
+    kw = dict(chunk_size=S, top_k=K, local_chunks=4)
+    o1, i1, l1 = ref_forward(q, k, v, lmk, bias, causal=True, **kw)
+    o2, i2, l2 = ref_decode(q[:, :, -1:], k, v, lmk, bias, **kw)
+    np.testing.assert_array_equal(i1[:, :, -1:], i2)
+    np.testing.assert_allclose(o1[:, :, -1:], o2, atol=1e-13)
+    np.testing.assert_allclose(l1[:, :, -1:], l2, atol=1e-13)
+    o3, i3, l3 = ref_forward(q, k, v, lmk, bias, causal=True, chunk_size=S, top_k=K,
+                             local_chunks=1)
+    o4, i4, l4 = ref_forward(q, k, v, lmk, bias, causal=True, chunk_size=S, top_k=K,
+                             keep_own_chunk=True)
+    np.testing.assert_array_equal(i3, i4)
+    np.testing.assert_array_equal(o3, o4)
 
 
 # --------------------------------------------------------------------------- landmark formation
