@@ -50,8 +50,9 @@ hils_status check_params(const hils_params* p, int op) {
   if (p->chunk_size < 1) return fail(HILS_ERR_INVALID_ARG, "chunk_size must be >= 1");
   if (p->top_k < 1) return fail(HILS_ERR_INVALID_ARG, "top_k must be >= 1");
   if (p->causal != 0 && p->causal != 1) return fail(HILS_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (p->keep_own_chunk != 0 && p->keep_own_chunk != 1)
-    return fail(HILS_ERR_INVALID_ARG, "keep_own_chunk must be 0 or 1");
+  if (p->local_chunks < 0 || p->local_chunks > hils::kMaxLocalChunks)
+    return fail(HILS_ERR_INVALID_ARG, "local_chunks must be in 0..%d (got %d)",
+                hils::kMaxLocalChunks, p->local_chunks);
   if (!std::isfinite(p->scale)) return fail(HILS_ERR_INVALID_ARG, "scale is not finite");
   if (p->heads_kv == 0 && p->heads_q != 0)
     return fail(HILS_ERR_INVALID_ARG, "heads_kv is 0 but heads_q is not");
@@ -93,7 +94,8 @@ hils::Geometry geometry(const hils_params* p, int op) {
   g.NC = p->seq_kv / p->chunk_size;
   g.NCcap = p->num_landmarks;
   g.causal = op == HILS_OP_DECODE ? 1 : p->causal;
-  g.keep_own = p->keep_own_chunk;
+  g.win = p->local_chunks;
+  g.keep_own = p->local_chunks > 0;
   g.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
   return g;
 }

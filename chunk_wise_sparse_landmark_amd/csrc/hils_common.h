@@ -7,6 +7,7 @@ namespace hils {
 
 constexpr int kWave = 64;
 constexpr int kMaxTopK = 64;
+constexpr int kMaxLocalChunks = 64;   // local window width bound, in chunk slots
 
 // ---------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -310,22 +311,31 @@ __device__ __forceinline__ float block_max4(float x, float* red) {
 
 // ---------------------------------------------------------------- geometry
 struct Geometry {
-  int B, Hq, Hkv, G, d, Lq, Lkv, S, K, NC, NCcap, causal, keep_own;
+  // win: chunk slots of the local window (0 none, 1 the own chunk); keep_own = win > 0
+  int B, Hq, Hkv, G, d, Lq, Lkv, S, K, NC, NCcap, causal, keep_own, win;
   float scale;
-  // candidate count and own-chunk token range [own_a, own_b) of query i
-  __device__ __forceinline__ void layout(int i, int& ncand, int& own_a, int& own_b) const {
+  // Query i: own slot `own` (causal: its chunk; non-causal: the trailing partial
+  // chunk NC), the end `own_b` of its visible tokens, and the candidate count
+  // (complete chunks before the local window).
+  __device__ __forceinline__ void layout(int i, int& ncand, int& own, int& own_b) const {
     if (causal) {
-      int t = Lkv - Lq + i;
-      int own = t / S;
-      ncand = own < NC ? own : NC;
-      own_a = own * S;
+      const int t = Lkv - Lq + i;
+      own = t / S;
       own_b = t + 1;
     } else {
-      ncand = NC;
-      own_a = NC * S;
+      own = NC;
       own_b = Lkv;
     }
-    if (!keep_own) own_b = own_a;
+    const int first = own - (win > 1 ? win - 1 : 0);
+    ncand = first < 0 ? 0 : (first < NC ? first : NC);
+  }
+  // Token range [a, b) of window member j (chunk own - j); false when absent or empty.
+  __device__ __forceinline__ bool window_member(int own, int own_b, int j, int& a, int& b) const {
+    const int c = own - j;
+    if (j < 0 || j >= win || c < 0) return false;
+    a = c * S;
+    b = j == 0 ? own_b : a + S;
+    return b > a;
   }
 };
 

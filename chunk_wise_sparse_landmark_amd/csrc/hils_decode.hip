@@ -431,7 +431,7 @@ DecodeWs carve(const Geometry& g, const DecodePlan& p, void* ws) {
 
 bool decode_fast_supported(const Geometry& g, int bf16) {
   return bf16 && g.d == kD && g.S == kS && g.G <= kMaxGd && g.K <= kMaxTopK && g.Lq == 1 &&
-         g.causal;
+         g.causal && g.win <= 1;
 }
 
 size_t decode_fast_ws(const Geometry& g) {

@@ -35,8 +35,8 @@ generic_select_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
   const int bkv = blockIdx.y;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  int ncand, oa, ob;
-  g.layout(i, ncand, oa, ob);
+  int ncand, own, ob;
+  g.layout(i, ncand, own, ob);
 
   // qbar = mean_h q_h (the group score is linear in q)
   for (int e = tid; e < g.d; e += kThreads) {
@@ -133,8 +133,8 @@ generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
   const int bkv = blockIdx.y;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x;
-  int ncand, oa, ob;
-  g.layout(i, ncand, oa, ob);
+  int ncand, own, ob;
+  g.layout(i, ncand, own, ob);
   if (tid < g.K) sel[tid] = sel_idx[((size_t)bkv * g.Lq + i) * g.K + tid];
   const T* Kg = k + (size_t)bkv * g.Lkv * g.d;
   const T* Vg = v + (size_t)bkv * g.Lkv * g.d;
@@ -142,13 +142,15 @@ generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   __syncthreads();
 
+  // members: slots 0..K-1 the selection, slots K..K+win-1 the window chunks
+  // (own chunk first), each window chunk fused with its exact lse
   for (int hh = 0; hh < g.G; ++hh) {
     const int h = kvh * g.G + hh;
     const size_t row = (size_t)(b * g.Hq + h) * g.Lq + i;
     if (tid < g.d) qh[tid] = Elem<T>::ld(q + row * g.d + tid);
     __syncthreads();
     float m = -INFINITY, z = 0.f, acc = 0.f;   // online fusion over members
-    for (int slot = 0; slot <= g.K; ++slot) {
+    for (int slot = 0; slot < g.K + g.win; ++slot) {
       int a, e;
       float s;
       if (slot < g.K) {
@@ -165,9 +167,9 @@ generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
         z = z * f_old + f_new;
         m = mn;
       } else {
-        if (ob <= oa) continue;
+        if (!g.window_member(own, ob, slot - g.K, a, e)) continue;
         float o_d;
-        s = member_attention<T>(g, qh, Kg, Vg, oa, ob, p, red, o_d);
+        s = member_attention<T>(g, qh, Kg, Vg, a, e, p, red, o_d);
         const float mn = fmaxf(m, s);
         const float f_old = __expf(m - mn), f_new = __expf(s - mn);
         acc = acc * f_old + f_new * o_d;
@@ -186,7 +188,7 @@ generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
 // and the fusion, then
 //   D = <dO, O>,  u_j = <dO, v_j>,  D_c = <dO, o_c>,
 //   retrieved: dl_j = w_c p_j (u_j - D_c),  ds_c = w_c (D_c - D)
-//   own:       dl_j = w_o p_j (u_j - D)      (its score is its own lse)
+//   window:    dl_j = w_c p_j (u_j - D)      (its score is its own lse)
 //   dq = scale (sum dl_j k_j + sum_c ds_c lmk_c).
 // Per (row, member) it stores (w, lse_c, Dt, ds) with Dt = D_c or D, which the
 // chunk pass needs: dl_j = w p_j (u_j - Dt).
@@ -204,13 +206,15 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
   __shared__ float dl[kMaxS];
   __shared__ float red[4];
   __shared__ int sel[kMaxTopK];
-  __shared__ float ms[kMaxTopK + 1], mlse[kMaxTopK + 1], mD[kMaxTopK + 1];
+  __shared__ float ms[kMaxTopK + kMaxLocalChunks], mlse[kMaxTopK + kMaxLocalChunks];
+  __shared__ float mD[kMaxTopK + kMaxLocalChunks];
+  const int nslot = g.K + g.win;
   const int i = blockIdx.x;
   const int bkv = blockIdx.y;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x;
-  int ncand, oa, ob;
-  g.layout(i, ncand, oa, ob);
+  int ncand, own, ob;
+  g.layout(i, ncand, own, ob);
   if (tid < g.K) sel[tid] = sel_idx[((size_t)bkv * g.Lq + i) * g.K + tid];
   const T* Kg = k + (size_t)bkv * g.Lkv * g.d;
   const T* Vg = v + (size_t)bkv * g.Lkv * g.d;
@@ -228,8 +232,8 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
     __syncthreads();
     // pass 1: member scores, lse, D_c; fused output
     float m = -INFINITY, z = 0.f, acc = 0.f;
-    for (int slot = 0; slot <= g.K; ++slot) {
-      int a, e;
+    for (int slot = 0; slot < nslot; ++slot) {
+      int a = 0, e = 0;
       float s;
       bool valid;
       if (slot < g.K) {
@@ -241,9 +245,7 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
           s = retrieval_score<T>(g, qh, Lg + (size_t)c * g.d, bb ? bb[c] : 0.f, red);
         }
       } else {
-        valid = ob > oa;
-        a = oa;
-        e = ob;
+        valid = g.window_member(own, ob, slot - g.K, a, e);
       }
       if (!valid) {
         if (tid == 0) { ms[slot] = -INFINITY; mlse[slot] = 0.f; mD[slot] = 0.f; }
@@ -251,7 +253,7 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
       }
       float o_d;
       float lc = member_attention<T>(g, qh, Kg, Vg, a, e, p, red, o_d);
-      if (slot == g.K) s = lc;
+      if (slot >= g.K) s = lc;
       float Dc = block_sum4(tid < g.d ? gh[tid] * o_d : 0.f, red);
       if (tid == 0) { ms[slot] = s; mlse[slot] = lc; mD[slot] = Dc; }
       const float mn = fmaxf(m, s);
@@ -266,18 +268,17 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
     const float D = block_sum4(tid < g.d ? gh[tid] * O_d : 0.f, red);
     // pass 2: gradients
     float dq_d = 0.f;
-    for (int slot = 0; slot <= g.K; ++slot) {
+    for (int slot = 0; slot < nslot; ++slot) {
       float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
       const float s = ms[slot];
       if (s != -INFINITY) {
-        int a, e, c = -1;
+        int a = 0, e = 0, c = -1;
         if (slot < g.K) {
           c = sel[slot];
           a = c * g.S;
           e = a + g.S;
         } else {
-          a = oa;
-          e = ob;
+          g.window_member(own, ob, slot - g.K, a, e);
         }
         const float wgt = __expf(s - LSE);
         const float lc = mlse[slot];
@@ -304,7 +305,7 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
         __syncthreads();
         st = make_float4(wgt, lc, Dt, slot < g.K ? wgt * (Dt - D) : 0.f);
       }
-      if (tid == 0) stats[row * (g.K + 1) + slot] = st;
+      if (tid == 0) stats[row * nslot + slot] = st;
     }
     if (tid < g.d) Elem<T>::st(dq + row * g.d + tid, dq_d);
     __syncthreads();
@@ -314,7 +315,7 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
 // ---------------------------------------------------------------------------
 // Backward, chunk pass.  grid (max(ceil(Lkv/S), NCcap), B*Hkv).  Workgroup c
 // owns keys [cS, cS+S) and landmark c: it walks the queries in order, and for
-// every (query, head) that selected c, or whose own chunk is c, adds
+// every (query, head) that selected c, or whose local window holds c, adds
 //   dk_j += scale dl_j q,  dv_j += w p_j dO,   and for a selection
 //   dlmk_c += scale ds q,  dbias_c += ds.
 // Deterministic: one owner per output row, fixed order.
@@ -351,10 +352,11 @@ generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restri
   __syncthreads();
 
   if (owns_keys) {
+    const int nslot = g.K + g.win;
     for (int i = 0; i < g.Lq; ++i) {
-      int ncand, oa, ob;
-      g.layout(i, ncand, oa, ob);
-      // which member is chunk c for query i: a selection slot, the own chunk, or none
+      int ncand, own, ob;
+      g.layout(i, ncand, own, ob);
+      // which member is chunk c for query i: a selection slot, a window slot, or none
       if (tid == 0) hit = -1;
       __syncthreads();
       if (c < g.NC && tid < g.K && sel_idx[((size_t)bkv * g.Lq + i) * g.K + tid] == c) hit = tid;
@@ -362,14 +364,19 @@ generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restri
       int slot = hit;
       int ta = a0, tb = a0 + g.S;
       if (slot < 0) {
-        if (ob > oa && oa == a0) { slot = g.K; ta = oa; tb = ob; } else { __syncthreads(); continue; }
+        if (g.window_member(own, ob, own - c, ta, tb)) {
+          slot = g.K + (own - c);
+        } else {
+          __syncthreads();
+          continue;
+        }
       }
       __syncthreads();
       const int n = tb - ta;
       for (int hh = 0; hh < g.G; ++hh) {
         const int h = kvh * g.G + hh;
         const size_t row = (size_t)(b * g.Hq + h) * g.Lq + i;
-        const float4 st = stats[row * (g.K + 1) + slot];   // w, lse_c, Dt, ds
+        const float4 st = stats[row * nslot + slot];   // w, lse_c, Dt, ds
         if (tid < g.d) {
           qh[tid] = Elem<T>::ld(q + row * g.d + tid);
           gh[tid] = Elem<T>::ld(dout + row * g.d + tid);
@@ -440,7 +447,7 @@ hipError_t launch_generic_forward(const Geometry& g, int bf16, const void* q, co
 }
 
 size_t generic_backward_ws(const Geometry& g) {
-  return (size_t)g.B * g.Hq * g.Lq * (g.K + 1) * sizeof(float4);
+  return (size_t)g.B * g.Hq * g.Lq * (g.K + g.win) * sizeof(float4);
 }
 
 template <typename T>

@@ -542,7 +542,7 @@ void launch_select(const Geometry& g, const uint16_t* q, const uint16_t* k, cons
 
 bool prefill_fast_supported(const Geometry& g, int bf16) {
   return bf16 && g.d == kD && g.S == kS && g.causal && g.Lq == g.Lkv && g.Lq % kWin == 0 &&
-         g.G == kG && g.K <= kMaxKf && g.NC <= kMaxNC && g.Lq > 0;
+         g.G == kG && g.K <= kMaxKf && g.NC <= kMaxNC && g.Lq > 0 && g.win <= 1;
 }
 
 size_t prefill_fast_ws(const Geometry& g) {

@@ -925,7 +925,7 @@ prefill_bwd_reduce(Geometry g, BwdWs ws, uint16_t* __restrict__ dk_out,
 
 bool prefill_bwd_fast_supported(const Geometry& g, int bf16) {
   return bf16 && g.d == kD && g.S == kS && g.G == kG && g.causal && g.Lq == g.Lkv &&
-         g.Lq % kWin == 0 && g.K <= kMaxKb && g.NC <= kMaxNCb && g.NC >= 1;
+         g.Lq % kWin == 0 && g.K <= kMaxKb && g.NC <= kMaxNCb && g.NC >= 1 && g.win <= 1;
 }
 
 size_t prefill_bwd_fast_ws(const Geometry& g) {

@@ -35,7 +35,7 @@ class HilsParams(ctypes.Structure):
                 ("seq_q", ctypes.c_int32), ("seq_kv", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("num_landmarks", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("keep_own_chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("local_chunks", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32)]
 
 
@@ -86,10 +86,17 @@ def load_library(path=None):
     return lib
 
 
+def _local(keep_own_chunk, local_chunks):
+    """Width of the local window in chunk slots: local_chunks if given, else 1 for
+    keep_own_chunk (the own chunk only) and 0 without it."""
+    return (1 if keep_own_chunk else 0) if local_chunks is None else int(local_chunks)
+
+
 def make_params(*, batch, heads_q, heads_kv, head_dim, seq_q, seq_kv, chunk_size, top_k,
-                num_landmarks, causal=True, keep_own_chunk=True, scale=0.0, dtype=HILS_BF16):
+                num_landmarks, causal=True, keep_own_chunk=True, scale=0.0, dtype=HILS_BF16,
+                local_chunks=None):
     return HilsParams(batch, heads_q, heads_kv, head_dim, seq_q, seq_kv, chunk_size, top_k,
-                      num_landmarks, int(bool(causal)), int(bool(keep_own_chunk)),
+                      num_landmarks, int(bool(causal)), _local(keep_own_chunk, local_chunks),
                       float(scale or 0.0), dtype)
 
 
@@ -116,7 +123,7 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale):
+def _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale, local_chunks=None):
     for name, t in (("q", q), ("k", k), ("lmk", lmk)):
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
@@ -125,7 +132,7 @@ def _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale):
     return make_params(batch=B, heads_q=Hq, heads_kv=Hkv, head_dim=d, seq_q=Lq, seq_kv=Lkv,
                        chunk_size=chunk_size, top_k=top_k, num_landmarks=lmk.shape[2],
                        causal=causal, keep_own_chunk=keep_own_chunk, scale=scale,
-                       dtype=_dtype_code(q))
+                       dtype=_dtype_code(q), local_chunks=local_chunks)
 
 
 def hils_workspace_size(params, op):
@@ -140,8 +147,8 @@ def _workspace(params, op, device, ws):
 
 
 def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_chunk, scale,
-         out, sel_idx, lse, ws, stream):
-    p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale)
+         out, sel_idx, lse, ws, stream, local_chunks):
+    p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale, local_chunks)
     B, Hq, Lq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
@@ -162,24 +169,28 @@ def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_
 
 def hils_forward(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, causal=True,
                  keep_own_chunk=True, scale=0.0, out=None, sel_idx=None, lse=None, ws=None,
-                 stream=None):
-    """HiLS forward: returns (out [B,Hq,Lq,d], sel_idx int32 [B,Hkv,Lq,K], lse fp32 [B,Hq,Lq])."""
+                 stream=None, local_chunks=None):
+    """HiLS forward: returns (out [B,Hq,Lq,d], sel_idx int32 [B,Hkv,Lq,K], lse fp32 [B,Hq,Lq]).
+
+    ``local_chunks`` (default: 1 with keep_own_chunk, else 0) is the width of the
+    chunk-aligned local window in chunk slots."""
     return _fwd("hils_forward", HILS_OP_FORWARD, q, k, v, lmk, lmk_bias, chunk_size, top_k,
-                causal, keep_own_chunk, scale, out, sel_idx, lse, ws, stream)
+                causal, keep_own_chunk, scale, out, sel_idx, lse, ws, stream, local_chunks)
 
 
 def hils_decode(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, keep_own_chunk=True,
-                scale=0.0, out=None, sel_idx=None, lse=None, ws=None, stream=None):
+                scale=0.0, out=None, sel_idx=None, lse=None, ws=None, stream=None,
+                local_chunks=None):
     """Single-token decode over the cache k, v (q: [B,Hq,1,d], position seq_kv-1)."""
     return _fwd("hils_decode", HILS_OP_DECODE, q, k, v, lmk, lmk_bias, chunk_size, top_k,
-                True, keep_own_chunk, scale, out, sel_idx, lse, ws, stream)
+                True, keep_own_chunk, scale, out, sel_idx, lse, ws, stream, local_chunks)
 
 
 def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size, top_k,
                   causal=True, keep_own_chunk=True, scale=0.0, need_dbias=None, ws=None,
-                  stream=None):
+                  stream=None, local_chunks=None):
     """Gradients (dq, dk, dv, dlmk, dbias-or-None) of <dout, out> with the selection fixed."""
-    p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale)
+    p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale, local_chunks)
     dq, dk, dv, dlmk = (torch.empty_like(t) for t in (q, k, v, lmk))
     if need_dbias is None:
         need_dbias = lmk_bias is not None

@@ -15,17 +15,24 @@
  *   selection    T_{g,i} = top min(K, |C_i|) chunks by the fp32 group score
  *                mean_{h in g} s_{h,i,c}, ties to the lower chunk id; the heads
  *                of a group share it   [HSADR §3 "Sparse training"; §4 GQA]
- *   attention    per chunk c in T (and the own chunk's visible tokens when
- *                keep_own_chunk): l_j = scale*<q, k_j>, lse_c = log sum exp l_j,
- *                o_c = sum_j exp(l_j - lse_c) v_j     [HSADR §3 "Hierarchical softmax"]
- *   fusion       F = T + {own}; s_own = lse_own; LSE = log sum_{c in F} exp s_c;
+ *   window       the chunk-aligned local window of w = local_chunks slots: the
+ *                query's own chunk (its visible tokens) and the w - 1 complete
+ *                chunks before it; candidates are the complete chunks before the
+ *                window, so window and retrieval never overlap.  w = 0: no
+ *                window; w = 1: the own chunk only  [HSADR §2 Preliminary]
+ *   attention    per chunk c in T and per window chunk: l_j = scale*<q, k_j>,
+ *                lse_c = log sum exp l_j, o_c = sum_j exp(l_j - lse_c) v_j
+ *                                                     [HSADR §3 "Hierarchical softmax"]
+ *   fusion       F = T + window chunks; a window chunk's score is its exact
+ *                lse_c; LSE = log sum_{c in F} exp s_c;
  *                O = sum_{c in F} exp(s_c - LSE) o_c  [HSADR Abstract; §3]
  *   backward     gradients of <dO, O> for q, k, v, lmk, bias with the selection
  *                held fixed; unselected chunks get none [HSADR §3; §9]
  *
  * Causal queries sit at key positions t_i = seq_kv - seq_q + i (prefill:
- * seq_q == seq_kv; decode: seq_q == 1, t = seq_kv - 1).  Non-causal: the
- * trailing partial chunk, if any, is the own chunk.  An empty fusion set gives
+ * seq_q == seq_kv; decode: seq_q == 1, t = seq_kv - 1); the own chunk is
+ * floor(t_i / chunk_size).  Non-causal: the own slot is the trailing partial
+ * chunk (possibly empty) and the window's other chunks precede it.  An empty fusion set gives
  * O = 0 and LSE = -inf.
  *
  * Layouts (all contiguous, row-major):
@@ -49,6 +56,7 @@
  *
  * Errors: arguments are validated before any launch.  A null required
  * pointer, a negative size, heads_q % heads_kv != 0, chunk_size or top_k < 1,
+ * local_chunks outside 0..64,
  * num_landmarks < seq_kv / chunk_size, a causal call with seq_q > seq_kv, a
  * decode call with seq_q != 1, a base pointer not 16-byte aligned, or a
  * workspace that is too small gives HILS_ERR_INVALID_ARG / HILS_ERR_WORKSPACE.
@@ -92,7 +100,7 @@ typedef struct {
   int32_t top_k;           /* K retrieved chunks per query (fewer if fewer exist)*/
   int32_t num_landmarks;   /* landmark rows per (batch, kv head), >= seq_kv / S  */
   int32_t causal;          /* 0 / 1                                              */
-  int32_t keep_own_chunk;  /* 0 / 1: attend the own chunk's visible tokens too   */
+  int32_t local_chunks;    /* chunk slots of the local window, 0..64 (below)     */
   float scale;             /* token-logit and score scale; <= 0 means 1/sqrt(d)  */
   int32_t dtype;           /* hils_dtype                                          */
 } hils_params;
@@ -138,7 +146,7 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* k, co
  * Rows c >= seq_kv / chunk_size of lmk and lmk_bias are written as 0; lq's rows
  * there are not read.  Fields used: dtype, batch, heads_kv, head_dim, seq_kv,
  * chunk_size, num_landmarks, scale (heads_q, seq_q, top_k, causal and
- * keep_own_chunk are ignored).  Errors: a null pointer to a non-empty buffer, a negative size,
+ * local_chunks are ignored).  Errors: a null pointer to a non-empty buffer, a negative size,
  * num_landmarks < seq_kv / chunk_size or a base pointer not 16-byte aligned give
  * HILS_ERR_INVALID_ARG; chunk_size or head_dim above 256, or
  * chunk_size * head_dim above 16384, give HILS_ERR_UNSUPPORTED.  No workspace. */

@@ -69,6 +69,7 @@ def check_selection(host, cfg, gpu_idx, b, g, qi, ref_idx_row):
     r = hils_query(host["q"][b, g * G:(g + 1) * G, qi].astype(np.float64), host["k"][b, g],
                    host["v"][b, g], lmk, bias, qi, Lq=cfg["Lq"], Lkv=cfg["Lkv"], S=cfg["S"],
                    K=cfg["K"], causal=bool(cfg["causal"]), keep_own=bool(cfg["keep_own"]),
+                   local_chunks=cfg.get("win"),
                    scale=scale)
     gb = dict(zip(r["cand"].tolist(), r["gbar"].tolist()))
     kth = sorted(gb[c] for c in want)[0]
@@ -87,7 +88,7 @@ def check_forward(host, cfg, out, idx, lse, queries=None, batches=None, heads_kv
     bs = list(range(B)) if batches is None else list(batches)
     gs = list(range(Hkv)) if heads_kv is None else list(heads_kv)
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=bool(cfg["causal"]),
-              keep_own_chunk=bool(cfg["keep_own"]))
+              keep_own_chunk=bool(cfg["keep_own"]), local_chunks=cfg.get("win"))
     kind, tol = tol_out(cfg["dtype"])
     lkind, ltol = ("rel", 1e-5) if cfg["dtype"] == "f32" else ("abs", 1e-3)
     swaps = 0

@@ -72,6 +72,8 @@ def _err():
     (dict(batch=-1), H.HILS_ERR_INVALID_ARG),
     (dict(dtype=7), H.HILS_ERR_INVALID_ARG),
     (dict(causal=2), H.HILS_ERR_INVALID_ARG),
+    (dict(keep_own_chunk=-1), H.HILS_ERR_INVALID_ARG),      # the local_chunks field
+    (dict(keep_own_chunk=65), H.HILS_ERR_INVALID_ARG),
     (dict(top_k=65), H.HILS_ERR_UNSUPPORTED),
     (dict(head_dim=512), H.HILS_ERR_UNSUPPORTED),
     (dict(chunk_size=512, seq_kv=1024, seq_q=1024, num_landmarks=2), H.HILS_ERR_UNSUPPORTED),
@@ -159,7 +161,7 @@ def test_landmarks_reject(kw, status):
 
 
 def test_landmarks_ignore_attention_only_fields():
-    """top_k, causal, keep_own_chunk, seq_q and heads_q take no part in landmark
+    """top_k, causal, local_chunks, seq_q and heads_q take no part in landmark
     formation: values that the attention entry points reject pass its checks
     (the call then fails only on the pointer it is given)."""
     p = _p(top_k=0, causal=5, keep_own_chunk=7, seq_q=-1, heads_q=3)

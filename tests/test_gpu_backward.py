@@ -23,7 +23,7 @@ def hl():
 def _grad_case(hl, cfg, queries=None):
     host, dev = make_device_inputs(cfg)
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=bool(cfg["causal"]),
-              keep_own_chunk=bool(cfg["keep_own"]))
+              keep_own_chunk=bool(cfg["keep_own"]), local_chunks=cfg.get("win"))
     out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"], **kw)
     dq, dk, dv, dl, db = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"],
                                           out, dev["dout"], idx, lse, need_dbias=True, **kw)
@@ -52,6 +52,13 @@ def test_tiny_f32_backward(hl):
     dict(B=2, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="iid",
          keep_own=0),
     dict(B=1, Hq=4, Hkv=1, d=128, Lq=1536, Lkv=1536, S=64, K=32, dtype="bf16", lmk="chunk_mean"),
+    # chunk-aligned local window of `win` chunk slots
+    dict(B=1, Hq=4, Hkv=2, d=64, Lq=150, Lkv=150, S=16, K=3, dtype="f32", lmk="iid", win=4,
+         bias=0.5),
+    dict(B=1, Hq=2, Hkv=2, d=64, Lq=45, Lkv=131, S=16, K=2, dtype="f32", lmk="iid", causal=0,
+         win=3),
+    dict(B=1, Hq=8, Hkv=2, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="chunk_mean",
+         win=4),
 ])
 def test_backward_shapes(hl, over):
     cfg = dict(config("tiny_f32"), seed=31, dout=True)

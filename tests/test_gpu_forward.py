@@ -19,7 +19,8 @@ def hl():
 
 
 def _run(hl, cfg, dev, entry="forward", **over):
-    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], keep_own_chunk=bool(cfg["keep_own"]))
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], keep_own_chunk=bool(cfg["keep_own"]),
+              local_chunks=cfg.get("win"))
     kw.update(over)
     if entry == "forward":
         out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"],
@@ -63,6 +64,17 @@ GENERIC_CASES = {
                             lmk="chunk_mean", seed=10),
     "mfma_g4_nc256_sortpath": _case(B=1, Hq=4, Hkv=1, d=128, Lq=16384, Lkv=16384, S=64, K=32,
                                     lmk="chunk_mean", seed=12),
+    # chunk-aligned local window of `win` chunk slots
+    "win3_causal_ragged": _case(B=2, Hq=4, Hkv=2, d=64, Lq=237, Lkv=237, S=16, K=3, win=3),
+    "win3_noncausal_tail": _case(B=1, Hq=4, Hkv=2, d=64, Lq=20, Lkv=203, S=32, K=2, causal=0,
+                                 win=3, dtype="f32"),
+    "win8_suffix_d128": _case(B=1, Hq=8, Hkv=2, d=128, Lq=100, Lkv=1100, S=64, K=8, win=8,
+                              bias=0.3, seed=13),
+    "win5_covers_cache": _case(B=1, Hq=2, Hkv=1, d=64, Lq=64, Lkv=64, S=16, K=2, win=5,
+                               dtype="f32"),
+    "win8_prefill_shape": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=8, win=8,
+                                lmk="chunk_mean", seed=14),
+    "win64_max": _case(B=1, Hq=4, Hkv=1, d=64, Lq=300, Lkv=300, S=4, K=4, win=64, seed=15),
 }
 
 
@@ -92,9 +104,10 @@ def test_values_one_give_output_one(hl, L):
     assert np.abs(out - 1.0).max() <= 2.0 ** -9 + 2.0 ** -8 + 1e-6
 
 
-@pytest.mark.parametrize("Lkv,K", [(8209, 32), (4096, 16), (100, 8), (64, 4)])
-def test_decode_small(hl, Lkv, K):
-    cfg = config("decode_128k", B=2, Lkv=Lkv, K=K)
+@pytest.mark.parametrize("Lkv,K,win", [(8209, 32, 1), (4096, 16, 1), (100, 8, 1), (64, 4, 1),
+                                       (8209, 32, 8), (1000, 8, 4), (300, 4, 9)])
+def test_decode_small(hl, Lkv, K, win):
+    cfg = config("decode_128k", B=2, Lkv=Lkv, K=K, win=win)
     host, dev = make_device_inputs(cfg)
     out, idx, lse = _run(hl, cfg, dev, entry="decode")
     check_forward(host, cfg, out, idx, lse)
