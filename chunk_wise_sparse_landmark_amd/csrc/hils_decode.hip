@@ -37,7 +37,7 @@ constexpr int kMaxGd = 16;            // heads per KV group on this path
 
 struct DecodeWs {
   uint64_t* lists;   // [B*Hkv][nsplit][K]
-  float* parts;      // [B*Hkv][asplit <= K+1][G][kPartStride]: (O, M, Z) per head
+  float* parts;      // [B*Hkv][asplit <= K+win][G][kPartStride]: (O, M, Z) per head
 };
 
 __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
@@ -222,9 +222,14 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     if (slot < g.K) {
       c = sel_idx[(size_t)bkv * g.K + slot];
       if (c >= 0) { a = c * kS; n = kS; }
-    } else if (slot == g.K && g.keep_own) {
-      a = (t / kS) * kS;
-      n = t - a + 1;
+    } else {
+      // local window slot j: chunk own - j (the own chunk's visible tokens for
+      // j = 0), fused with its exact log-sum-exp
+      const int j = slot - g.K, own = t / kS, cw = own - j;
+      if (j < g.win && cw >= 0) {
+        a = cw * kS;
+        n = j == 0 ? t - a + 1 : kS;
+      }
     }
     ca[tid] = a; cn[tid] = n; cc[tid] = c;
   }
@@ -297,7 +302,7 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
                          qs[h][2 * lane + 1] * __uint_as_float(cur.lm & 0xffff0000u);
         sv = g.scale * wave_sum(ps) + cur.bias;
       } else {
-        sv = m + __logf(z);   // own chunk: its exact log-sum-exp
+        sv = m + __logf(z);   // window chunk: its exact log-sum-exp
       }
       if (lane == 0) sc[h] = sv;
     }
@@ -399,7 +404,7 @@ struct DecodePlan {
 DecodePlan plan(const Geometry& g) {
   DecodePlan p;
   const int t = g.Lkv - 1;
-  p.ncand = min(t / kS, g.NC);
+  p.ncand = max(0, min(t / kS - max(g.win - 1, 0), g.NC));   // chunks before the window
   const int bkv = g.B * g.Hkv;
   // aim for about 1024 workgroups in the scoring launch
   int want_splits = max(1, 1024 / max(1, bkv));
@@ -411,7 +416,7 @@ DecodePlan plan(const Geometry& g) {
   p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
   // attention: one fusion slot per workgroup (latency hidden by parallelism)
   // unless that gives fewer than 256 workgroups; then up to 8 per workgroup
-  const int nslot = g.K + 1;
+  const int nslot = max(1, g.K + g.win);
   p.apc = min(8, max(1, 256 / max(1, nslot * bkv)));
   p.asplit = (nslot + p.apc - 1) / p.apc;
   return p;
@@ -431,13 +436,13 @@ DecodeWs carve(const Geometry& g, const DecodePlan& p, void* ws) {
 
 bool decode_fast_supported(const Geometry& g, int bf16) {
   return bf16 && g.d == kD && g.S == kS && g.G <= kMaxGd && g.K <= kMaxTopK && g.Lq == 1 &&
-         g.causal && g.win <= 1;
+         g.causal;
 }
 
 size_t decode_fast_ws(const Geometry& g) {
   DecodePlan p = plan(g);
   size_t off = ((size_t)g.B * g.Hkv * p.nsplit * g.K * 8 + 255) & ~(size_t)255;
-  off += ((size_t)g.B * g.Hkv * (g.K + 1) * g.G * kPartStride * 4 + 255) & ~(size_t)255;
+  off += ((size_t)g.B * g.Hkv * (g.K + g.win + 1) * g.G * kPartStride * 4 + 255) & ~(size_t)255;
   return off;
 }
 

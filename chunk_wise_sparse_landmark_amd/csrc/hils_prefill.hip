@@ -25,9 +25,10 @@
 //     row whose query did not select the chunk) and Z the chunk's softmax sum;
 //     a block none of whose queries selected the chunk is skipped.  Retrieval
 //     scores of the window's rows against its union come from one MFMA pass and
-//     the own chunk is attended first, so every fusion weight is final before
-//     any chunk is accumulated.  Chunk fragments are double-buffered in LDS:
-//     one barrier per chunk.
+//     the local window's exact lse from a statistics pass over its chunks, so
+//     every fusion weight is final before any chunk is accumulated; the window
+//     chunks then enter with P = exp(l - LSE).  Chunk fragments are
+//     double-buffered in LDS: one barrier per chunk.
 #include "hils_mfma.h"
 #include "hils_kernels.h"
 #include "hils_profile.h"
@@ -114,7 +115,9 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int i0 = win * kWin;
-  const int ncand = min(i0 / kS, g.NC);
+  // candidates: complete chunks before the local window (own chunk `win` and the
+  // g.win - 1 chunks before it)
+  const int ncand = max(0, min(win - max(g.win - 1, 0), g.NC));
   const int r16 = lane & 15, g4 = lane >> 4;
 
   // V of chunk `win` -> LDS (coalesced), later rewritten in fragment order
@@ -211,8 +214,8 @@ struct AttendSmem {
   uint8_t slotmap[kWin * kMaxNC];         // (query, chunk) -> slot, 0xff if not selected
   uint64_t qmask[kMaxNC];                 // chunk -> window queries that selected it
   uint16_t ulist[kMaxNC];
-  float lseown[kWin * kG];
-  float wown[kWin * kG];
+  float lsewin[kWin * kG];                // (query, head): lse of the local window's tokens
+  float lse2[kWin * kG];                  // (query, head): the row's LSE in log2 units
   int wcount[kAttWaves];
 };
 
@@ -275,6 +278,21 @@ __device__ __forceinline__ void block_softmax(f32x4 (&s)[4], float sc2, int vis,
   z_out = rowgroup_sum(z);
 }
 
+// Window chunks enter the fusion with their exact lse, so their tokens' fused
+// weight is exp(l - LSE): s <- exp2(sc2*s - lse2) with the row's final LSE in
+// log2 units, no per-chunk statistics.  kMasked hides keys >= vis.
+template <bool kMasked>
+__device__ __forceinline__ void block_direct(f32x4 (&s)[4], float sc2, int vis, float lse2) {
+  const int g4 = lane_id() >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -lse2));
+      s[mt][i] = (kMasked && mt * 16 + g4 * 4 + i >= vis) ? 0.f : e;
+    }
+}
+
 // P (scaled by f) as the A operand of O += P V: k-slot (g4, j) <-> key
 // 32ks + 16(j/4) + 4g4 + j%4, which is how S^T left the keys in the lane.
 __device__ __forceinline__ void pack_p(const f32x4 (&s)[4], float f, bf16x8 (&pa)[2]) {
@@ -295,11 +313,12 @@ __device__ __forceinline__ void load_frags(const uint4* __restrict__ src, bf16x8
   for (int x = 0; x < 16; ++x) f[x] = as_bf16x8(src[x * kWave + lane]);
 }
 
-// One staged chunk against the wave's four query blocks, in phases so the
-// MFMA work of one block overlaps the softmax of another: S^T of every active
-// block, then the softmaxes, then O += (rw / z) P V.  `act` has bit j set when
-// block j takes part (uniform over the wave); rw[j] is this lane's row weight.
-template <bool kMasked>
+// One staged chunk against the wave's query blocks, in phases so the MFMA work
+// of one block overlaps the softmax of another: S^T of every active block, then
+// the softmaxes, then O += (rw / z) P V.  `act` has bit j set when block j takes
+// part (uniform over the wave); rw[j] is this lane's row weight.  kDirect (a
+// local-window chunk): P = exp(l - LSE) with rw[j] = the row's LSE in log2 units.
+template <bool kMasked, bool kDirect>
 __device__ __forceinline__ void chunk_step(const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
                                            const uint16_t* __restrict__ nsrc,
                                            const bf16x8 (&qf)[kBlocksPerWave][4],
@@ -321,9 +340,14 @@ __device__ __forceinline__ void chunk_step(const uint4* __restrict__ kvb, uint4*
 #pragma unroll
   for (int j = 0; j < kBlocksPerWave; ++j) {
     if (act & (1u << j)) {
-      float m, z;
-      block_softmax<kMasked>(s[j], sc2, vis[j], m, z);
-      pack_p(s[j], rw[j] * __builtin_amdgcn_rcpf(z), pa[j]);
+      if (kDirect) {
+        block_direct<kMasked>(s[j], sc2, vis[j], rw[j]);
+        pack_p(s[j], 1.f, pa[j]);
+      } else {
+        float m, z;
+        block_softmax<kMasked>(s[j], sc2, vis[j], m, z);
+        pack_p(s[j], rw[j] * __builtin_amdgcn_rcpf(z), pa[j]);
+      }
     }
   }
   // keep the V fragment loads after the softmax (register pressure)
@@ -338,6 +362,31 @@ __device__ __forceinline__ void chunk_step(const uint4* __restrict__ kvb, uint4*
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) o[j][db] = mfma(pa[j][ks], vf[db * 2 + ks], o[j][db]);
     }
+}
+
+// Statistics of one staged local-window chunk for every block of the wave: the
+// chunk's row max (log2 units) and sum are folded into the running (M2, Z).
+template <bool kMasked>
+__device__ __forceinline__ void window_stats_step(const uint4* __restrict__ kvb,
+                                                  uint4* __restrict__ nxt,
+                                                  const uint16_t* __restrict__ nsrc,
+                                                  const bf16x8 (&qf)[kBlocksPerWave][4], float sc2,
+                                                  const int (&vis)[kBlocksPerWave],
+                                                  float (&M2)[kBlocksPerWave],
+                                                  float (&Z)[kBlocksPerWave]) {
+  if (nsrc) stage_async(nsrc, nxt);
+  bf16x8 kf[16];
+  load_frags(kvb, kf);
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j) {
+    f32x4 st[4];
+    float m2, z;
+    block_scores(kf, qf[j], st);
+    block_softmax<kMasked>(st, sc2, vis[j], m2, z);
+    const float mn = fmax2(M2[j], m2);
+    Z[j] = Z[j] * __builtin_amdgcn_exp2f(M2[j] - mn) + z * __builtin_amdgcn_exp2f(m2 - mn);
+    M2[j] = mn;
+  }
 }
 
 __global__ void __launch_bounds__(kAttThreads)
@@ -359,7 +408,9 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const int K = g.K;
   const int i0 = win * kWin;
   const int own = win;                    // the window is exactly chunk `win`
-  const int ncand = min(own, g.NC);
+  // local window: chunks own, own - 1, .., own - nwin + 1; candidates precede it
+  const int nwin = g.win > 0 ? 1 + min(g.win - 1, own) : 0;
+  const int ncand = max(0, min(own - max(g.win - 1, 0), g.NC));
   const uint16_t* KVg = kvf + (size_t)bkv * g.NC * kChunkElems;
   const uint16_t* Lg = lmk + (size_t)bkv * g.NCcap * kD;
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
@@ -405,9 +456,15 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int ks = 0; ks < 4; ++ks) qf[j][ks] = ld8(qr + ks * 32);
   }
 
-  // first staged chunk: the own chunk if kept, else the first of the union
-  const int first = g.keep_own ? own : (nunion > 0 ? sm.ulist[0] : -1);
-  if (first >= 0) stage_async(KVg + (size_t)first * kChunkElems, sm.kv[0]);
+  // staged chunk sequence: the window chunks (statistics pass), the window
+  // chunks again (accumulation), then the union
+  const int nseq = 2 * nwin + nunion;
+  auto seq_src = [&](int x) -> const uint16_t* {
+    if (x >= nseq) return nullptr;
+    const int c = x < nwin ? own - x : (x < 2 * nwin ? own - (x - nwin) : sm.ulist[x - 2 * nwin]);
+    return KVg + (size_t)c * kChunkElems;
+  };
+  if (nseq > 0) stage_async(seq_src(0), sm.kv[0]);
 
   // ---- retrieval scores of (row, selected chunk) by MFMA: rows x union columns
   for (int nt = 0; nt * 16 < nunion; ++nt) {
@@ -440,64 +497,81 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- own chunk, pass 1: lse of the visible tokens (key kk visible to query
-  //      qi when kk <= qi, as the window is the chunk)
+  // ---- local window, pass 1: lse of its visible tokens (key kk of the own
+  //      chunk visible to query qi when kk <= qi, as the window is the chunk)
   const float sc2 = scale * 1.4426950408889634f;   // scale * log2(e)
-  if (g.keep_own) {
-    bf16x8 kf[16];
-    load_frags(sm.kv[0], kf);
+  int cur = 0, x = 0;
+  if (nwin > 0) {
+    float M2[kBlocksPerWave], Z[kBlocksPerWave];
+    int vis[kBlocksPerWave];
+#pragma unroll
+    for (int j = 0; j < kBlocksPerWave; ++j) {
+      M2[j] = -INFINITY;
+      Z[j] = 0.f;
+      vis[j] = (w * kBlocksPerWave + j) * 4 + (r16 >> 2) + 1;
+    }
+    window_stats_step<true>(sm.kv[0], sm.kv[1], seq_src(1), qf, sc2, vis, M2, Z);
+    stage_wait();
+    __syncthreads();
+    cur = 1;
+    for (x = 1; x < nwin; ++x, cur ^= 1) {
+      window_stats_step<false>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, vis, M2, Z);
+      stage_wait();
+      __syncthreads();
+    }
+    // natural-log lse of the window's visible tokens: (M2 + log2 Z) * ln 2
 #pragma unroll
     for (int j = 0; j < kBlocksPerWave; ++j) {
       const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2);
-      f32x4 st[4];
-      float m2, z;
-      block_scores(kf, qf[j], st);
-      block_softmax<true>(st, sc2, qi + 1, m2, z);
-      // natural-log lse of the visible tokens: (m2 + log2 z) * ln 2
-      if (lane < 16) sm.lseown[qi * kG + (r16 & 3)] = (m2 + __log2f(z)) * 0.6931471805599453f;
+      if (lane < 16) sm.lsewin[qi * kG + (r16 & 3)] = (M2[j] + __log2f(Z[j])) * 0.6931471805599453f;
     }
   }
   __syncthreads();
-  // ---- fusion weights: LSE over the retrieval scores and the own chunk's lse
+  // ---- fusion weights: LSE over the retrieval scores and the window's lse
+  //      (the window chunks' own lse values combine into it exactly)
   if (tid < kWin * kG) {
     const int qi = tid >> 2, h = tid & 3;     // 64 queries x 4 heads
-    const float lo = g.keep_own ? sm.lseown[tid] : -INFINITY;
+    const float lo = nwin > 0 ? sm.lsewin[tid] : -INFINITY;
     float m = lo;
     for (int slot = 0; slot < K; ++slot)
       if (sm.sel[qi * K + slot] >= 0) m = fmaxf(m, sm.wts[(qi * K + slot) * kG + h]);
-    float z = g.keep_own ? __expf(lo - m) : 0.f;
+    float z = nwin > 0 ? __expf(lo - m) : 0.f;
     for (int slot = 0; slot < K; ++slot)
       if (sm.sel[qi * K + slot] >= 0) z += __expf(sm.wts[(qi * K + slot) * kG + h] - m);
     const float LSE = z > 0.f ? m + __logf(z) : -INFINITY;
     for (int slot = 0; slot < K; ++slot)
       if (sm.sel[qi * K + slot] >= 0)
         sm.wts[(qi * K + slot) * kG + h] = __expf(sm.wts[(qi * K + slot) * kG + h] - LSE);
-    sm.wown[tid] = (g.keep_own && z > 0.f) ? __expf(lo - LSE) : 0.f;
+    sm.lse2[tid] = LSE * 1.4426950408889634f;
     if (lse_out) lse_out[(size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + qi] = LSE;
   }
   __syncthreads();
 
-  // ---- the own chunk (staged in buffer 0), then the union; the next chunk is
-  //      copied into the other buffer while one is computed
-  int cur = 0;
-  if (g.keep_own) {
-    const uint16_t* nsrc = nunion > 0 ? KVg + (size_t)sm.ulist[0] * kChunkElems : nullptr;
+  // ---- the window chunks (P = exp(l - LSE)), then the union; the next chunk
+  //      is copied into the other buffer while one is computed
+  if (nwin > 0) {
     int vis[kBlocksPerWave];
     float rw[kBlocksPerWave];
 #pragma unroll
     for (int j = 0; j < kBlocksPerWave; ++j) {
       const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2);
-      vis[j] = qi + 1;                       // key kk of the chunk visible when kk <= qi
-      rw[j] = sm.wown[qi * kG + (r16 & 3)];
+      vis[j] = qi + 1;                       // key kk of the own chunk visible when kk <= qi
+      rw[j] = sm.lse2[qi * kG + (r16 & 3)];
     }
-    chunk_step<true>(sm.kv[0], sm.kv[1], nsrc, qf, sc2, (1u << kBlocksPerWave) - 1, vis, rw, o);
+    const unsigned all = (1u << kBlocksPerWave) - 1;
+    chunk_step<true, true>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, all, vis, rw, o);
     stage_wait();
     __syncthreads();
-    cur = 1;
+    cur ^= 1;
+    ++x;
+    for (; x < 2 * nwin; ++x, cur ^= 1) {
+      chunk_step<false, true>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, all, vis, rw, o);
+      stage_wait();
+      __syncthreads();
+    }
   }
-  for (int u = 0; u < nunion; ++u, cur ^= 1) {
+  for (int u = 0; u < nunion; ++u, ++x, cur ^= 1) {
     const int c = sm.ulist[u];
-    const uint16_t* nsrc = u + 1 < nunion ? KVg + (size_t)sm.ulist[u + 1] * kChunkElems : nullptr;
     const uint64_t qmk = sm.qmask[c];
     unsigned act = 0;
     int vis[kBlocksPerWave];
@@ -511,7 +585,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       vis[j] = kS;
       rw[j] = slot != 0xff ? sm.wts[(qi * K + slot) * kG + (r16 & 3)] : 0.f;
     }
-    chunk_step<false>(sm.kv[cur], sm.kv[cur ^ 1], nsrc, qf, sc2, act, vis, rw, o);
+    chunk_step<false, false>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, act, vis, rw, o);
     stage_wait();
     __syncthreads();
   }
@@ -542,7 +616,7 @@ void launch_select(const Geometry& g, const uint16_t* q, const uint16_t* k, cons
 
 bool prefill_fast_supported(const Geometry& g, int bf16) {
   return bf16 && g.d == kD && g.S == kS && g.causal && g.Lq == g.Lkv && g.Lq % kWin == 0 &&
-         g.G == kG && g.K <= kMaxKf && g.NC <= kMaxNC && g.Lq > 0 && g.win <= 1;
+         g.G == kG && g.K <= kMaxKf && g.NC <= kMaxNC && g.Lq > 0;
 }
 
 size_t prefill_fast_ws(const Geometry& g) {

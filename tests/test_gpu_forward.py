@@ -75,6 +75,14 @@ GENERIC_CASES = {
     "win8_prefill_shape": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=8, win=8,
                                 lmk="chunk_mean", seed=14),
     "win64_max": _case(B=1, Hq=4, Hkv=1, d=64, Lq=300, Lkv=300, S=4, K=4, win=64, seed=15),
+    # local window on the MFMA prefill path
+    "mfma_win2_bias": _case(B=2, Hq=4, Hkv=1, d=128, Lq=1024, Lkv=1024, S=64, K=16, win=2,
+                            bias=0.3, seed=16),
+    "mfma_win8_k32": _case(B=1, Hq=8, Hkv=2, d=128, Lq=2048, Lkv=2048, S=64, K=32, win=8,
+                           lmk="chunk_mean", seed=17),
+    "mfma_win20_covers": _case(B=1, Hq=4, Hkv=1, d=128, Lq=1024, Lkv=1024, S=64, K=4, win=20,
+                               seed=18),
+    "mfma_win0": _case(B=1, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, win=0, seed=19),
 }
 
 
@@ -92,9 +100,9 @@ def test_forward_shapes(hl, name):
     check_forward(host, cfg, out, idx, lse, queries=qs)
 
 
-@pytest.mark.parametrize("L", [700, 1024])
-def test_values_one_give_output_one(hl, L):
-    cfg = _case(B=1, Hq=8, Hkv=2, d=128, Lq=L, Lkv=L, S=64, K=4)
+@pytest.mark.parametrize("L,win", [(700, 1), (1024, 1), (1024, 8), (700, 3)])
+def test_values_one_give_output_one(hl, L, win):
+    cfg = _case(B=1, Hq=8, Hkv=2, d=128, Lq=L, Lkv=L, S=64, K=4, win=win)
     host, dev = make_device_inputs(cfg)
     dev["v"] = torch.ones_like(dev["v"])
     out, idx, lse = _run(hl, cfg, dev)
