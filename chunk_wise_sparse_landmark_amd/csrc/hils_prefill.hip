@@ -456,15 +456,12 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int ks = 0; ks < 4; ++ks) qf[j][ks] = ld8(qr + ks * 32);
   }
 
-  // staged chunk sequence: the window chunks (statistics pass), the window
-  // chunks again (accumulation), then the union
-  const int nseq = 2 * nwin + nunion;
-  auto seq_src = [&](int x) -> const uint16_t* {
-    if (x >= nseq) return nullptr;
-    const int c = x < nwin ? own - x : (x < 2 * nwin ? own - (x - nwin) : sm.ulist[x - 2 * nwin]);
-    return KVg + (size_t)c * kChunkElems;
-  };
-  if (nseq > 0) stage_async(seq_src(0), sm.kv[0]);
+  // staged chunks: the window chunks own, own - 1, .., own - nwin + 1
+  // (statistics pass), then the same chunks in the reverse order (the first of
+  // them is still staged), then the union
+  auto csrc = [&](int c) -> const uint16_t* { return KVg + (size_t)c * kChunkElems; };
+  const uint16_t* first_src = nwin > 0 ? csrc(own) : (nunion > 0 ? csrc(sm.ulist[0]) : nullptr);
+  if (first_src) stage_async(first_src, sm.kv[0]);
 
   // ---- retrieval scores of (row, selected chunk) by MFMA: rows x union columns
   for (int nt = 0; nt * 16 < nunion; ++nt) {
@@ -498,26 +495,27 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int db = 0; db < 8; ++db) o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- local window, pass 1: lse of its visible tokens (key kk of the own
-  //      chunk visible to query qi when kk <= qi, as the window is the chunk)
+  //      chunk visible to query qi when kk <= qi, as the window is the chunk;
+  //      the other window chunks are complete: vis = kS)
   const float sc2 = scale * 1.4426950408889634f;   // scale * log2(e)
-  int cur = 0, x = 0;
+  int cur = 0;
   if (nwin > 0) {
     float M2[kBlocksPerWave], Z[kBlocksPerWave];
-    int vis[kBlocksPerWave];
+    int vis_own[kBlocksPerWave], vis_full[kBlocksPerWave];
 #pragma unroll
     for (int j = 0; j < kBlocksPerWave; ++j) {
       M2[j] = -INFINITY;
       Z[j] = 0.f;
-      vis[j] = (w * kBlocksPerWave + j) * 4 + (r16 >> 2) + 1;
+      vis_own[j] = (w * kBlocksPerWave + j) * 4 + (r16 >> 2) + 1;
+      vis_full[j] = kS;
     }
-    window_stats_step<true>(sm.kv[0], sm.kv[1], seq_src(1), qf, sc2, vis, M2, Z);
-    stage_wait();
-    __syncthreads();
-    cur = 1;
-    for (x = 1; x < nwin; ++x, cur ^= 1) {
-      window_stats_step<false>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, vis, M2, Z);
+    for (int x = 0; x < nwin; ++x) {
+      const bool last = x + 1 == nwin;
+      window_stats_step<true>(sm.kv[cur], sm.kv[cur ^ 1], last ? nullptr : csrc(own - x - 1), qf,
+                              sc2, x == 0 ? vis_own : vis_full, M2, Z);
       stage_wait();
       __syncthreads();
+      if (!last) cur ^= 1;
     }
     // natural-log lse of the window's visible tokens: (M2 + log2 Z) * ln 2
 #pragma unroll
@@ -547,30 +545,29 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   }
   __syncthreads();
 
-  // ---- the window chunks (P = exp(l - LSE)), then the union; the next chunk
-  //      is copied into the other buffer while one is computed
+  // ---- the window chunks (P = exp(l - LSE)) from own - nwin + 1 (still
+  //      staged) up to the own chunk, then the union; the next chunk is copied
+  //      into the other buffer while one is computed
   if (nwin > 0) {
-    int vis[kBlocksPerWave];
+    int vis_own[kBlocksPerWave], vis_full[kBlocksPerWave];
     float rw[kBlocksPerWave];
 #pragma unroll
     for (int j = 0; j < kBlocksPerWave; ++j) {
       const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2);
-      vis[j] = qi + 1;                       // key kk of the own chunk visible when kk <= qi
+      vis_own[j] = qi + 1;                   // key kk of the own chunk visible when kk <= qi
+      vis_full[j] = kS;
       rw[j] = sm.lse2[qi * kG + (r16 & 3)];
     }
     const unsigned all = (1u << kBlocksPerWave) - 1;
-    chunk_step<true, true>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, all, vis, rw, o);
-    stage_wait();
-    __syncthreads();
-    cur ^= 1;
-    ++x;
-    for (; x < 2 * nwin; ++x, cur ^= 1) {
-      chunk_step<false, true>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, all, vis, rw, o);
+    for (int y = nwin - 1; y >= 0; --y, cur ^= 1) {
+      const uint16_t* nsrc = y > 0 ? csrc(own - y + 1) : (nunion > 0 ? csrc(sm.ulist[0]) : nullptr);
+      chunk_step<true, true>(sm.kv[cur], sm.kv[cur ^ 1], nsrc, qf, sc2, all,
+                             y == 0 ? vis_own : vis_full, rw, o);
       stage_wait();
       __syncthreads();
     }
   }
-  for (int u = 0; u < nunion; ++u, ++x, cur ^= 1) {
+  for (int u = 0; u < nunion; ++u, cur ^= 1) {
     const int c = sm.ulist[u];
     const uint64_t qmk = sm.qmask[c];
     unsigned act = 0;
@@ -585,7 +582,8 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       vis[j] = kS;
       rw[j] = slot != 0xff ? sm.wts[(qi * K + slot) * kG + (r16 & 3)] : 0.f;
     }
-    chunk_step<false, false>(sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), qf, sc2, act, vis, rw, o);
+    const uint16_t* nsrc = u + 1 < nunion ? csrc(sm.ulist[u + 1]) : nullptr;
+    chunk_step<false, false>(sm.kv[cur], sm.kv[cur ^ 1], nsrc, qf, sc2, act, vis, rw, o);
     stage_wait();
     __syncthreads();
   }

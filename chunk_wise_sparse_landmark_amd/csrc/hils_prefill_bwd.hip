@@ -5,10 +5,11 @@
 // page), §3 "Hierarchical softmax" (gradients of the LM loss reach the chunk
 // retrieval scores through the fusion weights) and §9 (unselected chunks get no
 // gradient).  With the selection fixed, for a query row with fusion weights w_c
-// (w_c = exp(s_c - LSE), s_own = lse_own) and chunk softmaxes p:
+// (w_c = exp(s_c - LSE); a local-window chunk's score is its exact lse_c) and
+// chunk softmaxes p:
 //   D   = <dO, O>,  u_j = <dO, v_j>,  D_c = sum_j p_j u_j
 //   retrieved chunk: dl_j = w_c p_j (u_j - D_c),  ds_c = w_c (D_c - D)
-//   own chunk:       dl_j = w_own p_j (u_j - D)
+//   window chunk:    dl_j = w_c p_j (u_j - D)
 //   dq = scale (sum_j dl_j k_j + sum_c ds_c lmk_c),  dk_j += scale dl_j q,
 //   dv_j += w p_j dO,  dlmk_c += scale ds_c q,  dbias_c += ds_c.
 //
@@ -23,7 +24,7 @@
 //     each (row, slot)'s (w, log2 lse_c, D_c) goes to a table; after the loop
 //     dq gains scale * sum ds_c lmk_c.
 //  3. prefill_bwd_chunks  per (b, kv head, chunk): gathers the queries that
-//     selected the chunk (and the chunk's own window) in tiles of 8 queries x
+//     selected the chunk (and those whose local window holds it) in tiles of 8 queries x
 //     4 heads = 32 rows, recomputes S = Q K^T and U = dO V^T for the wave's 16
 //     keys, turns them into w p and dl with the row table (no reductions), and
 //     accumulates dV += (w P)^T dO and dK += dL^T Q by MFMA over the rows, plus
@@ -56,9 +57,10 @@ constexpr int kPartFloats = 2 * kS * kD + kD + 4;  // dV, dK, dlmk, dbias (+pad 
 
 // Upper bound of the work items of one (b, kv head): a query selects at most K
 // chunks, so the retrieved tiles number at most L*K/8 plus one partial tile per
-// chunk; each chunk adds its own-window tiles and at most one short item.
+// chunk; each chunk adds the tiles of the local windows that hold it (8 per
+// window) and at most one short item.
 int max_items_of(const Geometry& g) {
-  const long tiles = (long)g.Lq * g.K / 8 + g.NC + (long)g.NC * (kWin / 8);
+  const long tiles = (long)g.Lq * g.K / 8 + g.NC + (long)g.NC * (kWin / 8) * max(g.win, 1);
   return (int)(tiles / kTilesPerItem + 2 * g.NC + 1);
 }
 
@@ -67,7 +69,7 @@ struct BwdWs {
   uint16_t* qi;      // [bkv][L][d][4 heads]
   uint16_t* doi;     // [bkv][L][d][4 heads]
   float* Drow;       // [B][Hq][L]
-  float4* stats;     // [B][Hq][L][K+1]: (w, log2 lse_c, D_c (own: D), ds_c (own: 0))
+  float4* stats;     // [B][Hq][L][K+win]: (w, log2 lse_c, D_c (window: D), ds_c (window: 0))
   uint64_t* qm;      // [bkv][NW][NC]: window queries that selected chunk c
   uint8_t* slot;     // [bkv][L][NC]: slot of chunk c in query i's selection, 0xff if none
   int4* items;       // [bkv][max_items]: (chunk, first tile, end tile, partial slot or -1)
@@ -93,7 +95,7 @@ BwdWs carve(const Geometry& g, void* base, size_t* total) {
   w.Drow = reinterpret_cast<float*>(c + off);
   off += align256((size_t)g.B * g.Hq * L * 4);
   w.stats = reinterpret_cast<float4*>(c + off);
-  off += align256((size_t)g.B * g.Hq * L * (g.K + 1) * 16);
+  off += align256((size_t)g.B * g.Hq * L * (g.K + g.win) * 16);
   w.qm = reinterpret_cast<uint64_t*>(c + off);
   off += align256(nbkv * NW * g.NC * 8);
   w.slot = reinterpret_cast<uint8_t*>(c + off);
@@ -293,13 +295,14 @@ __device__ __forceinline__ void pack_keys(const f32x4 (&x)[4], bf16x8 (&pa)[2]) 
   }
 }
 
-// One block against one staged chunk.  kOwn: keys >= vis hidden, D_c := D and
-// the weight is the own chunk's (computed here from its lse).  Returns the row's
+// One block against one staged chunk.  Keys >= vis are hidden.  A local-window
+// chunk (local): D_c := D and the weight exp(lse_c - LSE) is computed here from
+// the chunk's lse; otherwise the weight is w_in.  Returns the row's
 // (w, log2 lse_c, D_c) in lanes l < 16 (and in all lanes of the row group).
-template <bool kOwn>
 __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)[4],
-                                            const bf16x8 (&df)[4], float sc2, int vis, float w_in,
-                                            float Drow, float lse2_row, f32x4 (&dq)[8]) {
+                                            const bf16x8 (&df)[4], float sc2, int vis, bool local,
+                                            float w_in, float Drow, float lse2_row,
+                                            f32x4 (&dq)[8]) {
   const int g4 = lane_id() >> 4;
   f32x4 s[4], u[4];
   // one fragment set in registers at a time (the barriers keep the compiler
@@ -316,7 +319,7 @@ __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)
     keys_by_rows(f, df, u);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (kOwn) {
+  if (vis < kS) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -344,8 +347,8 @@ __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)
   const float rz = __builtin_amdgcn_rcpf(z);
   const float lse2 = mb + __log2f(z);
   const float Dc = y * rz;                               // sum_j p_j u_j
-  const float w = kOwn ? __builtin_amdgcn_exp2f(lse2 - lse2_row) : w_in;
-  const float ref = kOwn ? Drow : Dc;
+  const float w = local ? __builtin_amdgcn_exp2f(lse2 - lse2_row) : w_in;
+  const float ref = local ? Drow : Dc;
   const float f = w * rz;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -360,53 +363,41 @@ __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(pa[ks], kb[db * 2 + ks], dq[db]);
-  return make_float4(w, lse2, kOwn ? Drow : Dc, 0.f);
+  return make_float4(w, lse2, ref, 0.f);
 }
 
-// The own-chunk step and a union-chunk step of the rows pass.  Each first
-// starts the next chunk's copy into `nxt`; the chunk buffers and LDS tables are
-// restrict so the reads of `kvb` need not wait for that copy.
-__device__ __forceinline__ void rows_own_step(
-    const Geometry& g, const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
-    const uint16_t* __restrict__ nsrc, const float* __restrict__ Dr,
-    const float* __restrict__ LSE2, const bf16x8 (&qf)[kRowBlocks][4],
-    const bf16x8 (&df)[kRowBlocks][4], float sc2, const BwdWs& ws, int b, int kvh, int i0,
-    int w, f32x4 (&dq)[kRowBlocks][8]) {
-  const int lane = lane_id(), r16 = lane & 15;
-  const int K = g.K, L = g.Lq;
-  if (nsrc) stage48(nsrc, nxt);
-#pragma unroll
-  for (int j = 0; j < kRowBlocks; ++j) {
-    const int qi = (w * kRowBlocks + j) * 4 + (r16 >> 2), h = r16 & 3;
-    const float4 st = block_bwd<true>(kvb, qf[j], df[j], sc2, qi + 1, 0.f, Dr[qi * kG + h],
-                                      LSE2[qi * kG + h], dq[j]);
-    if (lane < 16)
-      ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * (size_t)(K + 1) + K] = st;
-  }
-}
-
-__device__ __forceinline__ void rows_union_step(
+// One step of the rows pass over a staged chunk c: first the next chunk's copy
+// into `nxt` starts (the chunk buffers and LDS tables are restrict, so the reads
+// of `kvb` need not wait for it).  jwin >= 0: member jwin of the local window
+// (chunk own - jwin, table slot K + jwin; only the own chunk, jwin = 0, is
+// masked), every block takes part.  jwin < 0: a union chunk; blocks none of
+// whose queries selected it are skipped, and each selecting row's ds_c replaces
+// its weight in `wts`.
+__device__ __forceinline__ void rows_step(
     const Geometry& g, const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
     const uint16_t* __restrict__ nsrc, const uint8_t* __restrict__ slotmap,
-    float* __restrict__ wts, const float* __restrict__ Dr, uint64_t qmk, int c,
-    const bf16x8 (&qf)[kRowBlocks][4], const bf16x8 (&df)[kRowBlocks][4], float sc2,
-    const BwdWs& ws, int b, int kvh, int i0, int w, f32x4 (&dq)[kRowBlocks][8]) {
+    float* __restrict__ wts, const float* __restrict__ Dr, const float* __restrict__ LSE2,
+    uint64_t qmk, int c, int jwin, const bf16x8 (&qf)[kRowBlocks][4],
+    const bf16x8 (&df)[kRowBlocks][4], float sc2, const BwdWs& ws, int b, int kvh, int i0, int w,
+    f32x4 (&dq)[kRowBlocks][8]) {
   const int lane = lane_id(), r16 = lane & 15;
   const int K = g.K, L = g.Lq;
+  const bool local = jwin >= 0;
   if (nsrc) stage48(nsrc, nxt);
 #pragma unroll
   for (int j = 0; j < kRowBlocks; ++j) {
     const int blk = w * kRowBlocks + j;
     if (((qmk >> (blk * 4)) & 0xfull) == 0) continue;
     const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
-    const int slot = slotmap[qi * kMaxNCb + c];
-    const float wv = slot != 0xff ? wts[(qi * K + slot) * kG + h] : 0.f;
+    const int slot = local ? K + jwin : slotmap[qi * kMaxNCb + c];
+    const float wv = (!local && slot != 0xff) ? wts[(qi * K + slot) * kG + h] : 0.f;
     const float dr = Dr[qi * kG + h];
-    float4 st = block_bwd<false>(kvb, qf[j], df[j], sc2, kS, wv, dr, 0.f, dq[j]);
-    st.w = wv * (st.z - dr);                                         // ds_c
+    float4 st = block_bwd(kvb, qf[j], df[j], sc2, jwin == 0 ? qi + 1 : kS, local, wv, dr,
+                          LSE2[qi * kG + h], dq[j]);
+    if (!local) st.w = wv * (st.z - dr);                           // ds_c
     if (lane < 16 && slot != 0xff) {
-      ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * (size_t)(K + 1) + slot] = st;
-      wts[(qi * K + slot) * kG + h] = st.w;
+      ws.stats[((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * (size_t)(K + g.win) + slot] = st;
+      if (!local) wts[(qi * K + slot) * kG + h] = st.w;
     }
   }
 }
@@ -426,7 +417,9 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
   const int r16 = lane & 15, g4 = lane >> 4;
   const int K = g.K, L = g.Lq;
   const int i0 = win * kWin, own = win;
-  const int ncand = min(own, g.NC);
+  // local window: chunks own, own - 1, .., own - nwin + 1; candidates precede it
+  const int nwin = g.win > 0 ? 1 + min(g.win - 1, own) : 0;
+  const int ncand = max(0, min(own - max(g.win - 1, 0), g.NC));
   const uint16_t* Fg = ws.frags + (size_t)bkv * g.NC * kBwdChunkElems;
   const uint16_t* Lg = lmk + (size_t)bkv * g.NCcap * kD;
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
@@ -481,8 +474,14 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     }
   }
 
-  const int first = g.keep_own ? own : (nunion > 0 ? sm.ulist[0] : -1);
-  if (first >= 0) stage48(Fg + (size_t)first * kBwdChunkElems, sm.kv[0]);
+  // staged chunk sequence: the window chunks, then the union
+  const int nseq = nwin + nunion;
+  auto seq_src = [&](int x) -> const uint16_t* {
+    if (x >= nseq) return nullptr;
+    const int c = x < nwin ? own - x : sm.ulist[x - nwin];
+    return Fg + (size_t)c * kBwdChunkElems;
+  };
+  if (nseq > 0) stage48(seq_src(0), sm.kv[0]);
 
   // ---- fusion weights of (row, selected chunk): exp(scale q.lmk + bias - LSE)
   for (int nt = 0; nt * 16 < nunion; ++nt) {
@@ -518,19 +517,25 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     for (int db = 0; db < 8; ++db) dq[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int cur = 0;
-  if (g.keep_own) {
-    rows_own_step(g, sm.kv[0], sm.kv[1],
-                  nunion > 0 ? Fg + (size_t)sm.ulist[0] * kBwdChunkElems : nullptr, sm.Dr, sm.LSE2,
-                  qf, df, sc2, ws, b, kvh, i0, w, dq);
+  int x0 = 0;
+  if (nwin > 0) {   // the own chunk (straight-line: its mode is known here)
+    rows_step(g, sm.kv[0], sm.kv[1], seq_src(1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2, ~0ull, own, 0,
+              qf, df, sc2, ws, b, kvh, i0, w, dq);
     stage_wait_all();
     __syncthreads();
     cur = 1;
+    x0 = 1;
   }
-  for (int uidx = 0; uidx < nunion; ++uidx, cur ^= 1) {
-    const int c = sm.ulist[uidx];
-    rows_union_step(g, sm.kv[cur], sm.kv[cur ^ 1],
-                    uidx + 1 < nunion ? Fg + (size_t)sm.ulist[uidx + 1] * kBwdChunkElems : nullptr,
-                    sm.slotmap, sm.wts, sm.Dr, sm.qmask[c], c, qf, df, sc2, ws, b, kvh, i0, w, dq);
+  for (int x = x0; x < nwin; ++x, cur ^= 1) {
+    rows_step(g, sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2,
+              ~0ull, own - x, x, qf, df, sc2, ws, b, kvh, i0, w, dq);
+    stage_wait_all();
+    __syncthreads();
+  }
+  for (int x = nwin; x < nseq; ++x, cur ^= 1) {
+    const int c = sm.ulist[x - nwin];
+    rows_step(g, sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2,
+              sm.qmask[c], c, -1, qf, df, sc2, ws, b, kvh, i0, w, dq);
     stage_wait_all();
     __syncthreads();
   }
@@ -567,8 +572,9 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
 // ----------------------------------------------------------------------------
 // (tile staging helpers and the chunk kernel follow the planner)
 
-// ---- work items: each chunk's tiles (own window first, then the retrieving
-//      queries in query order, 8 per tile) cut into items of kTilesPerItem.
+// ---- work items: each chunk's tiles (the local windows that hold it first, 8
+//      tiles per window, then the retrieving queries in query order, 8 per
+//      tile) cut into items of kTilesPerItem.
 //      One workgroup per (b, kv head).
 __global__ void __launch_bounds__(kChunkThreads)
 prefill_bwd_plan(Geometry g, BwdWs ws) {
@@ -579,8 +585,9 @@ prefill_bwd_plan(Geometry g, BwdWs ws) {
   if (tid < g.NC) {
     int n = 0;
 #pragma unroll 8
-    for (int wdw = tid + 1; wdw < NW; ++wdw) n += __popcll(ws.qm[((size_t)bkv * NW + wdw) * g.NC + tid]);
-    tiles = (n + 7) / 8 + (g.keep_own ? kWin / 8 : 0);
+    for (int wdw = tid + max(g.win, 1); wdw < NW; ++wdw)
+      n += __popcll(ws.qm[((size_t)bkv * NW + wdw) * g.NC + tid]);
+    tiles = (n + 7) / 8 + (kWin / 8) * min(g.win, NW - tid);
     nseg = max(1, (tiles + kTilesPerItem - 1) / kTilesPerItem);
   }
   scan[tid] = nseg;
@@ -620,7 +627,7 @@ struct TileBuf {
 struct ChunkSmem {
   TileBuf tb[2];
   uint16_t eq[kTilesPerItem * 8];   // tile entries: query
-  uint8_t es[kTilesPerItem * 8];    // slot (K = own chunk), 0xff = padding
+  uint8_t es[kTilesPerItem * 8];    // slot (K + j = window member j), 0xff = padding
   int scan[kChunkThreads];
 };
 
@@ -663,7 +670,7 @@ __device__ __forceinline__ void stage_tile(const Geometry& g, const uint16_t* __
       const int sl = es[ee];
       const int qq = eq[sl != 0xff ? ee : e0];
       const int slot = sl != 0xff ? sl : es[e0];
-      const float4* p = ws.stats + ((size_t)(b * g.Hq + kvh * kG + (lane & 3)) * L + qq) * (g.K + 1) + slot;
+      const float4* p = ws.stats + ((size_t)(b * g.Hq + kvh * kG + (lane & 3)) * L + qq) * (g.K + g.win) + slot;
       lds_load16(p, tb.st);
     }
   }
@@ -699,17 +706,17 @@ __device__ __forceinline__ void chunk_tile_step(
     const int e = t * 8 + 4 * mt + (lane >> 4);
     const int sl = es[e];
     const bool valid = sl != 0xff;
-    const bool own = sl == g.K;
+    const bool local = sl >= g.K;            // a window member (keys after the query hidden)
     const int qq = eq[valid ? e : t * 8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 st = tb.st[(4 * mt + (lane >> 4)) * 4 + i];
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], sc2, -st.y));
-      if (!valid || (own && key > qq)) p = 0.f;
+      if (!valid || (local && key > qq)) p = 0.f;
       const float wp = st.x * p;
       a8[4 * mt + i] = wp;
       d8[4 * mt + i] = wp * (u[mt][i] - st.z);
-      ds[mt][i] = (valid && !own) ? st.w : 0.f;
+      ds[mt][i] = (valid && !local) ? st.w : 0.f;
     }
   }
   const bf16x8 Awp = pack_bf16x8(a8), Adl = pack_bf16x8(d8);
@@ -760,25 +767,29 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = g.Lq, NW = L / kWin;
   const float scale = g.scale, sc2 = scale * 1.4426950408889634f;
-  const int own_tiles = g.keep_own ? kWin / 8 : 0;
+  // the local windows c, c+1, .., c+win-1 (those that exist) hold chunk c
+  const int own_tiles = (kWin / 8) * min(g.win, NW - c);
   const int ntile = t1 - t0;
 
-  // ---- tile entries of this item: own-window queries (slot K), then the
-  //      retrieving queries of later windows in query order
+  // ---- tile entries of this item: the queries of the windows that hold the
+  //      chunk (window c + j: slot K + j), then the retrieving queries of later
+  //      windows in query order
   for (int e = tid; e < kTilesPerItem * 8; e += kChunkThreads) sm.es[e] = 0xff;
   __syncthreads();
   for (int e = tid; e < ntile * 8; e += kChunkThreads) {
     const int t = t0 + e / 8;
     if (t < own_tiles) {
-      sm.eq[e] = (uint16_t)(c * kWin + t * 8 + e % 8);
-      sm.es[e] = (uint8_t)g.K;
+      const int jw = t / (kWin / 8);
+      sm.eq[e] = (uint16_t)((c + jw) * kWin + (t % (kWin / 8)) * 8 + e % 8);
+      sm.es[e] = (uint8_t)(g.K + jw);
     }
   }
   const int r0 = 8 * max(0, t0 - own_tiles), r1 = 8 * max(0, t1 - own_tiles);
   const int rbase = 8 * max(0, own_tiles - t0);   // entry index of the first retrieved query
-  const int nwin = NW - c - 1;
+  const int wret = c + max(g.win, 1);        // first window that may retrieve chunk c
+  const int nlater = NW - wret;
   uint64_t m = 0;
-  if (tid < nwin && r1 > r0) m = ws.qm[((size_t)bkv * NW + c + 1 + tid) * g.NC + c];
+  if (tid < nlater && r1 > r0) m = ws.qm[((size_t)bkv * NW + wret + tid) * g.NC + c];
   const int cnt = __popcll(m);
   sm.scan[tid] = cnt;
   __syncthreads();
@@ -796,7 +807,7 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
         const int bit = __ffsll((long long)mm) - 1;
         mm &= mm - 1;
         if (pos >= r0 && pos < r1) {
-          const int qq = (c + 1 + tid) * kWin + bit;
+          const int qq = (wret + tid) * kWin + bit;
           sm.eq[rbase + pos - r0] = (uint16_t)qq;
           sm.es[rbase + pos - r0] = ws.slot[((size_t)bkv * L + qq) * g.NC + c];
         }
@@ -925,7 +936,8 @@ prefill_bwd_reduce(Geometry g, BwdWs ws, uint16_t* __restrict__ dk_out,
 
 bool prefill_bwd_fast_supported(const Geometry& g, int bf16) {
   return bf16 && g.d == kD && g.S == kS && g.G == kG && g.causal && g.Lq == g.Lkv &&
-         g.Lq % kWin == 0 && g.K <= kMaxKb && g.NC <= kMaxNCb && g.NC >= 1 && g.win <= 1;
+         g.Lq % kWin == 0 && g.K <= kMaxKb && g.NC <= kMaxNCb && g.NC >= 1 &&
+         g.K + g.win < 0xff;
 }
 
 size_t prefill_bwd_fast_ws(const Geometry& g) {

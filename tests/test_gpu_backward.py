@@ -59,6 +59,12 @@ def test_tiny_f32_backward(hl):
          win=3),
     dict(B=1, Hq=8, Hkv=2, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="chunk_mean",
          win=4),
+    dict(B=2, Hq=4, Hkv=1, d=128, Lq=1024, Lkv=1024, S=64, K=16, dtype="bf16", lmk="iid",
+         win=8, bias=0.3),
+    dict(B=1, Hq=4, Hkv=1, d=128, Lq=768, Lkv=768, S=64, K=8, dtype="bf16", lmk="chunk_mean",
+         win=2),
+    dict(B=1, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="iid", win=12),
+    dict(B=1, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="iid", win=0),
 ])
 def test_backward_shapes(hl, over):
     cfg = dict(config("tiny_f32"), seed=31, dout=True)
