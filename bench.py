@@ -15,7 +15,9 @@ all candidates + K/V of the selected and own tokens + q, out, idx, lse; inputs
 rotate over several independent sets so the 256 MB last-level cache cannot hold
 them), the training step (forward + backward, TFLOP/s), and landmark formation
 with its backward over the training batch's keys (algorithmic HBM GB/s, 16
-rotating input sets).
+rotating input sets).  The `_swa512` lines repeat prefill_8k, decode_128k and
+train_8k with a 512-token chunk-aligned local window (8 chunk slots) beside the
+top-K retrieval.
 
 Every input is resident in HBM before timing.  Per-kernel durations come from
 HIP events the library records around each launch of the dominant kernel on
@@ -88,17 +90,28 @@ class HipEvents:
 
 
 # --------------------------------------------------------------------------- work counts
+def local_chunks(cfg):
+    """Width of the chunk-aligned local window in chunk slots (1 = own chunk only)."""
+    return int(cfg["win"]) if cfg.get("win") is not None else (1 if cfg["keep_own"] else 0)
+
+
 def query_counts(cfg):
-    """Per query position i: (#candidates, #selected, #own tokens)."""
+    """Per causal query position i: (#candidates, #selected, #local-window tokens).
+    The window is the own chunk's visible tokens and the w - 1 chunks before it;
+    candidates are the complete chunks before the window."""
     import numpy as np
     S, K, Lq, Lkv = cfg["S"], cfg["K"], cfg["Lq"], cfg["Lkv"]
     NC = Lkv // S
+    w = local_chunks(cfg)
     t = Lkv - Lq + np.arange(Lq)
     own = t // S
-    ncand = np.minimum(own, NC)
+    ncand = np.clip(own - max(w - 1, 0), 0, NC)
     nsel = np.minimum(ncand, K)
-    nown = (t - own * S + 1) if cfg["keep_own"] else np.zeros(Lq, dtype=np.int64)
-    return ncand.astype(np.int64), nsel.astype(np.int64), nown.astype(np.int64)
+    if w > 0:
+        nloc = (t - own * S + 1) + S * np.minimum(w - 1, own)
+    else:
+        nloc = np.zeros(Lq, dtype=np.int64)
+    return ncand.astype(np.int64), nsel.astype(np.int64), nloc.astype(np.int64)
 
 
 def forward_flops(cfg, queries=None):
@@ -333,13 +346,14 @@ def run_prefill(hl, cfg, steps, warmup, ev):
     out = torch.empty_like(dev["q"])
     idx = torch.empty((cfg["B"], cfg["Hkv"], cfg["Lq"], cfg["K"]), dtype=torch.int32, device="cuda")
     lse = torch.empty((cfg["B"], cfg["Hq"], cfg["Lq"]), dtype=torch.float32, device="cuda")
-    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]))
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]),
+              local_chunks=local_chunks(cfg))
     o, i, l = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
     ws = None
     p = hl.make_params(batch=cfg["B"], heads_q=cfg["Hq"], heads_kv=cfg["Hkv"], head_dim=cfg["d"],
                        seq_q=cfg["Lq"], seq_kv=cfg["Lkv"], chunk_size=cfg["S"], top_k=cfg["K"],
                        num_landmarks=dev["lmk"].shape[2], causal=True,
-                       keep_own_chunk=cfg["keep_own"])
+                       keep_own_chunk=cfg["keep_own"], local_chunks=local_chunks(cfg))
     need = hl.hils_workspace_size(p, hl.HILS_OP_FORWARD)
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -378,10 +392,12 @@ def run_decode(hl, cfg, steps, warmup, ev, nsets):
     lse = torch.empty((cfg["B"], cfg["Hq"], 1), dtype=torch.float32, device="cuda")
     p = hl.make_params(batch=cfg["B"], heads_q=cfg["Hq"], heads_kv=cfg["Hkv"], head_dim=cfg["d"],
                        seq_q=1, seq_kv=cfg["Lkv"], chunk_size=cfg["S"], top_k=cfg["K"],
-                       num_landmarks=cfg["Lkv"] // cfg["S"], keep_own_chunk=cfg["keep_own"])
+                       num_landmarks=cfg["Lkv"] // cfg["S"], keep_own_chunk=cfg["keep_own"],
+                       local_chunks=local_chunks(cfg))
     ws = torch.empty(max(1, hl.hils_workspace_size(p, hl.HILS_OP_DECODE)), dtype=torch.uint8,
                      device="cuda")
-    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], keep_own_chunk=bool(cfg["keep_own"]))
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], keep_own_chunk=bool(cfg["keep_own"]),
+              local_chunks=local_chunks(cfg))
 
     def step(i):
         s = sets[i % nsets]
@@ -407,7 +423,8 @@ def run_train(hl, cfg, steps, warmup, ev):
     import torch
     from hils_inputs.device import make_device_inputs
     _, dev = make_device_inputs(cfg)
-    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]))
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]),
+              local_chunks=local_chunks(cfg))
 
     def step(_):
         out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
@@ -502,7 +519,8 @@ def cpu_baseline(cfg, seconds):
     host = make_host_inputs(cfg)
     rng = np.random.default_rng(123)
     order = rng.permutation(cfg["Lq"])
-    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]))
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]),
+              local_chunks=local_chunks(cfg))
     done, flops, t_used = 0, 0.0, 0.0
     with threadpool_limits(limits=1):
         while t_used < seconds and done < cfg["Lq"]:
@@ -528,7 +546,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", default=None, help="run one workload: prefill_8k, decode_128k, "
-                                                     "decode_4m, train_8k, landmarks_8k, prefill_32k")
+                                                     "decode_4m, train_8k, landmarks_8k, prefill_32k, "
+                                                     "or prefill_8k, decode_128k, train_8k + _swa512")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain %d MiB device copy (HBM counter calibration)" % COPY_MIB)
     ap.add_argument("--traffic-summary", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
@@ -583,19 +602,26 @@ def main():
                 "roofline": r["roofline"]}
     todo = []
     if not args.no_extra and args.only is None:
-        todo = ["decode_128k", "decode_4m", "train_8k", "landmarks_8k"]
-    elif args.only in ("decode_128k", "decode_4m", "train_8k", "landmarks_8k"):
+        todo = ["decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
+                "decode_128k_swa512", "train_8k_swa512"]
+    elif args.only in ("decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
+                       "decode_128k_swa512", "train_8k_swa512"):
         todo = [args.only]
     for name in todo:
         cfg = dict(config("train_8k"), name=name) if name == "landmarks_8k" else config(name)
-        if name == "landmarks_8k":
+        if name.startswith("prefill"):
+            log("%s: %d warmup + %d timed steps" % (name, args.warmup, args.steps))
+            r = run_prefill(hl, cfg, args.steps, args.warmup, ev)
+            steps = args.steps
+            log("%s: %.3f ms/step, %.1f TFLOP/s" % (name, r["ms_per_step"], r["value"]))
+        elif name == "landmarks_8k":
             steps, warm = max(args.steps * 5, 50), max(args.warmup, 5)
             log("%s: 16 sets, %d warmup + %d timed steps" % (name, warm, steps))
             r = run_landmarks(hl, cfg, steps, warm, ev, 16)
             log("%s: %.1f us/step, %.0f GB/s" % (name, r["ms_per_step"] * 1e3, r["value"]))
         elif name.startswith("decode"):
             steps, warm = max(args.steps * 10, 100), max(args.warmup, 10)
-            nsets = 4 if name == "decode_128k" else 3
+            nsets = 4 if name.startswith("decode_128k") else 3
             log("%s: %d sets, %d warmup + %d timed steps" % (name, nsets, warm, steps))
             r = run_decode(hl, cfg, steps, warm, ev, nsets)
             log("%s: %.1f us/step, %.0f GB/s" % (name, r["ms_per_step"] * 1e3, r["value"]))

@@ -38,6 +38,10 @@ CONFIGS = {
     "prefill_32k": dict(B=1, Hq=32, Hkv=8, d=128, Lq=32768, Lkv=32768, S=64, K=16,
                         causal=1, keep_own=1, dtype="bf16", lmk="chunk_mean", seed=5),
 }
+# the same workloads with a 512-token chunk-aligned local window (8 chunk slots:
+# the own chunk and the 7 before it) next to the top-K retrieval
+for _name in ("prefill_8k", "decode_128k", "train_8k"):
+    CONFIGS[_name + "_swa512"] = dict(CONFIGS[_name], win=8)
 
 
 def config(name, **overrides):

@@ -100,3 +100,33 @@ def test_train_8k_sampled(hl):
     assert_close("dbias", to_np(db)[:, :, c], rdb[:, :, c], "norm", 2e-2)
     # rows past the complete chunks and chunks no query reaches get zero
     assert np.all(to_np(dl)[:, :, L // S - 1] == 0)
+
+
+def test_train_8k_swa512_sampled(hl):
+    """Training shape with a 512-token local window: dq on sampled rows; dk, dv of
+    the last two chunks, which only the queries of the last two windows reach
+    (through their local windows); dlmk, dbias of chunk NC - 9, which only the
+    last window can retrieve (candidates precede the 8-slot window)."""
+    cfg = config("train_8k_swa512")
+    host, dev = make_device_inputs(cfg)
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, local_chunks=8)
+    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
+    dq, dk, dv, dl, db = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out,
+                                          dev["dout"], idx, lse, need_dbias=True, **kw)
+    torch.cuda.synchronize()
+    L, S = cfg["Lq"], cfg["S"]
+    NC = L // S
+    rng = np.random.default_rng(4)
+    tail = set(range((NC - 2) * S, L))
+    qs = np.array(sorted(set(rng.choice((NC - 2) * S, 24, replace=False).tolist()) | tail))
+    gi = idx.cpu().numpy().astype(np.int64)[:, :, qs]
+    rdq, rdk, rdv, rdl, rdb = ref_backward(host["q"], host["k"], host["v"], host["lmk"], None,
+                                           host["dout"], forced_idx=gi, queries=qs, **kw)
+    assert_close("dq rows", to_np(dq)[:, :, qs], rdq[:, :, qs], "norm", 2e-2)
+    kt = slice(L - 2 * S, L)
+    assert_close("dk tail", to_np(dk)[:, :, kt], rdk[:, :, kt], "norm", 2e-2)
+    assert_close("dv tail", to_np(dv)[:, :, kt], rdv[:, :, kt], "norm", 2e-2)
+    c = NC - 9
+    assert_close("dlmk", to_np(dl)[:, :, c], rdl[:, :, c], "norm", 2e-2)
+    assert_close("dbias", to_np(db)[:, :, c], rdb[:, :, c], "norm", 2e-2)
+

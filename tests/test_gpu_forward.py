@@ -170,3 +170,26 @@ def test_prefill_8k_sampled(hl):
     own = np.arange(cfg["Lq"]) // cfg["S"]
     nsel = (idx[0] >= 0).sum(-1)
     np.testing.assert_array_equal(nsel, np.minimum(own, cfg["K"])[None, :].repeat(cfg["Hkv"], 0))
+
+
+def test_prefill_8k_swa512_sampled(hl):
+    """The prefill workload with a 512-token local window (8 chunk slots)."""
+    cfg = config("prefill_8k_swa512")
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev)
+    rng = np.random.default_rng(2)
+    qs = sorted(set(range(0, 70)) | set(range(440, 600)) | set(rng.choice(cfg["Lq"], 80, replace=False).tolist())
+                | set(range(cfg["Lq"] - 10, cfg["Lq"])))
+    check_forward(host, cfg, out, idx, lse, queries=qs)
+    own = np.arange(cfg["Lq"]) // cfg["S"]
+    nsel = (idx[0] >= 0).sum(-1)
+    np.testing.assert_array_equal(nsel, np.minimum(np.maximum(own - 7, 0), cfg["K"])[None, :]
+                                  .repeat(cfg["Hkv"], 0))
+
+
+def test_decode_128k_swa512(hl):
+    cfg = config("decode_128k_swa512")
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev, entry="decode")
+    check_forward(host, cfg, out, idx, lse)
+
