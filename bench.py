@@ -70,11 +70,17 @@ class HipEvents:
         self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
-    def create(self, n):
+    # no system-scope fence at the event record: the default one lengthens the
+    # bracketed interval of a short kernel
+    FLAGS = 0x20000000   # hipEventDisableSystemFence
+
+    def create(self, n, flags=None):
         out = []
+        self.rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         for _ in range(n):
             e = ctypes.c_void_p()
-            assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+            f = self.FLAGS if flags is None else flags
+            assert self.rt.hipEventCreateWithFlags(ctypes.byref(e), f) == 0
             out.append(e.value)
         return out
 
