@@ -17,7 +17,10 @@ them), the training step (forward + backward, TFLOP/s), and landmark formation
 with its backward over the training batch's keys (algorithmic HBM GB/s, 16
 rotating input sets).  The `_swa512` lines repeat prefill_8k, decode_128k and
 train_8k with a 512-token chunk-aligned local window (8 chunk slots) beside the
-top-K retrieval.
+top-K retrieval.  `prefill_8k_corr` repeats prefill_8k with correlated adjacent
+queries (first-order autoregressive along the sequence, rho = 0.98), the regime
+in which the query-block union kernel saves work; its line reports the measured
+share of chunks that adjacent queries have in common.
 
 Every input is resident in HBM before timing.  Per-kernel durations come from
 HIP events the library records around each launch of the dominant kernel on
@@ -345,6 +348,27 @@ def launched(hl, ev, kernel, fn):
     return n > 0
 
 
+def selection_stats(idx, cfg):
+    """From a selection idx [B, Hkv, L, K] (ascending, -1 padded): the mean share of
+    chunks a query has in common with the next query of the same chunk (over
+    queries with K selections), and the mean union size over 64-query windows."""
+    import numpy as np
+    B, Hkv, L, K = idx.shape
+    NC = cfg["Lkv"] // cfg["S"]
+    rows = idx.reshape(-1, K)
+    hot = np.zeros((rows.shape[0], NC + 1), dtype=bool)
+    hot[np.repeat(np.arange(rows.shape[0]), K), np.where(rows >= 0, rows, NC).reshape(-1)] = True
+    hot = hot[:, :NC].reshape(B * Hkv, L, NC)
+    full = (idx >= 0).sum(-1).reshape(B * Hkv, L) == K
+    pos = np.arange(L - 1)
+    same = (pos // cfg["S"]) == ((pos + 1) // cfg["S"])
+    pair = full[:, :-1] & full[:, 1:] & same[None, :]
+    shared = (hot[:, :-1] & hot[:, 1:]).sum(-1) / K
+    union = hot.reshape(B * Hkv, L // 64, 64, NC).any(axis=2).sum(-1)
+    return dict(adjacent_sharing=float(shared[pair].mean()) if pair.any() else None,
+                union_chunks_per_64_queries=float(union.mean()))
+
+
 def run_prefill(hl, cfg, steps, warmup, ev):
     import torch
     from hils_inputs.device import make_device_inputs
@@ -355,6 +379,7 @@ def run_prefill(hl, cfg, steps, warmup, ev):
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]),
               local_chunks=local_chunks(cfg))
     o, i, l = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
+    sel_stats = selection_stats(i.cpu().numpy(), cfg)
     ws = None
     p = hl.make_params(batch=cfg["B"], heads_q=cfg["Hq"], heads_kv=cfg["Hkv"], head_dim=cfg["d"],
                        seq_q=cfg["Lq"], seq_kv=cfg["Lkv"], chunk_size=cfg["S"], top_k=cfg["K"],
@@ -381,6 +406,7 @@ def run_prefill(hl, cfg, steps, warmup, ev):
                              traffic=recorded_traffic(kern, cfg.get("name", "")),
                              per_launch_flops=attn_flops))
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_BF16_TFLOPS
+    res["selection"] = sel_stats
     del dev
     return res
 
@@ -605,13 +631,13 @@ def main():
                            "heads_kv": cfg["Hkv"], "head_dim": cfg["d"], "seq_len": cfg["Lq"],
                            "chunk_size": cfg["S"], "top_k": cfg["K"], "causal": True,
                            "keep_own_chunk": True, "parallelism": "single GPU"},
-                "roofline": r["roofline"]}
+                "roofline": r["roofline"], "selection": r.get("selection")}
     todo = []
     if not args.no_extra and args.only is None:
         todo = ["decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
-                "decode_128k_swa512", "train_8k_swa512"]
+                "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr"]
     elif args.only in ("decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
-                       "decode_128k_swa512", "train_8k_swa512"):
+                       "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr"):
         todo = [args.only]
     for name in todo:
         cfg = dict(config("train_8k"), name=name) if name == "landmarks_8k" else config(name)
@@ -646,6 +672,9 @@ def main():
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                 "data": "synthetic", "config": {"workload": r["workload"]},
                 "roofline": r.get("roofline")}
+        for key in ("selection", "backward_kernels", "forward_kernel", "frac_of_hbm_peak"):
+            if key in r:
+                line[key] = r[key]
     line["extra"] = extra
     if args.calibrate_copy:
         copy_calibration()

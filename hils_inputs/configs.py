@@ -9,6 +9,12 @@ Every workload is defined by a small dict of sizes plus a landmark recipe:
                  whose landmark points along the group's mean query with
                  cosine 0.9 and norm sqrt(d).
 
+Queries are N(0, 1) and independent across positions, or, with ``qcorr`` = rho,
+a first-order autoregressive sequence along the positions of each head
+(q_0 = e_0, q_i = rho q_{i-1} + sqrt(1 - rho^2) e_i, e ~ N(0, 1) from the same
+draws), which keeps each q_i ~ N(0, 1) but makes adjacent queries similar, so
+that they retrieve mostly the same chunks.
+
 No part of the attention method is computed here.
 """
 import math
@@ -42,6 +48,9 @@ CONFIGS = {
 # the own chunk and the 7 before it) next to the top-K retrieval
 for _name in ("prefill_8k", "decode_128k", "train_8k"):
     CONFIGS[_name + "_swa512"] = dict(CONFIGS[_name], win=8)
+# prefill_8k with correlated adjacent queries (rho = 0.98: adjacent queries share
+# about 88% of their selected chunks on this generator)
+CONFIGS["prefill_8k_corr"] = dict(CONFIGS["prefill_8k"], qcorr=0.98)
 
 
 def config(name, **overrides):
@@ -171,7 +180,13 @@ def make_host_inputs(cfg, lazy_kv=None):
     if lazy_kv is None:
         lazy_kv = int(np.prod(kv_shape)) > (1 << 28)
     out = {"cfg": dict(cfg)}
-    out["q"] = _store(cfg, _draw(cfg, "q", (B, Hq, Lq, d)))
+    qraw = _draw(cfg, "q", (B, Hq, Lq, d))
+    if cfg.get("qcorr"):
+        rho = float(cfg["qcorr"])
+        a = np.float32(math.sqrt(1.0 - rho * rho))
+        for i in range(1, Lq):
+            qraw[:, :, i] = np.float32(rho) * qraw[:, :, i - 1] + a * qraw[:, :, i]
+    out["q"] = _store(cfg, qraw)
     if lazy_kv:
         if cfg["lmk"] == "chunk_mean":
             raise ValueError("chunk_mean landmarks need materialised keys")

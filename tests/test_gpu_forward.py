@@ -193,3 +193,22 @@ def test_decode_128k_swa512(hl):
     out, idx, lse = _run(hl, cfg, dev, entry="decode")
     check_forward(host, cfg, out, idx, lse)
 
+
+
+def test_prefill_8k_correlated_queries(hl):
+    """prefill_8k with correlated adjacent queries: parity on sampled queries, and
+    the workload's adjacent-query chunk sharing lies in the pages' 80-93% range."""
+    cfg = config("prefill_8k_corr")
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev)
+    rng = np.random.default_rng(5)
+    qs = sorted(set(range(0, 70)) | set(rng.choice(cfg["Lq"], 120, replace=False).tolist())
+                | set(range(cfg["Lq"] - 10, cfg["Lq"])))
+    check_forward(host, cfg, out, idx, lse, queries=qs)
+    K, S = cfg["K"], cfg["S"]
+    shares = []
+    for g in range(cfg["Hkv"]):
+        for i in range(2048, cfg["Lq"] - 1):
+            if i // S == (i + 1) // S:
+                shares.append(len(set(idx[0, g, i]) & set(idx[0, g, i + 1])) / K)
+    assert 0.80 <= float(np.mean(shares)) <= 0.93, np.mean(shares)
