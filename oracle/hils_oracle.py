@@ -47,6 +47,12 @@ design notes of the repository):
   measured models keep top-K retrieval plus a 512-token window].  Candidates
   are the complete chunks before the window; fusion weights are per head;
 * an empty fusion set gives O = 0 and LSE = -inf;
+* separate retrieval query (query calibration): when a retrieval query q_ret is
+  given, the chunk scores -- and so the selection and the fusion weights --
+  use q_ret in place of q, while the token logits inside each chunk keep q;
+  the score gradients then reach q_ret (and the landmarks through q_ret), not q
+  [HSADR §4 "Architecture": a low-rank query adaptation calibrates the
+  chunk-level surrogate scores; the adaptation itself is model-side];
 * landmark formation (the step before scoring): the chunk's landmark query lq_c
   induces p = softmax_j(scale <lq_c, k_j>) over its S keys; the landmark key is
   sum_j p_j k_j and the bias the entropy -sum_j p_j log p_j.  This is the
@@ -136,24 +142,26 @@ def _chunk_attention(q, k_blk, v_blk, scale):
 # one query of one KV group: forward and (optionally) backward
 # ----------------------------------------------------------------------------
 def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale,
-               forced=None, dout=None, local_chunks=None):
+               forced=None, dout=None, local_chunks=None, qrg=None):
     """Forward (and backward if ``dout``) of query i for the G heads of one KV group.
 
     qg: [G, d] query rows of the group; k, v: [Lkv, d] (indexable) this group's
     cache; lmk: [NCcap, d]; bias: [NCcap] or None; forced: chunk ids to use
     instead of the selection (ascending), or None; local_chunks: width w of the
-    local window in chunk slots (default: 1 if keep_own else 0).
+    local window in chunk slots (default: 1 if keep_own else 0); qrg: [G, d]
+    retrieval queries of the group (default: qg) -- chunk scores use them.
     Returns a dict with idx, out [G, d], lse [G], scores, and for backward dq
     [G, d] and the lists of contributions to dk, dv (per token range), dlmk and
     dbias (per chunk).
     """
     G, d = qg.shape
+    qr = qg if qrg is None else qrg
     w_loc = (1 if keep_own else 0) if local_chunks is None else int(local_chunks)
     cand, window = query_layout(i, Lq, Lkv, S, causal, w_loc)
 
     # retrieval scores of every candidate, per head  [HSADR §3 "Linear surrogate"]
     if len(cand):
-        s_all = scale * (qg @ lmk[cand].T)                  # [G, |C|]
+        s_all = scale * (qr @ lmk[cand].T)                  # [G, |C|]
         if bias is not None:
             s_all = s_all + bias[cand][None, :]
         gbar = s_all.mean(axis=0)                           # group score [HSADR §4 GQA]
@@ -175,7 +183,7 @@ def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale
     lse = np.full(G, -math.inf)
     res = {"idx": idx, "out": out, "lse": lse, "gbar": gbar, "cand": cand}
     if dout is not None:
-        res.update(dq=np.zeros((G, d)), dkv=[], dlmk=[], dbias=[])
+        res.update(dq=np.zeros((G, d)), dqr=np.zeros((G, d)), dkv=[], dlmk=[], dbias=[])
     if not members:
         return res
 
@@ -190,7 +198,7 @@ def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale
                 if c in pos_in_cand:
                     s_c = s_all[h, pos_in_cand[c]]
                 else:                                       # forced chunk outside C_i
-                    s_c = scale * float(q @ lmk[c]) + (0.0 if bias is None else float(bias[c]))
+                    s_c = scale * float(qr[h] @ lmk[c]) + (0.0 if bias is None else float(bias[c]))
             else:
                 s_c = lse_c                                  # exact mass of a window chunk
             parts.append((kind, c, a, b, kb, vb, p, o_c, s_c))
@@ -210,20 +218,25 @@ def hils_query(qg, k, v, lmk, bias, i, *, Lq, Lkv, S, K, causal, keep_own, scale
         g = np.asarray(dout[h], dtype=np.float64)
         D = float(g @ O)
         dq = np.zeros(d)
+        dqr = np.zeros(d)                                    # through the chunk scores
         for wc, (kind, c, a, b, kb, vb, p, o_c, s_c) in zip(w, parts):
             u = vb @ g                                       # <dO, v_j>
             Dc = float(p @ u)                                # <dO, o_c>
             if kind == "ret":
                 dl = wc * p * (u - Dc)                       # through the intra-chunk softmax
                 ds = wc * (Dc - D)                           # through the fusion softmax
-                dq = dq + scale * ds * np.asarray(lmk[c], dtype=np.float64)
-                res["dlmk"].append((c, scale * ds * q))
+                dqr = dqr + scale * ds * np.asarray(lmk[c], dtype=np.float64)
+                res["dlmk"].append((c, scale * ds * qr[h]))
                 res["dbias"].append((c, ds))
             else:
                 dl = wc * p * (u - D)                        # s_c = lse_c adds ds_c * p
             dq = dq + scale * (dl @ kb)
             res["dkv"].append((a, b, scale * np.outer(dl, q), np.outer(wc * p, g)))
-        res["dq"][h] = dq
+        if qrg is None:
+            res["dq"][h] = dq + dqr
+        else:
+            res["dq"][h] = dq
+            res["dqr"][h] = dqr
     return res
 
 
@@ -236,7 +249,7 @@ def _f64(x):
 
 def ref_forward(q, k, v, lmk, bias=None, *, chunk_size, top_k, causal=True,
                 keep_own_chunk=True, scale=None, queries=None, heads_kv=None,
-                batches=None, forced_idx=None, local_chunks=None):
+                batches=None, forced_idx=None, local_chunks=None, q_ret=None):
     """HiLS forward. q [B,Hq,Lq,d]; k, v [B,Hkv,Lkv,d]; lmk [B,Hkv,NCcap,d]; bias [B,Hkv,NCcap].
 
     Returns out [B,Hq,nq,d], idx [B,Hkv,nq,K] (int64, -1 padded), lse [B,Hq,nq]
@@ -244,7 +257,8 @@ def ref_forward(q, k, v, lmk, bias=None, *, chunk_size, top_k, causal=True,
     ([B,Hkv,nq,K], -1 padded) replaces the selection.  k and v may be lazy
     indexable objects; only the rows of the used chunks are read.
     ``local_chunks`` (default 1 if keep_own_chunk else 0) is the width of the
-    chunk-aligned local window in chunk slots.
+    chunk-aligned local window in chunk slots.  ``q_ret`` [B,Hq,Lq,d] (optional)
+    is the retrieval query the chunk scores use.
     """
     B, Hq, Lq, d = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
@@ -267,10 +281,11 @@ def ref_forward(q, k, v, lmk, bias=None, *, chunk_size, top_k, causal=True,
                 if forced_idx is not None:
                     f = np.asarray(forced_idx[b, g, n])
                     forced = f[f >= 0]
+                qrg = None if q_ret is None else _f64(q_ret[b, g * G:(g + 1) * G, i])
                 r = hils_query(_f64(q[b, g * G:(g + 1) * G, i]), kg, vg, lg, bg, int(i),
                                Lq=Lq, Lkv=Lkv, S=S, K=K, causal=bool(causal),
                                keep_own=bool(keep_own_chunk), scale=sc, forced=forced,
-                               local_chunks=local_chunks)
+                               local_chunks=local_chunks, qrg=qrg)
                 idx[b, g, n] = r["idx"]
                 out[b, g * G:(g + 1) * G, n] = r["out"]
                 lse[b, g * G:(g + 1) * G, n] = r["lse"]
@@ -287,12 +302,14 @@ def ref_decode(q, k, v, lmk, bias=None, **kw):
 
 def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
                  keep_own_chunk=True, scale=None, forced_idx=None, queries=None,
-                 local_chunks=None):
+                 local_chunks=None, q_ret=None):
     """Gradients of sum(<dout, out>) for every input, selection held fixed.
 
     Returns dq [B,Hq,Lq,d] (rows outside ``queries`` are zero), dk, dv
     [B,Hkv,Lkv,d], dlmk [B,Hkv,NCcap,d], dbias [B,Hkv,NCcap] -- the last four
     summed over the contributions of the queries in ``queries`` (default all).
+    With ``q_ret`` a sixth array dq_ret [B,Hq,Lq,d] follows (the score
+    gradients), and dq holds the token-attention part only.
     """
     B, Hq, Lq, d = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
@@ -301,6 +318,7 @@ def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
     sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
     qs = np.arange(Lq) if queries is None else np.asarray(queries)
     dq = np.zeros((B, Hq, Lq, d))
+    dqr = np.zeros((B, Hq, Lq, d))
     dk = np.zeros((B, Hkv, Lkv, d))
     dv = np.zeros((B, Hkv, Lkv, d))
     dlmk = np.zeros(lmk.shape)
@@ -315,12 +333,14 @@ def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
                 if forced_idx is not None:
                     f = np.asarray(forced_idx[b, g, n])
                     forced = f[f >= 0]
+                qrg = None if q_ret is None else _f64(q_ret[b, g * G:(g + 1) * G, i])
                 r = hils_query(_f64(q[b, g * G:(g + 1) * G, i]), kg, vg, lg, bg, int(i),
                                Lq=Lq, Lkv=Lkv, S=S, K=K, causal=bool(causal),
                                keep_own=bool(keep_own_chunk), scale=sc, forced=forced,
                                dout=_f64(dout[b, g * G:(g + 1) * G, i]),
-                               local_chunks=local_chunks)
+                               local_chunks=local_chunks, qrg=qrg)
                 dq[b, g * G:(g + 1) * G, i] = r["dq"]
+                dqr[b, g * G:(g + 1) * G, i] = r["dqr"]
                 for a, e, dkp, dvp in r["dkv"]:
                     dk[b, g, a:e] += dkp
                     dv[b, g, a:e] += dvp
@@ -328,6 +348,8 @@ def ref_backward(q, k, v, lmk, bias, dout, *, chunk_size, top_k, causal=True,
                     dlmk[b, g, c] += val
                 for c, val in r["dbias"]:
                     dbias[b, g, c] += val
+    if q_ret is not None:
+        return dq, dk, dv, dlmk, dbias, dqr
     return dq, dk, dv, dlmk, dbias
 
 

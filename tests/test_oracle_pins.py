@@ -18,6 +18,10 @@
   softmax restricted to the retrieved and window tokens; a token-level second
   formulation (window tokens weighted by their own logits); no overlap of
   window and retrieval; decode = last prefill row; finite differences;
+* separate retrieval query q_ret: zero q_ret makes the chunk scores the biases
+  (selection and fusion weights from scipy), exact-mass scores through q_ret
+  give the restricted softmax of q, q_ret = q splits the base gradient of q in
+  two, and finite differences for every gradient including dq_ret;
 * landmark formation: the surrogate score equals the exact chunk LogSumExp (and
   its gradient) at the landmark query, uniform and one-hot limits (bias log S and
   0), the entropy against scipy, and finite differences of its backward.
@@ -504,6 +508,122 @@ def test_window_decode_is_last_prefill_row():
                              keep_own_chunk=True)
     np.testing.assert_array_equal(i3, i4)
     np.testing.assert_array_equal(o3, o4)
+
+
+# --------------------------------------------------------------------------- retrieval query
+def test_qret_zero_scores_are_the_biases():
+    """q_ret = 0: every chunk score is its bias, so the selection is the top-K
+    biases and the fusion weights are a softmax over those biases and the own
+    chunk's exact lse of q; the token attention inside chunks still uses q."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, d, S, L, K = 1, 4, 2, 8, 4, 45, 3
+    q, k, v = _rand(rng, B, Hq, L, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    NC = L // S
+    lmk, bias = _rand(rng, B, Hkv, NC, d), _rand(rng, B, Hkv, NC)
+    out, idx, lse = ref_forward(q, k, v, lmk, bias, chunk_size=S, top_k=K, causal=True,
+                                q_ret=np.zeros_like(q))
+    scale = 1 / math.sqrt(d)
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        for i in range(L):
+            own = i // S
+            best = sorted(sorted(range(own), key=lambda c: (-bias[0, g, c], c))[:K])
+            assert [c for c in idx[0, g, i] if c >= 0] == best
+            parts, scores = [], []
+            for c in best:
+                m = np.zeros((1, L), dtype=bool)
+                m[0, c * S:(c + 1) * S] = True
+                o, _ = _dense_torch(q[:, h:h + 1, i:i + 1], k[:, g:g + 1], v[:, g:g + 1], scale, m)
+                parts.append(o[0, 0, 0])
+                scores.append(bias[0, g, c])
+            m = np.zeros((1, L), dtype=bool)
+            m[0, own * S:i + 1] = True
+            o, lo = _dense_torch(q[:, h:h + 1, i:i + 1], k[:, g:g + 1], v[:, g:g + 1], scale, m)
+            parts.append(o[0, 0, 0])
+            scores.append(lo[0, 0, 0])
+            wts = scipy.special.softmax(scores)
+            np.testing.assert_allclose(out[0, h, i], wts @ np.array(parts), atol=1e-12)
+            np.testing.assert_allclose(lse[0, h, i], scipy.special.logsumexp(scores), atol=1e-12)
+
+
+def test_qret_exact_mass_is_restricted_softmax_of_q():
+    """Scores made equal to the exact chunk mass of q through q_ret (bias_c =
+    lse_c(q) - scale <q_ret, lmk_c>): naive block-sparse attention of q."""
+    rng = np.random.default_rng(32)
+    B, H, d, S, NC, K = 1, 2, 8, 4, 9, 3
+    Lkv = NC * S + 2
+    q, k, v = _rand(rng, B, H, 1, d), _rand(rng, B, H, Lkv, d), _rand(rng, B, H, Lkv, d)
+    qr = _rand(rng, B, H, 1, d)
+    lmk = _rand(rng, B, H, NC, d)
+    scale = 1 / math.sqrt(d)
+    logits = scale * np.einsum("bhd,bhtd->bht", q[:, :, 0], k)
+    mass = scipy.special.logsumexp(logits[:, :, :NC * S].reshape(B, H, NC, S), axis=-1)
+    bias = mass - scale * np.einsum("bhd,bhcd->bhc", qr[:, :, 0], lmk)
+    out, idx, lse = ref_decode(q, k, v, lmk, bias, chunk_size=S, top_k=K, q_ret=qr)
+    own = (Lkv - 1) // S
+    for h in range(H):
+        best = sorted(np.argsort(-mass[0, h, :own], kind="stable")[:K].tolist())
+        assert idx[0, h, 0].tolist() == best
+        mask = np.zeros((1, Lkv), dtype=bool)
+        for c in best:
+            mask[0, c * S:(c + 1) * S] = True
+        mask[0, own * S:Lkv] = True
+        ro, rl = _dense_torch(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], scale, mask)
+        np.testing.assert_allclose(out[0, h, 0], ro[0, 0, 0], atol=1e-12)
+        np.testing.assert_allclose(lse[0, h, 0], rl[0, 0, 0], atol=1e-12)
+
+
+def test_qret_equal_to_q_splits_the_gradient():
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, d, S, L, K = 1, 4, 2, 8, 4, 40, 3
+    q, k, v = _rand(rng, B, Hq, L, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    lmk, bias = _rand(rng, B, Hkv, L // S, d), _rand(rng, B, Hkv, L // S)
+    dout = _rand(rng, B, Hq, L, d)
+    kw = dict(chunk_size=S, top_k=K, causal=True, local_chunks=2)
+    o1, i1, l1 = ref_forward(q, k, v, lmk, bias, **kw)
+    o2, i2, l2 = ref_forward(q, k, v, lmk, bias, q_ret=q.copy(), **kw)
+    np.testing.assert_array_equal(i1, i2)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    g1 = ref_backward(q, k, v, lmk, bias, dout, **kw)
+    g2 = ref_backward(q, k, v, lmk, bias, dout, q_ret=q.copy(), **kw)
+    np.testing.assert_allclose(g1[0], g2[0] + g2[5], atol=1e-12)
+    for a, b in zip(g1[1:], g2[1:5]):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_qret_finite_differences():
+    rng = np.random.default_rng(34)
+    B, Hq, Hkv, d, S, L, K = 1, 4, 2, 6, 4, 28, 2
+    q, k, v = _rand(rng, B, Hq, L, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    qr = _rand(rng, B, Hq, L, d)
+    lmk, bias = _rand(rng, B, Hkv, L // S, d), _rand(rng, B, Hkv, L // S)
+    R = _rand(rng, B, Hq, L, d)
+    kw = dict(chunk_size=S, top_k=K, causal=True, local_chunks=2)
+    dq, dk, dv, dlmk, dbias, dqr = ref_backward(q, k, v, lmk, bias, R, q_ret=qr, **kw)
+    params = [q, k, v, lmk, bias, qr]
+    grads = [dq, dk, dv, dlmk, dbias, dqr]
+
+    def loss():
+        out, idx, _ = ref_forward(q, k, v, lmk, bias, q_ret=qr, **kw)
+        return float(np.sum(out * R)), idx
+    _, idx0 = loss()
+    eps, checked = 1e-6, 0
+    for t, (x, gx) in enumerate(zip(params, grads)):
+        flat = x.reshape(-1)
+        for e in rng.choice(flat.size, size=min(flat.size, 20), replace=False):
+            old = flat[e]
+            flat[e] = old + eps
+            lp, ip = loss()
+            flat[e] = old - eps
+            lm, im = loss()
+            flat[e] = old
+            if not (np.array_equal(ip, idx0) and np.array_equal(im, idx0)):
+                continue
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - gx.reshape(-1)[e]) < 1e-7 * max(1.0, abs(fd)), (t, e, fd, gx.reshape(-1)[e])
+            checked += 1
+    assert checked > 90
 
 
 # --------------------------------------------------------------------------- landmark formation
