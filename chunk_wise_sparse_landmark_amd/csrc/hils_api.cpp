@@ -135,31 +135,36 @@ hils_status launch_status(hipError_t e, const char* what) {
   return HILS_OK;
 }
 
-hils_status forward_like(int op, const hils_params* p, const void* q, const void* k,
-                         const void* v, const void* lmk, const float* lmk_bias, void* out,
-                         int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes, void* stream) {
+hils_status forward_like(int op, const hils_params* p, const void* q, const void* q_ret,
+                         const void* k, const void* v, const void* lmk, const float* lmk_bias,
+                         void* out, int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
   hils_status s = check_params(p, op);
   if (s != HILS_OK) return s;
   if (is_empty(p)) return HILS_OK;
   if (!q || !k || !v || !lmk || !out || !sel_idx)
     return fail(HILS_ERR_INVALID_ARG, "a required pointer (q, k, v, lmk, out, sel_idx) is null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lmk) || !aligned16(out) ||
-      !aligned16(sel_idx) || (lse && !aligned16(lse)) || (lmk_bias && !aligned16(lmk_bias)))
+      !aligned16(sel_idx) || (lse && !aligned16(lse)) || (lmk_bias && !aligned16(lmk_bias)) ||
+      (q_ret && !aligned16(q_ret)))
     return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
   s = check_ws(p, op, ws, ws_bytes);
   if (s != HILS_OK) return s;
   hils::Geometry g = geometry(p, op);
   const int bf16 = p->dtype == HILS_BF16;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const void* qr = q_ret ? q_ret : q;
   hipGetLastError();   // clear a stale error so it is not reported as ours
   if (op == HILS_OP_DECODE && hils::decode_fast_supported(g, bf16))
-    return launch_status(hils::launch_decode_fast(g, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, st),
-                         "decode launch");
+    return launch_status(
+        hils::launch_decode_fast(g, q, qr, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, st),
+        "decode launch");
   if (op == HILS_OP_FORWARD && hils::prefill_fast_supported(g, bf16))
-    return launch_status(hils::launch_prefill_fast(g, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, st),
-                         "prefill launch");
+    return launch_status(
+        hils::launch_prefill_fast(g, q, qr, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, st),
+        "prefill launch");
   return launch_status(
-      hils::launch_generic_forward(g, bf16, q, k, v, lmk, lmk_bias, out, sel_idx, lse, st),
+      hils::launch_generic_forward(g, bf16, q, qr, k, v, lmk, lmk_bias, out, sel_idx, lse, st),
       "forward launch");
 }
 
@@ -207,25 +212,25 @@ size_t hils_workspace_size(const hils_params* p, int32_t op) {
   return ws_bytes_for(p, op);
 }
 
-hils_status hils_forward(const hils_params* p, const void* q, const void* k, const void* v,
-                         const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
-                         float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return forward_like(HILS_OP_FORWARD, p, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, ws_bytes,
-                      stream);
+hils_status hils_forward(const hils_params* p, const void* q, const void* q_ret, const void* k,
+                         const void* v, const void* lmk, const float* lmk_bias, void* out,
+                         int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return forward_like(HILS_OP_FORWARD, p, q, q_ret, k, v, lmk, lmk_bias, out, sel_idx, lse, ws,
+                      ws_bytes, stream);
 }
 
-hils_status hils_decode(const hils_params* p, const void* q, const void* k, const void* v,
-                        const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
-                        float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return forward_like(HILS_OP_DECODE, p, q, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, ws_bytes,
-                      stream);
+hils_status hils_decode(const hils_params* p, const void* q, const void* q_ret, const void* k,
+                        const void* v, const void* lmk, const float* lmk_bias, void* out,
+                        int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return forward_like(HILS_OP_DECODE, p, q, q_ret, k, v, lmk, lmk_bias, out, sel_idx, lse, ws,
+                      ws_bytes, stream);
 }
 
-hils_status hils_backward(const hils_params* p, const void* q, const void* k, const void* v,
-                          const void* lmk, const float* lmk_bias, const void* out,
+hils_status hils_backward(const hils_params* p, const void* q, const void* q_ret, const void* k,
+                          const void* v, const void* lmk, const float* lmk_bias, const void* out,
                           const void* dout, const int32_t* sel_idx, const float* lse, void* dq,
-                          void* dk, void* dv, void* dlmk, float* dlmk_bias, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          void* dq_ret, void* dk, void* dv, void* dlmk, float* dlmk_bias,
+                          void* ws, size_t ws_bytes, void* stream) {
   hils_status s = check_params(p, HILS_OP_BACKWARD);
   if (s != HILS_OK) return s;
   if (is_empty(p)) return HILS_OK;
@@ -234,21 +239,26 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* k, co
   const void* ptrs[] = {q, k, v, lmk, out, dout, sel_idx, lse, dq, dk, dv, dlmk};
   for (const void* x : ptrs)
     if (!aligned16(x)) return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
-  if ((lmk_bias && !aligned16(lmk_bias)) || (dlmk_bias && !aligned16(dlmk_bias)))
+  if ((lmk_bias && !aligned16(lmk_bias)) || (dlmk_bias && !aligned16(dlmk_bias)) ||
+      (q_ret && !aligned16(q_ret)) || (dq_ret && !aligned16(dq_ret)))
     return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
+  if ((q_ret != nullptr) != (dq_ret != nullptr))
+    return fail(HILS_ERR_INVALID_ARG, "q_ret and dq_ret must be given together");
   s = check_ws(p, HILS_OP_BACKWARD, ws, ws_bytes);
   if (s != HILS_OK) return s;
   hils::Geometry g = geometry(p, HILS_OP_BACKWARD);
   const int bf16 = p->dtype == HILS_BF16;
+  const void* qr = q_ret ? q_ret : q;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipGetLastError();
   if (hils::prefill_bwd_fast_supported(g, bf16))
-    return launch_status(hils::launch_prefill_bwd_fast(g, q, k, v, lmk, lmk_bias, out, dout, sel_idx,
-                                                       lse, dq, dk, dv, dlmk, dlmk_bias, ws,
-                                                       reinterpret_cast<hipStream_t>(stream)),
+    return launch_status(hils::launch_prefill_bwd_fast(g, q, qr, k, v, lmk, lmk_bias, out, dout,
+                                                       sel_idx, lse, dq, dq_ret, dk, dv, dlmk,
+                                                       dlmk_bias, ws, st),
                          "backward launch");
-  return launch_status(hils::launch_generic_backward(g, bf16, q, k, v, lmk, lmk_bias, dout, sel_idx,
-                                                     dq, dk, dv, dlmk, dlmk_bias, ws,
-                                                     reinterpret_cast<hipStream_t>(stream)),
+  return launch_status(hils::launch_generic_backward(g, bf16, q, qr, k, v, lmk, lmk_bias, dout,
+                                                     sel_idx, dq, dq_ret, dk, dv, dlmk, dlmk_bias,
+                                                     ws, st),
                        "backward launch");
 }
 

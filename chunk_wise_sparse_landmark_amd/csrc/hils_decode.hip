@@ -199,11 +199,13 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ Kc,
 }
 
 __global__ void __launch_bounds__(kThreads)
-decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-              const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
+decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
+              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+              const uint16_t* __restrict__ lmk,
               const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
               float* __restrict__ parts) {
   __shared__ float qs[kMaxGd][kD];
+  __shared__ float qrs[kMaxGd][kD];   // retrieval queries (chunk scores)
   __shared__ float lg[kMaxGd][kS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
   __shared__ float sc[kMaxGd];
@@ -233,8 +235,10 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     }
     ca[tid] = a; cn[tid] = n; cc[tid] = c;
   }
-  for (int x = tid; x < G * kD; x += kThreads)
+  for (int x = tid; x < G * kD; x += kThreads) {
     qs[x / kD][x % kD] = bf16_to_f32(q[(size_t)(b * g.Hq + kvh * G) * kD + x]);
+    qrs[x / kD][x % kD] = bf16_to_f32(qr[(size_t)(b * g.Hq + kvh * G) * kD + x]);
+  }
   __syncthreads();
 
   const uint16_t* Kb = k + (size_t)bkv * g.Lkv * kD;
@@ -298,8 +302,8 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
       lg[h][lane] = e / z;
       float sv;
       if (c >= 0) {
-        const float ps = qs[h][2 * lane] * __uint_as_float(cur.lm << 16) +
-                         qs[h][2 * lane + 1] * __uint_as_float(cur.lm & 0xffff0000u);
+        const float ps = qrs[h][2 * lane] * __uint_as_float(cur.lm << 16) +
+                         qrs[h][2 * lane + 1] * __uint_as_float(cur.lm & 0xffff0000u);
         sv = g.scale * wave_sum(ps) + cur.bias;
       } else {
         sv = m + __logf(z);   // window chunk: its exact log-sum-exp
@@ -446,20 +450,21 @@ size_t decode_fast_ws(const Geometry& g) {
   return off;
 }
 
-hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, const void* v,
-                              const void* lmk, const float* bias, void* out, int32_t* sel_idx,
-                              float* lse, void* ws, hipStream_t st) {
+hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, const void* k,
+                              const void* v, const void* lmk, const float* bias, void* out,
+                              int32_t* sel_idx, float* lse, void* ws, hipStream_t st) {
   DecodePlan p = plan(g);
   DecodeWs d = carve(g, p, ws);
   const int bkv = g.B * g.Hkv;
   const uint16_t* Q = (const uint16_t*)q;
+  const uint16_t* QR = (const uint16_t*)qr;
   const uint16_t* Lm = (const uint16_t*)lmk;
   dim3 g1(p.nsplit, bkv);
   prof_begin(kDecodeScore, st);
   switch (p.R) {
-    case 1: hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
-    case 2: hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
-    default: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, Q, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
+    case 1: hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
+    case 2: hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
+    default: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
   }
   prof_end(kDecodeScore, st);
   prof_begin(kDecodeMerge, st);
@@ -467,7 +472,7 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, c
                      sel_idx);
   prof_end(kDecodeMerge, st);
   prof_begin(kDecodeAttend, st);
-  hipLaunchKernelGGL(decode_attend, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc, Q,
+  hipLaunchKernelGGL(decode_attend, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc, Q, QR,
                      (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
   prof_end(kDecodeAttend, st);
   hipLaunchKernelGGL(decode_fuse, dim3(g.B * g.Hq), dim3(kThreads), 0, st, g, p.asplit, d.parts,

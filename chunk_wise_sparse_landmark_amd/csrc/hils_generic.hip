@@ -121,11 +121,12 @@ __device__ float retrieval_score(const Geometry& g, const float* qh, const T* lr
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__ k,
-                      const T* __restrict__ v, const T* __restrict__ lmk,
+generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__ qr,
+                      const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ lmk,
                       const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
                       T* __restrict__ out, float* __restrict__ lse_out) {
   __shared__ float qh[kMaxD];
+  __shared__ float qrh[kMaxD];     // the retrieval query of the row (chunk scores)
   __shared__ float p[kMaxS];
   __shared__ float red[4];
   __shared__ int sel[kMaxTopK];
@@ -147,7 +148,10 @@ generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
   for (int hh = 0; hh < g.G; ++hh) {
     const int h = kvh * g.G + hh;
     const size_t row = (size_t)(b * g.Hq + h) * g.Lq + i;
-    if (tid < g.d) qh[tid] = Elem<T>::ld(q + row * g.d + tid);
+    if (tid < g.d) {
+      qh[tid] = Elem<T>::ld(q + row * g.d + tid);
+      qrh[tid] = Elem<T>::ld(qr + row * g.d + tid);
+    }
     __syncthreads();
     float m = -INFINITY, z = 0.f, acc = 0.f;   // online fusion over members
     for (int slot = 0; slot < g.K + g.win; ++slot) {
@@ -158,7 +162,7 @@ generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
         if (c < 0) continue;
         a = c * g.S;
         e = a + g.S;
-        s = retrieval_score<T>(g, qh, Lg + (size_t)c * g.d, bb ? bb[c] : 0.f, red);
+        s = retrieval_score<T>(g, qrh, Lg + (size_t)c * g.d, bb ? bb[c] : 0.f, red);
         float o_d;
         member_attention<T>(g, qh, Kg, Vg, a, e, p, red, o_d);
         const float mn = fmaxf(m, s);
@@ -189,18 +193,20 @@ generic_attend_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__
 //   D = <dO, O>,  u_j = <dO, v_j>,  D_c = <dO, o_c>,
 //   retrieved: dl_j = w_c p_j (u_j - D_c),  ds_c = w_c (D_c - D)
 //   window:    dl_j = w_c p_j (u_j - D)      (its score is its own lse)
-//   dq = scale (sum dl_j k_j + sum_c ds_c lmk_c).
+//   dq = scale (sum dl_j k_j + sum_c ds_c lmk_c), the second sum going to dqr
+//   instead when a separate retrieval query is given (dqr non-null).
 // Per (row, member) it stores (w, lse_c, Dt, ds) with Dt = D_c or D, which the
 // chunk pass needs: dl_j = w p_j (u_j - Dt).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__ k,
-                        const T* __restrict__ v, const T* __restrict__ lmk,
-                        const float* __restrict__ bias, const T* __restrict__ dout,
-                        const int32_t* __restrict__ sel_idx, T* __restrict__ dq,
-                        float4* __restrict__ stats) {
+generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__ qr,
+                        const T* __restrict__ k, const T* __restrict__ v,
+                        const T* __restrict__ lmk, const float* __restrict__ bias,
+                        const T* __restrict__ dout, const int32_t* __restrict__ sel_idx,
+                        T* __restrict__ dq, T* __restrict__ dqr, float4* __restrict__ stats) {
   __shared__ float qh[kMaxD];
+  __shared__ float qrh[kMaxD];
   __shared__ float gh[kMaxD];
   __shared__ float p[kMaxS];
   __shared__ float dl[kMaxS];
@@ -227,6 +233,7 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
     const size_t row = (size_t)(b * g.Hq + h) * g.Lq + i;
     if (tid < g.d) {
       qh[tid] = Elem<T>::ld(q + row * g.d + tid);
+      qrh[tid] = Elem<T>::ld(qr + row * g.d + tid);
       gh[tid] = Elem<T>::ld(dout + row * g.d + tid);
     }
     __syncthreads();
@@ -242,7 +249,7 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
         if (valid) {
           a = c * g.S;
           e = a + g.S;
-          s = retrieval_score<T>(g, qh, Lg + (size_t)c * g.d, bb ? bb[c] : 0.f, red);
+          s = retrieval_score<T>(g, qrh, Lg + (size_t)c * g.d, bb ? bb[c] : 0.f, red);
         }
       } else {
         valid = g.window_member(own, ob, slot - g.K, a, e);
@@ -267,7 +274,7 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
     const float O_d = z > 0.f ? acc / z : 0.f;
     const float D = block_sum4(tid < g.d ? gh[tid] * O_d : 0.f, red);
     // pass 2: gradients
-    float dq_d = 0.f;
+    float dq_d = 0.f, dqr_d = 0.f;
     for (int slot = 0; slot < nslot; ++slot) {
       float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
       const float s = ms[slot];
@@ -300,14 +307,21 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
           float sacc = 0.f;
           for (int j = 0; j < n; ++j) sacc += dl[j] * Elem<T>::ld(Kg + (size_t)(a + j) * g.d + tid);
           dq_d += g.scale * sacc;
-          if (slot < g.K) dq_d += g.scale * wgt * (Dt - D) * Elem<T>::ld(Lg + (size_t)c * g.d + tid);
+          if (slot < g.K) dqr_d += g.scale * wgt * (Dt - D) * Elem<T>::ld(Lg + (size_t)c * g.d + tid);
         }
         __syncthreads();
         st = make_float4(wgt, lc, Dt, slot < g.K ? wgt * (Dt - D) : 0.f);
       }
       if (tid == 0) stats[row * nslot + slot] = st;
     }
-    if (tid < g.d) Elem<T>::st(dq + row * g.d + tid, dq_d);
+    if (tid < g.d) {
+      if (dqr) {
+        Elem<T>::st(dq + row * g.d + tid, dq_d);
+        Elem<T>::st(dqr + row * g.d + tid, dqr_d);
+      } else {
+        Elem<T>::st(dq + row * g.d + tid, dq_d + dqr_d);
+      }
+    }
     __syncthreads();
   }
 }
@@ -317,13 +331,14 @@ generic_bwd_rows_kernel(Geometry g, const T* __restrict__ q, const T* __restrict
 // owns keys [cS, cS+S) and landmark c: it walks the queries in order, and for
 // every (query, head) that selected c, or whose local window holds c, adds
 //   dk_j += scale dl_j q,  dv_j += w p_j dO,   and for a selection
-//   dlmk_c += scale ds q,  dbias_c += ds.
+//   dlmk_c += scale ds q_r,  dbias_c += ds  (q_r: the retrieval query).
 // Deterministic: one owner per output row, fixed order.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__ k,
-                          const T* __restrict__ v, const T* __restrict__ dout,
+generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restrict__ qr,
+                          const T* __restrict__ k, const T* __restrict__ v,
+                          const T* __restrict__ dout,
                           const int32_t* __restrict__ sel_idx, const float4* __restrict__ stats,
                           T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dlmk,
                           float* __restrict__ dbias) {
@@ -335,6 +350,7 @@ generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restri
   __shared__ float pw[kMaxS];
   __shared__ float dl[kMaxS];
   __shared__ float dlm[kMaxD];
+  __shared__ float qrh[kMaxD];
   __shared__ int hit;
   const int c = blockIdx.x;
   const int bkv = blockIdx.y;
@@ -379,6 +395,7 @@ generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restri
         const float4 st = stats[row * nslot + slot];   // w, lse_c, Dt, ds
         if (tid < g.d) {
           qh[tid] = Elem<T>::ld(q + row * g.d + tid);
+          qrh[tid] = Elem<T>::ld(qr + row * g.d + tid);
           gh[tid] = Elem<T>::ld(dout + row * g.d + tid);
         }
         __syncthreads();
@@ -402,7 +419,7 @@ generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restri
           dvacc[(off + j) * g.d + e] += pw[j] * gh[e];
         }
         if (slot < g.K) {
-          if (tid < g.d) dlm[tid] += g.scale * st.w * qh[tid];
+          if (tid < g.d) dlm[tid] += g.scale * st.w * qrh[tid];
           dbias_acc += st.w;
         }
         __syncthreads();
@@ -424,26 +441,27 @@ generic_bwd_chunks_kernel(Geometry g, const T* __restrict__ q, const T* __restri
 // launchers
 // ---------------------------------------------------------------------------
 template <typename T>
-hipError_t launch_generic_forward_t(const Geometry& g, const void* q, const void* k, const void* v,
-                                    const void* lmk, const float* bias, void* out, int32_t* sel_idx,
-                                    float* lse, hipStream_t st) {
+hipError_t launch_generic_forward_t(const Geometry& g, const void* q, const void* qr, const void* k,
+                                    const void* v, const void* lmk, const float* bias, void* out,
+                                    int32_t* sel_idx, float* lse, hipStream_t st) {
   dim3 grid(g.Lq, g.B * g.Hkv);
   prof_begin(kGenericSelect, st);
-  hipLaunchKernelGGL(generic_select_kernel<T>, grid, dim3(kThreads), 0, st, g, (const T*)q,
+  hipLaunchKernelGGL(generic_select_kernel<T>, grid, dim3(kThreads), 0, st, g, (const T*)qr,
                      (const T*)lmk, bias, sel_idx);
   prof_end(kGenericSelect, st);
   prof_begin(kGenericAttend, st);
   hipLaunchKernelGGL(generic_attend_kernel<T>, grid, dim3(kThreads), 0, st, g, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)lmk, bias, sel_idx, (T*)out, lse);
+                     (const T*)qr, (const T*)k, (const T*)v, (const T*)lmk, bias, sel_idx,
+                     (T*)out, lse);
   prof_end(kGenericAttend, st);
   return hipGetLastError();
 }
 
-hipError_t launch_generic_forward(const Geometry& g, int bf16, const void* q, const void* k,
-                                  const void* v, const void* lmk, const float* bias, void* out,
-                                  int32_t* sel_idx, float* lse, hipStream_t st) {
-  return bf16 ? launch_generic_forward_t<uint16_t>(g, q, k, v, lmk, bias, out, sel_idx, lse, st)
-              : launch_generic_forward_t<float>(g, q, k, v, lmk, bias, out, sel_idx, lse, st);
+hipError_t launch_generic_forward(const Geometry& g, int bf16, const void* q, const void* qr,
+                                  const void* k, const void* v, const void* lmk, const float* bias,
+                                  void* out, int32_t* sel_idx, float* lse, hipStream_t st) {
+  return bf16 ? launch_generic_forward_t<uint16_t>(g, q, qr, k, v, lmk, bias, out, sel_idx, lse, st)
+              : launch_generic_forward_t<float>(g, q, qr, k, v, lmk, bias, out, sel_idx, lse, st);
 }
 
 size_t generic_backward_ws(const Geometry& g) {
@@ -451,15 +469,16 @@ size_t generic_backward_ws(const Geometry& g) {
 }
 
 template <typename T>
-hipError_t launch_generic_backward_t(const Geometry& g, const void* q, const void* k, const void* v,
-                                     const void* lmk, const float* bias, const void* dout,
-                                     const int32_t* sel_idx, void* dq, void* dk, void* dv,
-                                     void* dlmk, float* dbias, void* ws, hipStream_t st) {
+hipError_t launch_generic_backward_t(const Geometry& g, const void* q, const void* qr,
+                                     const void* k, const void* v, const void* lmk,
+                                     const float* bias, const void* dout, const int32_t* sel_idx,
+                                     void* dq, void* dqr, void* dk, void* dv, void* dlmk,
+                                     float* dbias, void* ws, hipStream_t st) {
   float4* stats = (float4*)ws;
   prof_begin(kGenericBwdRows, st);
   hipLaunchKernelGGL(generic_bwd_rows_kernel<T>, dim3(g.Lq, g.B * g.Hkv), dim3(kThreads), 0, st, g,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)lmk, bias, (const T*)dout,
-                     sel_idx, (T*)dq, stats);
+                     (const T*)q, (const T*)qr, (const T*)k, (const T*)v, (const T*)lmk, bias,
+                     (const T*)dout, sel_idx, (T*)dq, (T*)dqr, stats);
   prof_end(kGenericBwdRows, st);
   const int nck = (g.Lkv + g.S - 1) / g.S;
   const int gx = nck > g.NCcap ? nck : g.NCcap;
@@ -469,21 +488,22 @@ hipError_t launch_generic_backward_t(const Geometry& g, const void* q, const voi
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     prof_begin(kGenericBwdChunks, st);
     hipLaunchKernelGGL(generic_bwd_chunks_kernel<T>, dim3(gx, g.B * g.Hkv), dim3(kThreads), sm, st,
-                       g, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, sel_idx, stats,
-                       (T*)dk, (T*)dv, (T*)dlmk, dbias);
+                       g, (const T*)q, (const T*)qr, (const T*)k, (const T*)v, (const T*)dout,
+                       sel_idx, stats, (T*)dk, (T*)dv, (T*)dlmk, dbias);
     prof_end(kGenericBwdChunks, st);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_generic_backward(const Geometry& g, int bf16, const void* q, const void* k,
-                                   const void* v, const void* lmk, const float* bias,
-                                   const void* dout, const int32_t* sel_idx, void* dq, void* dk,
-                                   void* dv, void* dlmk, float* dbias, void* ws, hipStream_t st) {
-  return bf16 ? launch_generic_backward_t<uint16_t>(g, q, k, v, lmk, bias, dout, sel_idx, dq, dk,
-                                                    dv, dlmk, dbias, ws, st)
-              : launch_generic_backward_t<float>(g, q, k, v, lmk, bias, dout, sel_idx, dq, dk, dv,
-                                                 dlmk, dbias, ws, st);
+hipError_t launch_generic_backward(const Geometry& g, int bf16, const void* q, const void* qr,
+                                   const void* k, const void* v, const void* lmk, const float* bias,
+                                   const void* dout, const int32_t* sel_idx, void* dq, void* dqr,
+                                   void* dk, void* dv, void* dlmk, float* dbias, void* ws,
+                                   hipStream_t st) {
+  return bf16 ? launch_generic_backward_t<uint16_t>(g, q, qr, k, v, lmk, bias, dout, sel_idx, dq,
+                                                    dqr, dk, dv, dlmk, dbias, ws, st)
+              : launch_generic_backward_t<float>(g, q, qr, k, v, lmk, bias, dout, sel_idx, dq, dqr,
+                                                 dk, dv, dlmk, dbias, ws, st);
 }
 
 }  // namespace hils

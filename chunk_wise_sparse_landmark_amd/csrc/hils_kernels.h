@@ -9,37 +9,40 @@
 namespace hils {
 
 // shape-generic path (fp32 or bf16)
-hipError_t launch_generic_forward(const Geometry& g, int bf16, const void* q, const void* k,
-                                  const void* v, const void* lmk, const float* bias, void* out,
-                                  int32_t* sel_idx, float* lse, hipStream_t st);
+// qr: the retrieval query the chunk scores use (q itself when none is given);
+// dqr: where the score gradients go (null: added into dq)
+hipError_t launch_generic_forward(const Geometry& g, int bf16, const void* q, const void* qr,
+                                  const void* k, const void* v, const void* lmk, const float* bias,
+                                  void* out, int32_t* sel_idx, float* lse, hipStream_t st);
 size_t generic_backward_ws(const Geometry& g);
-hipError_t launch_generic_backward(const Geometry& g, int bf16, const void* q, const void* k,
-                                   const void* v, const void* lmk, const float* bias,
-                                   const void* dout, const int32_t* sel_idx, void* dq, void* dk,
-                                   void* dv, void* dlmk, float* dbias, void* ws, hipStream_t st);
+hipError_t launch_generic_backward(const Geometry& g, int bf16, const void* q, const void* qr,
+                                   const void* k, const void* v, const void* lmk, const float* bias,
+                                   const void* dout, const int32_t* sel_idx, void* dq, void* dqr,
+                                   void* dk, void* dv, void* dlmk, float* dbias, void* ws,
+                                   hipStream_t st);
 
 // split decode path (bf16, d = 128, S = 64)
 bool decode_fast_supported(const Geometry& g, int bf16);
 size_t decode_fast_ws(const Geometry& g);
-hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* k, const void* v,
-                              const void* lmk, const float* bias, void* out, int32_t* sel_idx,
-                              float* lse, void* ws, hipStream_t st);
+hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, const void* k,
+                              const void* v, const void* lmk, const float* bias, void* out,
+                              int32_t* sel_idx, float* lse, void* ws, hipStream_t st);
 
 // MFMA prefill path (bf16, d = 128, S = 64, causal, seq_q == seq_kv)
 bool prefill_fast_supported(const Geometry& g, int bf16);
 size_t prefill_fast_ws(const Geometry& g);
-hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, const void* v,
-                               const void* lmk, const float* bias, void* out, int32_t* sel_idx,
-                               float* lse, void* ws, hipStream_t st);
+hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* qr, const void* k,
+                               const void* v, const void* lmk, const float* bias, void* out,
+                               int32_t* sel_idx, float* lse, void* ws, hipStream_t st);
 
 // MFMA prefill backward (same shapes as the MFMA forward)
 bool prefill_bwd_fast_supported(const Geometry& g, int bf16);
 size_t prefill_bwd_fast_ws(const Geometry& g);
-hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void* k, const void* v,
-                                   const void* lmk, const float* bias, const void* out,
-                                   const void* dout, const int32_t* sel_idx, const float* lse,
-                                   void* dq, void* dk, void* dv, void* dlmk, float* dbias,
-                                   void* ws, hipStream_t st);
+hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void* qr, const void* k,
+                                   const void* v, const void* lmk, const float* bias,
+                                   const void* out, const void* dout, const int32_t* sel_idx,
+                                   const float* lse, void* dq, void* dqr, void* dk, void* dv,
+                                   void* dlmk, float* dbias, void* ws, hipStream_t st);
 
 // landmark formation (weighted key sum + entropy bias per chunk) and its backward
 bool landmarks_supported(const Geometry& g);

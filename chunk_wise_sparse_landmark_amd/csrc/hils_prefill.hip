@@ -390,7 +390,8 @@ __device__ __forceinline__ void window_stats_step(const uint4* __restrict__ kvb,
 }
 
 __global__ void __launch_bounds__(kAttThreads)
-prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kvf,
+prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
+               const uint16_t* __restrict__ kvf,
                const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
                const int32_t* __restrict__ sel_idx, uint16_t* __restrict__ out,
                float* __restrict__ lse_out) {
@@ -463,7 +464,18 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const uint16_t* first_src = nwin > 0 ? csrc(own) : (nunion > 0 ? csrc(sm.ulist[0]) : nullptr);
   if (first_src) stage_async(first_src, sm.kv[0]);
 
-  // ---- retrieval scores of (row, selected chunk) by MFMA: rows x union columns
+  // ---- retrieval scores of (row, selected chunk) by MFMA: rows x union columns,
+  //      from the retrieval query's fragments (the query itself unless a
+  //      separate retrieval query is given)
+  bf16x8 rf[kBlocksPerWave][4];
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j) {
+    const int blk = w * kBlocksPerWave + j;
+    const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
+    const uint16_t* qrr = qr + ((size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + qi) * kD + g4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) rf[j][ks] = ld8(qrr + ks * 32);
+  }
   for (int nt = 0; nt * 16 < nunion; ++nt) {
     const int u = nt * 16 + r16;
     const int c = sm.ulist[u < nunion ? u : 0];
@@ -475,7 +487,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int j = 0; j < kBlocksPerWave; ++j) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma(qf[j][ks], bl[ks], acc);
+      for (int ks = 0; ks < 4; ++ks) acc = mfma(rf[j][ks], bl[ks], acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = g4 * 4 + i;                 // block row: query rr/4, head rr%4
@@ -621,25 +633,26 @@ size_t prefill_fast_ws(const Geometry& g) {
   return (size_t)g.B * g.Hkv * g.NC * kChunkElems * sizeof(uint16_t);
 }
 
-hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* k, const void* v,
-                               const void* lmk, const float* bias, void* out, int32_t* sel_idx,
-                               float* lse, void* ws, hipStream_t st) {
+hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* qr, const void* k,
+                               const void* v, const void* lmk, const float* bias, void* out,
+                               int32_t* sel_idx, float* lse, void* ws, hipStream_t st) {
   const uint16_t* Q = (const uint16_t*)q;
+  const uint16_t* QR = (const uint16_t*)qr;
   const uint16_t* Kp = (const uint16_t*)k;
   const uint16_t* Vp = (const uint16_t*)v;
   const uint16_t* Lm = (const uint16_t*)lmk;
   uint16_t* kvf = (uint16_t*)ws;
   prof_begin(kPrefillSelect, st);
-  if (g.NC <= 64) launch_select<1>(g, Q, Kp, Vp, Lm, bias, sel_idx, kvf, st);
-  else if (g.NC <= 128) launch_select<2>(g, Q, Kp, Vp, Lm, bias, sel_idx, kvf, st);
-  else launch_select<4>(g, Q, Kp, Vp, Lm, bias, sel_idx, kvf, st);
+  if (g.NC <= 64) launch_select<1>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
+  else if (g.NC <= 128) launch_select<2>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
+  else launch_select<4>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
   prof_end(kPrefillSelect, st);
   // dynamic LDS above 64 KB must be enabled for the kernel (per device; cheap)
   hipFuncSetAttribute((const void*)prefill_attend, hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)sizeof(AttendSmem));
   prof_begin(kPrefillAttend, st);
   hipLaunchKernelGGL(prefill_attend, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kAttThreads),
-                     sizeof(AttendSmem), st, g, Q, kvf, Lm, bias, sel_idx, (uint16_t*)out, lse);
+                     sizeof(AttendSmem), st, g, Q, QR, kvf, Lm, bias, sel_idx, (uint16_t*)out, lse);
   prof_end(kPrefillAttend, st);
   return hipGetLastError();
 }

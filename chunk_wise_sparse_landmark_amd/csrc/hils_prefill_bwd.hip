@@ -403,10 +403,11 @@ __device__ __forceinline__ void rows_step(
 }
 
 __global__ void __launch_bounds__(kRowThreads)
-prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-                 const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
-                 const int32_t* __restrict__ sel_idx, const float* __restrict__ lse,
-                 BwdWs ws, uint16_t* __restrict__ dq_out) {
+prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
+                 const uint16_t* __restrict__ dout, const uint16_t* __restrict__ lmk,
+                 const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
+                 const float* __restrict__ lse, BwdWs ws, uint16_t* __restrict__ dq_out,
+                 uint16_t* __restrict__ dqr_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
   const int nbkv = g.B * g.Hkv;
@@ -483,7 +484,17 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
   };
   if (nseq > 0) stage48(seq_src(0), sm.kv[0]);
 
-  // ---- fusion weights of (row, selected chunk): exp(scale q.lmk + bias - LSE)
+  // ---- fusion weights of (row, selected chunk): exp(scale q_r.lmk + bias - LSE),
+  //      q_r the retrieval query (the query itself unless a separate one is given)
+  bf16x8 rf[kRowBlocks][4];
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) {
+    const int blk = w * kRowBlocks + j;
+    const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
+    const size_t row = ((size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qi) * kD + g4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) rf[j][ks] = ld8(qr + row + ks * 32);
+  }
   for (int nt = 0; nt * 16 < nunion; ++nt) {
     const int uu = nt * 16 + r16;
     const int c = sm.ulist[uu < nunion ? uu : 0];
@@ -495,7 +506,7 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     for (int j = 0; j < kRowBlocks; ++j) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma(qf[j][ks], bl[ks], acc);
+      for (int ks = 0; ks < 4; ++ks) acc = mfma(rf[j][ks], bl[ks], acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = g4 * 4 + i;
@@ -540,11 +551,15 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     __syncthreads();
   }
 
-  // ---- dq += sum_c ds_c lmk_c, then scale; lane holds dQ[row 4*g4 + i][16*db + r16],
-  //      row 4*g4 + i = (query 4*blk + g4, head i)
+  // ---- the score gradients sum_c ds_c lmk_c: into dq, or into dq_r when a
+  //      separate retrieval query is given; then scale.  Lane holds
+  //      dQ[row 4*g4 + i][16*db + r16], row 4*g4 + i = (query 4*blk + g4, head i)
 #pragma unroll
   for (int j = 0; j < kRowBlocks; ++j) {
     const int qi = (w * kRowBlocks + j) * 4 + g4;
+    f32x4 dr[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) dr[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < K; ++s) {
       const int c = sm.sel[qi * K + s];
       if (c < 0) continue;
@@ -555,14 +570,23 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
       for (int i = 0; i < 4; ++i) {
         const float ds = sm.wts[(qi * K + s) * kG + i];
 #pragma unroll
-        for (int db = 0; db < 8; ++db) dq[j][db][i] = __builtin_fmaf(ds, lv[db], dq[j][db][i]);
+        for (int db = 0; db < 8; ++db) dr[db][i] = __builtin_fmaf(ds, lv[db], dr[db][i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint16_t* orow = dq_out + ((size_t)(b * g.Hq + kvh * kG + i) * L + i0 + qi) * kD + r16;
+      const size_t ro = ((size_t)(b * g.Hq + kvh * kG + i) * L + i0 + qi) * kD + r16;
+      if (dqr_out) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) orow[16 * db] = f32_to_bf16(scale * dq[j][db][i]);
+        for (int db = 0; db < 8; ++db) {
+          dq_out[ro + 16 * db] = f32_to_bf16(scale * dq[j][db][i]);
+          dqr_out[ro + 16 * db] = f32_to_bf16(scale * dr[db][i]);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          dq_out[ro + 16 * db] = f32_to_bf16(scale * (dq[j][db][i] + dr[db][i]));
+      }
     }
   }
 }
@@ -932,6 +956,38 @@ prefill_bwd_reduce(Geometry g, BwdWs ws, uint16_t* __restrict__ dk_out,
   }
 }
 
+// ---- landmark gradients when a separate retrieval query is given: dlmk_c =
+//      scale sum ds_c q_r over the rows that retrieved chunk c (windows in order,
+//      queries in order, heads in order), overwriting the chunk pass's values,
+//      which used the query itself.  One workgroup per (b, kv head, chunk),
+//      thread x = dimension x.
+__global__ void __launch_bounds__(kD)
+prefill_bwd_dlmk_qret(Geometry g, const uint16_t* __restrict__ qr, BwdWs ws,
+                      uint16_t* __restrict__ dlmk_out) {
+  const int nbkv = g.B * g.Hkv;
+  const int bkv = blockIdx.x % nbkv, c = blockIdx.x / nbkv;
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int x = threadIdx.x;
+  const int L = g.Lq, NW = L / kWin;
+  const size_t nslot = (size_t)(g.K + g.win);
+  float acc = 0.f;
+  for (int wdw = c + max(g.win, 1); wdw < NW; ++wdw) {
+    uint64_t m = ws.qm[((size_t)bkv * NW + wdw) * g.NC + c];
+    while (m) {
+      const int bit = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      const int qq = wdw * kWin + bit;
+      const int slot = ws.slot[((size_t)bkv * L + qq) * g.NC + c];
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
+        const size_t row = (size_t)(b * g.Hq + kvh * kG + h) * L + qq;
+        acc = __builtin_fmaf(ws.stats[row * nslot + slot].w, bf16_to_f32(qr[row * kD + x]), acc);
+      }
+    }
+  }
+  dlmk_out[((size_t)bkv * g.NCcap + c) * kD + x] = f32_to_bf16(g.scale * acc);
+}
+
 }  // namespace
 
 bool prefill_bwd_fast_supported(const Geometry& g, int bf16) {
@@ -946,11 +1002,11 @@ size_t prefill_bwd_fast_ws(const Geometry& g) {
   return total;
 }
 
-hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void* k, const void* v,
-                                   const void* lmk, const float* bias, const void* out,
-                                   const void* dout, const int32_t* sel_idx, const float* lse,
-                                   void* dq, void* dk, void* dv, void* dlmk, float* dbias,
-                                   void* wsp, hipStream_t st) {
+hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void* qr, const void* k,
+                                   const void* v, const void* lmk, const float* bias,
+                                   const void* out, const void* dout, const int32_t* sel_idx,
+                                   const float* lse, void* dq, void* dqr, void* dk, void* dv,
+                                   void* dlmk, float* dbias, void* wsp, hipStream_t st) {
   BwdWs ws = carve(g, wsp, nullptr);
   const int nbkv = g.B * g.Hkv, NW = g.Lq / kWin;
   const uint16_t* Q = (const uint16_t*)q;
@@ -962,7 +1018,8 @@ hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void*
   if (e != hipSuccess) return e;
   prof_begin(kPrefillBwdRows, st);
   hipLaunchKernelGGL(prefill_bwd_rows, dim3(nbkv * NW), dim3(kRowThreads), sizeof(RowsSmem), st, g,
-                     Q, DO, (const uint16_t*)lmk, bias, sel_idx, lse, ws, (uint16_t*)dq);
+                     Q, (const uint16_t*)qr, DO, (const uint16_t*)lmk, bias, sel_idx, lse, ws,
+                     (uint16_t*)dq, (uint16_t*)dqr);
   prof_end(kPrefillBwdRows, st);
   hipLaunchKernelGGL(prefill_bwd_plan, dim3(nbkv), dim3(kChunkThreads), 0, st, g, ws);
   prof_begin(kPrefillBwdChunks, st);
@@ -972,6 +1029,9 @@ hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void*
   prof_end(kPrefillBwdChunks, st);
   hipLaunchKernelGGL(prefill_bwd_reduce, dim3(nbkv * g.NCcap), dim3(kChunkThreads), 0, st, g, ws,
                      (uint16_t*)dk, (uint16_t*)dv, (uint16_t*)dlmk, dbias);
+  if (dqr)
+    hipLaunchKernelGGL(prefill_bwd_dlmk_qret, dim3(nbkv * g.NC), dim3(kD), 0, st, g,
+                       (const uint16_t*)qr, ws, (uint16_t*)dlmk);
   return hipGetLastError();
 }
 

@@ -63,11 +63,11 @@ def load_library(path=None):
     P = ctypes.POINTER(HilsParams)
     lib.hils_workspace_size.argtypes = [P, i32]
     lib.hils_workspace_size.restype = sz
-    lib.hils_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hils_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hils_forward.restype = ctypes.c_int
-    lib.hils_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hils_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hils_decode.restype = ctypes.c_int
-    lib.hils_backward.argtypes = [P] + [vp] * 14 + [vp, sz, vp]
+    lib.hils_backward.argtypes = [P] + [vp] * 16 + [vp, sz, vp]
     lib.hils_backward.restype = ctypes.c_int
     lib.hils_landmarks.argtypes = [P, vp, vp, vp, vp, vp]
     lib.hils_landmarks.restype = ctypes.c_int
@@ -146,9 +146,16 @@ def _workspace(params, op, device, ws):
     return ws, need if ws is None else ws.numel()
 
 
+def _check_qret(q, q_ret):
+    if q_ret is not None and (q_ret.shape != q.shape or q_ret.dtype != q.dtype
+                              or not q_ret.is_contiguous()):
+        raise ValueError("q_ret must be contiguous with q's shape and dtype")
+
+
 def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_chunk, scale,
-         out, sel_idx, lse, ws, stream, local_chunks):
+         out, sel_idx, lse, ws, stream, local_chunks, q_ret):
     p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale, local_chunks)
+    _check_qret(q, q_ret)
     B, Hq, Lq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
@@ -160,7 +167,7 @@ def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
     ws, nbytes = _workspace(p, op, dev, ws)
     lib = load_library()
-    st = getattr(lib, entry)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lmk),
+    st = getattr(lib, entry)(ctypes.byref(p), _ptr(q), _ptr(q_ret), _ptr(k), _ptr(v), _ptr(lmk),
                              _ptr(lmk_bias), _ptr(out), _ptr(sel_idx), _ptr(lse), _ptr(ws),
                              nbytes, _stream(stream))
     _check(st)
@@ -169,38 +176,45 @@ def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_
 
 def hils_forward(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, causal=True,
                  keep_own_chunk=True, scale=0.0, out=None, sel_idx=None, lse=None, ws=None,
-                 stream=None, local_chunks=None):
+                 stream=None, local_chunks=None, q_ret=None):
     """HiLS forward: returns (out [B,Hq,Lq,d], sel_idx int32 [B,Hkv,Lq,K], lse fp32 [B,Hq,Lq]).
 
     ``local_chunks`` (default: 1 with keep_own_chunk, else 0) is the width of the
-    chunk-aligned local window in chunk slots."""
+    chunk-aligned local window in chunk slots; ``q_ret`` (shape of q) is an
+    optional separate retrieval query for the chunk scores."""
     return _fwd("hils_forward", HILS_OP_FORWARD, q, k, v, lmk, lmk_bias, chunk_size, top_k,
-                causal, keep_own_chunk, scale, out, sel_idx, lse, ws, stream, local_chunks)
+                causal, keep_own_chunk, scale, out, sel_idx, lse, ws, stream, local_chunks, q_ret)
 
 
 def hils_decode(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, keep_own_chunk=True,
                 scale=0.0, out=None, sel_idx=None, lse=None, ws=None, stream=None,
-                local_chunks=None):
+                local_chunks=None, q_ret=None):
     """Single-token decode over the cache k, v (q: [B,Hq,1,d], position seq_kv-1)."""
     return _fwd("hils_decode", HILS_OP_DECODE, q, k, v, lmk, lmk_bias, chunk_size, top_k,
-                True, keep_own_chunk, scale, out, sel_idx, lse, ws, stream, local_chunks)
+                True, keep_own_chunk, scale, out, sel_idx, lse, ws, stream, local_chunks, q_ret)
 
 
 def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size, top_k,
                   causal=True, keep_own_chunk=True, scale=0.0, need_dbias=None, ws=None,
-                  stream=None, local_chunks=None):
-    """Gradients (dq, dk, dv, dlmk, dbias-or-None) of <dout, out> with the selection fixed."""
+                  stream=None, local_chunks=None, q_ret=None):
+    """Gradients (dq, dk, dv, dlmk, dbias-or-None) of <dout, out> with the selection fixed;
+    with ``q_ret`` a sixth tensor dq_ret follows and dq is the token-attention part."""
     p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale, local_chunks)
+    _check_qret(q, q_ret)
     dq, dk, dv, dlmk = (torch.empty_like(t) for t in (q, k, v, lmk))
+    dqr = torch.empty_like(q) if q_ret is not None else None
     if need_dbias is None:
         need_dbias = lmk_bias is not None
     dbias = torch.empty(lmk.shape[:3], dtype=torch.float32, device=q.device) if need_dbias else None
     ws, nbytes = _workspace(p, HILS_OP_BACKWARD, q.device, ws)
     lib = load_library()
-    st = lib.hils_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lmk), _ptr(lmk_bias),
-                           _ptr(out), _ptr(dout), _ptr(sel_idx), _ptr(lse), _ptr(dq), _ptr(dk),
-                           _ptr(dv), _ptr(dlmk), _ptr(dbias), _ptr(ws), nbytes, _stream(stream))
+    st = lib.hils_backward(ctypes.byref(p), _ptr(q), _ptr(q_ret), _ptr(k), _ptr(v), _ptr(lmk),
+                           _ptr(lmk_bias), _ptr(out), _ptr(dout), _ptr(sel_idx), _ptr(lse),
+                           _ptr(dq), _ptr(dqr), _ptr(dk), _ptr(dv), _ptr(dlmk), _ptr(dbias),
+                           _ptr(ws), nbytes, _stream(stream))
     _check(st)
+    if q_ret is not None:
+        return dq, dk, dv, dlmk, dbias, dqr
     return dq, dk, dv, dlmk, dbias
 
 

@@ -15,6 +15,10 @@ a first-order autoregressive sequence along the positions of each head
 draws), which keeps each q_i ~ N(0, 1) but makes adjacent queries similar, so
 that they retrieve mostly the same chunks.
 
+With ``qret`` = r a separate retrieval query is drawn as a rank-r adaptation of
+each head's query, q_ret = q + A (B^T q) with A, B [d, r] per head (entries
+N(0, 1/r) / 2 and N(0, 1/d)), the form of a low-rank query calibration.
+
 No part of the attention method is computed here.
 """
 import math
@@ -210,6 +214,14 @@ def make_host_inputs(cfg, lazy_kv=None):
         else:
             out["needle_pos"] = None
         out["lmk"] = lmk
+    out["q_ret"] = None
+    if cfg.get("qret"):
+        r = int(cfg["qret"])
+        A = _draw(cfg, "qret_a", (Hq, d, r), scale=0.5 / math.sqrt(r)).astype(np.float64)
+        Bm = _draw(cfg, "qret_b", (Hq, d, r), scale=1.0 / math.sqrt(d)).astype(np.float64)
+        q64 = out["q"].astype(np.float64)
+        low = np.einsum("hdr,bhld->bhlr", Bm, q64)
+        out["q_ret"] = _store(cfg, (q64 + np.einsum("hdr,bhlr->bhld", A, low)).astype(np.float32))
     out["bias"] = None
     if cfg.get("bias"):
         out["bias"] = _draw(cfg, "bias", (B, Hkv, NC), scale=float(cfg["bias"]))

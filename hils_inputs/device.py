@@ -72,7 +72,7 @@ def make_device_inputs(cfg, device="cuda", host=None):
     dt = cfg["dtype"]
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     dev = {}
-    for name in ("q", "lmk", "dout"):
+    for name in ("q", "q_ret", "lmk", "dout"):
         if host.get(name) is not None:
             dev[name] = to_device(host[name], dt, device)
     dev["bias"] = None if host.get("bias") is None else torch.from_numpy(

@@ -36,14 +36,15 @@
  * O = 0 and LSE = -inf.
  *
  * Layouts (all contiguous, row-major):
- *   q, out, dout, dq   [batch, heads_q,  seq_q,  head_dim]
+ *   q, q_ret, out,     [batch, heads_q,  seq_q,  head_dim]
+ *   dout, dq, dq_ret
  *   k, v, dk, dv       [batch, heads_kv, seq_kv, head_dim]
  *   lmk, dlmk          [batch, heads_kv, num_landmarks, head_dim]
  *   lmk_bias, dbias    [batch, heads_kv, num_landmarks]          fp32, nullable
  *   sel_idx            [batch, heads_kv, seq_q, top_k]           int32, ascending
  *                                                               chunk ids, -1 padded
  *   lse                [batch, heads_q,  seq_q]                  fp32
- * dtype HILS_BF16: q, k, v, lmk, out, dout, dq, dk, dv, dlmk are bf16 (raw 16-bit
+ * dtype HILS_BF16: q, q_ret, k, v, lmk, out, dout, dq, dq_ret, dk, dv, dlmk are bf16 (raw 16-bit
  * patterns); arithmetic is fp32. HILS_F32: all of them fp32.
  *
  * Ownership and concurrency: every pointer is a device pointer owned by the
@@ -110,28 +111,34 @@ typedef struct {
 size_t hils_workspace_size(const hils_params* p, int32_t op);
 
 /* Forward pass (prefill or any seq_q): scores, group top-K selection, per-chunk
- * attention and fusion [HSADR §3].  Writes out, sel_idx and (if non-null) lse. */
-hils_status hils_forward(const hils_params* p, const void* q, const void* k, const void* v,
-                         const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
-                         float* lse, void* ws, size_t ws_bytes, void* stream);
+ * attention and fusion [HSADR §3].  Writes out, sel_idx and (if non-null) lse.
+ * q_ret (nullable, layout and dtype of q): a separate retrieval query, e.g. one
+ * calibrated by a low-rank query adaptation [HSADR §4 "Architecture"]: the chunk
+ * scores, and so the selection and the fusion weights, use q_ret; the token
+ * logits inside every chunk use q.  NULL: the scores use q. */
+hils_status hils_forward(const hils_params* p, const void* q, const void* q_ret, const void* k,
+                         const void* v, const void* lmk, const float* lmk_bias, void* out,
+                         int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Single-token decode over a KV cache: seq_q must be 1 and causal is implied
  * (the query is the newest token, at position seq_kv - 1, its K/V already in
  * the cache).  Same math as hils_forward's last row; candidate scoring and
  * chunk attention are split across the GPU and merged by log-sum-exp. */
-hils_status hils_decode(const hils_params* p, const void* q, const void* k, const void* v,
-                        const void* lmk, const float* lmk_bias, void* out, int32_t* sel_idx,
-                        float* lse, void* ws, size_t ws_bytes, void* stream);
+hils_status hils_decode(const hils_params* p, const void* q, const void* q_ret, const void* k,
+                        const void* v, const void* lmk, const float* lmk_bias, void* out,
+                        int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward pass with the selection `sel_idx` (from hils_forward) held fixed
  * [HSADR §3 "Hierarchical softmax"; §9].  Writes (overwrites) dq, dk, dv,
  * dlmk and, if non-null, dlmk_bias.  `out` and `lse` are the forward's
- * outputs; `lse` must be non-null. */
-hils_status hils_backward(const hils_params* p, const void* q, const void* k, const void* v,
-                          const void* lmk, const float* lmk_bias, const void* out,
+ * outputs; `lse` must be non-null.  With q_ret (the forward's retrieval query)
+ * the score gradients go to dq_ret (layout of dq) and dq holds the
+ * token-attention part; q_ret and dq_ret are both given or both NULL. */
+hils_status hils_backward(const hils_params* p, const void* q, const void* q_ret, const void* k,
+                          const void* v, const void* lmk, const float* lmk_bias, const void* out,
                           const void* dout, const int32_t* sel_idx, const float* lse,
-                          void* dq, void* dk, void* dv, void* dlmk, float* dlmk_bias,
-                          void* ws, size_t ws_bytes, void* stream);
+                          void* dq, void* dq_ret, void* dk, void* dv, void* dlmk,
+                          float* dlmk_bias, void* ws, size_t ws_bytes, void* stream);
 
 /* Landmark formation [HSADR §3 "Linear surrogate for chunk mass"]: for every
  * complete chunk c < seq_kv / chunk_size of each (batch, kv head), the landmark

@@ -66,11 +66,11 @@ def check_selection(host, cfg, gpu_idx, b, g, qi, ref_idx_row):
     scale = 1.0 / math.sqrt(d)
     lmk = host["lmk"][b, g].astype(np.float64)
     bias = None if host.get("bias") is None else host["bias"][b, g].astype(np.float64)
+    qrg = None if host.get("q_ret") is None else host["q_ret"][b, g * G:(g + 1) * G, qi].astype(np.float64)
     r = hils_query(host["q"][b, g * G:(g + 1) * G, qi].astype(np.float64), host["k"][b, g],
                    host["v"][b, g], lmk, bias, qi, Lq=cfg["Lq"], Lkv=cfg["Lkv"], S=cfg["S"],
                    K=cfg["K"], causal=bool(cfg["causal"]), keep_own=bool(cfg["keep_own"]),
-                   local_chunks=cfg.get("win"),
-                   scale=scale)
+                   local_chunks=cfg.get("win"), scale=scale, qrg=qrg)
     gb = dict(zip(r["cand"].tolist(), r["gbar"].tolist()))
     kth = sorted(gb[c] for c in want)[0]
     for c in set(got) ^ set(want):
@@ -95,7 +95,8 @@ def check_forward(host, cfg, out, idx, lse, queries=None, batches=None, heads_kv
     for b in bs:
         for g in gs:
             ro, ri, rl = ref_forward(host["q"], host["k"], host["v"], host["lmk"], host.get("bias"),
-                                     queries=qs, batches=[b], heads_kv=[g], **kw)
+                                     queries=qs, batches=[b], heads_kv=[g],
+                                     q_ret=host.get("q_ret"), **kw)
             forced = np.array(idx[b, g][qs])[None, None]       # GPU selection for these queries
             need_forced = False
             for n, i in enumerate(qs):
@@ -108,7 +109,7 @@ def check_forward(host, cfg, out, idx, lse, queries=None, batches=None, heads_kv
                 fidx[b, g] = forced[0, 0]
                 ro, _, rl = ref_forward(host["q"], host["k"], host["v"], host["lmk"],
                                         host.get("bias"), queries=qs, batches=[b], heads_kv=[g],
-                                        forced_idx=fidx, **kw)
+                                        forced_idx=fidx, q_ret=host.get("q_ret"), **kw)
             hs = slice(g * G, (g + 1) * G)
             assert_close("out[b=%d,g=%d]" % (b, g), out[b, hs][:, qs], ro[b, hs], kind, tol)
             assert_close("lse[b=%d,g=%d]" % (b, g), lse[b, hs][:, qs], rl[b, hs], lkind, ltol)

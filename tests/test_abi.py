@@ -52,10 +52,10 @@ MIS = ctypes.c_void_p((1 << 20) + 4)   # not 16-byte aligned
 
 
 def _fwd(p, q=FAKE, k=FAKE, v=FAKE, lmk=FAKE, bias=None, out=FAKE, idx=FAKE, lse=None, ws=None,
-         ws_bytes=0, entry="hils_forward"):
+         ws_bytes=0, entry="hils_forward", q_ret=None):
     lib = H.load_library()
-    return getattr(lib, entry)(ctypes.byref(p), q, k, v, lmk, bias, out, idx, lse, ws, ws_bytes,
-                               None)
+    return getattr(lib, entry)(ctypes.byref(p), q, q_ret, k, v, lmk, bias, out, idx, lse, ws,
+                               ws_bytes, None)
 
 
 def _err():
@@ -113,16 +113,32 @@ def test_workspace_size_of_invalid_params_is_zero():
     assert H.hils_workspace_size(_p(), 7) == 0
 
 
+def _bwd_args(**over):
+    names = ["q", "q_ret", "k", "v", "lmk", "lmk_bias", "out", "dout", "sel_idx", "lse", "dq",
+             "dq_ret", "dk", "dv", "dlmk", "dlmk_bias", "ws", "ws_bytes", "stream"]
+    a = dict(zip(names, [FAKE] * 16 + [FAKE, 1 << 30, None]))
+    a.update(q_ret=None, dq_ret=None, lmk_bias=None)
+    a.update(over)
+    return [a[n] for n in names]
+
+
 def test_backward_rejections():
     lib = H.load_library()
     p = _p()
-    args = [FAKE] * 14 + [FAKE, 1 << 30, None]
-    args[4] = None                                   # lmk_bias may be null
-    args[8] = None                                   # lse is required
-    assert lib.hils_backward(ctypes.byref(p), *args) == H.HILS_ERR_INVALID_ARG
+    assert lib.hils_backward(ctypes.byref(p), *_bwd_args(lse=None)) == H.HILS_ERR_INVALID_ARG
     assert "null" in _err()
     p2 = _p(chunk_size=128, head_dim=128, num_landmarks=2)
-    assert lib.hils_backward(ctypes.byref(p2), *args) == H.HILS_ERR_UNSUPPORTED
+    assert lib.hils_backward(ctypes.byref(p2), *_bwd_args()) == H.HILS_ERR_UNSUPPORTED
+
+
+def test_retrieval_query_pointer_checks():
+    lib = H.load_library()
+    assert _fwd(_p(), q_ret=MIS) == H.HILS_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    # q_ret and dq_ret come together
+    assert lib.hils_backward(ctypes.byref(_p()), *_bwd_args(q_ret=FAKE)) == H.HILS_ERR_INVALID_ARG
+    assert "together" in _err()
+    assert lib.hils_backward(ctypes.byref(_p()), *_bwd_args(dq_ret=FAKE)) == H.HILS_ERR_INVALID_ARG
 
 
 def test_empty_problem_is_a_no_op():

@@ -24,16 +24,18 @@ def _grad_case(hl, cfg, queries=None):
     host, dev = make_device_inputs(cfg)
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=bool(cfg["causal"]),
               keep_own_chunk=bool(cfg["keep_own"]), local_chunks=cfg.get("win"))
-    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"], **kw)
-    dq, dk, dv, dl, db = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"],
-                                          out, dev["dout"], idx, lse, need_dbias=True, **kw)
+    qr = dev.get("q_ret")
+    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"],
+                                    q_ret=qr, **kw)
+    grads = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"],
+                             out, dev["dout"], idx, lse, need_dbias=True, q_ret=qr, **kw)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy().astype(np.int64)
     ref = ref_backward(host["q"], host["k"], host["v"], host["lmk"], host.get("bias"),
-                       host["dout"], forced_idx=gi, **kw)
+                       host["dout"], forced_idx=gi, q_ret=host.get("q_ret"), **kw)
     tol = 1e-5 if cfg["dtype"] == "f32" else 2e-2
-    for name, got, want in zip(("dq", "dk", "dv", "dlmk", "dbias"),
-                               (dq, dk, dv, dl, db), ref):
+    assert len(grads) == len(ref)
+    for name, got, want in zip(("dq", "dk", "dv", "dlmk", "dbias", "dq_ret"), grads, ref):
         assert_close(name, to_np(got), want, "norm", tol)
 
 
@@ -65,6 +67,14 @@ def test_tiny_f32_backward(hl):
          win=2),
     dict(B=1, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="iid", win=12),
     dict(B=1, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, dtype="bf16", lmk="iid", win=0),
+    # separate retrieval query: generic (fp32, bf16) and MFMA paths
+    dict(B=1, Hq=4, Hkv=2, d=64, Lq=150, Lkv=150, S=16, K=3, dtype="f32", lmk="iid", qret=8,
+         bias=0.4, win=2),
+    dict(B=1, Hq=4, Hkv=2, d=64, Lq=40, Lkv=200, S=16, K=3, dtype="bf16", lmk="iid", qret=8),
+    dict(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=8, dtype="bf16", lmk="chunk_mean",
+         qret=8, bias=0.3),
+    dict(B=1, Hq=4, Hkv=1, d=128, Lq=768, Lkv=768, S=64, K=4, dtype="bf16", lmk="iid", qret=8,
+         win=3),
 ])
 def test_backward_shapes(hl, over):
     cfg = dict(config("tiny_f32"), seed=31, dout=True)

@@ -20,7 +20,7 @@ def hl():
 
 def _run(hl, cfg, dev, entry="forward", **over):
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], keep_own_chunk=bool(cfg["keep_own"]),
-              local_chunks=cfg.get("win"))
+              local_chunks=cfg.get("win"), q_ret=dev.get("q_ret"))
     kw.update(over)
     if entry == "forward":
         out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"],
@@ -83,6 +83,13 @@ GENERIC_CASES = {
     "mfma_win20_covers": _case(B=1, Hq=4, Hkv=1, d=128, Lq=1024, Lkv=1024, S=64, K=4, win=20,
                                seed=18),
     "mfma_win0": _case(B=1, Hq=4, Hkv=1, d=128, Lq=512, Lkv=512, S=64, K=4, win=0, seed=19),
+    # separate retrieval query (rank-8 adaptation of q)
+    "qret_generic_f32": _case(B=1, Hq=4, Hkv=2, d=64, Lq=200, Lkv=200, S=16, K=3, qret=8,
+                              dtype="f32", bias=0.3, seed=20),
+    "qret_generic_suffix": _case(B=1, Hq=4, Hkv=2, d=96, Lq=40, Lkv=300, S=32, K=3, qret=8,
+                                 win=2, seed=21),
+    "qret_mfma": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=8, qret=8, win=3,
+                       lmk="chunk_mean", seed=22),
 }
 
 
@@ -112,10 +119,11 @@ def test_values_one_give_output_one(hl, L, win):
     assert np.abs(out - 1.0).max() <= 2.0 ** -9 + 2.0 ** -8 + 1e-6
 
 
-@pytest.mark.parametrize("Lkv,K,win", [(8209, 32, 1), (4096, 16, 1), (100, 8, 1), (64, 4, 1),
-                                       (8209, 32, 8), (1000, 8, 4), (300, 4, 9)])
-def test_decode_small(hl, Lkv, K, win):
-    cfg = config("decode_128k", B=2, Lkv=Lkv, K=K, win=win)
+@pytest.mark.parametrize("Lkv,K,win,qret", [(8209, 32, 1, 0), (4096, 16, 1, 0), (100, 8, 1, 0),
+                                            (64, 4, 1, 0), (8209, 32, 8, 0), (1000, 8, 4, 0),
+                                            (300, 4, 9, 0), (4096, 16, 1, 8), (2000, 8, 4, 8)])
+def test_decode_small(hl, Lkv, K, win, qret):
+    cfg = config("decode_128k", B=2, Lkv=Lkv, K=K, win=win, qret=qret)
     host, dev = make_device_inputs(cfg)
     out, idx, lse = _run(hl, cfg, dev, entry="decode")
     check_forward(host, cfg, out, idx, lse)
