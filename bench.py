@@ -20,7 +20,8 @@ train_8k with a 512-token chunk-aligned local window (8 chunk slots) beside the
 top-K retrieval.  `prefill_8k_corr` repeats prefill_8k with correlated adjacent
 queries (first-order autoregressive along the sequence, rho = 0.98), the regime
 in which the query-block union kernel saves work; its line reports the measured
-share of chunks that adjacent queries have in common.
+share of chunks that adjacent queries have in common.  `train_8k_qcal` repeats the
+training step with a separate rank-8 retrieval query (score gradients to it).
 
 Every input is resident in HBM before timing.  Per-kernel durations come from
 HIP events the library records around each launch of the dominant kernel on
@@ -458,10 +459,13 @@ def run_train(hl, cfg, steps, warmup, ev):
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]),
               local_chunks=local_chunks(cfg))
 
+    qr = dev.get("q_ret")
+
     def step(_):
-        out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
+        out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, q_ret=qr,
+                                        **kw)
         hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out, dev["dout"], idx,
-                         lse, **kw)
+                         lse, q_ret=qr, **kw)
 
     mfma = launched(hl, ev, "prefill_bwd_rows", lambda: step(0))
     kernels = ["prefill_bwd_rows", "prefill_bwd_chunks"] if mfma else ["generic_bwd_rows", "generic_bwd_chunks"]
@@ -635,9 +639,9 @@ def main():
     todo = []
     if not args.no_extra and args.only is None:
         todo = ["decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
-                "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr"]
+                "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr", "train_8k_qcal"]
     elif args.only in ("decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
-                       "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr"):
+                       "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr", "train_8k_qcal"):
         todo = [args.only]
     for name in todo:
         cfg = dict(config("train_8k"), name=name) if name == "landmarks_8k" else config(name)

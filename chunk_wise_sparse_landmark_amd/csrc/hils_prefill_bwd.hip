@@ -957,35 +957,75 @@ prefill_bwd_reduce(Geometry g, BwdWs ws, uint16_t* __restrict__ dk_out,
 }
 
 // ---- landmark gradients when a separate retrieval query is given: dlmk_c =
-//      scale sum ds_c q_r over the rows that retrieved chunk c (windows in order,
-//      queries in order, heads in order), overwriting the chunk pass's values,
-//      which used the query itself.  One workgroup per (b, kv head, chunk),
-//      thread x = dimension x.
-__global__ void __launch_bounds__(kD)
+//      scale sum ds_c q_r over the rows that retrieved chunk c, overwriting the
+//      chunk pass's values (which used the query itself).  One workgroup per
+//      (b, kv head, chunk): the retrieving queries are listed in query order
+//      (one window per thread, a prefix sum places them), wave w takes entries
+//      w, w + 4, .. with lane l on dims 2l, 2l + 1, and the four wave sums are
+//      added in wave order, so the result does not depend on timing.
+constexpr int kQrThreads = 256;
+
+__global__ void __launch_bounds__(kQrThreads)
 prefill_bwd_dlmk_qret(Geometry g, const uint16_t* __restrict__ qr, BwdWs ws,
                       uint16_t* __restrict__ dlmk_out) {
+  __shared__ uint16_t eq[kMaxL];
+  __shared__ uint8_t es[kMaxL];
+  __shared__ int scan[kQrThreads];
+  __shared__ float red[kQrThreads / kWave][kD];
   const int nbkv = g.B * g.Hkv;
   const int bkv = blockIdx.x % nbkv, c = blockIdx.x / nbkv;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
-  const int x = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = g.Lq, NW = L / kWin;
   const size_t nslot = (size_t)(g.K + g.win);
-  float acc = 0.f;
-  for (int wdw = c + max(g.win, 1); wdw < NW; ++wdw) {
-    uint64_t m = ws.qm[((size_t)bkv * NW + wdw) * g.NC + c];
-    while (m) {
-      const int bit = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      const int qq = wdw * kWin + bit;
-      const int slot = ws.slot[((size_t)bkv * L + qq) * g.NC + c];
-#pragma unroll
-      for (int h = 0; h < kG; ++h) {
-        const size_t row = (size_t)(b * g.Hq + kvh * kG + h) * L + qq;
-        acc = __builtin_fmaf(ws.stats[row * nslot + slot].w, bf16_to_f32(qr[row * kD + x]), acc);
-      }
+  const int wret = c + max(g.win, 1);       // first window that may retrieve chunk c
+  const int nlater = NW - wret;
+  const uint64_t m = tid < nlater ? ws.qm[((size_t)bkv * NW + wret + tid) * g.NC + c] : 0ull;
+  const int cnt = __popcll(m);
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kQrThreads; off <<= 1) {
+    const int t = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += t;
+    __syncthreads();
+  }
+  {
+    int pos = scan[tid] - cnt;
+    uint64_t mm = m;
+    while (mm) {
+      const int bit = __ffsll((long long)mm) - 1;
+      mm &= mm - 1;
+      const int qq = (wret + tid) * kWin + bit;
+      eq[pos] = (uint16_t)qq;
+      es[pos] = ws.slot[((size_t)bkv * L + qq) * g.NC + c];
+      ++pos;
     }
   }
-  dlmk_out[((size_t)bkv * g.NCcap + c) * kD + x] = f32_to_bf16(g.scale * acc);
+  const int total = scan[kQrThreads - 1];
+  __syncthreads();
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll 4
+  for (int n = w; n < total; n += kQrThreads / kWave) {
+    const int qq = eq[n], slot = es[n];
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+      const size_t row = (size_t)(b * g.Hq + kvh * kG + h) * L + qq;
+      const float ds = ws.stats[row * nslot + slot].w;
+      const uint32_t pr = reinterpret_cast<const uint32_t*>(qr + row * kD)[lane];
+      a0 = __builtin_fmaf(ds, __uint_as_float(pr << 16), a0);
+      a1 = __builtin_fmaf(ds, __uint_as_float(pr & 0xffff0000u), a1);
+    }
+  }
+  red[w][2 * lane] = a0;
+  red[w][2 * lane + 1] = a1;
+  __syncthreads();
+  if (tid < kD) {
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < kQrThreads / kWave; ++x) acc += red[x][tid];
+    dlmk_out[((size_t)bkv * g.NCcap + c) * kD + tid] = f32_to_bf16(g.scale * acc);
+  }
 }
 
 }  // namespace
@@ -1030,7 +1070,7 @@ hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void*
   hipLaunchKernelGGL(prefill_bwd_reduce, dim3(nbkv * g.NCcap), dim3(kChunkThreads), 0, st, g, ws,
                      (uint16_t*)dk, (uint16_t*)dv, (uint16_t*)dlmk, dbias);
   if (dqr)
-    hipLaunchKernelGGL(prefill_bwd_dlmk_qret, dim3(nbkv * g.NC), dim3(kD), 0, st, g,
+    hipLaunchKernelGGL(prefill_bwd_dlmk_qret, dim3(nbkv * g.NC), dim3(kQrThreads), 0, st, g,
                        (const uint16_t*)qr, ws, (uint16_t*)dlmk);
   return hipGetLastError();
 }

@@ -55,6 +55,8 @@ for _name in ("prefill_8k", "decode_128k", "train_8k"):
 # prefill_8k with correlated adjacent queries (rho = 0.98: adjacent queries share
 # about 88% of their selected chunks on this generator)
 CONFIGS["prefill_8k_corr"] = dict(CONFIGS["prefill_8k"], qcorr=0.98)
+# the training step with a separate rank-8 retrieval query
+CONFIGS["train_8k_qcal"] = dict(CONFIGS["train_8k"], qret=8)
 
 
 def config(name, **overrides):

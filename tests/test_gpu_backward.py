@@ -82,26 +82,33 @@ def test_backward_shapes(hl, over):
     _grad_case(hl, cfg)
 
 
-def test_train_8k_sampled(hl):
-    """Full training shape through the product path.  dq is checked on sampled
-    query rows; dk, dv of the last two chunks and dlmk, dbias of the second-to-
-    last one are complete once every query of the last two windows is included
-    (no earlier query can reach those chunks)."""
-    cfg = config("train_8k")
+@pytest.mark.parametrize("name", ["train_8k", "train_8k_qcal"])
+def test_train_8k_sampled(hl, name):
+    """Full training shape through the product path (and with a separate retrieval
+    query).  dq (and dq_ret) are checked on sampled query rows; dk, dv of the last
+    two chunks and dlmk, dbias of the second-to-last one are complete once every
+    query of the last two windows is included (no earlier query can reach those
+    chunks)."""
+    cfg = config(name)
     host, dev = make_device_inputs(cfg)
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=True)
-    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
-    dq, dk, dv, dl, db = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out,
-                                          dev["dout"], idx, lse, need_dbias=True, **kw)
+    qr = dev.get("q_ret")
+    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, q_ret=qr, **kw)
+    grads = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out, dev["dout"], idx,
+                             lse, need_dbias=True, q_ret=qr, **kw)
+    dq, dk, dv, dl, db = grads[:5]
     torch.cuda.synchronize()
     L, S = cfg["Lq"], cfg["S"]
     rng = np.random.default_rng(3)
     qs = np.array(sorted(set(rng.choice(L - 2 * S, 24, replace=False).tolist())
                          | set(range(L - 2 * S, L))))
     gi = idx.cpu().numpy().astype(np.int64)[:, :, qs]
-    rdq, rdk, rdv, rdl, rdb = ref_backward(host["q"], host["k"], host["v"], host["lmk"], None,
-                                           host["dout"], forced_idx=gi, queries=qs, **kw)
+    ref = ref_backward(host["q"], host["k"], host["v"], host["lmk"], None, host["dout"],
+                       forced_idx=gi, queries=qs, q_ret=host.get("q_ret"), **kw)
+    rdq, rdk, rdv, rdl, rdb = ref[:5]
     assert_close("dq rows", to_np(dq)[:, :, qs], rdq[:, :, qs], "norm", 2e-2)
+    if qr is not None:
+        assert_close("dq_ret rows", to_np(grads[5])[:, :, qs], ref[5][:, :, qs], "norm", 2e-2)
     tail = slice(L - 2 * S, L)
     assert_close("dk tail", to_np(dk)[:, :, tail], rdk[:, :, tail], "norm", 2e-2)
     assert_close("dv tail", to_np(dv)[:, :, tail], rdv[:, :, tail], "norm", 2e-2)
