@@ -163,40 +163,16 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
 // ----------------------------------------------------------------------------
 // 3. chunk attention with online fusion.  grid (nsplit, B*Hkv): workgroup
 //    `split` walks fusion slots [split*apc, split*apc + apc) of its (b, kv
-//    head) -- slot < K is the slot-th selected chunk, slot K the own chunk --
-//    reading each chunk's 16 KB of K and 16 KB of V once for all G heads, with
-//    the next chunk's loads in flight while one is computed.  Per head it keeps
-//    (M, Z, O) = (max s, sum e^{s-M}, sum e^{s-M} o_c) over its chunks, s the
-//    retrieval score (own chunk: its exact lse), and writes them as a partial.
+//    head) -- slot < K is the slot-th selected chunk, slot K + j the local
+//    window's chunk own - j -- reading each chunk's 16 KB of K and 16 KB of V
+//    once for all G heads: K into registers (thread -> key, quarter of the
+//    dims), V by direct global->LDS copies, both issued before any arithmetic.
+//    Per head it keeps (M, Z, O) = (max s, sum e^{s-M}, sum e^{s-M} o_c) over
+//    its chunks, s the retrieval score (a window chunk: its exact lse), and
+//    writes them as a partial.  No cross-chunk prefetch: with the registers
+//    that frees, more workgroups stay resident and hide each other's loads.
 // ----------------------------------------------------------------------------
 constexpr int kPartStride = kD + 4;   // O[128], M, Z, pad  (floats)
-
-struct ChunkLoads {
-  uint4 k[4];   // key tid/4, dims 32*(tid%4) .. +31
-  uint4 v[4];   // V rows, 16 B per thread per step, coalesced
-  uint32_t lm;  // landmark dims 2*(tid%64), +1 (selected chunks)
-  float bias;
-};
-
-__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ Kc,
-                                           const uint16_t* __restrict__ Vc, int n,
-                                           const uint16_t* __restrict__ lrow,
-                                           const float* __restrict__ brow, ChunkLoads& L) {
-  const int tid = threadIdx.x;
-  L.lm = lrow ? reinterpret_cast<const uint32_t*>(lrow)[tid & 63] : 0u;
-  L.bias = brow ? *brow : 0.f;
-  const int j = tid >> 2, qd = tid & 3;
-#pragma unroll
-  for (int p4 = 0; p4 < 4; ++p4)
-    L.k[p4] = j < n ? *reinterpret_cast<const uint4*>(Kc + (size_t)j * kD + qd * 32 + p4 * 8)
-                    : make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int idx = x * kThreads + tid;          // uint4 index within the chunk's V
-    const int row = idx / (kD / 8);
-    L.v[x] = row < n ? reinterpret_cast<const uint4*>(Vc)[idx] : make_uint4(0, 0, 0, 0);
-  }
-}
 
 __global__ void __launch_bounds__(kThreads)
 decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
@@ -205,9 +181,8 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
               const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
               float* __restrict__ parts) {
   __shared__ float qs[kMaxGd][kD];
-  __shared__ float qrs[kMaxGd][kD];   // retrieval queries (chunk scores)
   __shared__ float lg[kMaxGd][kS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
+  __shared__ __attribute__((aligned(16))) uint4 vs[kS * kD / 8];
   __shared__ float sc[kMaxGd];
   __shared__ int ca[8], cn[8], cc[8];
   const int split = blockIdx.x, bkv = blockIdx.y;
@@ -235,48 +210,57 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     }
     ca[tid] = a; cn[tid] = n; cc[tid] = c;
   }
-  for (int x = tid; x < G * kD; x += kThreads) {
+  for (int x = tid; x < G * kD; x += kThreads)
     qs[x / kD][x % kD] = bf16_to_f32(q[(size_t)(b * g.Hq + kvh * G) * kD + x]);
-    qrs[x / kD][x % kD] = bf16_to_f32(qr[(size_t)(b * g.Hq + kvh * G) * kD + x]);
+  // retrieval query of this wave's heads (w, w+4, ..), lane -> dims 2l, 2l+1
+  uint32_t qrv[kMaxGd / 4];
+#pragma unroll
+  for (int x = 0; x < kMaxGd / 4; ++x) {
+    const int h = w + 4 * x;
+    qrv[x] = h < G ? reinterpret_cast<const uint32_t*>(qr + (size_t)(b * g.Hq + kvh * G + h) * kD)[lane]
+                   : 0u;
   }
   __syncthreads();
 
   const uint16_t* Kb = k + (size_t)bkv * g.Lkv * kD;
   const uint16_t* Vb = v + (size_t)bkv * g.Lkv * kD;
+  const uint16_t* Lb = lmk + (size_t)bkv * g.NCcap * kD;
+  const float* Bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   const int dp = tid & 63, hg = tid >> 6;      // PV: dims 2dp, 2dp+1 of heads hg, hg+4, ...
+  const int wbase = w * kWave;
   float M[4], Z[4], O0[4], O1[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) { M[x] = -INFINITY; Z[x] = 0.f; O0[x] = 0.f; O1[x] = 0.f; }
 
-  const uint16_t* Lb = lmk + (size_t)bkv * g.NCcap * kD;
-  const float* Bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
-  ChunkLoads cur, nxt;
-  int first = 0;
-  while (first < apc && cn[first] == 0) ++first;
-  if (first < apc) {
-    const int c0 = cc[first];
-    load_chunk(Kb + (size_t)ca[first] * kD, Vb + (size_t)ca[first] * kD, cn[first],
-               c0 >= 0 ? Lb + (size_t)c0 * kD : nullptr, (c0 >= 0 && Bb) ? Bb + c0 : nullptr, cur);
-  }
-  for (int s = first; s < apc; ) {
-    int nx = s + 1;
-    while (nx < apc && cn[nx] == 0) ++nx;
-    if (nx < apc) {
-      const int c1 = cc[nx];
-      load_chunk(Kb + (size_t)ca[nx] * kD, Vb + (size_t)ca[nx] * kD, cn[nx],
-                 c1 >= 0 ? Lb + (size_t)c1 * kD : nullptr, (c1 >= 0 && Bb) ? Bb + c1 : nullptr, nxt);
-    }
+  for (int s = 0; s < apc; ++s) {
     const int n = cn[s], c = cc[s];
-    // V of this chunk -> LDS
+    if (n == 0) continue;
+    // all loads first: K rows into registers, V rows (full rows only: a
+    // partial own chunk copies the rows it has) straight into LDS, landmark
+    const uint16_t* Kc = Kb + (size_t)ca[s] * kD;
+    const uint4* Vc = reinterpret_cast<const uint4*>(Vb + (size_t)ca[s] * kD);
+    const int j = tid >> 2, qd = tid & 3;
+    uint4 kr[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) reinterpret_cast<uint4*>(vs)[x * kThreads + tid] = cur.v[x];
+    for (int p4 = 0; p4 < 4; ++p4)
+      kr[p4] = j < n ? *reinterpret_cast<const uint4*>(Kc + (size_t)j * kD + qd * 32 + p4 * 8)
+                     : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int idx = x * kThreads + tid;            // uint4 index within the chunk's V
+      if (idx / (kD / 8) < n)
+        __builtin_amdgcn_global_load_lds((const void*)(Vc + idx),
+                                         (__attribute__((address_space(3))) void*)(vs + x * kThreads + wbase),
+                                         16, 0, 0);
+    }
+    const uint32_t lm = c >= 0 ? reinterpret_cast<const uint32_t*>(Lb + (size_t)c * kD)[tid & 63] : 0u;
+    const float bc = (c >= 0 && Bb) ? Bb[c] : 0.f;
     // logits: thread -> key j, 32 dims
     {
-      const int j = tid >> 2, qd = tid & 3;
       float kx[32];
 #pragma unroll
       for (int p4 = 0; p4 < 4; ++p4) {
-        const uint32_t u[4] = {cur.k[p4].x, cur.k[p4].y, cur.k[p4].z, cur.k[p4].w};
+        const uint32_t u[4] = {kr[p4].x, kr[p4].y, kr[p4].z, kr[p4].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kx[p4 * 8 + 2 * e] = __uint_as_float(u[e] << 16);
@@ -294,7 +278,10 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     }
     __syncthreads();
     // chunk softmax per head (wave w: heads w, w+4, ...) and the fusion score
-    for (int h = w; h < G; h += 4) {
+#pragma unroll
+    for (int x = 0; x < kMaxGd / 4; ++x) {
+      const int h = w + 4 * x;
+      if (h >= G) break;
       const float l = lg[h][lane];
       const float m = wave_max(l);
       const float e = __expf(l - m);
@@ -302,14 +289,15 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
       lg[h][lane] = e / z;
       float sv;
       if (c >= 0) {
-        const float ps = qrs[h][2 * lane] * __uint_as_float(cur.lm << 16) +
-                         qrs[h][2 * lane + 1] * __uint_as_float(cur.lm & 0xffff0000u);
-        sv = g.scale * wave_sum(ps) + cur.bias;
+        const float ps = __uint_as_float(qrv[x] << 16) * __uint_as_float(lm << 16) +
+                         __uint_as_float(qrv[x] & 0xffff0000u) * __uint_as_float(lm & 0xffff0000u);
+        sv = g.scale * wave_sum(ps) + bc;
       } else {
         sv = m + __logf(z);   // window chunk: its exact log-sum-exp
       }
       if (lane == 0) sc[h] = sv;
     }
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's V copies have landed
     __syncthreads();
     // o_c = P V, folded into the running (M, Z, O) of each head
 #pragma unroll
@@ -318,7 +306,7 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
       if (h >= G) break;
       float o0 = 0.f, o1 = 0.f;
 #pragma unroll 8
-      for (int jj = 0; jj < kS; ++jj) {
+      for (int jj = 0; jj < n; ++jj) {
         const uint32_t pr = reinterpret_cast<const uint32_t*>(vs)[jj * (kD / 2) + dp];
         const float pj = lg[h][jj];
         o0 = __builtin_fmaf(pj, __uint_as_float(pr << 16), o0);
@@ -333,8 +321,6 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
       M[x] = mn;
     }
     __syncthreads();
-    cur = nxt;
-    s = nx;
   }
   float* part = parts + ((size_t)bkv * nsplit + split) * G * kPartStride;
 #pragma unroll
