@@ -289,6 +289,25 @@ __device__ __forceinline__ uint64_t wave_merge_into(uint64_t run, uint64_t list,
   return head > kth ? wave_merge_sorted(run, list, buf) : run;
 }
 
+// ---------------------------------------------------------------- lane reductions
+// Sum of v[i] over 16 lanes (the lanes that differ only in bits 0..3, i.e. an
+// aligned group of 16), returned to the lane whose bits 0..3 equal i (t = lane & 15).
+// At the step with mask h the lane keeps the half of its values whose index bit
+// matches its own lane bit and adds the partner's copy of that half.
+__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int t) {
+#pragma unroll
+  for (int h = 8; h >= 1; h >>= 1) {
+    const bool up = (t & h) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      float a = v[i], b = v[i + h];
+      asm("" : "+v"(a), "+v"(b));   // keep the selects on registers (no indexed array access)
+      v[i] = (up ? b : a) + __shfl_xor(up ? a : b, h, kWave);
+    }
+  }
+  return v[0];
+}
+
 // ---------------------------------------------------------------- block reductions
 // 256-thread (4-wave) block sum / max; `red` is 4 floats of LDS.  All threads
 // receive the result.

@@ -174,13 +174,18 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
 // ----------------------------------------------------------------------------
 constexpr int kPartStride = kD + 4;   // O[128], M, Z, pad  (floats)
 
+// kG4 (G = 4): K is loaded 1 KB of consecutive rows per instruction (thread t
+// holds dims 8(t%16)..+7 of rows 16p + t/16) and the per-(key, head) dot
+// products are summed over each 16-lane group by a butterfly; otherwise thread
+// t holds a quarter of key t/4's dims and two lane swaps finish each dot product.
+template <bool kG4>
 __global__ void __launch_bounds__(kThreads)
 decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
               const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
               const uint16_t* __restrict__ lmk,
               const float* __restrict__ bias, const int32_t* __restrict__ sel_idx,
               float* __restrict__ parts) {
-  __shared__ float qs[kMaxGd][kD];
+  __shared__ __attribute__((aligned(16))) float qs[kMaxGd][kD];
   __shared__ float lg[kMaxGd][kS];
   __shared__ __attribute__((aligned(16))) uint4 vs[kS * kD / 8];
   __shared__ float sc[kMaxGd];
@@ -239,12 +244,20 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     // partial own chunk copies the rows it has) straight into LDS, landmark
     const uint16_t* Kc = Kb + (size_t)ca[s] * kD;
     const uint4* Vc = reinterpret_cast<const uint4*>(Vb + (size_t)ca[s] * kD);
-    const int j = tid >> 2, qd = tid & 3;
     uint4 kr[4];
+    if (kG4) {
 #pragma unroll
-    for (int p4 = 0; p4 < 4; ++p4)
-      kr[p4] = j < n ? *reinterpret_cast<const uint4*>(Kc + (size_t)j * kD + qd * 32 + p4 * 8)
-                     : make_uint4(0, 0, 0, 0);
+      for (int p4 = 0; p4 < 4; ++p4) {
+        const int idx = p4 * kThreads + tid;           // uint4 index within the chunk's K
+        kr[p4] = idx / (kD / 8) < n ? reinterpret_cast<const uint4*>(Kc)[idx] : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int j = tid >> 2, qd = tid & 3;
+#pragma unroll
+      for (int p4 = 0; p4 < 4; ++p4)
+        kr[p4] = j < n ? *reinterpret_cast<const uint4*>(Kc + (size_t)j * kD + qd * 32 + p4 * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int idx = x * kThreads + tid;            // uint4 index within the chunk's V
@@ -252,11 +265,40 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
         __builtin_amdgcn_global_load_lds((const void*)(Vc + idx),
                                          (__attribute__((address_space(3))) void*)(vs + x * kThreads + wbase),
                                          16, 0, 0);
+      else
+        vs[idx] = make_uint4(0, 0, 0, 0);            // rows past a partial chunk: zero
     }
     const uint32_t lm = c >= 0 ? reinterpret_cast<const uint32_t*>(Lb + (size_t)c * kD)[tid & 63] : 0u;
     const float bc = (c >= 0 && Bb) ? Bb[c] : 0.f;
-    // logits: thread -> key j, 32 dims
-    {
+    if (kG4) {
+      // partial dots of this thread's 8 dims: pv[4p + h] for row 16p + tid/16, head h
+      const int cs = tid & 15;
+      float pv[16];
+#pragma unroll
+      for (int p4 = 0; p4 < 4; ++p4) {
+        const uint32_t u[4] = {kr[p4].x, kr[p4].y, kr[p4].z, kr[p4].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 qa = *reinterpret_cast<const float4*>(&qs[h][cs * 8]);
+          const float4 qb = *reinterpret_cast<const float4*>(&qs[h][cs * 8 + 4]);
+          float d = __uint_as_float(u[0] << 16) * qa.x;
+          d = __builtin_fmaf(__uint_as_float(u[0] & 0xffff0000u), qa.y, d);
+          d = __builtin_fmaf(__uint_as_float(u[1] << 16), qa.z, d);
+          d = __builtin_fmaf(__uint_as_float(u[1] & 0xffff0000u), qa.w, d);
+          float e2 = __uint_as_float(u[2] << 16) * qb.x;
+          e2 = __builtin_fmaf(__uint_as_float(u[2] & 0xffff0000u), qb.y, e2);
+          e2 = __builtin_fmaf(__uint_as_float(u[3] << 16), qb.z, e2);
+          e2 = __builtin_fmaf(__uint_as_float(u[3] & 0xffff0000u), qb.w, e2);
+          pv[p4 * 4 + h] = d + e2;
+        }
+      }
+      // lane group sum: this lane gets index cs = 4p + h, i.e. row 16p + tid/16, head h
+      const float d = reduce_scatter16(pv, cs);
+      const int row = 16 * (cs >> 2) + (tid >> 4);
+      lg[cs & 3][row] = row < n ? g.scale * d : -INFINITY;
+    } else {
+      // logits: thread -> key j, 32 dims
+      const int j = tid >> 2, qd = tid & 3;
       float kx[32];
 #pragma unroll
       for (int p4 = 0; p4 < 4; ++p4) {
@@ -268,9 +310,10 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
         }
       }
       for (int h = 0; h < G; ++h) {
-        float d = 0.f;
+        float d4[4] = {0.f, 0.f, 0.f, 0.f};           // four independent chains
 #pragma unroll
-        for (int e = 0; e < 32; ++e) d = __builtin_fmaf(qs[h][qd * 32 + e], kx[e], d);
+        for (int e = 0; e < 32; ++e) d4[e & 3] = __builtin_fmaf(qs[h][qd * 32 + e], kx[e], d4[e & 3]);
+        float d = (d4[0] + d4[1]) + (d4[2] + d4[3]);
         d += __shfl_xor(d, 1, kWave);
         d += __shfl_xor(d, 2, kWave);
         if (qd == 0) lg[h][j] = j < n ? g.scale * d : -INFINITY;
@@ -304,14 +347,16 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     for (int x = 0; x < 4; ++x) {
       const int h = hg + 4 * x;
       if (h >= G) break;
-      float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-      for (int jj = 0; jj < n; ++jj) {
+      float a0[4] = {0.f, 0.f, 0.f, 0.f}, a1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+      for (int jj = 0; jj < kS; ++jj) {   // rows past a partial chunk are zero (p too)
         const uint32_t pr = reinterpret_cast<const uint32_t*>(vs)[jj * (kD / 2) + dp];
         const float pj = lg[h][jj];
-        o0 = __builtin_fmaf(pj, __uint_as_float(pr << 16), o0);
-        o1 = __builtin_fmaf(pj, __uint_as_float(pr & 0xffff0000u), o1);
+        a0[jj & 3] = __builtin_fmaf(pj, __uint_as_float(pr << 16), a0[jj & 3]);
+        a1[jj & 3] = __builtin_fmaf(pj, __uint_as_float(pr & 0xffff0000u), a1[jj & 3]);
       }
+      const float o0 = (a0[0] + a0[1]) + (a0[2] + a0[3]);
+      const float o1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
       const float sv = sc[h];
       const float mn = fmaxf(M[x], sv);
       const float fo = __expf(M[x] - mn), fn = __expf(sv - mn);
@@ -458,8 +503,12 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
                      sel_idx);
   prof_end(kDecodeMerge, st);
   prof_begin(kDecodeAttend, st);
-  hipLaunchKernelGGL(decode_attend, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc, Q, QR,
-                     (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
+  if (g.G == 4)
+    hipLaunchKernelGGL(decode_attend<true>, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,
+                       Q, QR, (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
+  else
+    hipLaunchKernelGGL(decode_attend<false>, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,
+                       Q, QR, (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
   prof_end(kDecodeAttend, st);
   hipLaunchKernelGGL(decode_fuse, dim3(g.B * g.Hq), dim3(kThreads), 0, st, g, p.asplit, d.parts,
                      (uint16_t*)out, lse);

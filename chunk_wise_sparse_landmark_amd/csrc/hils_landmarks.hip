@@ -188,23 +188,6 @@ __device__ __forceinline__ void partial_dots(const uint4 (&kr)[16], const float*
   }
 }
 
-// Sum of v[i] over the 16 lanes of the row group, returned to lane t for i = t.
-// At the step with mask h the lane keeps the half of its values whose index bit
-// matches its own lane bit and adds the partner's copy of that half.
-__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int t) {
-#pragma unroll
-  for (int h = 8; h >= 1; h >>= 1) {
-    const bool up = (t & h) != 0;
-#pragma unroll
-    for (int i = 0; i < h; ++i) {
-      float a = v[i], b = v[i + h];
-      asm("" : "+v"(a), "+v"(b));   // keep the selects on registers (no indexed array access)
-      v[i] = (up ? b : a) + __shfl_xor(up ? a : b, h, kWave);
-    }
-  }
-  return v[0];
-}
-
 // acc[x] (lane's 8 dims, partial over its row group's keys) summed over the four
 // row groups; lane (r, t) receives dims 8t + 2r and 8t + 2r + 1.
 __device__ __forceinline__ float2 reduce_groups(float (&acc)[8], int lane) {

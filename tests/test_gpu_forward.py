@@ -133,6 +133,15 @@ def test_decode_small(hl, Lkv, K, win, qret):
     assert_close("decode vs forward", out, o2, "abs", 8e-3)
 
 
+@pytest.mark.parametrize("Hq,Hkv,K", [(8, 8, 8), (32, 2, 16), (6, 3, 4)])
+def test_decode_group_sizes(hl, Hq, Hkv, K):
+    """The split decode path at group sizes 1, 16 and 2 (the benchmark uses 4)."""
+    cfg = config("decode_128k", B=2, Hq=Hq, Hkv=Hkv, Lkv=5000, K=K, win=2)
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev, entry="decode")
+    check_forward(host, cfg, out, idx, lse)
+
+
 def test_decode_is_last_prefill_row(hl):
     cfg = _case(B=1, Hq=8, Hkv=2, d=128, Lq=1000, Lkv=1000, S=64, K=8, lmk="iid", seed=9)
     host, dev = make_device_inputs(cfg)
