@@ -194,7 +194,7 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
   const int nsplit = gridDim.x;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int G = g.G;
+  const int G = kG4 ? 4 : g.G;
   const int t = g.Lkv - 1;
 
   // token ranges of this workgroup's slots
