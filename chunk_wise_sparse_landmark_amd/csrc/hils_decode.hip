@@ -49,12 +49,17 @@ __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
 }
 
 // ----------------------------------------------------------------------------
-// 1. scores + local top-K.  R blocks of 64 candidates per wave.
+// 1. scores + local top-K.  A workgroup owns cps = nit * R * 256 consecutive
+//    candidates; in iteration i wave w scores R blocks of 64 rows (all their
+//    row loads in flight before any arithmetic: 16 lanes x 16 B per 256 B row)
+//    and folds them into its running sorted top-K list -- skipped when no key
+//    of the blocks beats the list's K-th, which after the first blocks is the
+//    common case.  The four wave lists are merged at the end.
 // ----------------------------------------------------------------------------
 template <int R>
 __global__ void __launch_bounds__(kThreads)
 decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ lmk,
-                    const float* __restrict__ bias, int ncand, int cps, int nsplit,
+                    const float* __restrict__ bias, int ncand, int cps, int nit, int nsplit,
                     uint64_t* __restrict__ lists) {
   __shared__ uint64_t buf[4][kWave];
   __shared__ uint64_t wl[4][kWave];
@@ -62,6 +67,7 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int sub = lane & 15, grp = lane >> 4;
+  const int K = g.K;
 
   // this lane's 8 dims of the mean query
   float qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -79,47 +85,61 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   const int c1 = min(c0 + cps, ncand);
   const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
-  // every row load of the wave's R blocks in flight before any arithmetic
-  uint4 raw[R][16];
+  uint64_t run = 0;   // running top-K of this wave, sorted descending over lanes
+  bool have = false;
+  for (int it = 0; it < nit; ++it) {
+    const int ib = c0 + it * R * 4 * kWave;
+    if (ib >= c1) break;
+    uint4 raw[R][16];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int base = c0 + (r * 4 + w) * kWave;   // this wave's block of 64
+    for (int r = 0; r < R; ++r) {
+      const int base = ib + (r * 4 + w) * kWave;   // this wave's block of 64
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int c = base + grp * 16 + it;
-      raw[r][it] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
-                          : make_uint4(0, 0, 0, 0);
+      for (int x = 0; x < 16; ++x) {
+        const int c = base + grp * 16 + x;
+        raw[r][x] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
+                           : make_uint4(0, 0, 0, 0);
+      }
+    }
+    uint64_t keys[R];
+    uint64_t kmax = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int base = ib + (r * 4 + w) * kWave;
+      float mine = 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const uint4 u = raw[r][x];
+        float sc = qb[0] * __uint_as_float(u.x << 16) + qb[1] * __uint_as_float(u.x & 0xffff0000u)
+                 + qb[2] * __uint_as_float(u.y << 16) + qb[3] * __uint_as_float(u.y & 0xffff0000u)
+                 + qb[4] * __uint_as_float(u.z << 16) + qb[5] * __uint_as_float(u.z & 0xffff0000u)
+                 + qb[6] * __uint_as_float(u.w << 16) + qb[7] * __uint_as_float(u.w & 0xffff0000u);
+        // sum over the 16 lanes of the row: rotations within a 16-lane DPP row
+        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x128, 0xf, 0xf, false));
+        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x124, 0xf, 0xf, false));
+        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x122, 0xf, 0xf, false));
+        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x121, 0xf, 0xf, false));
+        if (x == sub) mine = sc;
+      }
+      const int c = base + lane;   // = base + grp*16 + sub
+      keys[r] = c < c1 ? make_key(mine + (bb ? bb[c] : 0.f), c) : 0ull;
+      kmax = keys[r] > kmax ? keys[r] : kmax;
+    }
+    kmax = wave_max_u64(kmax);
+    const uint64_t kth = have ? shfl_u64(run, K - 1) : 0ull;
+    if (kmax > kth) {
+      uint64_t top = wave_topk<R>(keys, K, buf[w]);
+      top = lane < K ? top : 0ull;
+      run = have ? wave_merge_into(run, top, K, buf[w]) : top;
+      have = true;
     }
   }
-  uint64_t keys[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int base = c0 + (r * 4 + w) * kWave;
-    float mine = 0.f;
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const uint4 u = raw[r][it];
-      float s = qb[0] * __uint_as_float(u.x << 16) + qb[1] * __uint_as_float(u.x & 0xffff0000u)
-              + qb[2] * __uint_as_float(u.y << 16) + qb[3] * __uint_as_float(u.y & 0xffff0000u)
-              + qb[4] * __uint_as_float(u.z << 16) + qb[5] * __uint_as_float(u.z & 0xffff0000u)
-              + qb[6] * __uint_as_float(u.w << 16) + qb[7] * __uint_as_float(u.w & 0xffff0000u);
-      // sum over the 16 lanes of the row: rotations within a 16-lane DPP row
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x128, 0xf, 0xf, false));
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x124, 0xf, 0xf, false));
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x122, 0xf, 0xf, false));
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x121, 0xf, 0xf, false));
-      if (it == sub) mine = s;
-    }
-    const int c = base + lane;   // = base + grp*16 + sub
-    keys[r] = c < c1 ? make_key(mine + (bb ? bb[c] : 0.f), c) : 0ull;
-  }
-  uint64_t top = wave_topk<R>(keys, g.K, buf[w]);
-  wl[w][lane] = lane < g.K ? top : 0ull;
+  wl[w][lane] = lane < K ? run : 0ull;
   __syncthreads();
   if (w == 0) {
     uint64_t t = wl[0][lane];
-    for (int x = 1; x < 4; ++x) t = wave_merge_into(t, wl[x][lane], g.K, buf[0]);
-    if (lane < g.K) lists[((size_t)bkv * nsplit + split) * g.K + lane] = t;
+    for (int x = 1; x < 4; ++x) t = wave_merge_into(t, wl[x][lane], K, buf[0]);
+    if (lane < K) lists[((size_t)bkv * nsplit + split) * K + lane] = t;
   }
 }
 
@@ -135,11 +155,20 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
   const int bkv = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const uint64_t* src = lists + (size_t)bkv * nsplit * g.K;
-  // each wave merges every 16th local list (each is sorted descending) ...
+  // each wave merges every 16th local list (each is sorted descending), with
+  // the loads of eight lists issued before their merges (the merges' LDS
+  // fences would otherwise hold every load back until the previous merge) ...
   uint64_t run = 0;
-  for (int j = w; j < nsplit; j += kMergeWaves) {
-    const uint64_t key = lane < g.K ? src[(size_t)j * g.K + lane] : 0ull;
-    run = wave_merge_into(run, key, g.K, buf[w]);
+  for (int j0 = w; j0 < nsplit; j0 += 8 * kMergeWaves) {
+    uint64_t key[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int j = j0 + x * kMergeWaves;
+      key[x] = (j < nsplit && lane < g.K) ? src[(size_t)j * g.K + lane] : 0ull;
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      if (j0 + x * kMergeWaves < nsplit) run = wave_merge_into(run, key[x], g.K, buf[w]);
   }
   wl[w][lane] = lane < g.K ? run : 0ull;
   __syncthreads();
@@ -432,7 +461,7 @@ decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* _
 }
 
 struct DecodePlan {
-  int ncand, R, cps, nsplit;
+  int ncand, R, nit, cps, nsplit;
   int apc, asplit;      // attention: fusion slots per workgroup, workgroups per (b, kv head)
 };
 
@@ -441,13 +470,14 @@ DecodePlan plan(const Geometry& g) {
   const int t = g.Lkv - 1;
   p.ncand = max(0, min(t / kS - max(g.win - 1, 0), g.NC));   // chunks before the window
   const int bkv = g.B * g.Hkv;
-  // aim for about 1024 workgroups in the scoring launch
-  int want_splits = max(1, 1024 / max(1, bkv));
-  int per = (p.ncand + want_splits - 1) / want_splits;
-  int R = 1;
-  while (R < 4 && R * 256 < per) R <<= 1;
-  p.R = R;
-  p.cps = 256 * R;
+  // scoring: about 512 workgroups (all resident at once), each streaming its
+  // candidates in iterations of R blocks of 64 rows per wave; fewer, longer
+  // splits also leave fewer lists to merge
+  const int want_splits = max(1, 512 / max(1, bkv));
+  const int per = (p.ncand + want_splits - 1) / want_splits;
+  p.R = per > 256 ? 2 : 1;
+  p.nit = max(1, (per + 256 * p.R - 1) / (256 * p.R));
+  p.cps = 256 * p.R * p.nit;
   p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
   // attention: one fusion slot per workgroup (latency hidden by parallelism)
   // unless that gives fewer than 256 workgroups; then up to 8 per workgroup
@@ -492,11 +522,12 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
   const uint16_t* Lm = (const uint16_t*)lmk;
   dim3 g1(p.nsplit, bkv);
   prof_begin(kDecodeScore, st);
-  switch (p.R) {
-    case 1: hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
-    case 2: hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
-    default: hipLaunchKernelGGL(decode_score_select<4>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, d.lists); break;
-  }
+  if (p.R == 1)
+    hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand,
+                       p.cps, p.nit, p.nsplit, d.lists);
+  else
+    hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand,
+                       p.cps, p.nit, p.nsplit, d.lists);
   prof_end(kDecodeScore, st);
   prof_begin(kDecodeMerge, st);
   hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kMergeWaves * kWave), 0, st, g, p.nsplit, d.lists,

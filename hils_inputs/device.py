@@ -88,12 +88,13 @@ def make_device_inputs(cfg, device="cuda", host=None):
     return host, dev
 
 
-def make_decode_inputs_on_device(cfg, device="cuda"):
+def make_decode_inputs_on_device(cfg, device="cuda", kv_from=None):
     """Decode workload with every large tensor generated on the device.
 
     q (small) and the needle rows are computed on the host; the landmark table,
     K and V are filled in place by the counter generator.  Same values as
-    make_host_inputs(cfg) for the same seed."""
+    make_host_inputs(cfg) for the same seed.  ``kv_from``: another set whose K
+    and V tensors are reused instead of generating new ones."""
     from .configs import _draw, _store, _needle_landmarks
     assert cfg["lmk"] in ("iid", "needle") and cfg["dtype"] == "bf16"
     B, Hq, Hkv, d, Lkv, S = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["Lkv"], cfg["S"]
@@ -112,6 +113,9 @@ def make_decode_inputs_on_device(cfg, device="cuda"):
                     lmk[b, g, c] = to_device(rows[b, g, c], "bf16", device)
     dev["lmk"] = lmk
     for name in ("k", "v"):
+        if kv_from is not None:
+            dev[name] = kv_from[name]
+            continue
         t = torch.empty((B, Hkv, Lkv, d), dtype=torch.bfloat16, device=device)
         fill_normal(t, cfg["seed"], name)
         dev[name] = t
