@@ -49,18 +49,45 @@ __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
 }
 
 // ----------------------------------------------------------------------------
-// 1. scores + local top-K.  A workgroup owns cps = nit * R * 256 consecutive
-//    candidates; in iteration i wave w scores R blocks of 64 rows (all their
-//    row loads in flight before any arithmetic: 16 lanes x 16 B per 256 B row)
-//    and folds them into its running sorted top-K list -- skipped when no key
-//    of the blocks beats the list's K-th, which after the first blocks is the
-//    common case.  The four wave lists are merged at the end.
+// 1. scores + local top-K.  A workgroup owns cps = nit * 256 consecutive
+//    candidates (nit <= kMaxIt); in iteration i wave w scores a block of 64
+//    rows (16 lanes x 16 B per 256 B row, each load instruction covering 4
+//    consecutive rows = 1 KB, the next block's loads issued before
+//    this one is scored) and keeps the block's keys in registers.  The wave's
+//    exact top-K is then found by a bit-by-bit search for the K-th largest key
+//    (wave ballots, no sorting), compacted, sorted once, and the four wave
+//    lists are merged.
 // ----------------------------------------------------------------------------
-template <int R>
+constexpr int kMaxIt = 4;
+
+// The K-th largest of the wave's valid keys (0 = empty) when there are at least
+// K of them, else a value no larger than the smallest valid key.  The low word
+// of a key is the complemented chunk id; ids below 2^idbits leave its bits
+// idbits..31 set, so only the 32 score bits and idbits id bits are searched.
+__device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&kk)[kMaxIt], int K, int idbits) {
+  uint64_t p = 0;
+  for (int bit = 63; bit >= 32; --bit) {
+    const uint64_t t = p | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxIt; ++r) cnt += __popcll(__ballot(kk[r] >= t));
+    if (cnt >= K) p = t;
+  }
+  p |= (uint64_t)(0xffffffffu << idbits);
+  for (int bit = idbits - 1; bit >= 0; --bit) {
+    const uint64_t t = p | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxIt; ++r) cnt += __popcll(__ballot(kk[r] >= t));
+    if (cnt >= K) p = t;
+  }
+  return p;
+}
+
 __global__ void __launch_bounds__(kThreads)
 decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ lmk,
                     const float* __restrict__ bias, int ncand, int cps, int nit, int nsplit,
-                    uint64_t* __restrict__ lists) {
+                    int idbits, uint64_t* __restrict__ lists) {
   __shared__ uint64_t buf[4][kWave];
   __shared__ uint64_t wl[4][kWave];
   const int split = blockIdx.x, bkv = blockIdx.y;
@@ -68,6 +95,22 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int sub = lane & 15, grp = lane >> 4;
   const int K = g.K;
+
+  const int c0 = split * cps;
+  const int c1 = min(c0 + cps, ncand);
+  const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
+  const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
+  auto load_block = [&](int it, uint4 (&raw)[16]) {
+    const int base = c0 + (it * 4 + w) * kWave;   // this wave's block of 64
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int c = base + 4 * x + grp;           // 4 consecutive rows (1 KB) per load
+      raw[x] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 cur[16], nxt[16];
+  load_block(0, cur);
 
   // this lane's 8 dims of the mean query
   float qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -81,59 +124,51 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
 #pragma unroll
   for (int e = 0; e < 8; ++e) qb[e] *= inv;
 
-  const int c0 = split * cps;
-  const int c1 = min(c0 + cps, ncand);
-  const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
-  const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
-  uint64_t run = 0;   // running top-K of this wave, sorted descending over lanes
-  bool have = false;
-  for (int it = 0; it < nit; ++it) {
-    const int ib = c0 + it * R * 4 * kWave;
-    if (ib >= c1) break;
-    uint4 raw[R][16];
+  uint64_t kk[kMaxIt];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int base = ib + (r * 4 + w) * kWave;   // this wave's block of 64
+  for (int it = 0; it < kMaxIt; ++it) {
+    kk[it] = 0ull;
+    if (it >= nit) continue;
+    if (it + 1 < nit) load_block(it + 1, nxt);
+    const int base = c0 + (it * 4 + w) * kWave;
+    float mine = 0.f;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int c = base + grp * 16 + x;
-        raw[r][x] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
-                           : make_uint4(0, 0, 0, 0);
-      }
+    for (int x = 0; x < 16; ++x) {
+      const uint4 u = cur[x];
+      float sc = qb[0] * __uint_as_float(u.x << 16) + qb[1] * __uint_as_float(u.x & 0xffff0000u)
+               + qb[2] * __uint_as_float(u.y << 16) + qb[3] * __uint_as_float(u.y & 0xffff0000u)
+               + qb[4] * __uint_as_float(u.z << 16) + qb[5] * __uint_as_float(u.z & 0xffff0000u)
+               + qb[6] * __uint_as_float(u.w << 16) + qb[7] * __uint_as_float(u.w & 0xffff0000u);
+      // sum over the 16 lanes of the row: rotations within a 16-lane DPP row
+      sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x128, 0xf, 0xf, false));
+      sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x124, 0xf, 0xf, false));
+      sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x122, 0xf, 0xf, false));
+      sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x121, 0xf, 0xf, false));
+      if (x == sub) mine = sc;
     }
-    uint64_t keys[R];
-    uint64_t kmax = 0;
+    const int c = base + 4 * sub + grp;   // the row this lane scored (x == sub)
+    kk[it] = c < c1 ? make_key(mine + (bb ? bb[c] : 0.f), c) : 0ull;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int base = ib + (r * 4 + w) * kWave;
-      float mine = 0.f;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const uint4 u = raw[r][x];
-        float sc = qb[0] * __uint_as_float(u.x << 16) + qb[1] * __uint_as_float(u.x & 0xffff0000u)
-                 + qb[2] * __uint_as_float(u.y << 16) + qb[3] * __uint_as_float(u.y & 0xffff0000u)
-                 + qb[4] * __uint_as_float(u.z << 16) + qb[5] * __uint_as_float(u.z & 0xffff0000u)
-                 + qb[6] * __uint_as_float(u.w << 16) + qb[7] * __uint_as_float(u.w & 0xffff0000u);
-        // sum over the 16 lanes of the row: rotations within a 16-lane DPP row
-        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x128, 0xf, 0xf, false));
-        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x124, 0xf, 0xf, false));
-        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x122, 0xf, 0xf, false));
-        sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x121, 0xf, 0xf, false));
-        if (x == sub) mine = sc;
-      }
-      const int c = base + lane;   // = base + grp*16 + sub
-      keys[r] = c < c1 ? make_key(mine + (bb ? bb[c] : 0.f), c) : 0ull;
-      kmax = keys[r] > kmax ? keys[r] : kmax;
-    }
-    kmax = wave_max_u64(kmax);
-    const uint64_t kth = have ? shfl_u64(run, K - 1) : 0ull;
-    if (kmax > kth) {
-      uint64_t top = wave_topk<R>(keys, K, buf[w]);
-      top = lane < K ? top : 0ull;
-      run = have ? wave_merge_into(run, top, K, buf[w]) : top;
-      have = true;
-    }
+    for (int x = 0; x < 16; ++x) cur[x] = nxt[x];
   }
+  // exact top-K of the wave's keys: the keys >= the K-th largest, compacted and sorted
+  const uint64_t p = wave_kth_key(kk, K, idbits);
+  int cntk = 0;
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const bool pred = kk[it] != 0ull && kk[it] >= p;
+    const uint64_t m = __ballot(pred);
+    if (pred) buf[w][cntk + mask_rank(m)] = kk[it];
+    cntk += __popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t sel = lane < cntk ? buf[w][lane] : 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t run = wave_rank_sort64(sel, buf[w]);
   wl[w][lane] = lane < K ? run : 0ull;
   __syncthreads();
   if (w == 0) {
@@ -461,7 +496,7 @@ decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* _
 }
 
 struct DecodePlan {
-  int ncand, R, nit, cps, nsplit;
+  int ncand, nit, cps, nsplit, idbits;
   int apc, asplit;      // attention: fusion slots per workgroup, workgroups per (b, kv head)
 };
 
@@ -470,15 +505,16 @@ DecodePlan plan(const Geometry& g) {
   const int t = g.Lkv - 1;
   p.ncand = max(0, min(t / kS - max(g.win - 1, 0), g.NC));   // chunks before the window
   const int bkv = g.B * g.Hkv;
-  // scoring: about 512 workgroups (all resident at once), each streaming its
-  // candidates in iterations of R blocks of 64 rows per wave; fewer, longer
-  // splits also leave fewer lists to merge
+  // scoring: about 512 workgroups (all resident at once), each streaming up to
+  // kMaxIt blocks of 64 candidates per wave; fewer, longer splits also leave
+  // fewer lists to merge
   const int want_splits = max(1, 512 / max(1, bkv));
   const int per = (p.ncand + want_splits - 1) / want_splits;
-  p.R = per > 256 ? 2 : 1;
-  p.nit = max(1, (per + 256 * p.R - 1) / (256 * p.R));
-  p.cps = 256 * p.R * p.nit;
+  p.nit = min(kMaxIt, max(1, (per + 255) / 256));
+  p.cps = 256 * p.nit;
   p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
+  p.idbits = 1;
+  while (p.idbits < 32 && (1ll << p.idbits) < (long long)max(p.ncand, 1)) ++p.idbits;
   // attention: one fusion slot per workgroup (latency hidden by parallelism)
   // unless that gives fewer than 256 workgroups; then up to 8 per workgroup
   const int nslot = max(1, g.K + g.win);
@@ -522,12 +558,8 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
   const uint16_t* Lm = (const uint16_t*)lmk;
   dim3 g1(p.nsplit, bkv);
   prof_begin(kDecodeScore, st);
-  if (p.R == 1)
-    hipLaunchKernelGGL(decode_score_select<1>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand,
-                       p.cps, p.nit, p.nsplit, d.lists);
-  else
-    hipLaunchKernelGGL(decode_score_select<2>, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand,
-                       p.cps, p.nit, p.nsplit, d.lists);
+  hipLaunchKernelGGL(decode_score_select, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand,
+                     p.cps, p.nit, p.nsplit, p.idbits, d.lists);
   prof_end(kDecodeScore, st);
   prof_begin(kDecodeMerge, st);
   hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kMergeWaves * kWave), 0, st, g, p.nsplit, d.lists,
