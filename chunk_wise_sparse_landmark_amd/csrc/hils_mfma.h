@@ -47,9 +47,18 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8]) {
   return r;
 }
 
-// max(a, b) in one v_med3_f32 (inputs are finite values or -inf)
+// max(a, b) and max(a, b, c) as single instructions: inputs are finite values
+// or -inf, never NaN, so no canonicalising of the MFMA results (which the
+// compiler inserts before a max it builds itself) is needed
 __device__ __forceinline__ float fmax2(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 // reductions over the four lanes l, l^16, l^32, l^48 (one MFMA D column) with
 // the lane-swap VALU instructions instead of LDS permutes

@@ -326,10 +326,10 @@ __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)
       for (int i = 0; i < 4; ++i)
         if (mt * 16 + g4 * 4 + i >= vis) s[mt][i] = -INFINITY;
   }
-  float mx = fmax2(fmax2(s[0][0], s[0][1]), fmax2(s[0][2], s[0][3]));
-#pragma unroll
-  for (int mt = 1; mt < 4; ++mt)
-    mx = fmax2(mx, fmax2(fmax2(s[mt][0], s[mt][1]), fmax2(s[mt][2], s[mt][3])));
+  const float t0 = fmax3(s[0][0], s[0][1], s[0][2]), t1 = fmax3(s[0][3], s[1][0], s[1][1]);
+  const float t2 = fmax3(s[1][2], s[1][3], s[2][0]), t3 = fmax3(s[2][1], s[2][2], s[2][3]);
+  const float t4 = fmax3(s[3][0], s[3][1], s[3][2]);
+  float mx = fmax3(fmax3(t0, t1, t2), fmax3(t3, t4, s[3][3]), -INFINITY);
   mx = rowgroup_max(mx);
   const float mb = mx * sc2;
   float z = 0.f, y = 0.f;
