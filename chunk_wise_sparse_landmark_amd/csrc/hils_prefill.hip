@@ -461,6 +461,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   // (statistics pass), then the same chunks in the reverse order (the first of
   // them is still staged), then the union
   auto csrc = [&](int c) -> const uint16_t* { return KVg + (size_t)c * kChunkElems; };
+  __syncthreads();                        // the union list is complete
   const uint16_t* first_src = nwin > 0 ? csrc(own) : (nunion > 0 ? csrc(sm.ulist[0]) : nullptr);
   if (first_src) stage_async(first_src, sm.kv[0]);
 

@@ -477,6 +477,7 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
 
   // staged chunk sequence: the window chunks, then the union
   const int nseq = nwin + nunion;
+  __syncthreads();                        // the union list is complete
   auto seq_src = [&](int x) -> const uint16_t* {
     if (x >= nseq) return nullptr;
     const int c = x < nwin ? own - x : sm.ulist[x - nwin];
