@@ -23,6 +23,7 @@
 //     reduction -- writes back and invalidates L2 and costs far more than one
 //     more launch.)
 #include "hils_common.h"
+#include "hils_mfma.h"
 #include "hils_kernels.h"
 #include "hils_profile.h"
 
@@ -238,11 +239,8 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
 // ----------------------------------------------------------------------------
 constexpr int kPartStride = kD + 4;   // O[128], M, Z, pad  (floats)
 
-// kG4 (G = 4): K is loaded 1 KB of consecutive rows per instruction (thread t
-// holds dims 8(t%16)..+7 of rows 16p + t/16) and the per-(key, head) dot
-// products are summed over each 16-lane group by a butterfly; otherwise thread
-// t holds a quarter of key t/4's dims and two lane swaps finish each dot product.
-template <bool kG4>
+// Any G up to 16: thread t holds a quarter of key t/4's dims and two lane
+// swaps finish each (key, head) dot product.
 __global__ void __launch_bounds__(kThreads)
 decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
               const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -258,7 +256,7 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
   const int nsplit = gridDim.x;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int G = kG4 ? 4 : g.G;
+  const int G = g.G;
   const int t = g.Lkv - 1;
 
   // token ranges of this workgroup's slots
@@ -309,13 +307,7 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     const uint16_t* Kc = Kb + (size_t)ca[s] * kD;
     const uint4* Vc = reinterpret_cast<const uint4*>(Vb + (size_t)ca[s] * kD);
     uint4 kr[4];
-    if (kG4) {
-#pragma unroll
-      for (int p4 = 0; p4 < 4; ++p4) {
-        const int idx = p4 * kThreads + tid;           // uint4 index within the chunk's K
-        kr[p4] = idx / (kD / 8) < n ? reinterpret_cast<const uint4*>(Kc)[idx] : make_uint4(0, 0, 0, 0);
-      }
-    } else {
+    {
       const int j = tid >> 2, qd = tid & 3;
 #pragma unroll
       for (int p4 = 0; p4 < 4; ++p4)
@@ -334,33 +326,7 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     }
     const uint32_t lm = c >= 0 ? reinterpret_cast<const uint32_t*>(Lb + (size_t)c * kD)[tid & 63] : 0u;
     const float bc = (c >= 0 && Bb) ? Bb[c] : 0.f;
-    if (kG4) {
-      // partial dots of this thread's 8 dims: pv[4p + h] for row 16p + tid/16, head h
-      const int cs = tid & 15;
-      float pv[16];
-#pragma unroll
-      for (int p4 = 0; p4 < 4; ++p4) {
-        const uint32_t u[4] = {kr[p4].x, kr[p4].y, kr[p4].z, kr[p4].w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float4 qa = *reinterpret_cast<const float4*>(&qs[h][cs * 8]);
-          const float4 qb = *reinterpret_cast<const float4*>(&qs[h][cs * 8 + 4]);
-          float d = __uint_as_float(u[0] << 16) * qa.x;
-          d = __builtin_fmaf(__uint_as_float(u[0] & 0xffff0000u), qa.y, d);
-          d = __builtin_fmaf(__uint_as_float(u[1] << 16), qa.z, d);
-          d = __builtin_fmaf(__uint_as_float(u[1] & 0xffff0000u), qa.w, d);
-          float e2 = __uint_as_float(u[2] << 16) * qb.x;
-          e2 = __builtin_fmaf(__uint_as_float(u[2] & 0xffff0000u), qb.y, e2);
-          e2 = __builtin_fmaf(__uint_as_float(u[3] << 16), qb.z, e2);
-          e2 = __builtin_fmaf(__uint_as_float(u[3] & 0xffff0000u), qb.w, e2);
-          pv[p4 * 4 + h] = d + e2;
-        }
-      }
-      // lane group sum: this lane gets index cs = 4p + h, i.e. row 16p + tid/16, head h
-      const float d = reduce_scatter16(pv, cs);
-      const int row = 16 * (cs >> 2) + (tid >> 4);
-      lg[cs & 3][row] = row < n ? g.scale * d : -INFINITY;
-    } else {
+    {
       // logits: thread -> key j, 32 dims
       const int j = tid >> 2, qd = tid & 3;
       float kx[32];
@@ -440,6 +406,146 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
     reinterpret_cast<float2*>(ph)[dp] = make_float2(O0[x], O1[x]);
     if (dp == 0) { ph[kD] = M[x]; ph[kD + 1] = Z[x]; }
   }
+}
+
+// G = 4: the same walk with the arithmetic on packed bf16 pairs, so that a
+// workgroup needs few registers and 18 KB of LDS and many stay resident while
+// others wait for their chunks.  Thread t holds K dims 8(t%16)..+7 of rows
+// 16p + t/16 (1 KB of consecutive rows per load) and the matching dims of the
+// four queries; each (key, head) dot product is four bf16 pair dots summed over
+// the 16-lane group by a butterfly.  Wave w then owns head w: its chunk softmax,
+// the retrieval score, P rounded to bf16 pairs of consecutive keys, and o_c for
+// dims 2 lane, 2 lane + 1 as pair dots of P with V columns gathered by byte
+// permutes.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// (80 registers: six waves per SIMD, so six workgroups per CU)
+__global__ void __launch_bounds__(kThreads, 6)
+decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
+               const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+               const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
+               const int32_t* __restrict__ sel_idx, float* __restrict__ parts) {
+  __shared__ __attribute__((aligned(16))) uint4 vs[kS * kD / 8];
+  __shared__ float lg[4][kS];
+  __shared__ __attribute__((aligned(16))) uint16_t pb[4][kS];
+  __shared__ int ca[8], cn[8], cc[8];
+  const int split = blockIdx.x, bkv = blockIdx.y;
+  const int nsplit = gridDim.x;
+  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave, cs = tid & 15;
+  const int t = g.Lkv - 1;
+
+  if (tid < apc) {
+    const int slot = split * apc + tid;
+    int a = 0, n = 0, c = -1;
+    if (slot < g.K) {
+      c = sel_idx[(size_t)bkv * g.K + slot];
+      if (c >= 0) { a = c * kS; n = kS; }
+    } else {
+      const int j = slot - g.K, own = t / kS, cw = own - j;
+      if (j < g.win && cw >= 0) {
+        a = cw * kS;
+        n = j == 0 ? t - a + 1 : kS;
+      }
+    }
+    ca[tid] = a; cn[tid] = n; cc[tid] = c;
+  }
+  const uint16_t* qg = q + (size_t)(b * g.Hq + kvh * 4) * kD;
+  uint4 qh[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) qh[h] = reinterpret_cast<const uint4*>(qg + h * kD)[cs];
+  const uint32_t qrv = reinterpret_cast<const uint32_t*>(qr + (size_t)(b * g.Hq + kvh * 4 + w) * kD)[lane];
+  __syncthreads();
+
+  const uint16_t* Kb = k + (size_t)bkv * g.Lkv * kD;
+  const uint16_t* Vb = v + (size_t)bkv * g.Lkv * kD;
+  const uint16_t* Lb = lmk + (size_t)bkv * g.NCcap * kD;
+  const float* Bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
+  const int wbase = w * kWave;
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(vs);
+  float M = -INFINITY, Z = 0.f, O0 = 0.f, O1 = 0.f;     // head w, dims 2 lane, 2 lane + 1
+
+  for (int s = 0; s < apc; ++s) {
+    const int n = cn[s], c = cc[s];
+    if (n == 0) continue;
+    const uint4* Kc = reinterpret_cast<const uint4*>(Kb + (size_t)ca[s] * kD);
+    const uint4* Vc = reinterpret_cast<const uint4*>(Vb + (size_t)ca[s] * kD);
+    uint4 kr[4];
+#pragma unroll
+    for (int p4 = 0; p4 < 4; ++p4) {
+      const int idx = p4 * kThreads + tid;
+      kr[p4] = idx / (kD / 8) < n ? Kc[idx] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int idx = x * kThreads + tid;
+      if (idx / (kD / 8) < n)
+        __builtin_amdgcn_global_load_lds((const void*)(Vc + idx),
+                                         (__attribute__((address_space(3))) void*)(vs + x * kThreads + wbase),
+                                         16, 0, 0);
+      else
+        vs[idx] = make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t lm = c >= 0 ? reinterpret_cast<const uint32_t*>(Lb + (size_t)c * kD)[lane] : 0u;
+    const float bc = (c >= 0 && Bb) ? Bb[c] : 0.f;
+    float pv[16];
+#pragma unroll
+    for (int p4 = 0; p4 < 4; ++p4)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float d = dot2_bf16(kr[p4].x, qh[h].x, 0.f);
+        float e2 = dot2_bf16(kr[p4].y, qh[h].y, 0.f);
+        d = dot2_bf16(kr[p4].z, qh[h].z, d);
+        e2 = dot2_bf16(kr[p4].w, qh[h].w, e2);
+        pv[p4 * 4 + h] = d + e2;
+      }
+    {
+      const float d = reduce_scatter16(pv, cs);
+      const int row = 16 * (cs >> 2) + (tid >> 4);
+      lg[cs & 3][row] = row < n ? g.scale * d : -INFINITY;
+    }
+    __syncthreads();
+    // head w: chunk softmax, P as bf16, retrieval score (window chunk: its lse)
+    const float l = lg[w][lane];
+    const float m = wave_max(l);
+    const float e = __expf(l - m);
+    const float z = wave_sum(e);
+    pb[w][lane] = f32_to_bf16(e * __builtin_amdgcn_rcpf(z));
+    const float sv = c >= 0 ? g.scale * wave_sum(dot2_bf16(qrv, lm, 0.f)) + bc : m + __logf(z);
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's V copies have landed
+    __syncthreads();
+    // o_c = P V for head w, dims 2 lane, 2 lane + 1 (rows past a partial chunk: zero)
+    const uint4* pw = reinterpret_cast<const uint4*>(pb[w]);
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int j8 = 0; j8 < kS / 8; ++j8) {
+      const uint4 pp = pw[j8];                         // P of keys 8 j8 .. 8 j8 + 7 (pairs)
+      const uint32_t pr[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int j = 8 * j8 + 2 * e4;
+        const uint32_t w0 = vw[j * (kD / 2) + lane], w1 = vw[(j + 1) * (kD / 2) + lane];
+        const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // dim 2 lane of keys j, j + 1
+        const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07060302u);   // dim 2 lane + 1
+        if (e4 & 1) { b0 = dot2_bf16(lo, pr[e4], b0); b1 = dot2_bf16(hi, pr[e4], b1); }
+        else        { a0 = dot2_bf16(lo, pr[e4], a0); a1 = dot2_bf16(hi, pr[e4], a1); }
+      }
+    }
+    const float o0 = a0 + b0, o1 = a1 + b1;
+    const float mn = fmaxf(M, sv);
+    const float fo = __expf(M - mn), fn = __expf(sv - mn);
+    Z = Z * fo + fn;
+    O0 = O0 * fo + fn * o0;
+    O1 = O1 * fo + fn * o1;
+    M = mn;
+    __syncthreads();
+  }
+  float* ph = parts + (((size_t)bkv * nsplit + split) * 4 + w) * kPartStride;
+  reinterpret_cast<float2*>(ph)[lane] = make_float2(O0, O1);
+  if (lane == 0) { ph[kD] = M; ph[kD + 1] = Z; }
 }
 
 // ----------------------------------------------------------------------------
@@ -567,10 +673,10 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
   prof_end(kDecodeMerge, st);
   prof_begin(kDecodeAttend, st);
   if (g.G == 4)
-    hipLaunchKernelGGL(decode_attend<true>, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,
+    hipLaunchKernelGGL(decode_attend4, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,
                        Q, QR, (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
   else
-    hipLaunchKernelGGL(decode_attend<false>, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,
+    hipLaunchKernelGGL(decode_attend, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,
                        Q, QR, (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
   prof_end(kDecodeAttend, st);
   hipLaunchKernelGGL(decode_fuse, dim3(g.B * g.Hq), dim3(kThreads), 0, st, g, p.asplit, d.parts,
