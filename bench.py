@@ -638,8 +638,9 @@ def main():
                 "roofline": r["roofline"], "selection": r.get("selection")}
     todo = []
     if not args.no_extra and args.only is None:
-        todo = ["decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
-                "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr", "train_8k_qcal"]
+        todo = ["decode_128k", "decode_4m", "prefill_32k", "train_8k", "landmarks_8k",
+                "prefill_8k_swa512", "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr",
+                "train_8k_qcal"]
     elif args.only in ("decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
                        "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr", "train_8k_qcal"):
         todo = [args.only]

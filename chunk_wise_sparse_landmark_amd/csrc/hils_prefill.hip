@@ -47,7 +47,8 @@ constexpr int kWin = 64;         // queries per window (one chunk), both kernels
 constexpr int kBlocks = kWin / 4;          // 16 query blocks of 4 queries
 constexpr int kBlocksPerWave = kBlocks / kAttWaves;
 constexpr int kMaxKf = 32;       // top-K bound on this path
-constexpr int kMaxNC = 256;      // chunks bound on this path (L <= 16384)
+constexpr int kMaxNC = 512;      // chunks bound on this path (L <= 32768)
+static_assert(kAttThreads >= kMaxNC, "the union list is built with one thread per chunk");
 constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
 constexpr int kChunkFrags = 32;            // 16 K + 16 V fragments per chunk
 constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
@@ -57,8 +58,8 @@ constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
 // empty), written as ascending chunk ids (-1 padded) to dst[0..K).  The K-th
 // largest key is found bit by bit from the top with wave ballots (count of
 // keys >= prefix); keys are unique, so exactly the keys >= it are selected.
-// With chunk ids below 256 the low word of every key is 0xffffff00 | ~id, so
-// only the 32 score bits and the 8 id bits are searched.
+// With chunk ids below R*64 = 2^b the low word of every key is ~id with bits
+// b..31 set, so only the 32 score bits and the b id bits are searched.
 // ----------------------------------------------------------------------------
 template <int R>
 __device__ __forceinline__ void select_ascending(const uint64_t (&keys)[R], int K, int32_t* dst) {
@@ -71,8 +72,9 @@ __device__ __forceinline__ void select_ascending(const uint64_t (&keys)[R], int 
     for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[r] >= t));
     if (cnt >= K) p = t;
   }
-  p |= 0xffffff00ull;
-  for (int bit = 7; bit >= 0; --bit) {
+  constexpr int kIdBits = R == 1 ? 6 : (R == 2 ? 7 : (R == 4 ? 8 : 9));
+  p |= static_cast<uint64_t>(0xffffffffu << kIdBits);
+  for (int bit = kIdBits - 1; bit >= 0; --bit) {
     const uint64_t t = p | (1ull << bit);
     int cnt = 0;
 #pragma unroll
@@ -646,7 +648,8 @@ hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* qr,
   prof_begin(kPrefillSelect, st);
   if (g.NC <= 64) launch_select<1>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
   else if (g.NC <= 128) launch_select<2>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
-  else launch_select<4>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
+  else if (g.NC <= 256) launch_select<4>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
+  else launch_select<8>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
   prof_end(kPrefillSelect, st);
   // dynamic LDS above 64 KB must be enabled for the kernel (per device; cheap)
   hipFuncSetAttribute((const void*)prefill_attend, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -189,6 +189,25 @@ def test_prefill_8k_sampled(hl):
     np.testing.assert_array_equal(nsel, np.minimum(own, cfg["K"])[None, :].repeat(cfg["Hkv"], 0))
 
 
+@pytest.mark.parametrize("name,over", [
+    ("prefill_32k", {}),                                   # 512 chunks: the widest selection
+    ("prefill_8k", dict(Hq=8, Hkv=2, Lq=19200, Lkv=19200, seed=11)),   # 300 chunks, ragged 64-block
+])
+def test_prefill_long_sampled(hl, name, over):
+    """The MFMA prefill path past 256 chunks (8 candidate blocks of 64 per row)."""
+    cfg = config(name, **over)
+    host, dev = make_device_inputs(cfg)
+    out, idx, lse = _run(hl, cfg, dev)
+    L = cfg["Lq"]
+    rng = np.random.default_rng(4)
+    qs = sorted(set(range(0, 70)) | set(rng.choice(L, 50, replace=False).tolist())
+                | set(range(L - 6, L)))
+    check_forward(host, cfg, out, idx, lse, queries=qs, heads_kv=[0, cfg["Hkv"] - 1])
+    own = np.arange(L) // cfg["S"]
+    nsel = (idx[0] >= 0).sum(-1)
+    np.testing.assert_array_equal(nsel, np.minimum(own, cfg["K"])[None, :].repeat(cfg["Hkv"], 0))
+
+
 def test_prefill_8k_swa512_sampled(hl):
     """The prefill workload with a 512-token local window (8 chunk slots)."""
     cfg = config("prefill_8k_swa512")
