@@ -48,7 +48,6 @@ constexpr int kBlocks = kWin / 4;          // 16 query blocks of 4 queries
 constexpr int kBlocksPerWave = kBlocks / kAttWaves;
 constexpr int kMaxKf = 32;       // top-K bound on this path
 constexpr int kMaxNC = 512;      // chunks bound on this path (L <= 32768)
-static_assert(kAttThreads >= kMaxNC, "the union list is built with one thread per chunk");
 constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
 constexpr int kChunkFrags = 32;            // 16 K + 16 V fragments per chunk
 constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
@@ -434,18 +433,19 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     }
   }
   __syncthreads();
-  {
-    const int c = tid;
+  int nunion = 0;
+  for (int c0 = 0; c0 < kMaxNC; c0 += kAttThreads) {
+    const int c = c0 + tid;
     const bool f = c < ncand && sm.qmask[c] != 0ull;
     const uint64_t m = __ballot(f);
     if (lane == 0) sm.wcount[w] = __popcll(m);
     __syncthreads();
-    int off = 0;
+    int off = nunion;
     for (int x = 0; x < w; ++x) off += sm.wcount[x];
     if (f) sm.ulist[off + mask_rank(m)] = (uint16_t)c;
+    for (int x = 0; x < kAttWaves; ++x) nunion += sm.wcount[x];
+    __syncthreads();                      // wcount is rewritten by the next group
   }
-  int nunion = 0;
-  for (int x = 0; x < kAttWaves; ++x) nunion += sm.wcount[x];
 
   // Q fragments of this wave's four blocks (B operand of S^T, also the A operand
   // of the retrieval scores): row r16 = (query 4*blk + r16/4, head r16%4)
