@@ -182,7 +182,9 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
 // ----------------------------------------------------------------------------
 // 2. merge the nsplit local lists of one (b, kv head); write ascending ids.
 // ----------------------------------------------------------------------------
-constexpr int kMergeWaves = 16;
+// kMergeWaves = 1 when there are few lists: one wave merges them all, with no
+// workgroup barriers.
+template <int kMergeWaves>
 __global__ void __launch_bounds__(kMergeWaves * kWave)
 decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
              int32_t* __restrict__ sel_idx) {
@@ -191,7 +193,7 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
   const int bkv = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const uint64_t* src = lists + (size_t)bkv * nsplit * g.K;
-  // each wave merges every 16th local list (each is sorted descending), with
+  // each wave merges every kMergeWaves-th local list (each sorted descending), with
   // the loads of eight lists issued before their merges (the merges' LDS
   // fences would otherwise hold every load back until the previous merge) ...
   uint64_t run = 0;
@@ -668,8 +670,11 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
                      p.cps, p.nit, p.nsplit, p.idbits, d.lists);
   prof_end(kDecodeScore, st);
   prof_begin(kDecodeMerge, st);
-  hipLaunchKernelGGL(decode_merge, dim3(bkv), dim3(kMergeWaves * kWave), 0, st, g, p.nsplit, d.lists,
-                     sel_idx);
+  if (p.nsplit <= 8)
+    hipLaunchKernelGGL(decode_merge<1>, dim3(bkv), dim3(kWave), 0, st, g, p.nsplit, d.lists, sel_idx);
+  else
+    hipLaunchKernelGGL(decode_merge<16>, dim3(bkv), dim3(16 * kWave), 0, st, g, p.nsplit, d.lists,
+                       sel_idx);
   prof_end(kDecodeMerge, st);
   prof_begin(kDecodeAttend, st);
   if (g.G == 4)
