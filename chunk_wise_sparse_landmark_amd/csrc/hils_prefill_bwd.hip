@@ -15,9 +15,8 @@
 //
 // Three launches:
 //  1. prefill_bwd_prep    per (b, kv head, 64-query window): the window's
-//     chunk of K and V in operand-fragment order, q and dO with the four heads
-//     interleaved per dimension, D per row, and the (query, chunk) -> slot map
-//     with per-window query masks.
+//     chunk of K and V in operand-fragment order, D per row, and the (query,
+//     chunk) -> slot map with per-window query masks.
 //  2. prefill_bwd_rows    per window (like the forward's attention kernel):
 //     for every chunk of the window's union, S^T = K Q^T and U^T = V dO^T by
 //     MFMA, the chunk softmax, D_c, dl, and dQ += dL K in MFMA accumulators;
@@ -25,7 +24,9 @@
 //     dq gains scale * sum ds_c lmk_c.
 //  3. prefill_bwd_chunks  per (b, kv head, chunk): gathers the queries that
 //     selected the chunk (and those whose local window holds it) in tiles of 8 queries x
-//     4 heads = 32 rows, recomputes S = Q K^T and U = dO V^T for the wave's 16
+//     4 heads = 32 rows (q and dO read once, straight from the inputs; the
+//     transposed operands come from LDS transpose reads), recomputes S = Q K^T
+//     and U = dO V^T for the wave's 16
 //     keys, turns them into w p and dl with the row table (no reductions), and
 //     accumulates dV += (w P)^T dO and dK += dL^T Q by MFMA over the rows, plus
 //     dlmk and dbias.  Each chunk is owned by one workgroup: no atomics.
@@ -66,8 +67,6 @@ int max_items_of(const Geometry& g) {
 
 struct BwdWs {
   uint16_t* frags;   // [bkv][NC][48 fragments][64 lanes][8]
-  uint16_t* qi;      // [bkv][L][d][4 heads]
-  uint16_t* doi;     // [bkv][L][d][4 heads]
   float* Drow;       // [B][Hq][L]
   float4* stats;     // [B][Hq][L][K+win]: (w, log2 lse_c, D_c (window: D), ds_c (window: 0))
   uint64_t* qm;      // [bkv][NW][NC]: window queries that selected chunk c
@@ -88,10 +87,6 @@ BwdWs carve(const Geometry& g, void* base, size_t* total) {
   BwdWs w;
   w.frags = reinterpret_cast<uint16_t*>(c + off);
   off += align256(nbkv * g.NC * kBwdChunkElems * 2);
-  w.qi = reinterpret_cast<uint16_t*>(c + off);
-  off += align256(nbkv * L * kD * kG * 2);
-  w.doi = reinterpret_cast<uint16_t*>(c + off);
-  off += align256(nbkv * L * kD * kG * 2);
   w.Drow = reinterpret_cast<float*>(c + off);
   off += align256((size_t)g.B * g.Hq * L * 4);
   w.stats = reinterpret_cast<float4*>(c + off);
@@ -170,31 +165,6 @@ prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
       val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
     reinterpret_cast<uint4*>(fd)[e] = val;
-  }
-
-  // q and dO with the heads interleaved: xi[bkv][i][d][h]
-  for (int e = tid; e < 2 * kWin * (kD / 8); e += kPrepThreads) {
-    const int which = e / (kWin * (kD / 8)), r = e % (kWin * (kD / 8));
-    const int qq = r / (kD / 8), dg = r % (kD / 8);
-    const int i = win * kWin + qq;
-    const uint16_t* src = which ? dout : q;
-    uint16_t* dst = (which ? ws.doi : ws.qi) + (((size_t)bkv * L + i) * kD + dg * 8) * kG;
-    uint16_t hv[kG][8];
-#pragma unroll
-    for (int h = 0; h < kG; ++h) {
-      const uint4 u = *reinterpret_cast<const uint4*>(
-          src + ((size_t)(b * g.Hq + kvh * kG + h) * L + i) * kD + dg * 8);
-      __builtin_memcpy(hv[h], &u, 16);
-    }
-    uint32_t o[16];
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      o[2 * dd] = hv[0][dd] | ((uint32_t)hv[1][dd] << 16);
-      o[2 * dd + 1] = hv[2][dd] | ((uint32_t)hv[3][dd] << 16);
-    }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      reinterpret_cast<uint4*>(dst)[x] = make_uint4(o[4 * x], o[4 * x + 1], o[4 * x + 2], o[4 * x + 3]);
   }
 
   // D = <dO, O> per (query, head)
@@ -637,16 +607,16 @@ prefill_bwd_plan(Geometry g, BwdWs ws) {
 
 // One tile of 8 queries x 4 heads = 32 rows, staged in LDS by the four waves
 // with direct global->LDS loads:
-//   qa, da  [8 fragments][64 lanes] x 16 B: A operands of S = Q K^T, U = dO V^T;
-//           fragment mt*4+ks, lane l: row (query 4mt + (l%16)/4, head l%4),
-//           dims 32ks + 8(l/16) .. +7
-//   qi, di  [8 queries][128 dims][4 heads] bf16: rows of the B operands
-//   st      [32 rows] (w, log2 lse_c, D_c, ds_c), row r = (query r/4, head r%4)
+//   qn, dn  q and dO rows, row r = (query r/4, head r%4), 128 dims = 16 chunks
+//           of 16 B; chunk c of row r sits at position c ^ 2(r%4) of the row
+//           (so that four consecutive rows of one 32-B column band fall in
+//           different banks).  The A operands of S = Q K^T and U = dO V^T are
+//           16-B reads of a row; the B operands of dV and dK (four heads of a
+//           query at one dim) come out of LDS transpose reads.
+//   st      [32 rows] (w, log2 lse_c, D_c, ds_c)
 struct TileBuf {
-  uint4 qa[8 * kWave];
-  uint4 da[8 * kWave];
-  uint4 qi[8 * kD * kG / 8];
-  uint4 di[8 * kD * kG / 8];
+  uint4 qn[32 * kD / 8];
+  uint4 dn[32 * kD / 8];
   float4 st[32];
 };
 struct ChunkSmem {
@@ -661,7 +631,11 @@ __device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst_wave_bas
                                    16, 0, 0);
 }
 
-// wave w stages its share of tile t into buffer tb
+__device__ __forceinline__ int tile_pos(int r, int c) { return r * (kD / 8) + (c ^ (2 * (r & 3))); }
+
+// wave w stages its share of tile t into buffer tb: waves 0, 1 the q rows,
+// waves 2, 3 the dO rows (four rows = 1 KB per load instruction), wave 2 also
+// the row table
 __device__ __forceinline__ void stage_tile(const Geometry& g, const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ dout, const BwdWs& ws,
                                            int b, int kvh, int bkv, const uint16_t* eq,
@@ -669,36 +643,40 @@ __device__ __forceinline__ void stage_tile(const Geometry& g, const uint16_t* __
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int L = g.Lq;
   const int e0 = t * 8;
-  if (w < 2) {   // A fragments of q (wave 0) or dO (wave 1)
-    const uint16_t* src = w == 0 ? q : dout;
-    uint4* dst = w == 0 ? tb.qa : tb.da;
+  const uint16_t* src = w < 2 ? q : dout;
+  uint4* dst = w < 2 ? tb.qn : tb.dn;
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int mt = f / 4, ks = f % 4;
-      const int e = e0 + 4 * mt + ((lane & 15) >> 2);
-      const int qq = eq[es[e] != 0xff ? e : e0];
-      const uint16_t* p = src + ((size_t)(b * g.Hq + kvh * kG + (lane & 3)) * L + qq) * kD +
-                          32 * ks + 8 * (lane >> 4);
-      lds_load16(p, dst + f * kWave);
-    }
-  } else {       // head-interleaved rows of q (wave 2) or dO (wave 3), 1 KB per query
-    const uint16_t* src = w == 2 ? ws.qi : ws.doi;
-    uint4* dst = w == 2 ? tb.qi : tb.di;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int ee = e0 + e;
-      const int qq = eq[es[ee] != 0xff ? ee : e0];
-      lds_load16(src + ((size_t)bkv * L + qq) * kD * kG + lane * 8, dst + e * kWave);
-    }
-    if (w == 2 && lane < 32) {   // the row table: row r = (query r/4, head r%4)
-      const int ee = e0 + (lane >> 2);
-      const int sl = es[ee];
-      const int qq = eq[sl != 0xff ? ee : e0];
-      const int slot = sl != 0xff ? sl : es[e0];
-      const float4* p = ws.stats + ((size_t)(b * g.Hq + kvh * kG + (lane & 3)) * L + qq) * (g.K + g.win) + slot;
-      lds_load16(p, tb.st);
-    }
+  for (int x4 = 0; x4 < 4; ++x4) {
+    const int x = (w & 1) * 4 + x4;            // rows 4x .. 4x + 3
+    const int r = 4 * x + (lane >> 4);         // this lane's slot: row r, position lane % 16
+    const int c = (lane & 15) ^ (2 * (r & 3)); // the chunk that belongs there
+    const int e = e0 + (r >> 2);
+    const int qq = eq[es[e] != 0xff ? e : e0];
+    lds_load16(src + ((size_t)(b * g.Hq + kvh * kG + (r & 3)) * L + qq) * kD + 8 * c, dst + 64 * x);
   }
+  if (w == 2 && lane < 32) {   // the row table: row r = (query r/4, head r%4)
+    const int ee = e0 + (lane >> 2);
+    const int sl = es[ee];
+    const int qq = eq[sl != 0xff ? ee : e0];
+    const int slot = sl != 0xff ? sl : es[e0];
+    const float4* p = ws.stats + ((size_t)(b * g.Hq + kvh * kG + (lane & 3)) * L + qq) * (g.K + g.win) + slot;
+    lds_load16(p, tb.st);
+  }
+}
+
+// B operand half of dV / dK for dims 16db..16db+15: the four heads of query
+// slot qs (rows 4qs .. 4qs+3) at dim 16db + l%16, by an LDS transpose read:
+// source lane t of a 16-lane group points at row 4qs + t/4, dims 16db + 4(t%4)
+// .. +3; lane i then holds the four rows at dim 16db + i.
+__device__ __forceinline__ uint2 tile_heads_at_dim(const uint4* __restrict__ tile, int qs, int db) {
+  const int t = lane_id() & 15;
+  const int r = 4 * qs + (t >> 2);
+  const int c = 2 * db + ((t & 3) >> 1);
+  const char* p = reinterpret_cast<const char*>(tile + tile_pos(r, c)) + 8 * (t & 1);
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+  uint2 u;
+  __builtin_memcpy(&u, &v, 8);
+  return u;
 }
 
 // One tile: start copying the next tile into `nxt`, then accumulate this one.
@@ -719,8 +697,9 @@ __device__ __forceinline__ void chunk_tile_step(
     f32x4 as = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      as = mfma(as_bf16x8(tb.qa[(mt * 4 + ks) * kWave + lane]), kB[ks], as);
-      au = mfma(as_bf16x8(tb.da[(mt * 4 + ks) * kWave + lane]), vB[ks], au);
+      const int pos = tile_pos(16 * mt + (lane & 15), 4 * ks + (lane >> 4));
+      as = mfma(as_bf16x8(tb.qn[pos]), kB[ks], as);
+      au = mfma(as_bf16x8(tb.dn[pos]), vB[ks], au);
     }
     s[mt] = as;
     u[mt] = au;
@@ -745,17 +724,13 @@ __device__ __forceinline__ void chunk_tile_step(
     }
   }
   const bf16x8 Awp = pack_bf16x8(a8), Adl = pack_bf16x8(d8);
-  const uint16_t* qi0 = reinterpret_cast<const uint16_t*>(tb.qi) + (lane >> 4) * kD * kG;
-  const uint16_t* qi1 = qi0 + 4 * kD * kG;
-  const uint16_t* di0 = reinterpret_cast<const uint16_t*>(tb.di) + (lane >> 4) * kD * kG;
-  const uint16_t* di1 = di0 + 4 * kD * kG;
+  const int qs0 = lane >> 4, qs1 = 4 + (lane >> 4);   // k-slots: rows of query slots l/16 and 4 + l/16
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const int col = (16 * db + (lane & 15)) * kG;
-    const uint2 q0 = *reinterpret_cast<const uint2*>(qi0 + col);
-    const uint2 q1 = *reinterpret_cast<const uint2*>(qi1 + col);
-    const uint2 d0 = *reinterpret_cast<const uint2*>(di0 + col);
-    const uint2 d1 = *reinterpret_cast<const uint2*>(di1 + col);
+    const uint2 q0 = tile_heads_at_dim(tb.qn, qs0, db);
+    const uint2 q1 = tile_heads_at_dim(tb.qn, qs1, db);
+    const uint2 d0 = tile_heads_at_dim(tb.dn, qs0, db);
+    const uint2 d1 = tile_heads_at_dim(tb.dn, qs1, db);
     dv[db] = mfma(Awp, as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dv[db]);
     dk[db] = mfma(Adl, as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dk[db]);
     if (w == 0) {
