@@ -200,7 +200,8 @@ def make_host_inputs(cfg, lazy_kv=None):
         out["k"] = LazyNormalBF16(cfg["seed"], "k", kv_shape, as_bf16)
         out["v"] = LazyNormalBF16(cfg["seed"], "v", kv_shape, as_bf16)
     else:
-        out["k"] = _store(cfg, _draw(cfg, "k", kv_shape))
+        # kscale: keys of a larger norm (logits far below the norm bound of a row)
+        out["k"] = _store(cfg, _draw(cfg, "k", kv_shape, scale=float(cfg.get("kscale", 1.0))))
         out["v"] = _store(cfg, _draw(cfg, "v", kv_shape))
     recipe = cfg["lmk"]
     if recipe == "chunk_mean":

@@ -57,6 +57,10 @@ GENERIC_CASES = {
     # MFMA prefill path (bf16, d=128, S=64, causal, L % 64 == 0, G in {1,2,4}, K <= 32)
     "mfma_g4_k16": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=16,
                          lmk="chunk_mean", seed=6),
+    # keys 24x larger: logits of tens (in natural-log units) with spreads far
+    # beyond the N(0,1) workloads
+    "mfma_large_keys": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=16,
+                             lmk="chunk_mean", seed=7, kscale=24.0),
     "mfma_g2_k8_bias": _case(B=2, Hq=4, Hkv=2, d=128, Lq=2048, Lkv=2048, S=64, K=8, bias=0.3,
                              seed=7),
     "mfma_g1_k32": _case(B=1, Hq=2, Hkv=2, d=128, Lq=4096, Lkv=4096, S=64, K=32, seed=8),
