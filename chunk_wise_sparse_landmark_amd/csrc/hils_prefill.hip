@@ -46,6 +46,9 @@ constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kWin = 64;         // queries per window (one chunk), both kernels
 constexpr int kBlocks = kWin / 4;          // 16 query blocks of 4 queries
 constexpr int kBlocksPerWave = kBlocks / kAttWaves;
+// rows searched together by the select kernel's waves: with 4 or 8 candidate
+// blocks per row the score table fills the LDS (one wave per SIMD)
+constexpr int sel_rows(int R) { return R >= 4 ? 8 : 1; }
 constexpr int kMaxKf = 32;       // top-K bound on this path
 constexpr int kMaxNC = 512;      // chunks bound on this path (L <= 32768)
 constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
@@ -54,41 +57,74 @@ constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
 
 // ----------------------------------------------------------------------------
 // Top-K of R composite keys per lane (candidate c = r*64 + lane, key 0 =
-// empty), written as ascending chunk ids (-1 padded) to dst[0..K).  The K-th
+// empty), written as ascending chunk ids (-1 padded) to dst[n*dstride ..).  The K-th
 // largest key is found bit by bit from the top with wave ballots (count of
 // keys >= prefix); keys are unique, so exactly the keys >= it are selected.
-// With chunk ids below R*64 = 2^b the low word of every key is ~id with bits
-// b..31 set, so only the 32 score bits and the b id bits are searched.
+// The 32 score bits are searched first with 32-bit compares of the keys' high
+// words; only a tie at the K-th score (or a zero score word among the top K)
+// needs the id bits: with chunk ids below R*64 = 2^b the low word of every key
+// is ~id with bits b..31 set, so b bits are searched.
 // ----------------------------------------------------------------------------
-template <int R>
-__device__ __forceinline__ void select_ascending(const uint64_t (&keys)[R], int K, int32_t* dst) {
+// NR rows are searched together: their ballot and scalar chains are
+// independent, so they overlap where a single row's chain would wait.
+template <int R, int NR>
+__device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], int K, int32_t* dst,
+                                                 size_t dstride) {
   const int lane = lane_id();
-  uint64_t p = 0;
-  for (int bit = 63; bit >= 32; --bit) {
-    const uint64_t t = p | (1ull << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[r] >= t));
-    if (cnt >= K) p = t;
-  }
   constexpr int kIdBits = R == 1 ? 6 : (R == 2 ? 7 : (R == 4 ? 8 : 9));
-  p |= static_cast<uint64_t>(0xffffffffu << kIdBits);
-  for (int bit = kIdBits - 1; bit >= 0; --bit) {
-    const uint64_t t = p | (1ull << bit);
-    int cnt = 0;
+  uint64_t p[NR];
+  // the score word first, with 32-bit compares of the keys' high words
+  uint32_t ph[NR];
+  int nge[NR];
 #pragma unroll
-    for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[r] >= t));
-    if (cnt >= K) p = t;
-  }
-  int base = 0;
+  for (int n = 0; n < NR; ++n) { ph[n] = 0u; nge[n] = 0; }
+  for (int bit = 31; bit >= 0; --bit) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool pred = keys[r] != 0ull && keys[r] >= p;
-    const uint64_t m = __ballot(pred);
-    if (pred) dst[base + mask_rank(m)] = r * kWave + lane;
-    base += __popcll(m);
+    for (int n = 0; n < NR; ++n) {
+      const uint32_t th = ph[n] | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(static_cast<uint32_t>(keys[n][r] >> 32) >= th));
+      if (cnt >= K) { ph[n] = th; nge[n] = cnt; }
+    }
   }
-  for (int x = base + lane; x < K; x += kWave) dst[x] = -1;
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    p[n] = static_cast<uint64_t>(ph[n]) << 32;
+    if (ph[n] == 0u) {
+      // fewer than K valid keys (then all of them), or a zero score word among the top K
+      p[n] = 1ull;
+      int nvalid = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) nvalid += __popcll(__ballot(keys[n][r] != 0ull));
+      if (nvalid > K) nge[n] = K + 1;
+    }
+    if (nge[n] > K) {
+      // a tie at the K-th score word: the id bits decide
+      uint64_t q = (p[n] == 1ull ? 0ull : p[n]) | static_cast<uint64_t>(0xffffffffu << kIdBits);
+      for (int bit = kIdBits - 1; bit >= 0; --bit) {
+        const uint64_t t = q | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(keys[n][r] >= t));
+        if (cnt >= K) q = t;
+      }
+      p[n] = q;
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    int32_t* d = dst + n * dstride;
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool pred = keys[n][r] != 0ull && keys[n][r] >= p[n];
+      const uint64_t m = __ballot(pred);
+      if (pred) d[base + mask_rank(m)] = r * kWave + lane;
+      base += __popcll(m);
+    }
+    for (int x = base + lane; x < K; x += kWave) d[x] = -1;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -193,15 +229,20 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     reinterpret_cast<uint4*>(vdst)[f] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 
-  for (int qq = 0; qq < 16; ++qq) {
-    const int qrow = w * 16 + qq;
-    uint64_t keys[R];
+  // the wave's 16 rows, NR at a time (one wave per SIMD when the score table
+  // is large: the interleaved searches hide each other's latency)
+  constexpr int NR = sel_rows(R);
+  for (int q0 = 0; q0 < 16; q0 += NR) {
+    uint64_t keys[NR][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int c = r * kWave + lane;
-      keys[r] = c < ncand ? make_key(gs[qrow][c], c) : 0ull;
-    }
-    select_ascending<R>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + qrow) * g.K);
+    for (int n = 0; n < NR; ++n)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int c = r * kWave + lane;
+        keys[n][r] = c < ncand ? make_key(gs[w * 16 + q0 + n][c], c) : 0ull;
+      }
+    select_ascending<R, NR>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + w * 16 + q0) * g.K,
+                            (size_t)g.K);
   }
 }
 
