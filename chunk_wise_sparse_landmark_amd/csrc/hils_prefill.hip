@@ -48,7 +48,7 @@ constexpr int kBlocks = kWin / 4;          // 16 query blocks of 4 queries
 constexpr int kBlocksPerWave = kBlocks / kAttWaves;
 // rows searched together by the select kernel's waves: with 4 or 8 candidate
 // blocks per row the score table fills the LDS (one wave per SIMD)
-constexpr int sel_rows(int R) { return R >= 4 ? 8 : 1; }
+constexpr int sel_rows(int R) { return R >= 4 ? 1 : 1; }
 constexpr int kMaxKf = 32;       // top-K bound on this path
 constexpr int kMaxNC = 512;      // chunks bound on this path (L <= 32768)
 constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
@@ -67,12 +67,10 @@ constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
 // ----------------------------------------------------------------------------
 // NR rows are searched together: their ballot and scalar chains are
 // independent, so they overlap where a single row's chain would wait.
-template <int R, int NR>
-__device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], int K, int32_t* dst,
-                                                 size_t dstride) {
-  const int lane = lane_id();
-  constexpr int kIdBits = R == 1 ? 6 : (R == 2 ? 7 : (R == 4 ? 8 : 9));
-  uint64_t p[NR];
+// The floor p[n] of row n's top K: the nonzero keys >= p[n] are exactly its
+// min(K, valid) largest.  kIdBits: the id bits a key's low word can vary in.
+template <int R, int NR, int kIdBits>
+__device__ __forceinline__ void floor_search(const uint64_t (&keys)[NR][R], int K, uint64_t (&p)[NR]) {
   // the score word first, with 32-bit compares of the keys' high words
   uint32_t ph[NR];
   int nge[NR];
@@ -111,6 +109,64 @@ __device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], 
       }
       p[n] = q;
     }
+  }
+}
+
+template <int R, int NR>
+__device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], int K, int32_t* dst,
+                                                 size_t dstride, uint64_t* buf) {
+  const int lane = lane_id();
+  constexpr int kIdBits = R == 1 ? 6 : (R == 2 ? 7 : (R == 4 ? 8 : 9));
+  uint64_t p[NR];
+  if (R >= 4) {
+    // every top-K key is >= the K-th largest lane maximum; when at most 64 keys
+    // are, the search runs over those alone, one per lane
+    uint64_t lm[NR][1];
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+      lm[n][0] = keys[n][0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) lm[n][0] = keys[n][r] > lm[n][0] ? keys[n][r] : lm[n][0];
+    }
+    uint64_t tau[NR];
+    floor_search<1, NR, kIdBits>(lm, K, tau);
+    int most = 0;
+    int cnt[NR];
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+      cnt[n] = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) cnt[n] += __popcll(__ballot(keys[n][r] != 0ull && keys[n][r] >= tau[n]));
+      most = cnt[n] > most ? cnt[n] : most;
+    }
+    if (most <= kWave) {
+      uint64_t k1[NR][1];
+#pragma unroll
+      for (int n = 0; n < NR; ++n) {
+        int base = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool pred = keys[n][r] != 0ull && keys[n][r] >= tau[n];
+          const uint64_t m = __ballot(pred);
+          if (pred) buf[n * kWave + base + mask_rank(m)] = keys[n][r];
+          base += __popcll(m);
+        }
+        if (lane >= base) buf[n * kWave + lane] = 0ull;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int n = 0; n < NR; ++n) k1[n][0] = buf[n * kWave + lane];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      floor_search<1, NR, kIdBits>(k1, K, p);
+    } else {
+      floor_search<R, NR, kIdBits>(keys, K, p);
+    }
+  } else {
+    floor_search<R, NR, kIdBits>(keys, K, p);
   }
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
@@ -230,8 +286,12 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   }
 
   // the wave's 16 rows, NR at a time (one wave per SIMD when the score table
-  // is large: the interleaved searches hide each other's latency)
+  // is large: the interleaved searches hide each other's latency); the V
+  // staging area is each wave's compaction buffer from here on
   constexpr int NR = sel_rows(R);
+  __syncthreads();
+  uint64_t* sbuf = reinterpret_cast<uint64_t*>(vs) + w * (kS * kD / 4 / (kThreads / kWave));
+  static_assert(NR * kWave <= kS * kD / 4 / (kThreads / kWave), "compaction buffer");
   for (int q0 = 0; q0 < 16; q0 += NR) {
     uint64_t keys[NR][R];
 #pragma unroll
@@ -242,7 +302,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
         keys[n][r] = c < ncand ? make_key(gs[w * 16 + q0 + n][c], c) : 0ull;
       }
     select_ascending<R, NR>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + w * 16 + q0) * g.K,
-                            (size_t)g.K);
+                            (size_t)g.K, sbuf);
   }
 }
 
