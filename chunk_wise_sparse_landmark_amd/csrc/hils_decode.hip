@@ -419,13 +419,28 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
 // the retrieval score, P rounded to bf16 pairs of consecutive keys, and o_c for
 // dims 2 lane, 2 lane + 1 as pair dots of P with V columns gathered by byte
 // permutes.
+// Keys r0 .. r0+3 (r0 % 4 == 0) at dim 16db + l%16 of the swizzled V rows, by
+// an LDS transpose read: source lane t of a 16-lane group points at key
+// r0 + t/4, dims 16db + 4(t%4) .. +3; lane i receives the four keys at dim
+// 16db + i.
+__device__ __forceinline__ uint2 v_rows4_at_dim(const uint4* __restrict__ vs, int r0, int db) {
+  const int t = lane_id() & 15;
+  const int row = r0 + (t >> 2);
+  const int slot = (2 * db + ((t & 3) >> 1)) ^ (2 * (row & 3));
+  const char* p = reinterpret_cast<const char*>(vs + row * (kD / 8) + slot) + 8 * (t & 1);
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+  uint2 u;
+  __builtin_memcpy(&u, &v, 8);
+  return u;
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // (80 registers: six waves per SIMD, so six workgroups per CU)
-__global__ void __launch_bounds__(kThreads, 6)
+__global__ void __launch_bounds__(kThreads)
 decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
                const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
@@ -433,6 +448,7 @@ decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16
   __shared__ __attribute__((aligned(16))) uint4 vs[kS * kD / 8];
   __shared__ float lg[4][kS];
   __shared__ __attribute__((aligned(16))) uint16_t pb[4][kS];
+  __shared__ float sc[4];
   __shared__ int ca[8], cn[8], cc[8];
   const int split = blockIdx.x, bkv = blockIdx.y;
   const int nsplit = gridDim.x;
@@ -456,9 +472,13 @@ decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16
     ca[tid] = a; cn[tid] = n; cc[tid] = c;
   }
   const uint16_t* qg = q + (size_t)(b * g.Hq + kvh * 4) * kD;
-  uint4 qh[4];
+  // B operand of S^T = K Q^T: column n < 4 is head n (dims 32ks + 8(l/16) ..
+  // +7 in lane l), the other twelve columns zero
+  bf16x8 qb[4];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) qh[h] = reinterpret_cast<const uint4*>(qg + h * kD)[cs];
+  for (int ks = 0; ks < 4; ++ks)
+    qb[ks] = cs < 4 ? as_bf16x8(reinterpret_cast<const uint4*>(qg + cs * kD + 32 * ks + 8 * (lane >> 4))[0])
+                    : as_bf16x8(make_uint4(0, 0, 0, 0));
   const uint32_t qrv = reinterpret_cast<const uint32_t*>(qr + (size_t)(b * g.Hq + kvh * 4 + w) * kD)[lane];
   __syncthreads();
 
@@ -468,24 +488,31 @@ decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16
   const float* Bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   const int wbase = w * kWave;
   const uint32_t* vw = reinterpret_cast<const uint32_t*>(vs);
-  float M = -INFINITY, Z = 0.f, O0 = 0.f, O1 = 0.f;     // head w, dims 2 lane, 2 lane + 1
+  // lane l of wave w: head l/16, dims 32w + l%16 and 32w + 16 + l%16
+  float M = -INFINITY, Z = 0.f, O0 = 0.f, O1 = 0.f;
 
   for (int s = 0; s < apc; ++s) {
     const int n = cn[s], c = cc[s];
     if (n == 0) continue;
     const uint4* Kc = reinterpret_cast<const uint4*>(Kb + (size_t)ca[s] * kD);
     const uint4* Vc = reinterpret_cast<const uint4*>(Vb + (size_t)ca[s] * kD);
-    uint4 kr[4];
+    // A operand: wave w's keys 16w + l%16, dims 32ks + 8(l/16) .. +7
+    bf16x8 kr[4];
+    {
+      const int key = 16 * w + (lane & 15);
 #pragma unroll
-    for (int p4 = 0; p4 < 4; ++p4) {
-      const int idx = p4 * kThreads + tid;
-      kr[p4] = idx / (kD / 8) < n ? Kc[idx] : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks)
+        kr[ks] = key < n ? as_bf16x8(Kc[key * (kD / 8) + 4 * ks + (lane >> 4)]) : as_bf16x8(make_uint4(0, 0, 0, 0));
     }
+    // V rows into LDS row-major, chunk j of row r at position j ^ 2(r%4) (so
+    // that the transpose reads below hit distinct banks); rows past a partial
+    // chunk are zero
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int idx = x * kThreads + tid;
-      if (idx / (kD / 8) < n)
-        __builtin_amdgcn_global_load_lds((const void*)(Vc + idx),
+      const int idx = x * kThreads + tid;             // LDS position: row idx/16, slot idx%16
+      const int row = idx / (kD / 8);
+      if (row < n)
+        __builtin_amdgcn_global_load_lds((const void*)(Vc + row * (kD / 8) + ((idx & 15) ^ (2 * (row & 3)))),
                                          (__attribute__((address_space(3))) void*)(vs + x * kThreads + wbase),
                                          16, 0, 0);
       else
@@ -493,21 +520,18 @@ decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16
     }
     const uint32_t lm = c >= 0 ? reinterpret_cast<const uint32_t*>(Lb + (size_t)c * kD)[lane] : 0u;
     const float bc = (c >= 0 && Bb) ? Bb[c] : 0.f;
-    float pv[16];
-#pragma unroll
-    for (int p4 = 0; p4 < 4; ++p4)
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float d = dot2_bf16(kr[p4].x, qh[h].x, 0.f);
-        float e2 = dot2_bf16(kr[p4].y, qh[h].y, 0.f);
-        d = dot2_bf16(kr[p4].z, qh[h].z, d);
-        e2 = dot2_bf16(kr[p4].w, qh[h].w, e2);
-        pv[p4 * 4 + h] = d + e2;
-      }
     {
-      const float d = reduce_scatter16(pv, cs);
-      const int row = 16 * (cs >> 2) + (tid >> 4);
-      lg[cs & 3][row] = row < n ? g.scale * d : -INFINITY;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma(kr[ks], qb[ks], acc);
+      // lane l: head l%16 (valid below 4), keys 16w + 4(l/16) + i
+      if (cs < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * w + 4 * (lane >> 4) + i;
+          lg[cs][row] = row < n ? g.scale * acc[i] : -INFINITY;
+        }
+      }
     }
     __syncthreads();
     // head w: chunk softmax, P as bf16, retrieval score (window chunk: its lse)
@@ -517,37 +541,48 @@ decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16
     const float z = wave_sum(e);
     pb[w][lane] = f32_to_bf16(e * __builtin_amdgcn_rcpf(z));
     const float sv = c >= 0 ? g.scale * wave_sum(dot2_bf16(qrv, lm, 0.f)) + bc : m + __logf(z);
+    if (lane == 0) sc[w] = sv;
     __builtin_amdgcn_s_waitcnt(0);   // this thread's V copies have landed
     __syncthreads();
-    // o_c = P V for head w, dims 2 lane, 2 lane + 1 (rows past a partial chunk: zero)
-    const uint4* pw = reinterpret_cast<const uint4*>(pb[w]);
-    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    // o_c = P V by MFMA: head h is row 4h of the 16 (the other rows zero), so
+    // it comes out in lane group h; k = keys, columns = this wave's dims 32w ..
+    // 32w + 31.  P (A operand) from the bf16 rows above; V (B operand: 8 keys
+    // at one dim per lane) from LDS transpose reads, each handing a lane four
+    // consecutive keys at its dim
+    bf16x8 pa[2];
 #pragma unroll
-    for (int j8 = 0; j8 < kS / 8; ++j8) {
-      const uint4 pp = pw[j8];                         // P of keys 8 j8 .. 8 j8 + 7 (pairs)
-      const uint32_t pr[4] = {pp.x, pp.y, pp.z, pp.w};
+    for (int ks = 0; ks < 2; ++ks)
+      pa[ks] = (lane & 3) == 0
+                   ? as_bf16x8(*reinterpret_cast<const uint4*>(&pb[(lane & 15) >> 2][32 * ks + 8 * (lane >> 4)]))
+                   : as_bf16x8(make_uint4(0, 0, 0, 0));
+    f32x4 oc[2];
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int j = 8 * j8 + 2 * e4;
-        const uint32_t w0 = vw[j * (kD / 2) + lane], w1 = vw[(j + 1) * (kD / 2) + lane];
-        const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // dim 2 lane of keys j, j + 1
-        const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07060302u);   // dim 2 lane + 1
-        if (e4 & 1) { b0 = dot2_bf16(lo, pr[e4], b0); b1 = dot2_bf16(hi, pr[e4], b1); }
-        else        { a0 = dot2_bf16(lo, pr[e4], a0); a1 = dot2_bf16(hi, pr[e4], a1); }
+    for (int nt = 0; nt < 2; ++nt) {
+      oc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int r0 = 32 * ks + 8 * (lane >> 4);
+        const uint2 lo = v_rows4_at_dim(vs, r0, 2 * w + nt);
+        const uint2 hi = v_rows4_at_dim(vs, r0 + 4, 2 * w + nt);
+        oc[nt] = mfma(pa[ks], as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), oc[nt]);
       }
     }
-    const float o0 = a0 + b0, o1 = a1 + b1;
-    const float mn = fmaxf(M, sv);
-    const float fo = __expf(M - mn), fn = __expf(sv - mn);
-    Z = Z * fo + fn;
-    O0 = O0 * fo + fn * o0;
-    O1 = O1 * fo + fn * o1;
-    M = mn;
+    // lane l holds o_c[head l/16][dim 32w + 16nt + l%16] in oc[nt][0]
+    {
+      const float svh = sc[lane >> 4];
+      const float mn = fmaxf(M, svh);
+      const float fo = __expf(M - mn), fn = __expf(svh - mn);
+      Z = Z * fo + fn;
+      O0 = O0 * fo + fn * oc[0][0];
+      O1 = O1 * fo + fn * oc[1][0];
+      M = mn;
+    }
     __syncthreads();
   }
-  float* ph = parts + (((size_t)bkv * nsplit + split) * 4 + w) * kPartStride;
-  reinterpret_cast<float2*>(ph)[lane] = make_float2(O0, O1);
-  if (lane == 0) { ph[kD] = M; ph[kD + 1] = Z; }
+  float* ph = parts + (((size_t)bkv * nsplit + split) * 4 + (lane >> 4)) * kPartStride;
+  ph[32 * w + (lane & 15)] = O0;
+  ph[32 * w + 16 + (lane & 15)] = O1;
+  if (w == 0 && (lane & 15) == 0) { ph[kD] = M; ph[kD + 1] = Z; }
 }
 
 // ----------------------------------------------------------------------------
