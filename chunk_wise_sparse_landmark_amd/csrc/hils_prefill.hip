@@ -18,8 +18,10 @@
 //     lane per fragment), so the attention kernel stages a chunk with plain
 //     coalesced copies and reads conflict-free 16-B fragments from LDS.
 //  2. prefill_attend  one workgroup per 64-query window = 16 query blocks of
-//     M = 4 queries x G = 4 heads = 16 rows.  Each wave owns four blocks and
-//     keeps their fp32 output tiles in MFMA accumulators across all chunks.
+//     M = 4 queries x G = 4 heads = 16 rows.  Each of the eight waves owns two
+//     blocks and keeps their fp32 output tiles in MFMA accumulators across all
+//     chunks; the two waves of a SIMD run out of phase (one does its O += P V
+//     a step late), so one's softmax overlaps the other's MFMA work.
 //     For every chunk of the window's union it computes S^T = K Q^T, the chunk
 //     softmax, and O += (w/Z) P V, where w is the row's fusion weight (0 for a
 //     row whose query did not select the chunk) and Z the chunk's softmax sum;
@@ -27,8 +29,9 @@
 //     scores of the window's rows against its union come from one MFMA pass and
 //     the local window's exact lse from a statistics pass over its chunks, so
 //     every fusion weight is final before any chunk is accumulated; the window
-//     chunks then enter with P = exp(l - LSE).  Chunk fragments are
-//     double-buffered in LDS: one barrier per chunk.
+//     chunks then enter with P = exp(l - LSE).  Chunk fragments are staged
+//     in LDS while the previous chunk is computed (K in two buffers, V in
+//     three for the lagging waves): one barrier per chunk.
 #include "hils_mfma.h"
 #include "hils_kernels.h"
 #include "hils_profile.h"
@@ -310,7 +313,11 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
 // 2. attention
 // ----------------------------------------------------------------------------
 struct AttendSmem {
-  uint4 kv[2][kChunkFrags * kWave];      // double-buffered chunk fragments (2 x 32 KB)
+  // staged chunk t: its K fragments in kb[t % 2], its V fragments in vb[t % 3]
+  // (a V buffer lives one step longer: the lagging waves multiply it in the
+  // step after its scores)
+  uint4 kb[2][16 * kWave];
+  uint4 vb[3][16 * kWave];
   float wts[kWin * kMaxKf * kG];          // (query, slot, head): score, then weight
   int sel[kWin * kMaxKf];
   uint8_t slotmap[kWin * kMaxNC];         // (query, chunk) -> slot, 0xff if not selected
@@ -320,18 +327,23 @@ struct AttendSmem {
   float lse2[kWin * kG];                  // (query, head): the row's LSE in log2 units
   int wcount[kAttWaves];
 };
+static_assert(sizeof(AttendSmem) <= 160 * 1024, "attention LDS exceeds one CU's 160 KB");
 
-// Start copying one chunk's 32 KB of fragments into an LDS buffer with direct
-// global->LDS loads (16 B per lane; lane i of a wave lands at the wave's LDS
-// base + 16 i).  Completion: s_waitcnt vmcnt(0), then a barrier.
-__device__ __forceinline__ void stage_async(const uint16_t* __restrict__ src, uint4* __restrict__ dst) {
+// Start copying one chunk's 16 KB of K fragments and 16 KB of V fragments
+// into two LDS buffers with direct global->LDS loads (16 B per lane; lane i of
+// a wave lands at the wave's LDS base + 16 i).  Completion: s_waitcnt
+// vmcnt(0), then a barrier.
+__device__ __forceinline__ void stage_async(const uint16_t* __restrict__ src, uint4* __restrict__ kdst,
+                                            uint4* __restrict__ vdst) {
+  static_assert(16 * kWave == 2 * kAttThreads, "two copies per thread for each half");
   const uint4* s = reinterpret_cast<const uint4*>(src);
   const int wbase = (threadIdx.x / kWave) * kWave;
 #pragma unroll
-  for (int x = 0; x < kChunkFrags * kWave / kAttThreads; ++x)
+  for (int x = 0; x < 4; ++x) {
+    uint4* dst = x < 2 ? kdst + x * kAttThreads : vdst + (x - 2) * kAttThreads;
     __builtin_amdgcn_global_load_lds((const void*)(s + x * kAttThreads + threadIdx.x),
-                                     (__attribute__((address_space(3))) void*)(dst + x * kAttThreads + wbase),
-                                     16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(dst + wbase), 16, 0, 0);
+  }
 }
 __device__ __forceinline__ void stage_wait() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -415,30 +427,28 @@ __device__ __forceinline__ void load_frags(const uint4* __restrict__ src, bf16x8
   for (int x = 0; x < 16; ++x) f[x] = as_bf16x8(src[x * kWave + lane]);
 }
 
-// One staged chunk against the wave's query blocks, in phases so the MFMA work
-// of one block overlaps the softmax of another: S^T of every active block, then
-// the softmaxes, then O += (rw / z) P V.  `act` has bit j set when block j takes
-// part (uniform over the wave); rw[j] is this lane's row weight.  kDirect (a
-// local-window chunk): P = exp(l - LSE) with rw[j] = the row's LSE in log2 units.
+// Scores, chunk softmax and P of one staged chunk for the wave's active query
+// blocks (`act` bit j: block j takes part, uniform over the wave); S^T of
+// every active block first, then the softmaxes, so the MFMA work of one block
+// overlaps the softmax of another.  rw[j] is this lane's row weight; P leaves
+// scaled by rw / z.  kDirect (a local-window chunk): P = exp(l - LSE) with
+// rw[j] = the row's LSE in log2 units.
 template <bool kMasked, bool kDirect>
-__device__ __forceinline__ void chunk_step(const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
-                                           const uint16_t* __restrict__ nsrc,
-                                           const bf16x8 (&qf)[kBlocksPerWave][4],
-                                           float sc2, unsigned act, const int (&vis)[kBlocksPerWave],
-                                           const float (&rw)[kBlocksPerWave],
-                                           f32x4 (&o)[kBlocksPerWave][8]) {
-  // the next chunk's direct global->LDS copy into the other buffer (disjoint
-  // from kvb: both are restrict, so the reads below need not wait for it)
-  if (nsrc) stage_async(nsrc, nxt);
+__device__ __forceinline__ void chunk_probs(const uint4* __restrict__ kbuf,
+                                            const bf16x8 (&qf)[kBlocksPerWave][4], float sc2,
+                                            unsigned act, const int (&vis)[kBlocksPerWave],
+                                            const float (&rw)[kBlocksPerWave],
+                                            bf16x8 (&pa)[kBlocksPerWave][2]) {
   f32x4 s[kBlocksPerWave][4];
   {
     bf16x8 kf[16];
-    load_frags(kvb, kf);
+    load_frags(kbuf, kf);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < kBlocksPerWave; ++j)
       if (act & (1u << j)) block_scores(kf, qf[j], s[j]);
+    __builtin_amdgcn_s_setprio(0);
   }
-  bf16x8 pa[kBlocksPerWave][2];
 #pragma unroll
   for (int j = 0; j < kBlocksPerWave; ++j) {
     if (act & (1u << j)) {
@@ -452,10 +462,15 @@ __device__ __forceinline__ void chunk_step(const uint4* __restrict__ kvb, uint4*
       }
     }
   }
-  // keep the V fragment loads after the softmax (register pressure)
-  __builtin_amdgcn_sched_barrier(0);
+}
+
+// O += P V for the active blocks of `act`, V from one staged chunk.
+__device__ __forceinline__ void chunk_pv(const uint4* __restrict__ vbuf, unsigned act,
+                                         const bf16x8 (&pa)[kBlocksPerWave][2],
+                                         f32x4 (&o)[kBlocksPerWave][8]) {
   bf16x8 vf[16];
-  load_frags(kvb + 16 * kWave, vf);
+  load_frags(vbuf, vf);
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int j = 0; j < kBlocksPerWave; ++j)
     if (act & (1u << j)) {
@@ -464,21 +479,54 @@ __device__ __forceinline__ void chunk_step(const uint4* __restrict__ kvb, uint4*
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) o[j][db] = mfma(pa[j][ks], vf[db * 2 + ks], o[j][db]);
     }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// One accumulation step.  The two waves that share a SIMD run it out of phase:
+// a leading wave does this chunk's scores and softmax, then its O += P V; a
+// lagging wave first does O += P V of the previous step's chunk (P and the
+// block mask kept in pa / pact, V still staged), then this chunk's scores and
+// softmax.  So one wave's softmax (vector ALU) runs against the other's MFMA
+// work instead of both waves doing the same phase between two barriers.  The
+// next chunk's copy is started first, into buffers no wave reads in this step.
+template <bool kMasked, bool kDirect>
+__device__ __forceinline__ void chunk_step(bool lag, const uint4* __restrict__ kbuf,
+                                           const uint4* __restrict__ vbuf,
+                                           const uint4* __restrict__ vprev,
+                                           uint4* __restrict__ knx, uint4* __restrict__ vnx,
+                                           const uint16_t* __restrict__ nsrc,
+                                           const bf16x8 (&qf)[kBlocksPerWave][4], float sc2,
+                                           unsigned act, const int (&vis)[kBlocksPerWave],
+                                           const float (&rw)[kBlocksPerWave], unsigned& pact,
+                                           bf16x8 (&pa)[kBlocksPerWave][2],
+                                           f32x4 (&o)[kBlocksPerWave][8]) {
+  if (nsrc) stage_async(nsrc, knx, vnx);
+  if (lag) {
+    if (pact) chunk_pv(vprev, pact, pa, o);
+    __builtin_amdgcn_sched_barrier(0);
+    chunk_probs<kMasked, kDirect>(kbuf, qf, sc2, act, vis, rw, pa);
+  } else {
+    chunk_probs<kMasked, kDirect>(kbuf, qf, sc2, act, vis, rw, pa);
+    // keep the V fragment loads after the softmax (register pressure)
+    __builtin_amdgcn_sched_barrier(0);
+    chunk_pv(vbuf, act, pa, o);
+  }
+  pact = act;
 }
 
 // Statistics of one staged local-window chunk for every block of the wave: the
 // chunk's row max (log2 units) and sum are folded into the running (M2, Z).
 template <bool kMasked>
-__device__ __forceinline__ void window_stats_step(const uint4* __restrict__ kvb,
-                                                  uint4* __restrict__ nxt,
+__device__ __forceinline__ void window_stats_step(const uint4* __restrict__ kbuf,
+                                                  uint4* __restrict__ knx, uint4* __restrict__ vnx,
                                                   const uint16_t* __restrict__ nsrc,
                                                   const bf16x8 (&qf)[kBlocksPerWave][4], float sc2,
                                                   const int (&vis)[kBlocksPerWave],
                                                   float (&M2)[kBlocksPerWave],
                                                   float (&Z)[kBlocksPerWave]) {
-  if (nsrc) stage_async(nsrc, nxt);
+  if (nsrc) stage_async(nsrc, knx, vnx);
   bf16x8 kf[16];
-  load_frags(kvb, kf);
+  load_frags(kbuf, kf);
 #pragma unroll
   for (int j = 0; j < kBlocksPerWave; ++j) {
     f32x4 st[4];
@@ -566,7 +614,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   auto csrc = [&](int c) -> const uint16_t* { return KVg + (size_t)c * kChunkElems; };
   __syncthreads();                        // the union list is complete
   const uint16_t* first_src = nwin > 0 ? csrc(own) : (nunion > 0 ? csrc(sm.ulist[0]) : nullptr);
-  if (first_src) stage_async(first_src, sm.kv[0]);
+  if (first_src) stage_async(first_src, sm.kb[0], sm.vb[0]);
 
   // ---- retrieval scores of (row, selected chunk) by MFMA: rows x union columns,
   //      from the retrieval query's fragments (the query itself unless a
@@ -614,7 +662,7 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   //      chunk visible to query qi when kk <= qi, as the window is the chunk;
   //      the other window chunks are complete: vis = kS)
   const float sc2 = scale * 1.4426950408889634f;   // scale * log2(e)
-  int cur = 0;
+  int t = 0;                              // staged chunk: K in kb[t % 2], V in vb[t % 3]
   if (nwin > 0) {
     float M2[kBlocksPerWave], Z[kBlocksPerWave];
     int vis_own[kBlocksPerWave], vis_full[kBlocksPerWave];
@@ -627,11 +675,12 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     }
     for (int x = 0; x < nwin; ++x) {
       const bool last = x + 1 == nwin;
-      window_stats_step<true>(sm.kv[cur], sm.kv[cur ^ 1], last ? nullptr : csrc(own - x - 1), qf,
-                              sc2, x == 0 ? vis_own : vis_full, M2, Z);
+      window_stats_step<true>(sm.kb[t & 1], sm.kb[(t + 1) & 1], sm.vb[(t + 1) % 3],
+                              last ? nullptr : csrc(own - x - 1), qf, sc2,
+                              x == 0 ? vis_own : vis_full, M2, Z);
       stage_wait();
       __syncthreads();
-      if (!last) cur ^= 1;
+      if (!last) ++t;
     }
     // natural-log lse of the window's visible tokens: (M2 + log2 Z) * ln 2
 #pragma unroll
@@ -663,7 +712,12 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
 
   // ---- the window chunks (P = exp(l - LSE)) from own - nwin + 1 (still
   //      staged) up to the own chunk, then the union; the next chunk is copied
-  //      into the other buffer while one is computed
+  //      into free buffers while one is computed.  Waves 4..7 lag one step
+  //      behind in their O += P V (each SIMD holds one leading and one lagging
+  //      wave when waves are placed round-robin).
+  const bool lag = w >= kAttWaves / 2;
+  unsigned pact = 0;
+  bf16x8 pa[kBlocksPerWave][2];
   if (nwin > 0) {
     int vis_own[kBlocksPerWave], vis_full[kBlocksPerWave];
     float rw[kBlocksPerWave];
@@ -675,15 +729,16 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       rw[j] = sm.lse2[qi * kG + (r16 & 3)];
     }
     const unsigned all = (1u << kBlocksPerWave) - 1;
-    for (int y = nwin - 1; y >= 0; --y, cur ^= 1) {
+    for (int y = nwin - 1; y >= 0; --y, ++t) {
       const uint16_t* nsrc = y > 0 ? csrc(own - y + 1) : (nunion > 0 ? csrc(sm.ulist[0]) : nullptr);
-      chunk_step<true, true>(sm.kv[cur], sm.kv[cur ^ 1], nsrc, qf, sc2, all,
-                             y == 0 ? vis_own : vis_full, rw, o);
+      chunk_step<true, true>(lag, sm.kb[t & 1], sm.vb[t % 3], sm.vb[(t + 2) % 3], sm.kb[(t + 1) & 1],
+                             sm.vb[(t + 1) % 3], nsrc, qf, sc2, all, y == 0 ? vis_own : vis_full,
+                             rw, pact, pa, o);
       stage_wait();
       __syncthreads();
     }
   }
-  for (int u = 0; u < nunion; ++u, cur ^= 1) {
+  for (int u = 0; u < nunion; ++u, ++t) {
     const int c = sm.ulist[u];
     const uint64_t qmk = sm.qmask[c];
     unsigned act = 0;
@@ -699,10 +754,14 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       rw[j] = slot != 0xff ? sm.wts[(qi * K + slot) * kG + (r16 & 3)] : 0.f;
     }
     const uint16_t* nsrc = u + 1 < nunion ? csrc(sm.ulist[u + 1]) : nullptr;
-    chunk_step<false, false>(sm.kv[cur], sm.kv[cur ^ 1], nsrc, qf, sc2, act, vis, rw, o);
+    chunk_step<false, false>(lag, sm.kb[t & 1], sm.vb[t % 3], sm.vb[(t + 2) % 3],
+                             sm.kb[(t + 1) & 1], sm.vb[(t + 1) % 3], nsrc, qf, sc2, act, vis, rw,
+                             pact, pa, o);
     stage_wait();
     __syncthreads();
   }
+  // the lagging waves' last O += P V (the last chunk's V is still staged)
+  if (lag && pact) chunk_pv(sm.vb[(t + 2) % 3], pact, pa, o);
 
   // ---- output: lane holds O[row 4*g4 + i][16*db + r16] of each block;
   //      row 4*g4 + i = (query 4*blk + g4, head i)
