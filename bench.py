@@ -48,14 +48,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "chunk_wise_sparse_landmark_amd", "csrc")
 # source files whose text fixes each timed kernel's machine code
 KERNEL_SOURCES = {
-    "prefill_attend": ["hils_prefill.hip", "hils_common.h"],
-    "prefill_select": ["hils_prefill.hip", "hils_common.h"],
-    "decode_attend": ["hils_decode.hip", "hils_common.h"],
-    "decode_score": ["hils_decode.hip", "hils_common.h"],
+    "prefill_attend": ["hils_prefill.hip", "hils_mfma.h", "hils_common.h"],
+    "prefill_select": ["hils_prefill.hip", "hils_mfma.h", "hils_common.h"],
+    "decode_attend": ["hils_decode.hip", "hils_mfma.h", "hils_common.h"],
+    "decode_score": ["hils_decode.hip", "hils_mfma.h", "hils_common.h"],
     "generic_attend": ["hils_generic.hip", "hils_common.h"],
     "generic_bwd_chunks": ["hils_generic.hip", "hils_common.h"],
-    "prefill_bwd_chunks": ["hils_prefill_bwd.hip", "hils_common.h"],
-    "prefill_bwd_rows": ["hils_prefill_bwd.hip", "hils_common.h"],
+    "prefill_bwd_chunks": ["hils_prefill_bwd.hip", "hils_mfma.h", "hils_common.h"],
+    "prefill_bwd_rows": ["hils_prefill_bwd.hip", "hils_mfma.h", "hils_common.h"],
     "landmarks": ["hils_landmarks.hip", "hils_common.h"],
     "landmarks_bwd": ["hils_landmarks.hip", "hils_common.h"],
 }

@@ -410,15 +410,15 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
   }
 }
 
-// G = 4: the same walk with the arithmetic on packed bf16 pairs, so that a
+// G = 4: the same walk with both products on 16x16x32 bf16 MFMA, so that a
 // workgroup needs few registers and 18 KB of LDS and many stay resident while
-// others wait for their chunks.  Thread t holds K dims 8(t%16)..+7 of rows
-// 16p + t/16 (1 KB of consecutive rows per load) and the matching dims of the
-// four queries; each (key, head) dot product is four bf16 pair dots summed over
-// the 16-lane group by a butterfly.  Wave w then owns head w: its chunk softmax,
-// the retrieval score, P rounded to bf16 pairs of consecutive keys, and o_c for
-// dims 2 lane, 2 lane + 1 as pair dots of P with V columns gathered by byte
-// permutes.
+// others wait for their chunks.  Logits: wave w multiplies keys 16w .. 16w+15
+// (A operand, straight from the K rows in registers) by the four queries (B
+// operand columns 0..3, the other twelve zero).  Wave w then owns head w: its
+// chunk softmax, the retrieval score, and P rounded to bf16.  O_c = P V: the
+// four P rows sit in A rows 0, 4, 8, 12 (the rest zero), so one MFMA chain
+// serves every head, and V (copied to LDS with chunk c of row r stored at
+// position c ^ 2(r % 4)) comes in as the B operand by transpose reads.
 // Keys r0 .. r0+3 (r0 % 4 == 0) at dim 16db + l%16 of the swizzled V rows, by
 // an LDS transpose read: source lane t of a 16-lane group points at key
 // r0 + t/4, dims 16db + 4(t%4) .. +3; lane i receives the four keys at dim
@@ -439,7 +439,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// (80 registers: six waves per SIMD, so six workgroups per CU)
+// (88 registers: five waves per SIMD, so five workgroups per CU)
 __global__ void __launch_bounds__(kThreads)
 decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
                const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
