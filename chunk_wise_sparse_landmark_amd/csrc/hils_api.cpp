@@ -154,7 +154,7 @@ hils_status forward_like(int op, const hils_params* p, const void* q, const void
   const int bf16 = p->dtype == HILS_BF16;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const void* qr = q_ret ? q_ret : q;
-  hipGetLastError();   // clear a stale error so it is not reported as ours
+  (void)hipGetLastError();   // clear a stale error so it is not reported as ours
   if (op == HILS_OP_DECODE && hils::decode_fast_supported(g, bf16))
     return launch_status(
         hils::launch_decode_fast(g, q, qr, k, v, lmk, lmk_bias, out, sel_idx, lse, ws, st),
@@ -250,7 +250,7 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* q_ret
   const int bf16 = p->dtype == HILS_BF16;
   const void* qr = q_ret ? q_ret : q;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipGetLastError();
+  (void)hipGetLastError();   // clear a stale error so it is not reported as ours
   if (hils::prefill_bwd_fast_supported(g, bf16))
     return launch_status(hils::launch_prefill_bwd_fast(g, q, qr, k, v, lmk, lmk_bias, out, dout,
                                                        sel_idx, lse, dq, dq_ret, dk, dv, dlmk,
@@ -269,7 +269,7 @@ hils_status hils_landmarks(const hils_params* p, const void* lq, const void* k, 
   const bool full = p->seq_kv >= p->chunk_size;
   s = check_landmarks(p, {{lq, full}, {k, full}, {lmk, p->num_landmarks > 0}, {lmk_bias, false}});
   if (s != HILS_OK) return s;
-  hipGetLastError();
+  (void)hipGetLastError();   // clear a stale error so it is not reported as ours
   return launch_status(hils::launch_landmarks(geometry(p, HILS_OP_FORWARD), p->dtype == HILS_BF16,
                                               lq, k, lmk, lmk_bias,
                                               reinterpret_cast<hipStream_t>(stream)),
@@ -285,7 +285,7 @@ hils_status hils_landmarks_backward(const hils_params* p, const void* lq, const 
   s = check_landmarks(p, {{lq, full}, {k, p->seq_kv > 0}, {dlmk, full}, {dlmk_bias, false},
                           {dlq, p->num_landmarks > 0}, {dk, p->seq_kv > 0}});
   if (s != HILS_OK) return s;
-  hipGetLastError();
+  (void)hipGetLastError();   // clear a stale error so it is not reported as ours
   return launch_status(
       hils::launch_landmarks_backward(geometry(p, HILS_OP_FORWARD), p->dtype == HILS_BF16, lq, k,
                                       dlmk, dlmk_bias, dlq, dk,

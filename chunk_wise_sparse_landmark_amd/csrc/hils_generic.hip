@@ -484,8 +484,10 @@ hipError_t launch_generic_backward_t(const Geometry& g, const void* q, const voi
   const int gx = nck > g.NCcap ? nck : g.NCcap;
   if (gx > 0) {
     const size_t sm = (size_t)2 * g.S * g.d * sizeof(float);
-    hipFuncSetAttribute((const void*)generic_bwd_chunks_kernel<T>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    if (const hipError_t e = hipFuncSetAttribute((const void*)generic_bwd_chunks_kernel<T>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+        e != hipSuccess)
+      return e;
     prof_begin(kGenericBwdChunks, st);
     hipLaunchKernelGGL(generic_bwd_chunks_kernel<T>, dim3(gx, g.B * g.Hkv), dim3(kThreads), sm, st,
                        g, (const T*)q, (const T*)qr, (const T*)k, (const T*)v, (const T*)dout,

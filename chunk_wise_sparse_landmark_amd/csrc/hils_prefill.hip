@@ -812,8 +812,11 @@ hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* qr,
   else launch_select<8>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
   prof_end(kPrefillSelect, st);
   // dynamic LDS above 64 KB must be enabled for the kernel (per device; cheap)
-  hipFuncSetAttribute((const void*)prefill_attend, hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)sizeof(AttendSmem));
+  if (const hipError_t e = hipFuncSetAttribute((const void*)prefill_attend,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)sizeof(AttendSmem));
+      e != hipSuccess)
+    return e;
   prof_begin(kPrefillAttend, st);
   hipLaunchKernelGGL(prefill_attend, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kAttThreads),
                      sizeof(AttendSmem), st, g, Q, QR, kvf, Lm, bias, sel_idx, (uint16_t*)out, lse);

@@ -22,13 +22,16 @@ struct ProfileSlot {
 
 ProfileSlot& profile_slot();
 
+// A failed event record only loses that timing: the caller reads the events
+// back with hipEventElapsedTime, which then reports the error; the launch
+// status is not affected.
 inline void prof_begin(int kernel, hipStream_t st) {
   ProfileSlot& p = profile_slot();
-  if (p.kernel == kernel && p.next < p.n) hipEventRecord(p.starts[p.next], st);
+  if (p.kernel == kernel && p.next < p.n) (void)hipEventRecord(p.starts[p.next], st);
 }
 inline void prof_end(int kernel, hipStream_t st) {
   ProfileSlot& p = profile_slot();
-  if (p.kernel == kernel && p.next < p.n) hipEventRecord(p.stops[p.next++], st);
+  if (p.kernel == kernel && p.next < p.n) (void)hipEventRecord(p.stops[p.next++], st);
 }
 
 }  // namespace hils
