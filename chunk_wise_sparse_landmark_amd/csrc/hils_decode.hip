@@ -172,9 +172,11 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   const uint64_t run = wave_rank_sort64(sel, buf[w]);
   wl[w][lane] = lane < K ? run : 0ull;
   __syncthreads();
+  // the four wave lists merged in a tree: waves 0 and 2 in parallel, then wave 0
+  if (w == 0 || w == 2) wl[w][lane] = wave_merge_into(wl[w][lane], wl[w + 1][lane], K, buf[w]);
+  __syncthreads();
   if (w == 0) {
-    uint64_t t = wl[0][lane];
-    for (int x = 1; x < 4; ++x) t = wave_merge_into(t, wl[x][lane], K, buf[0]);
+    const uint64_t t = wave_merge_into(wl[0][lane], wl[2][lane], K, buf[0]);
     if (lane < K) lists[((size_t)bkv * nsplit + split) * K + lane] = t;
   }
 }
