@@ -650,10 +650,11 @@ DecodePlan plan(const Geometry& g) {
   const int t = g.Lkv - 1;
   p.ncand = max(0, min(t / kS - max(g.win - 1, 0), g.NC));   // chunks before the window
   const int bkv = g.B * g.Hkv;
-  // scoring: about 512 workgroups (all resident at once), each streaming up to
-  // kMaxIt blocks of 64 candidates per wave; fewer, longer splits also leave
-  // fewer lists to merge
-  const int want_splits = max(1, 512 / max(1, bkv));
+  // scoring: about 256 workgroups (one per CU), each streaming up to kMaxIt
+  // blocks of 64 candidates per wave; fewer, longer splits leave fewer lists
+  // to merge (at 16 x 8 (b, kv head) pairs and 2047 candidates, two splits of
+  // four blocks per wave beat four splits of two by about 2 us per step)
+  const int want_splits = max(1, 256 / max(1, bkv));
   const int per = (p.ncand + want_splits - 1) / want_splits;
   p.nit = min(kMaxIt, max(1, (per + 255) / 256));
   p.cps = 256 * p.nit;
