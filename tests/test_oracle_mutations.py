@@ -38,6 +38,13 @@ MUTATIONS = [
     # softmax backward removes any constant added to every dp_j)
     ("landmark_bwd_uncentred", "dl = p * (dp - float(p @ dp))", "dl = p * dp"),
     ("landmark_bwd_entropy_sign", "dp = kb @ dm - db * (logp + 1.0)", "dp = kb @ dm + db * (logp + 1.0)"),
+    ("query_position_shift", "t = Lkv - Lq + i", "t = Lkv - Lq + i - 1"),
+    ("window_gap", "first_local = own - max(w - 1, 0)", "first_local = own - w"),
+    ("window_chunk_short", "else (c * S, c * S + S)", "else (c * S, c * S + S - 1)"),
+    ("one_selection_short", "order[:min(K, len(cand))]", "order[:min(K - 1, len(cand))]"),
+    ("dq_without_score_term", 'res["dq"][h] = dq + dqr', 'res["dq"][h] = dq'),
+    ("dk_unscaled", "scale * np.outer(dl, q)", "np.outer(dl, q)"),
+    ("dlmk_unscaled", 'res["dlmk"].append((c, scale * ds * qr[h]))', 'res["dlmk"].append((c, ds * qr[h]))'),
 ]
 
 
