@@ -49,7 +49,7 @@ MUTATIONS = [
 
 
 def _copy_tree(dst):
-    for name in ("oracle", "hils_inputs"):
+    for name in ("oracle",):
         shutil.copytree(os.path.join(ROOT, name), os.path.join(dst, name),
                         ignore=shutil.ignore_patterns("__pycache__", "*.so", "*.o"))
     os.makedirs(os.path.join(dst, "tests"))
