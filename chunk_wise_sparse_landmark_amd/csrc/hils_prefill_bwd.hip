@@ -242,6 +242,7 @@ __device__ __forceinline__ void load16(const uint4* __restrict__ src, bf16x8 (&f
 // fragments; lane l gets keys 16mt + 4(l/16) + i of row l%16.
 __device__ __forceinline__ void keys_by_rows(const bf16x8 (&f)[16], const bf16x8 (&y)[4],
                                              f32x4 (&x)[4]) {
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -249,6 +250,7 @@ __device__ __forceinline__ void keys_by_rows(const bf16x8 (&f)[16], const bf16x8
     for (int ks = 0; ks < 4; ++ks) acc = mfma(f[mt * 4 + ks], y[ks], acc);
     x[mt] = acc;
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // dl (scaled values as bf16) in the A layout of dQ = dL K: k-slot (g4, j) <->
@@ -329,10 +331,12 @@ __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 kb[16];
   load16(kvb + 32 * kWave, kb);
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) dq[db] = mfma(pa[ks], kb[db * 2 + ks], dq[db]);
+  __builtin_amdgcn_s_setprio(0);
   return make_float4(w, lse2, ref, 0.f);
 }
 
