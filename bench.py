@@ -447,6 +447,8 @@ def run_decode(hl, cfg, steps, warmup, ev, nsets):
                              per_launch_bytes=kbytes))
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBS
     res["frac_of_hbm_peak"] = res["value"] / PEAK_HBM_GBS
+    # the generated queries and landmarks of set 0, for the CPU baseline
+    res["_host"] = (sets[0]["q"].float().cpu().numpy(), sets[0]["lmk"].float().cpu().numpy())
     del sets, outs
     torch.cuda.empty_cache()
     return res
@@ -546,30 +548,88 @@ def run_landmarks(hl, cfg, steps, warmup, ev, nsets):
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg, seconds):
-    """The CPU oracle, as it stands, on a bounded sample of the workload's queries."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_pool():
+    from oracle.pool import default_workers, make_pool, warm_up
+    workers = default_workers()
+    pool = make_pool(workers)
+    warm_up(pool, workers)
+    return pool, workers
+
+
+def _cpu_meta(workers):
+    return dict(cores=workers, host_cpus=os.cpu_count(), cpu_model=cpu_model(),
+                blas_threads_per_core=1, kind="oracle")
+
+
+def cpu_baseline_prefill(pool, workers, cfg, seconds):
+    """The CPU oracle, as it stands (fp64 numpy, one BLAS thread per process), on
+    all host cores: random blocks of 16 query positions of every (batch, kv head)
+    group, handed out to a process pool until ``seconds`` of wall time are spent."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
     from hils_inputs.configs import make_host_inputs
-    from oracle.hils_oracle import ref_forward
+    from oracle.pool import forward_tasks
     host = make_host_inputs(cfg)
     rng = np.random.default_rng(123)
+    groups = [(b, g) for b in range(cfg["B"]) for g in range(cfg["Hkv"])]
     order = rng.permutation(cfg["Lq"])
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]),
               local_chunks=local_chunks(cfg))
-    done, flops, t_used = 0, 0.0, 0.0
-    with threadpool_limits(limits=1):
-        while t_used < seconds and done < cfg["Lq"]:
-            qs = np.sort(order[done:done + 16])
-            t0 = time.perf_counter()
-            ref_forward(host["q"], host["k"], host["v"], host["lmk"], None, queries=qs, **kw)
-            t_used += time.perf_counter() - t0
+    per_group = 1.0 / (cfg["B"] * cfg["Hkv"])
+    done, flops, ntask, t_used = 0, 0.0, 0, 0.0
+    nblk = max(1, -(-2 * workers // len(groups)))     # at least two tasks per worker a round
+    while t_used < seconds and done < cfg["Lq"]:
+        blocks = [np.sort(order[x:x + 16]) for x in range(done, min(done + 16 * nblk, cfg["Lq"]), 16)]
+        tasks = [(b, g, qs) for (b, g) in groups for qs in blocks]
+        t0 = time.perf_counter()
+        forward_tasks(pool, host, tasks, **kw)
+        t_used += time.perf_counter() - t0
+        for qs in blocks:
             flops += forward_flops(cfg, queries=qs)
             done += len(qs)
-    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample="%d of %d query positions (random), all %d batch x kv-head groups, "
-                       "fp64 numpy, one thread, %.1f s" % (done, cfg["Lq"], cfg["B"] * cfg["Hkv"],
-                                                          t_used))
+        ntask += len(tasks)
+    r = dict(value=flops / t_used / 1e12, unit="TFLOP/s",
+             sample="%d of %d query positions (random, blocks of 16), all %d batch x kv-head "
+                    "groups (%d pool tasks), %.1f s wall" % (done, cfg["Lq"], len(groups), ntask,
+                                                              t_used))
+    r.update(_cpu_meta(workers))
+    return r
+
+
+def cpu_baseline_decode(pool, workers, cfg, host_q, host_lmk, seconds):
+    """The CPU oracle on the decode workload (input set 0: its queries and landmark
+    table as generated; K and V regenerated lazily, chunk by chunk): one pool task
+    per (batch, kv head) group, repeated until ``seconds`` of wall time are spent.
+    Throughput uses the GPU line's algorithmic bytes per step."""
+    from hils_inputs.configs import LazyNormalBF16
+    from oracle.pool import forward_tasks
+    shape = (cfg["B"], cfg["Hkv"], cfg["Lkv"], cfg["d"])
+    host = dict(q=host_q, lmk=host_lmk, bias=None, q_ret=None,
+                k=LazyNormalBF16(cfg["seed"], "k", shape), v=LazyNormalBF16(cfg["seed"], "v", shape))
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=bool(cfg["keep_own"]),
+              local_chunks=local_chunks(cfg))
+    tasks = [(b, g, [0]) for b in range(cfg["B"]) for g in range(cfg["Hkv"])]
+    total, _, _ = decode_bytes(cfg)
+    steps, t_used = 0, 0.0
+    while t_used < seconds and steps < 50:
+        t0 = time.perf_counter()
+        forward_tasks(pool, host, tasks, **kw)
+        t_used += time.perf_counter() - t0
+        steps += 1
+    r = dict(value=total * steps / t_used / 1e9, unit="GB/s", ms_per_step=1e3 * t_used / steps,
+             sample="%d whole decode steps (%d batch x kv-head pool tasks each), %.1f s wall"
+                    % (steps, len(tasks), t_used))
+    r.update(_cpu_meta(workers))
+    return r
 
 
 # --------------------------------------------------------------------------- main
@@ -580,7 +640,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and training lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", default=None, help="run one workload: prefill_8k, decode_128k, "
                                                      "decode_4m, train_8k, landmarks_8k, prefill_32k, "
                                                      "or prefill_8k, decode_128k, train_8k + _swa512")
@@ -677,15 +737,31 @@ def main():
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                 "data": "synthetic", "config": {"workload": r["workload"]},
                 "roofline": r.get("roofline")}
-        for key in ("selection", "backward_kernels", "forward_kernel", "frac_of_hbm_peak"):
+        for key in ("selection", "backward_kernels", "forward_kernel", "frac_of_hbm_peak", "_host"):
             if key in r:
                 line[key] = r[key]
     line["extra"] = extra
     if args.calibrate_copy:
         copy_calibration()
-    if not args.no_cpu and main_name is not None:
-        log("cpu baseline: oracle on a sample (~%.0f s)" % args.cpu_seconds)
-        line["cpu_baseline"] = cpu_baseline(config(main_name), args.cpu_seconds)
+    if not args.no_cpu:
+        pool, workers = _cpu_pool()
+        try:
+            if main_name is not None:
+                log("cpu baseline: oracle on %d cores, %s (~%.0f s)" % (workers, main_name,
+                                                                       args.cpu_seconds))
+                line["cpu_baseline"] = cpu_baseline_prefill(pool, workers, config(main_name),
+                                                            args.cpu_seconds)
+            for r in [line] + extra:
+                name = r.get("workload") or r.get("config", {}).get("workload")
+                if name in ("decode_128k", "decode_4m") and "_host" in r:
+                    log("cpu baseline: oracle on %d cores, %s (~%.0f s)" % (workers, name,
+                                                                           args.cpu_seconds / 2))
+                    r["cpu_baseline"] = cpu_baseline_decode(pool, workers, config(name),
+                                                            *r["_host"], args.cpu_seconds / 2)
+        finally:
+            pool.shutdown()
+    for r in [line] + extra:
+        r.pop("_host", None)
     print(json.dumps(line), flush=True)
 
 

@@ -112,8 +112,10 @@ size_t ws_bytes_for(const hils_params* p, int op) {
     case HILS_OP_DECODE:
       return hils::decode_fast_supported(g, bf16) ? round256(hils::decode_fast_ws(g)) : 0;
     case HILS_OP_BACKWARD:
-      return hils::prefill_bwd_fast_supported(g, bf16) ? round256(hils::prefill_bwd_fast_ws(g))
-                                                       : round256(hils::generic_backward_ws(g));
+      // the sanitised selection first, then the kernels' own scratch
+      return round256(hils::sanitized_selection_bytes(g)) +
+             (hils::prefill_bwd_fast_supported(g, bf16) ? round256(hils::prefill_bwd_fast_ws(g))
+                                                        : round256(hils::generic_backward_ws(g)));
     default:
       return 0;
   }
@@ -198,6 +200,30 @@ hils_status check_landmarks(const hils_params* p, std::initializer_list<Buf> buf
   return HILS_OK;
 }
 
+// hils_backward with no query rows (batch, heads_q or seq_q zero): the key-side
+// gradients it promises to overwrite are all zero.
+hils_status zero_key_grads(const hils_params* p, void* dk, void* dv, void* dlmk, float* dbias,
+                           void* stream) {
+  const size_t elem = p->dtype == HILS_BF16 ? 2 : 4;
+  const size_t groups = (size_t)p->batch * p->heads_kv;
+  const size_t kv = groups * p->seq_kv * p->head_dim * elem;
+  const size_t lm = groups * p->num_landmarks * p->head_dim * elem;
+  const size_t lb = groups * p->num_landmarks * sizeof(float);
+  if ((kv && (!dk || !dv)) || (lm && !dlmk))
+    return fail(HILS_ERR_INVALID_ARG, "a required gradient pointer of hils_backward is null");
+  if ((dk && !aligned16(dk)) || (dv && !aligned16(dv)) || (dlmk && !aligned16(dlmk)) ||
+      (dbias && !aligned16(dbias)))
+    return fail(HILS_ERR_INVALID_ARG, "base pointers must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();   // clear a stale error so it is not reported as ours
+  hils_status s = HILS_OK;
+  if (kv && s == HILS_OK) s = launch_status(hils::launch_zero_fill(dk, kv, st), "zero fill");
+  if (kv && s == HILS_OK) s = launch_status(hils::launch_zero_fill(dv, kv, st), "zero fill");
+  if (lm && s == HILS_OK) s = launch_status(hils::launch_zero_fill(dlmk, lm, st), "zero fill");
+  if (lb && dbias && s == HILS_OK) s = launch_status(hils::launch_zero_fill(dbias, lb, st), "zero fill");
+  return s;
+}
+
 bool landmarks_empty(const hils_params* p) {
   return p->batch == 0 || p->heads_kv == 0 || (p->seq_kv == 0 && p->num_landmarks == 0);
 }
@@ -233,7 +259,7 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* q_ret
                           void* ws, size_t ws_bytes, void* stream) {
   hils_status s = check_params(p, HILS_OP_BACKWARD);
   if (s != HILS_OK) return s;
-  if (is_empty(p)) return HILS_OK;
+  if (is_empty(p)) return zero_key_grads(p, dk, dv, dlmk, dlmk_bias, stream);
   if (!q || !k || !v || !lmk || !out || !dout || !sel_idx || !lse || !dq || !dk || !dv || !dlmk)
     return fail(HILS_ERR_INVALID_ARG, "a required pointer of hils_backward is null");
   const void* ptrs[] = {q, k, v, lmk, out, dout, sel_idx, lse, dq, dk, dv, dlmk};
@@ -251,14 +277,20 @@ hils_status hils_backward(const hils_params* p, const void* q, const void* q_ret
   const void* qr = q_ret ? q_ret : q;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();   // clear a stale error so it is not reported as ours
+  // the kernels read a copy of the selection in which every id the query may not
+  // use (not one of its candidates, or a repeat within its row) is -1
+  int32_t* sel = reinterpret_cast<int32_t*>(ws);
+  void* kws = reinterpret_cast<char*>(ws) + round256(hils::sanitized_selection_bytes(g));
+  s = launch_status(hils::launch_sanitize_selection(g, sel_idx, sel, st), "selection check launch");
+  if (s != HILS_OK) return s;
   if (hils::prefill_bwd_fast_supported(g, bf16))
     return launch_status(hils::launch_prefill_bwd_fast(g, q, qr, k, v, lmk, lmk_bias, out, dout,
-                                                       sel_idx, lse, dq, dq_ret, dk, dv, dlmk,
-                                                       dlmk_bias, ws, st),
+                                                       sel, lse, dq, dq_ret, dk, dv, dlmk,
+                                                       dlmk_bias, kws, st),
                          "backward launch");
   return launch_status(hils::launch_generic_backward(g, bf16, q, qr, k, v, lmk, lmk_bias, dout,
-                                                     sel_idx, dq, dq_ret, dk, dv, dlmk, dlmk_bias,
-                                                     ws, st),
+                                                     sel, dq, dq_ret, dk, dv, dlmk, dlmk_bias,
+                                                     kws, st),
                        "backward launch");
 }
 

@@ -44,6 +44,14 @@ hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void*
                                    const float* lse, void* dq, void* dqr, void* dk, void* dv,
                                    void* dlmk, float* dbias, void* ws, hipStream_t st);
 
+// backward service: a copy of a caller's selection with the ids a query may not
+// use (not among its candidates, or repeated in its row) set to -1
+size_t sanitized_selection_bytes(const Geometry& g);
+hipError_t launch_sanitize_selection(const Geometry& g, const int32_t* in, int32_t* out,
+                                     hipStream_t st);
+// bytes of zeros (a fill kernel, no memset)
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
+
 // landmark formation (weighted key sum + entropy bias per chunk) and its backward
 bool landmarks_supported(const Geometry& g);
 hipError_t launch_landmarks(const Geometry& g, int bf16, const void* lq, const void* k, void* lmk,

@@ -49,9 +49,6 @@ constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kWin = 64;         // queries per window (one chunk), both kernels
 constexpr int kBlocks = kWin / 4;          // 16 query blocks of 4 queries
 constexpr int kBlocksPerWave = kBlocks / kAttWaves;
-// rows searched together by the select kernel's waves: with 4 or 8 candidate
-// blocks per row the score table fills the LDS (one wave per SIMD)
-constexpr int sel_rows(int R) { return R >= 4 ? 1 : 1; }
 constexpr int kMaxKf = 32;       // top-K bound on this path
 constexpr int kMaxNC = 512;      // chunks bound on this path (L <= 32768)
 constexpr int kFrag = kWave * 8;           // bf16 per operand fragment (64 lanes x 16 B)
@@ -288,10 +285,9 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     reinterpret_cast<uint4*>(vdst)[f] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 
-  // the wave's 16 rows, NR at a time (one wave per SIMD when the score table
-  // is large: the interleaved searches hide each other's latency); the V
-  // staging area is each wave's compaction buffer from here on
-  constexpr int NR = sel_rows(R);
+  // the wave's 16 rows, one at a time; the V staging area is each wave's
+  // compaction buffer from here on
+  constexpr int NR = 1;
   __syncthreads();
   uint64_t* sbuf = reinterpret_cast<uint64_t*>(vs) + w * (kS * kD / 4 / (kThreads / kWave));
   static_assert(NR * kWave <= kS * kD / 4 / (kThreads / kWave), "compaction buffer");

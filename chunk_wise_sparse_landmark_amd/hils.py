@@ -123,12 +123,33 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _require(name, t, dtype, shape, device):
+    """A tensor argument the library reads or writes through a raw pointer: it must
+    have exactly the dtype, shape and device the call implies and be contiguous
+    (the kernels index it as a dense row-major array).  None passes."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
 def _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale, local_chunks=None):
-    for name, t in (("q", q), ("k", k), ("lmk", lmk)):
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
+    if q.dim() != 4 or k.dim() != 4 or lmk.dim() != 4:
+        raise ValueError("q, k and lmk must be 4-d [batch, heads, length, head_dim]")
     B, Hq, Lq, d = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
+    _dtype_code(q)
+    _require("q", q, q.dtype, q.shape, q.device)
+    _require("k", k, q.dtype, (B, Hkv, Lkv, d), q.device)
+    _require("lmk", lmk, q.dtype, (B, Hkv, lmk.shape[2], d), q.device)
     return make_params(batch=B, heads_q=Hq, heads_kv=Hkv, head_dim=d, seq_q=Lq, seq_kv=Lkv,
                        chunk_size=chunk_size, top_k=top_k, num_landmarks=lmk.shape[2],
                        causal=causal, keep_own_chunk=keep_own_chunk, scale=scale,
@@ -143,13 +164,13 @@ def _workspace(params, op, device, ws):
     need = hils_workspace_size(params, op)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws is not None:
+        _require("ws", ws, torch.uint8, (ws.numel(),), device)
     return ws, need if ws is None else ws.numel()
 
 
 def _check_qret(q, q_ret):
-    if q_ret is not None and (q_ret.shape != q.shape or q_ret.dtype != q.dtype
-                              or not q_ret.is_contiguous()):
-        raise ValueError("q_ret must be contiguous with q's shape and dtype")
+    _require("q_ret", q_ret, q.dtype, q.shape, q.device)
 
 
 def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_chunk, scale,
@@ -159,8 +180,13 @@ def _fwd(entry, op, q, k, v, lmk, lmk_bias, chunk_size, top_k, causal, keep_own_
     B, Hq, Lq, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
+    _require("v", v, q.dtype, k.shape, dev)
+    _require("lmk_bias", lmk_bias, torch.float32, lmk.shape[:3], dev)
+    _require("out", out, q.dtype, q.shape, dev)
+    _require("sel_idx", sel_idx, torch.int32, (B, Hkv, Lq, top_k), dev)
+    _require("lse", lse, torch.float32, (B, Hq, Lq), dev)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=dev)
     if sel_idx is None:
         sel_idx = torch.empty((B, Hkv, Lq, top_k), dtype=torch.int32, device=dev)
     if lse is None:
@@ -201,8 +227,16 @@ def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size
     with ``q_ret`` a sixth tensor dq_ret follows and dq is the token-attention part."""
     p = _params_from(q, k, lmk, chunk_size, top_k, causal, keep_own_chunk, scale, local_chunks)
     _check_qret(q, q_ret)
-    dq, dk, dv, dlmk = (torch.empty_like(t) for t in (q, k, v, lmk))
-    dqr = torch.empty_like(q) if q_ret is not None else None
+    B, Hq, Lq, d = q.shape
+    dev = q.device
+    _require("v", v, q.dtype, k.shape, dev)
+    _require("lmk_bias", lmk_bias, torch.float32, lmk.shape[:3], dev)
+    _require("out", out, q.dtype, q.shape, dev)
+    _require("dout", dout, q.dtype, q.shape, dev)
+    _require("sel_idx", sel_idx, torch.int32, (B, k.shape[1], Lq, top_k), dev)
+    _require("lse", lse, torch.float32, (B, Hq, Lq), dev)
+    dq, dk, dv, dlmk = (torch.empty(t.shape, dtype=t.dtype, device=dev) for t in (q, k, k, lmk))
+    dqr = torch.empty(q.shape, dtype=q.dtype, device=dev) if q_ret is not None else None
     if need_dbias is None:
         need_dbias = lmk_bias is not None
     dbias = torch.empty(lmk.shape[:3], dtype=torch.float32, device=q.device) if need_dbias else None
@@ -219,12 +253,14 @@ def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size
 
 
 def _landmark_params(lq, k, chunk_size, scale):
-    for name, t in (("lq", lq), ("k", k)):
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
+    if lq.dim() != 4 or k.dim() != 4:
+        raise ValueError("lq and k must be 4-d [batch, kv heads, length, head_dim]")
     if lq.dtype != k.dtype:
         raise TypeError("lq and k must share a dtype")
     B, Hkv, Lkv, d = k.shape
+    _dtype_code(k)
+    _require("k", k, k.dtype, k.shape, k.device)
+    _require("lq", lq, k.dtype, (B, Hkv, lq.shape[2], d), k.device)
     return make_params(batch=B, heads_q=Hkv, heads_kv=Hkv, head_dim=d, seq_q=0, seq_kv=Lkv,
                        chunk_size=chunk_size, top_k=1, num_landmarks=lq.shape[2], scale=scale,
                        dtype=_dtype_code(k))
@@ -234,7 +270,7 @@ def hils_landmarks(lq, k, *, chunk_size, scale=0.0, need_bias=True, stream=None)
     """Landmark keys [B,Hkv,NCcap,d] and entropy biases (fp32 [B,Hkv,NCcap], or None)
     from landmark queries lq [B,Hkv,NCcap,d] and keys k [B,Hkv,Lkv,d]."""
     p = _landmark_params(lq, k, chunk_size, scale)
-    lmk = torch.empty_like(lq)
+    lmk = torch.empty(lq.shape, dtype=lq.dtype, device=lq.device)
     bias = torch.empty(lq.shape[:3], dtype=torch.float32, device=lq.device) if need_bias else None
     _check(load_library().hils_landmarks(ctypes.byref(p), _ptr(lq), _ptr(k), _ptr(lmk), _ptr(bias),
                                          _stream(stream)))
@@ -244,9 +280,10 @@ def hils_landmarks(lq, k, *, chunk_size, scale=0.0, need_bias=True, stream=None)
 def hils_landmarks_backward(lq, k, dlmk, dbias=None, *, chunk_size, scale=0.0, stream=None):
     """Gradients (dlq, dk) of the landmark formation; dk is its own contribution."""
     p = _landmark_params(lq, k, chunk_size, scale)
-    if not dlmk.is_contiguous() or dlmk.dtype != lq.dtype or dlmk.shape != lq.shape:
-        raise ValueError("dlmk must be contiguous with lq's shape and dtype")
-    dlq, dk = torch.empty_like(lq), torch.empty_like(k)
+    _require("dlmk", dlmk, lq.dtype, lq.shape, lq.device)
+    _require("dbias", dbias, torch.float32, lq.shape[:3], lq.device)
+    dlq = torch.empty(lq.shape, dtype=lq.dtype, device=lq.device)
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device)
     _check(load_library().hils_landmarks_backward(ctypes.byref(p), _ptr(lq), _ptr(k), _ptr(dlmk),
                                                   _ptr(dbias), _ptr(dlq), _ptr(dk),
                                                   _stream(stream)))

@@ -232,6 +232,62 @@ def make_host_inputs(cfg, lazy_kv=None):
     return out
 
 
+def plant_ties(host, cfg, mode):
+    """Exact score ties for the tie-break tests (modifies host["lmk"] and host["bias"]).
+
+    * ``all_equal``: every landmark row of a (b, kv head) is that group's row 0 and
+      the bias is 0, so every candidate of a query has the same score (bit for bit,
+      on any side that scores the rows alike) and the lowest ids must win.
+    * ``kth``: per (b, kv head), K - 1 "strong" chunks get bias 100 + K - r (r = 1
+      .. K - 1: distinct, far above every other score), a "tie" set of four chunks
+      shares one landmark row (the first member's) and gets bias 50, and every
+      other chunk bias 0.  A query that sees all of them has a four-way exact tie
+      at its K-th score, which the lowest tied id must win.  Positions are drawn
+      from the counter generator among the candidates of the last query.
+
+    Returns {(b, g): (strong ids, tie ids)} for ``kth``, {} otherwise.
+    """
+    B, Hkv, S, K = cfg["B"], cfg["Hkv"], cfg["S"], cfg["K"]
+    lmk = np.array(host["lmk"], dtype=np.float32, copy=True)
+    NC = lmk.shape[2]
+    bias = np.zeros((B, Hkv, NC), dtype=np.float32)
+    planted = {}
+    if mode == "all_equal":
+        lmk[:] = lmk[:, :, :1, :]
+    elif mode == "kth":
+        win = cfg.get("win")
+        win = (1 if cfg.get("keep_own", 1) else 0) if win is None else int(win)
+        t_last = cfg["Lkv"] - 1 if cfg["causal"] else cfg["Lkv"]
+        ncand = min(NC, max(0, t_last // S - max(win - 1, 0))) if cfg["causal"] else NC
+        need = K - 1 + 4
+        assert ncand >= need, "too few candidates to plant the ties"
+        for b in range(B):
+            for g in range(Hkv):
+                draws = uniform_u64(cfg["seed"], TENSOR_IDS["ties"],
+                                    np.arange((b * Hkv + g) * 4 * need,
+                                              (b * Hkv + g + 1) * 4 * need, dtype=np.uint64))
+                chosen = []
+                for u in draws:
+                    c = int(u % np.uint64(ncand))
+                    if c not in chosen:
+                        chosen.append(c)
+                    if len(chosen) == need:
+                        break
+                assert len(chosen) == need
+                strong, tie = chosen[:K - 1], sorted(chosen[K - 1:])
+                for r, c in enumerate(strong):
+                    bias[b, g, c] = 100.0 + (K - 1 - r)
+                for c in tie:
+                    lmk[b, g, c] = lmk[b, g, tie[0]]
+                    bias[b, g, c] = 50.0
+                planted[(b, g)] = (sorted(strong), tie)
+    else:
+        raise ValueError(mode)
+    host["lmk"] = lmk
+    host["bias"] = bias if mode == "kth" else None
+    return planted
+
+
 def make_landmark_inputs(cfg, lq_scale=1.0, num_landmarks=None, grads=False):
     """Inputs of landmark formation: landmark queries lq [B, Hkv, NCcap, d] drawn
     N(0, lq_scale^2) (a query-like vector per chunk; a larger scale gives sharper

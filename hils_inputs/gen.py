@@ -36,7 +36,7 @@ IH_INV_SD = np.float32(1.0 / np.sqrt((65536.0 ** 2 - 1.0) / 3.0))
 TENSOR_IDS = {
     "q": 1, "k": 2, "v": 3, "lmk": 4, "lmk_noise": 5, "bias": 6, "dout": 7,
     "needle_u": 8, "needle_pos": 9, "resid": 10, "lq": 11, "dlmk": 12, "dbias": 13,
-    "qret_a": 14, "qret_b": 15,
+    "qret_a": 14, "qret_b": 15, "ties": 16,
 }
 
 

@@ -61,12 +61,14 @@
  * num_landmarks < seq_kv / chunk_size, a causal call with seq_q > seq_kv, a
  * decode call with seq_q != 1, a base pointer not 16-byte aligned, or a
  * workspace that is too small gives HILS_ERR_INVALID_ARG / HILS_ERR_WORKSPACE.
- * Shapes the kernels do not cover (top_k > 64, head_dim > 256,
+ * Shapes the kernels do not cover (top_k > 64: the selection kernels keep
+ * one composite key per lane of a 64-wide wave; head_dim > 256,
  * chunk_size > 256, heads_q / heads_kv > 64, or a backward with
  * chunk_size * head_dim > 8192) give HILS_ERR_UNSUPPORTED.  A failed launch
  * gives HILS_ERR_HIP.  Nothing throws across the ABI; hils_last_error() holds
  * a message for the calling thread.  Empty problems (batch, seq_q or heads
- * equal to 0) are valid and launch nothing.
+ * equal to 0) are valid; they launch nothing, except that hils_backward
+ * zero-fills the key-side gradients.
  */
 #ifndef HILS_H_
 #define HILS_H_
@@ -133,7 +135,14 @@ hils_status hils_decode(const hils_params* p, const void* q, const void* q_ret, 
  * dlmk and, if non-null, dlmk_bias.  `out` and `lse` are the forward's
  * outputs; `lse` must be non-null.  With q_ret (the forward's retrieval query)
  * the score gradients go to dq_ret (layout of dq) and dq holds the
- * token-attention part; q_ret and dq_ret are both given or both NULL. */
+ * token-attention part; q_ret and dq_ret are both given or both NULL.
+ * sel_idx is read, never trusted: an entry that is not a candidate of its
+ * query (negative, or not a complete chunk before the query's local window)
+ * or that repeats an earlier entry of its row is skipped like -1, so any
+ * int32 contents are safe; a row hils_forward wrote is used as it is.
+ * With no query rows (batch, heads_q or seq_q zero) dk, dv, dlmk and
+ * dlmk_bias are still overwritten, with zeros (null allowed where a buffer
+ * is empty). */
 hils_status hils_backward(const hils_params* p, const void* q, const void* q_ret, const void* k,
                           const void* v, const void* lmk, const float* lmk_bias, const void* out,
                           const void* dout, const int32_t* sel_idx, const float* lse,

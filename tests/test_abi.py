@@ -199,3 +199,75 @@ def test_landmarks_empty_is_a_no_op():
     assert _lmk_call(_p(heads_kv=0, heads_q=0), lq=None, k=None, lmk=None) == H.HILS_OK
     assert _lmk_call(_p(seq_kv=0, num_landmarks=0), lq=None, k=None, lmk=None) == H.HILS_OK
     assert _lmk_bwd_call(_p(batch=0), lq=None, k=None, dlmk=None, dlq=None, dk=None) == H.HILS_OK
+
+
+# ---- the binding checks every tensor before any call into the library
+torch = pytest.importorskip("torch")
+
+
+def _cpu_inputs(dtype=None):
+    dt = dtype or torch.bfloat16
+    q = torch.zeros(1, 4, 128, 64, dtype=dt)
+    k = torch.zeros(1, 2, 128, 64, dtype=dt)
+    v = torch.zeros(1, 2, 128, 64, dtype=dt)
+    lmk = torch.zeros(1, 2, 8, 64, dtype=dt)
+    return q, k, v, lmk
+
+
+@pytest.mark.parametrize("case", ["v_dtype", "v_shape", "v_strided", "bias_dtype", "bias_shape",
+                                  "out_shape", "sel_dtype", "lse_shape", "qret_dtype"])
+def test_binding_rejects_mismatched_forward_tensors(case):
+    q, k, v, lmk = _cpu_inputs()
+    kw = dict(chunk_size=16, top_k=2)
+    if case == "v_dtype":
+        v = v.float()
+    elif case == "v_shape":
+        v = v[:, :, :64]
+    elif case == "v_strided":
+        v = torch.zeros(1, 2, 64, 128, dtype=q.dtype).transpose(2, 3)
+    elif case == "bias_dtype":
+        kw["lmk_bias"] = torch.zeros(1, 2, 8, dtype=torch.bfloat16)
+    elif case == "bias_shape":
+        kw["lmk_bias"] = torch.zeros(1, 2, 9, dtype=torch.float32)
+    elif case == "out_shape":
+        kw["out"] = torch.zeros(1, 4, 127, 64, dtype=q.dtype)
+    elif case == "sel_dtype":
+        kw["sel_idx"] = torch.zeros(1, 2, 128, 2, dtype=torch.int64)
+    elif case == "lse_shape":
+        kw["lse"] = torch.zeros(1, 2, 128, dtype=torch.float32)
+    elif case == "qret_dtype":
+        kw["q_ret"] = q.float()
+    bias = kw.pop("lmk_bias", None)
+    with pytest.raises(ValueError):
+        H.hils_forward(q, k, v, lmk, bias, **kw)
+
+
+@pytest.mark.parametrize("case", ["dout_strided", "sel_shape", "lse_dtype", "out_dtype"])
+def test_binding_rejects_mismatched_backward_tensors(case):
+    q, k, v, lmk = _cpu_inputs()
+    out, dout = torch.zeros_like(q), torch.zeros_like(q)
+    sel = torch.zeros(1, 2, 128, 2, dtype=torch.int32)
+    lse = torch.zeros(1, 4, 128, dtype=torch.float32)
+    if case == "dout_strided":
+        dout = torch.zeros(1, 4, 64, 128, dtype=q.dtype).transpose(2, 3)
+    elif case == "sel_shape":
+        sel = torch.zeros(1, 2, 128, 3, dtype=torch.int32)
+    elif case == "lse_dtype":
+        lse = lse.double()
+    elif case == "out_dtype":
+        out = out.float()
+    with pytest.raises(ValueError):
+        H.hils_backward(q, k, v, lmk, None, out, dout, sel, lse, chunk_size=16, top_k=2)
+
+
+def test_backward_without_queries_needs_gradient_buffers():
+    """seq_q = 0 with a non-empty cache zero-fills dk, dv, dlmk: null ones are rejected
+    before any launch."""
+    p = _p(seq_q=0, causal=False)
+    lib = H.load_library()
+    st = lib.hils_backward(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
+                           None, None, None, None, FAKE, FAKE, None, None, 0, None)
+    assert st == H.HILS_ERR_INVALID_ARG
+    st = lib.hils_backward(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
+                           None, None, None, FAKE, FAKE, FAKE, MIS, None, 0, None)
+    assert st == H.HILS_ERR_INVALID_ARG

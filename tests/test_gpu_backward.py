@@ -119,6 +119,42 @@ def test_train_8k_sampled(hl, name):
     assert np.all(to_np(dl)[:, :, L // S - 1] == 0)
 
 
+def test_train_8k_full_group(hl):
+    """One (batch, KV head) group of train_8k over all 8192 of its queries, so
+    that every chunk's dk, dv, dlmk and dbias is complete -- including the early
+    chunks that thousands of queries retrieve, which the backward splits into
+    several work items and sums in its reduce pass.  The oracle runs on the host
+    cores (a process pool over query blocks)."""
+    from oracle.pool import default_workers, group_backward, make_pool
+    cfg = config("train_8k")
+    host, dev = make_device_inputs(cfg)
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=True)
+    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
+    dq, dk, dv, dl, db = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out,
+                                          dev["dout"], idx, lse, need_dbias=True, **kw)
+    torch.cuda.synchronize()
+    b, g, G, L, S = 1, 2, cfg["Hq"] // cfg["Hkv"], cfg["Lq"], cfg["S"]
+    gi = idx.cpu().numpy().astype(np.int64)[b, g]
+    nitems = np.bincount(gi[gi >= 0].ravel(), minlength=L // S)
+    assert nitems[0] > 8 * 64, "the early chunks are retrieved by many query tiles"
+    workers = default_workers()
+    with make_pool(workers) as pool:
+        rdq, rdk, rdv, rdl, rdb = group_backward(pool, host, b, g, np.arange(L), gi, 4 * workers,
+                                                 **kw)
+    hs = slice(g * G, (g + 1) * G)
+    assert_close("dq group", to_np(dq)[b, hs], rdq, "norm", 2e-2)
+    assert_close("dk group", to_np(dk)[b, g], rdk, "norm", 2e-2)
+    assert_close("dv group", to_np(dv)[b, g], rdv, "norm", 2e-2)
+    assert_close("dlmk group", to_np(dl)[b, g], rdl, "norm", 2e-2)
+    assert_close("dbias group", to_np(db)[b, g], rdb, "norm", 2e-2)
+    # chunk by chunk for the most-retrieved ones (norm-relative per chunk)
+    for c in np.argsort(-nitems)[:6]:
+        rows = slice(c * S, (c + 1) * S)
+        assert_close("dk chunk %d" % c, to_np(dk)[b, g, rows], rdk[rows], "norm", 2e-2)
+        assert_close("dv chunk %d" % c, to_np(dv)[b, g, rows], rdv[rows], "norm", 2e-2)
+        assert_close("dlmk chunk %d" % c, to_np(dl)[b, g, c], rdl[c], "norm", 2e-2)
+
+
 def test_train_8k_swa512_sampled(hl):
     """Training shape with a 512-token local window: dq on sampled rows; dk, dv of
     the last two chunks, which only the queries of the last two windows reach
@@ -147,3 +183,96 @@ def test_train_8k_swa512_sampled(hl):
     assert_close("dlmk", to_np(dl)[:, :, c], rdl[:, :, c], "norm", 2e-2)
     assert_close("dbias", to_np(db)[:, :, c], rdb[:, :, c], "norm", 2e-2)
 
+
+
+def _layout_ncand(cfg, i):
+    win = cfg.get("win")
+    win = (1 if cfg["keep_own"] else 0) if win is None else int(win)
+    NC = cfg["Lkv"] // cfg["S"]
+    if not cfg["causal"]:
+        return NC
+    own = (cfg["Lkv"] - cfg["Lq"] + i) // cfg["S"]
+    return max(0, min(own - max(win - 1, 0), NC))
+
+
+@pytest.mark.parametrize("over", [
+    # MFMA backward path (G = 4) and the generic kernels (G = 2, fp32)
+    dict(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=8, dtype="bf16", lmk="chunk_mean"),
+    dict(B=1, Hq=4, Hkv=2, d=64, Lq=200, Lkv=200, S=16, K=4, dtype="f32", lmk="iid", win=2),
+])
+def test_backward_ignores_unusable_ids(hl, over):
+    """A caller's selection with ids the query may not use -- its own or a later
+    chunk (in bounds, not candidates), ids past the last chunk, negative ids and
+    repeats within a row -- is read safely: those entries are skipped, so the
+    gradients equal the oracle's for the selection without them."""
+    cfg = dict(config("tiny_f32"), seed=61, dout=True)
+    cfg.update(over)
+    host, dev = make_device_inputs(cfg)
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True,
+              keep_own_chunk=bool(cfg["keep_own"]), local_chunks=cfg.get("win"))
+    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, **kw)
+    torch.cuda.synchronize()
+    sel = idx.cpu().numpy().copy()
+    L, S, K = cfg["Lq"], cfg["S"], cfg["K"]
+    NC = L // S
+    rng = np.random.default_rng(9)
+    bad = [lambda i: i // S, lambda i: min(NC - 1, i // S + 1), lambda i: NC + 3,
+           lambda i: 10 ** 6, lambda i: -5, lambda i: 2 ** 31 - 1]
+    for b in range(cfg["B"]):
+        for g in range(cfg["Hkv"]):
+            for i in range(L):
+                row = sel[b, g, i]
+                for _ in range(2):
+                    s = int(rng.integers(K))
+                    if rng.random() < 0.3 and row[0] >= 0:
+                        row[s] = row[0] if s else row[-1]          # a repeat within the row
+                    else:
+                        row[s] = bad[int(rng.integers(len(bad)))](i)
+    # what the backward must use: the candidates of each row, first occurrence only
+    want = np.full_like(sel, -1)
+    for b in range(cfg["B"]):
+        for g in range(cfg["Hkv"]):
+            for i in range(L):
+                nc = _layout_ncand(cfg, i)
+                seen, keep = set(), []
+                for c in sel[b, g, i]:
+                    c = int(c)
+                    if 0 <= c < nc and c not in seen:
+                        seen.add(c)
+                        keep.append(c)
+                want[b, g, i, :len(keep)] = keep
+    gsel = torch.from_numpy(sel.astype(np.int32)).to(dev["q"].device)
+    grads = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out, dev["dout"],
+                             gsel, lse, need_dbias=True, **kw)
+    torch.cuda.synchronize()
+    ref = ref_backward(host["q"], host["k"], host["v"], host["lmk"], None, host["dout"],
+                       forced_idx=want.astype(np.int64), **kw)
+    tol = 1e-5 if cfg["dtype"] == "f32" else 2e-2
+    for name, got, w in zip(("dq", "dk", "dv", "dlmk", "dbias"), grads, ref):
+        assert_close(name, to_np(got), w, "norm", tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_without_queries_zero_fills(hl, dtype):
+    """seq_q = 0 (non-causal, a non-empty cache): the key-side gradients the call
+    overwrites are all zero, not left as they were."""
+    import ctypes
+    H = hl.hils
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, Hq, Hkv, d, Lkv, S, NCc = 2, 4, 2, 64, 200, 16, 13
+    p = H.make_params(batch=B, heads_q=Hq, heads_kv=Hkv, head_dim=d, seq_q=0, seq_kv=Lkv,
+                      chunk_size=S, top_k=3, num_landmarks=NCc, causal=False,
+                      dtype=H.HILS_BF16 if dtype == "bf16" else H.HILS_F32)
+    dk = torch.full((B, Hkv, Lkv, d), float("nan"), dtype=tdt, device="cuda")
+    dv = torch.full_like(dk, float("nan"))
+    dl = torch.full((B, Hkv, NCc, d), float("nan"), dtype=tdt, device="cuda")
+    db = torch.full((B, Hkv, NCc), float("nan"), dtype=torch.float32, device="cuda")
+    lib = H.load_library()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.hils_backward(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
+                           None, None, None, vp(dk), vp(dv), vp(dl), vp(db), None, 0,
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == H.HILS_OK, lib.hils_last_error()
+    for t in (dk, dv, dl, db):
+        assert bool((t == 0).all())

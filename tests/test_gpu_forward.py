@@ -54,16 +54,17 @@ GENERIC_CASES = {
     "f32_mha_k_exceeds": _case(B=1, Hq=3, Hkv=3, d=48, Lq=90, Lkv=90, S=8, K=20, dtype="f32"),
     "bf16_d128_s64_k64": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1100, Lkv=1100, S=64, K=64,
                                keep_own=1, seed=5),
-    # MFMA prefill path (bf16, d=128, S=64, causal, L % 64 == 0, G in {1,2,4}, K <= 32)
+    # MFMA prefill path (bf16, d=128, S=64, causal, L % 64 == 0, G = 4, K <= 32)
     "mfma_g4_k16": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=16,
                          lmk="chunk_mean", seed=6),
     # keys 24x larger: logits of tens (in natural-log units) with spreads far
     # beyond the N(0,1) workloads
     "mfma_large_keys": _case(B=1, Hq=8, Hkv=2, d=128, Lq=1024, Lkv=1024, S=64, K=16,
                              lmk="chunk_mean", seed=7, kscale=24.0),
-    "mfma_g2_k8_bias": _case(B=2, Hq=4, Hkv=2, d=128, Lq=2048, Lkv=2048, S=64, K=8, bias=0.3,
+    # the same bf16 d=128 S=64 shapes at G = 2 and G = 1 take the generic kernels
+    "generic_g2_k8_bias": _case(B=2, Hq=4, Hkv=2, d=128, Lq=2048, Lkv=2048, S=64, K=8, bias=0.3,
                              seed=7),
-    "mfma_g1_k32": _case(B=1, Hq=2, Hkv=2, d=128, Lq=4096, Lkv=4096, S=64, K=32, seed=8),
+    "generic_g1_k32": _case(B=1, Hq=2, Hkv=2, d=128, Lq=4096, Lkv=4096, S=64, K=32, seed=8),
     "mfma_g4_no_own": _case(B=1, Hq=4, Hkv=1, d=128, Lq=1024, Lkv=1024, S=64, K=4, keep_own=0,
                             lmk="chunk_mean", seed=10),
     "mfma_g4_nc256_sortpath": _case(B=1, Hq=4, Hkv=1, d=128, Lq=16384, Lkv=16384, S=64, K=32,
