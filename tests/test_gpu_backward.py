@@ -6,7 +6,7 @@ import torch
 
 from hils_inputs.configs import config
 from hils_inputs.device import make_device_inputs
-from oracle.hils_oracle import ref_backward
+from oracle.hils_oracle import ref_backward, ref_forward
 from tests.parity import assert_close, to_np
 
 pytestmark = pytest.mark.gpu
@@ -241,6 +241,13 @@ def test_backward_ignores_unusable_ids(hl, over):
                         seen.add(c)
                         keep.append(c)
                 want[b, g, i, :len(keep)] = keep
+    # the forward outputs that go with that selection (the backward reads O and its
+    # LSE), from the oracle, rounded as the library stores them
+    from hils_inputs.device import to_device
+    ro, _, rl = ref_forward(host["q"], host["k"], host["v"], host["lmk"], None,
+                            forced_idx=want.astype(np.int64), **kw)
+    out = to_device(ro.astype(np.float32), cfg["dtype"], dev["q"].device)
+    lse = torch.from_numpy(rl.astype(np.float32)).to(dev["q"].device)
     gsel = torch.from_numpy(sel.astype(np.int32)).to(dev["q"].device)
     grads = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out, dev["dout"],
                              gsel, lse, need_dbias=True, **kw)
