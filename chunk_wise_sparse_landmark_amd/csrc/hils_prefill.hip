@@ -779,389 +779,6 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   }
 }
 
-// ----------------------------------------------------------------------------
-// 2b. attention over packed query groups.  One workgroup per (b, kv head,
-//     64-query window) as above, but the retrieved chunks are no longer walked
-//     by the fixed 16-row blocks of the window: for every chunk of the window's
-//     union, the window queries that selected it are packed four at a time
-//     into 16-row groups (4 queries x 4 heads), so a group's MFMA rows are
-//     wasted only in the last, partly filled group of a chunk.  The output rows
-//     of the whole window live in LDS as fp32 accumulators (64 queries x 4
-//     heads x 128 dims); a group's O tile is added into its four queries' rows
-//     with LDS atomic adds.  Each wave takes whole chunks (all their groups)
-//     from a shared counter and reads the chunk's K and V fragments straight
-//     into registers, so no barrier separates chunks and time follows the
-//     selections made, not the window's union.
-//
-//     Before that, each wave settles its own 8 queries (two blocks of 4): the
-//     LSE of their retrieval scores (per head, over the selected chunks, by
-//     MFMA), the exact lse of the local window's tokens (statistics pass), the
-//     row LSE, and the window's share of the output (P = exp(l - LSE)), which
-//     initialises the LDS accumulators.  A chunk's fusion weight is then
-//     exp(s - LSE) with s recomputed in the group (a 128-term dot per row).
-//     The accumulation order of the atomic adds follows the wave schedule, so
-//     the fp32 sums (not the selection) may differ in their last bits between
-//     runs.
-// ----------------------------------------------------------------------------
-// the packed kernel is parity-green but slower than the union kernel so far
-constexpr bool kUsePacked = false;
-constexpr int kPkWaves = 8;
-constexpr int kPkThreads = kPkWaves * kWave;
-constexpr int kQStride = kG * kD + 16;     // floats per query in the accumulators (bank offset)
-
-struct PackedSmem {
-  float oacc[kWin * kQStride];            // (query, head, dim) fp32 output accumulators
-  uint64_t qmask[kMaxNC];                 // chunk -> window queries that selected it
-  float lse2[kWin * kG];                  // (query, head): row LSE, log2 units
-  float lret[kWin * kG];                  // (query, head): LSE of the retrieval scores
-  uint16_t ulist[kMaxNC];
-  int wcount[kPkWaves];
-  int next;
-};
-static_assert(sizeof(PackedSmem) <= 160 * 1024, "packed attention LDS exceeds 160 KB");
-
-__device__ __forceinline__ void load_frags_global(const uint4* __restrict__ src, bf16x8 (&f)[16]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int x = 0; x < 16; ++x) f[x] = as_bf16x8(src[x * kWave + lane]);
-}
-
-// sum over the 16 lanes of this lane's 16-lane row (lanes differing in bits 0..3)
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __shfl_xor(x, 1, kWave);
-  x += __shfl_xor(x, 2, kWave);
-  x += __shfl_xor(x, 4, kWave);
-  x += __shfl_xor(x, 8, kWave);
-  return x;
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmax2(x, __shfl_xor(x, 1, kWave));
-  x = fmax2(x, __shfl_xor(x, 2, kWave));
-  x = fmax2(x, __shfl_xor(x, 4, kWave));
-  x = fmax2(x, __shfl_xor(x, 8, kWave));
-  return x;
-}
-
-// 32 of the 128 dims (those this lane holds as an MFMA operand: 8 (l/16) +
-// 32 ks + j) of the dot product of two bf16 rows, then the sum over the four
-// lanes holding the other dims.
-__device__ __forceinline__ float frag_dot(const bf16x8 (&a)[4], const uint4 (&b)[4]) {
-  float acc = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    uint32_t aw[4];
-    __builtin_memcpy(aw, &a[ks], 16);
-    const uint32_t bw[4] = {b[ks].x, b[ks].y, b[ks].z, b[ks].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw[e]),
-                                            __builtin_bit_cast(bf16x2_t, bw[e]), acc, false);
-  }
-  return rowgroup_sum(acc);
-}
-
-__global__ void __launch_bounds__(kPkThreads)
-prefill_attend_packed(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
-                      int sep_qr, const uint16_t* __restrict__ kvf,
-                      const uint16_t* __restrict__ lmk, const float* __restrict__ bias,
-                      const int32_t* __restrict__ sel_idx, uint16_t* __restrict__ out,
-                      float* __restrict__ lse_out) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  PackedSmem& sm = *reinterpret_cast<PackedSmem*>(smem_raw);
-  const int nbkv = g.B * g.Hkv;
-  const int bkv = blockIdx.x % nbkv;                 // one head per XCD's L2
-  const int win = (g.Lq / kWin - 1) - blockIdx.x / nbkv;
-  const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int K = g.K;
-  const int i0 = win * kWin;
-  const int own = win;
-  const int nwin = g.win > 0 ? 1 + min(g.win - 1, own) : 0;
-  const int ncand = max(0, min(own - max(g.win - 1, 0), g.NC));
-  const uint4* KVg = reinterpret_cast<const uint4*>(kvf) + (size_t)bkv * g.NC * (kChunkElems / 8);
-  const uint16_t* Lg = lmk + (size_t)bkv * g.NCcap * kD;
-  const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
-  const int32_t* selw = sel_idx + ((size_t)bkv * g.Lq + i0) * K;
-  const float scale = g.scale;
-  const float sc2 = scale * 1.4426950408889634f;     // scale * log2(e)
-  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
-  const size_t qhead0 = (size_t)(b * g.Hq + kvh * kG) * g.Lq;   // row index of head 0, query 0
-
-  // ---- setup: chunk -> query masks and the union list
-  for (int c = tid; c < kMaxNC; c += kPkThreads) sm.qmask[c] = 0ull;
-  if (tid == 0) sm.next = 0;
-  __syncthreads();
-  for (int x = tid; x < kWin * K; x += kPkThreads) {
-    const int c = selw[x];
-    if (c >= 0 && c < ncand)
-      atomicOr((unsigned long long*)&sm.qmask[c], 1ull << (x / K));
-  }
-  __syncthreads();
-  int nunion = 0;
-  for (int c0 = 0; c0 < kMaxNC; c0 += kPkThreads) {
-    const int c = c0 + tid;
-    const bool f = c < ncand && sm.qmask[c] != 0ull;
-    const uint64_t m = __ballot(f);
-    if (lane == 0) sm.wcount[w] = __popcll(m);
-    __syncthreads();
-    int off = nunion;
-    for (int x = 0; x < w; ++x) off += sm.wcount[x];
-    if (f) sm.ulist[off + mask_rank(m)] = (uint16_t)c;
-    for (int x = 0; x < kPkWaves; ++x) nunion += sm.wcount[x];
-    __syncthreads();
-  }
-
-  // ---- this wave's 8 queries (blocks 2w, 2w+1; block row r16 = (query
-  //      4 blk + r16/4, head r16%4)): LSE of their retrieval scores
-  {
-    // A operand: row m = head m%4 of query qq; B operand: column n = slot n
-    for (int x = 0; x < 8; ++x) {
-      const int qq = w * 8 + x;
-      bf16x8 af[4];
-      const uint16_t* qrow = qr + (qhead0 + (size_t)(r16 & 3) * g.Lq + i0 + qq) * kD + 8 * g4;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) af[ks] = ld8(qrow + 32 * ks);
-      float m = -INFINITY, zsum = 0.f;
-      float sv[4];
-      for (int t0 = 0; t0 < K; t0 += 16) {
-        const int slot = t0 + r16;
-        const int c = slot < K ? selw[qq * K + slot] : -1;
-        const bool ok = c >= 0 && c < ncand;
-        const uint16_t* lrow = Lg + (size_t)(ok ? c : 0) * kD + 8 * g4;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma(af[ks], ld8(lrow + 32 * ks), acc);
-        const float bc = (ok && bb) ? bb[c] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = ok ? scale * acc[i] + bc : -INFINITY;
-        // lane (g4, r16): head i's score for slot r16 in sv[i]; lane group g4
-        // combines head g4's over the slots
-        const float mine = g4 == 0 ? sv[0] : g4 == 1 ? sv[1] : g4 == 2 ? sv[2] : sv[3];
-        if (t0 == 0) {
-          m = row16_max(mine);
-          zsum = row16_sum(m == -INFINITY ? 0.f : __expf(mine - m));
-        } else {
-          const float m2 = row16_max(mine);
-          const float mn = fmax2(m, m2);
-          const float z2 = row16_sum(mn == -INFINITY ? 0.f : __expf(mine - mn));
-          zsum = (m == -INFINITY ? 0.f : zsum * __expf(m - mn)) + z2;
-          m = mn;
-        }
-      }
-      // lane group g4 holds head g4's LSE over the selected chunks
-      if (r16 == 0) sm.lret[qq * kG + g4] = zsum > 0.f ? m + __logf(zsum) : -INFINITY;
-    }
-  }
-  wave_sync_lds();
-
-  // ---- local window: exact lse of its tokens, then the row LSE
-  bf16x8 qf[kBlocksPerWave][4];
-#pragma unroll
-  for (int j = 0; j < kBlocksPerWave; ++j) {
-    const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2), h = r16 & 3;
-    const uint16_t* qrow = q + (qhead0 + (size_t)h * g.Lq + i0 + qi) * kD + g4 * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[j][ks] = ld8(qrow + ks * 32);
-  }
-  float lse2r[kBlocksPerWave];            // this lane's column: row LSE, log2 units
-  {
-    float M2[kBlocksPerWave], Z[kBlocksPerWave];
-#pragma unroll
-    for (int j = 0; j < kBlocksPerWave; ++j) { M2[j] = -INFINITY; Z[j] = 0.f; }
-    for (int x = 0; x < nwin; ++x) {
-      bf16x8 kf[16];
-      load_frags_global(KVg + (size_t)(own - x) * (kChunkElems / 8), kf);
-#pragma unroll
-      for (int j = 0; j < kBlocksPerWave; ++j) {
-        f32x4 st[4];
-        float m2, z;
-        block_scores(kf, qf[j], st);
-        const int vis = x == 0 ? (w * kBlocksPerWave + j) * 4 + (r16 >> 2) + 1 : kS;
-        block_softmax<true>(st, sc2, vis, m2, z);
-        const float mn = fmax2(M2[j], m2);
-        Z[j] = Z[j] * __builtin_amdgcn_exp2f(M2[j] - mn) + z * __builtin_amdgcn_exp2f(m2 - mn);
-        M2[j] = mn;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kBlocksPerWave; ++j) {
-      const int qi = (w * kBlocksPerWave + j) * 4 + (r16 >> 2), h = r16 & 3;
-      const float lw = nwin > 0 ? (M2[j] + __log2f(Z[j])) * kLn2 : -INFINITY;   // natural log
-      const float lr = sm.lret[qi * kG + h];
-      const float mx = fmaxf(lw, lr);
-      const float LSE = mx == -INFINITY ? -INFINITY
-                                        : mx + __logf(__expf(lw - mx) + __expf(lr - mx));
-      lse2r[j] = LSE * kLog2e;
-      if (g4 == 0) {
-        sm.lse2[qi * kG + h] = lse2r[j];
-        if (lse_out) lse_out[(qhead0 + (size_t)h * g.Lq) + i0 + qi] = LSE;
-      }
-    }
-  }
-
-  // ---- the window's share of the output (P = exp(l - LSE)) initialises the
-  //      accumulators of this wave's queries
-  {
-    f32x4 o[kBlocksPerWave][8];
-#pragma unroll
-    for (int j = 0; j < kBlocksPerWave; ++j)
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int x = 0; x < nwin; ++x) {
-      const uint4* src = KVg + (size_t)(own - x) * (kChunkElems / 8);
-      bf16x8 pa[kBlocksPerWave][2];
-      {
-        bf16x8 kf[16];
-        load_frags_global(src, kf);
-#pragma unroll
-        for (int j = 0; j < kBlocksPerWave; ++j) {
-          f32x4 st[4];
-          block_scores(kf, qf[j], st);
-          const int vis = x == 0 ? (w * kBlocksPerWave + j) * 4 + (r16 >> 2) + 1 : kS;
-          block_direct<true>(st, sc2, vis, lse2r[j]);
-          pack_p(st, 1.f, pa[j]);
-        }
-      }
-      bf16x8 vf[16];
-      load_frags_global(src + 16 * kWave, vf);
-#pragma unroll
-      for (int j = 0; j < kBlocksPerWave; ++j)
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) o[j][db] = mfma(pa[j][ks], vf[db * 2 + ks], o[j][db]);
-    }
-    // lane holds O[row 4 g4 + i][16 db + r16] of block j; row = (query 4 blk + g4, head i)
-#pragma unroll
-    for (int j = 0; j < kBlocksPerWave; ++j) {
-      float* row = sm.oacc + ((w * kBlocksPerWave + j) * 4 + g4) * kQStride + r16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int db = 0; db < 8; ++db) row[i * kD + 16 * db] = o[j][db][i];
-    }
-  }
-  __syncthreads();
-
-  // ---- retrieved chunks: whole chunks from a shared counter, their selecting
-  //      queries packed four to a group; the next group's query rows are loaded
-  //      while a group is computed
-  const int slot_of_lane = r16 >> 2, head_of_lane = r16 & 3;
-  for (;;) {
-    int u = 0;
-    if (lane == 0) u = atomicAdd(&sm.next, 1);
-    u = __builtin_amdgcn_readfirstlane(__shfl(u, 0, kWave));
-    if (u >= nunion) break;
-    const int c = sm.ulist[u];
-    uint64_t mask = sm.qmask[c];
-    const float bc2 = bb ? bb[c] * kLog2e : 0.f;
-    uint4 lm[4];
-    {
-      const uint4* lrow = reinterpret_cast<const uint4*>(Lg + (size_t)c * kD);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) lm[ks] = lrow[4 * ks + g4];
-    }
-    const uint4* src = KVg + (size_t)c * (kChunkElems / 8);
-    bf16x8 kf[16], vf[16];
-    load_frags_global(src, kf);
-    load_frags_global(src + 16 * kWave, vf);
-    // the next group: up to 4 queries (the lowest set bits of the mask)
-    int qs[4], n;
-    bf16x8 gq[4];
-    auto next_group = [&](int (&qn)[4], int& nn, bf16x8 (&q4)[4]) {
-      nn = 0;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (mask != 0ull) {
-          qn[s] = __builtin_ctzll(mask);
-          mask &= mask - 1;
-          ++nn;
-        } else {
-          qn[s] = qn[0];
-        }
-      }
-      const int qc = slot_of_lane == 0 ? qn[0]
-                   : slot_of_lane == 1 ? qn[1] : slot_of_lane == 2 ? qn[2] : qn[3];
-      const size_t row = (qhead0 + (size_t)head_of_lane * g.Lq + i0 + qc) * kD + 8 * g4;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) q4[ks] = ld8(q + row + 32 * ks);
-    };
-    next_group(qs, n, gq);
-    for (;;) {
-      const bool more = mask != 0ull;
-      int qs2[4], n2 = 0;
-      bf16x8 gq2[4];
-      if (more) next_group(qs2, n2, gq2);
-      const int qcol = slot_of_lane == 0 ? qs[0]
-                     : slot_of_lane == 1 ? qs[1] : slot_of_lane == 2 ? qs[2] : qs[3];
-      // fusion weight of this lane's column: exp(s - LSE), s = scale <qr, lmk> + bias
-      float dot;
-      if (sep_qr) {
-        bf16x8 gr[4];
-        const size_t row = (qhead0 + (size_t)head_of_lane * g.Lq + i0 + qcol) * kD + 8 * g4;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) gr[ks] = ld8(qr + row + 32 * ks);
-        dot = frag_dot(gr, lm);
-      } else {
-        dot = frag_dot(gq, lm);
-      }
-      const float wgt = slot_of_lane < n
-          ? __builtin_amdgcn_exp2f(__builtin_fmaf(dot, sc2, bc2) - sm.lse2[qcol * kG + head_of_lane])
-          : 0.f;
-      f32x4 st[4];
-      __builtin_amdgcn_s_setprio(1);
-      block_scores(kf, gq, st);
-      __builtin_amdgcn_s_setprio(0);
-      float mrow, z;
-      block_softmax<false>(st, sc2, kS, mrow, z);
-      bf16x8 pa[2];
-      pack_p(st, wgt * __builtin_amdgcn_rcpf(z), pa);
-      f32x4 o[8];
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) o[db] = mfma(pa[ks], vf[db * 2 + ks], o[db]);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // lane (g4, r16) holds O[slot g4][head i][16 db + r16]
-      if (g4 < n) {
-        const int qd = g4 == 0 ? qs[0] : g4 == 1 ? qs[1] : g4 == 2 ? qs[2] : qs[3];
-        float* row = sm.oacc + qd * kQStride + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int db = 0; db < 8; ++db)
-            __hip_atomic_fetch_add(row + i * kD + 16 * db, o[db][i], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      if (!more) break;
-      n = n2;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qs[s] = qs2[s];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) gq[ks] = gq2[ks];
-    }
-  }
-  __syncthreads();
-
-  // ---- output: this wave's 8 queries x 4 heads, 8 dims (16 B) per lane
-#pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int rr = pass * 4 + (lane >> 4);          // 0..31: (query x, head h)
-    const int qq = w * 8 + (rr >> 2), h = rr & 3;
-    const float* src = sm.oacc + qq * kQStride + h * kD + 8 * r16;
-    const float4 a = *reinterpret_cast<const float4*>(src);
-    const float4 c4 = *reinterpret_cast<const float4*>(src + 4);
-    const float x8[8] = {a.x, a.y, a.z, a.w, c4.x, c4.y, c4.z, c4.w};
-    const bf16x8 o8 = pack_bf16x8(x8);
-    uint16_t* dst = out + (qhead0 + (size_t)h * g.Lq + i0 + qq) * kD + 8 * r16;
-    *reinterpret_cast<bf16x8*>(dst) = o8;
-  }
-}
-
 template <int R>
 void launch_select(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const uint16_t* lmk, const float* bias, int32_t* sel_idx, uint16_t* kvf,
@@ -1197,19 +814,6 @@ hipError_t launch_prefill_fast(const Geometry& g, const void* q, const void* qr,
   else launch_select<8>(g, QR, Kp, Vp, Lm, bias, sel_idx, kvf, st);
   prof_end(kPrefillSelect, st);
   // dynamic LDS above 64 KB must be enabled for the kernel (per device; cheap)
-  if (kUsePacked) {
-    if (const hipError_t e = hipFuncSetAttribute((const void*)prefill_attend_packed,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)sizeof(PackedSmem));
-        e != hipSuccess)
-      return e;
-    prof_begin(kPrefillAttend, st);
-    hipLaunchKernelGGL(prefill_attend_packed, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kPkThreads),
-                       sizeof(PackedSmem), st, g, Q, QR, (int)(QR != Q), kvf, Lm, bias, sel_idx,
-                       (uint16_t*)out, lse);
-    prof_end(kPrefillAttend, st);
-    return hipGetLastError();
-  }
   if (const hipError_t e = hipFuncSetAttribute((const void*)prefill_attend,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)sizeof(AttendSmem));
