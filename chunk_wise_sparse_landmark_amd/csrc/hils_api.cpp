@@ -230,6 +230,31 @@ bool landmarks_empty(const hils_params* p) {
 
 }  // namespace
 
+namespace hils {
+
+// hils_decode on a scratch buffer the library owns (the allocation-free entry
+// point): `ws` is that buffer (null when it could not be found on the current
+// device) and `ws_limit` its size; a call that needs more fails before any launch.
+hils_status decode_with_scratch(const hils_params* p, const void* q, const void* q_ret,
+                                     const void* k, const void* v, const void* lmk,
+                                     const float* lmk_bias, void* out, int32_t* sel_idx, float* lse,
+                                     void* ws, size_t ws_bytes, size_t ws_limit, void* stream) {
+  hils_status s = check_params(p, HILS_OP_DECODE);
+  if (s != HILS_OK) return s;
+  const size_t need = ws_bytes_for(p, HILS_OP_DECODE);
+  if (need > ws_limit)
+    return fail(HILS_ERR_UNSUPPORTED,
+                "hils_decode_noalloc: these sizes need %zu bytes of scratch, its fixed buffer "
+                "holds %zu (use hils_decode with a workspace)", need, ws_limit);
+  if (need > 0 && !ws)
+    return fail(HILS_ERR_HIP, "hils_decode_noalloc: the scratch buffer of the current device "
+                              "could not be located");
+  return forward_like(HILS_OP_DECODE, p, q, q_ret, k, v, lmk, lmk_bias, out, sel_idx, lse, ws,
+                      ws_bytes, stream);
+}
+
+}  // namespace hils
+
 extern "C" {
 
 size_t hils_workspace_size(const hils_params* p, int32_t op) {

@@ -20,7 +20,8 @@ HILS_OK, HILS_ERR_INVALID_ARG, HILS_ERR_UNSUPPORTED, HILS_ERR_WORKSPACE, HILS_ER
 HILS_F32, HILS_BF16 = 0, 1
 HILS_OP_FORWARD, HILS_OP_DECODE, HILS_OP_BACKWARD = 0, 1, 2
 
-EXPORTS = ("hils_workspace_size", "hils_forward", "hils_decode", "hils_backward",
+EXPORTS = ("hils_workspace_size", "hils_forward", "hils_decode", "hils_decode_noalloc",
+           "hils_decode_noalloc_scratch_bytes", "hils_backward",
            "hils_landmarks", "hils_landmarks_backward", "hils_profile_kernel", "hils_profile_count", "hils_status_string", "hils_last_error")
 
 KERNEL_IDS = {"generic_select": 1, "generic_attend": 2, "generic_bwd_rows": 3,
@@ -67,6 +68,10 @@ def load_library(path=None):
     lib.hils_forward.restype = ctypes.c_int
     lib.hils_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hils_decode.restype = ctypes.c_int
+    lib.hils_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hils_decode_noalloc.restype = ctypes.c_int
+    lib.hils_decode_noalloc_scratch_bytes.argtypes = []
+    lib.hils_decode_noalloc_scratch_bytes.restype = sz
     lib.hils_backward.argtypes = [P] + [vp] * 16 + [vp, sz, vp]
     lib.hils_backward.restype = ctypes.c_int
     lib.hils_landmarks.argtypes = [P, vp, vp, vp, vp, vp]
@@ -218,6 +223,32 @@ def hils_decode(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, keep_own_chun
     """Single-token decode over the cache k, v (q: [B,Hq,1,d], position seq_kv-1)."""
     return _fwd("hils_decode", HILS_OP_DECODE, q, k, v, lmk, lmk_bias, chunk_size, top_k,
                 True, keep_own_chunk, scale, out, sel_idx, lse, ws, stream, local_chunks, q_ret)
+
+
+def hils_decode_noalloc(q, k, v, lmk, lmk_bias=None, *, chunk_size, top_k, keep_own_chunk=True,
+                        scale=0.0, out=None, sel_idx=None, lse=None, stream=None,
+                        local_chunks=None, q_ret=None):
+    """hils_decode on the library's own fixed scratch array (no workspace); outputs
+    are allocated here only when not given."""
+    p = _params_from(q, k, lmk, chunk_size, top_k, True, keep_own_chunk, scale, local_chunks)
+    _check_qret(q, q_ret)
+    B, Hq, Lq, d = q.shape
+    dev = q.device
+    _require("v", v, q.dtype, k.shape, dev)
+    _require("lmk_bias", lmk_bias, torch.float32, lmk.shape[:3], dev)
+    _require("out", out, q.dtype, q.shape, dev)
+    _require("sel_idx", sel_idx, torch.int32, (B, k.shape[1], Lq, top_k), dev)
+    _require("lse", lse, torch.float32, (B, Hq, Lq), dev)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, k.shape[1], Lq, top_k), dtype=torch.int32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
+    _check(load_library().hils_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(q_ret), _ptr(k),
+                                              _ptr(v), _ptr(lmk), _ptr(lmk_bias), _ptr(out),
+                                              _ptr(sel_idx), _ptr(lse), _stream(stream)))
+    return out, sel_idx, lse
 
 
 def hils_backward(q, k, v, lmk, lmk_bias, out, dout, sel_idx, lse, *, chunk_size, top_k,

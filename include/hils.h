@@ -130,6 +130,27 @@ hils_status hils_decode(const hils_params* p, const void* q, const void* q_ret, 
                         const void* v, const void* lmk, const float* lmk_bias, void* out,
                         int32_t* sel_idx, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* hils_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, math and results as hils_decode; its
+ * scratch memory (per-split top-K lists and per-chunk partial outputs) is a
+ * fixed array of hils_decode_noalloc_scratch_bytes() = 16 MiB inside the
+ * library, one per GPU, held until the process ends.  Nothing is allocated
+ * and nothing needs clearing between calls (every scratch entry a call reads,
+ * that call writes first).  Sizes that need more scratch than that
+ * (hils_workspace_size(p, HILS_OP_DECODE) > 16 MiB; decode_128k-sized
+ * batches need about 9 MB) give HILS_ERR_UNSUPPORTED before any launch.
+ * All calls on one GPU share its array: calls that may overlap on one GPU
+ * (different streams, or unordered host threads) race and must be serialised
+ * by the caller. */
+hils_status hils_decode_noalloc(const hils_params* p, const void* q, const void* q_ret,
+                                const void* k, const void* v, const void* lmk,
+                                const float* lmk_bias, void* out, int32_t* sel_idx, float* lse,
+                                void* stream);
+
+/* Size in bytes of hils_decode_noalloc's fixed scratch array. */
+size_t hils_decode_noalloc_scratch_bytes(void);
+
 /* Backward pass with the selection `sel_idx` (from hils_forward) held fixed
  * [HSADR §3 "Hierarchical softmax"; §9].  Writes (overwrites) dq, dk, dv,
  * dlmk and, if non-null, dlmk_bias.  `out` and `lse` are the forward's
