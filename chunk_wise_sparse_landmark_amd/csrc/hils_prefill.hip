@@ -43,7 +43,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kS = 64;
 constexpr int kG = 4;            // query heads per KV group on this path
-constexpr int kThreads = 256;            // prefill_select
+constexpr int kThreads = 512;            // prefill_select: eight waves, two per SIMD
 constexpr int kAttWaves = 8;             // prefill_attend: two waves per SIMD
 constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kWin = 64;         // queries per window (one chunk), both kernels
@@ -226,11 +226,15 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   for (int x = tid; x < kS * kD / 8; x += kThreads)
     reinterpret_cast<uint4*>(vs)[x] = reinterpret_cast<const uint4*>(Vc)[x];
 
-  // A operand: 16 queries of this wave x 4 heads x 4 k-steps
+  // scores: wave w computes the 16 rows of row group w % 4 against every
+  // other batch of 8 column tiles (half w / 4), so the two waves of a SIMD share
+  // the landmark loads of a row group and each searches its own 8 rows below
+  // A operand: 16 queries of this row group x 4 heads x 4 k-steps
+  const int rg = w & 3, ch = w >> 2;
   bf16x8 a[kG][4];
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
-    const uint16_t* qr = q + ((size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + w * 16 + r16) * kD + g4 * 8;
+    const uint16_t* qr = q + ((size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + rg * 16 + r16) * kD + g4 * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[h][ks] = ld8(qr + ks * 32);
   }
@@ -238,7 +242,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   const float sc = g.scale / (float)kG;
   const int ntile = (ncand + 15) / 16;
-  for (int nt0 = 0; nt0 < ntile; nt0 += 8) {
+  for (int nt0 = 8 * ch; nt0 < ntile; nt0 += 16) {
     bf16x8 bv[8][4];   // the loads of up to 8 column tiles in flight together
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
@@ -259,7 +263,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
       const int c = nt * 16 + r16;
       const float bc = (bb && c < ncand) ? bb[c] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gs[w * 16 + g4 * 4 + i][c] = acc[i] * sc + bc;
+      for (int i = 0; i < 4; ++i) gs[rg * 16 + g4 * 4 + i][c] = acc[i] * sc + bc;
     }
   }
 
@@ -291,22 +295,24 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     reinterpret_cast<uint4*>(vdst)[f] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 
-  // the wave's 16 rows, one at a time; the V staging area is each wave's
+  // the wave's 8 rows, one at a time; the V staging area is each wave's
   // compaction buffer from here on
   constexpr int NR = 1;
   __syncthreads();
   uint64_t* sbuf = reinterpret_cast<uint64_t*>(vs) + w * (kS * kD / 4 / (kThreads / kWave));
   static_assert(NR * kWave <= kS * kD / 4 / (kThreads / kWave), "compaction buffer");
-  for (int q0 = 0; q0 < 16; q0 += NR) {
+  constexpr int kRowsPerWave = kWin / (kThreads / kWave);
+  for (int q0 = 0; q0 < kRowsPerWave; q0 += NR) {
+    const int row = w * kRowsPerWave + q0;
     uint64_t keys[NR][R];
 #pragma unroll
     for (int n = 0; n < NR; ++n)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int c = r * kWave + lane;
-        keys[n][r] = c < ncand ? make_key(gs[w * 16 + q0 + n][c], c) : 0ull;
+        keys[n][r] = c < ncand ? make_key(gs[row + n][c], c) : 0ull;
       }
-    select_ascending<R, NR>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + w * 16 + q0) * g.K,
+    select_ascending<R, NR>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + row) * g.K,
                             (size_t)g.K, sbuf);
   }
 }
