@@ -43,7 +43,10 @@ namespace {
 constexpr int kD = 128;
 constexpr int kS = 64;
 constexpr int kG = 4;            // query heads per KV group on this path
-constexpr int kThreads = 512;            // prefill_select: eight waves, two per SIMD
+// prefill_select: with 4+ candidate blocks per row the score table fills the
+// LDS (one workgroup per CU), so eight waves (two per SIMD) interleave their
+// serial searches; with fewer, two workgroups of four waves share a CU
+constexpr int sel_threads(int R) { return R >= 4 ? 512 : 256; }
 constexpr int kAttWaves = 8;             // prefill_attend: two waves per SIMD
 constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kWin = 64;         // queries per window (one chunk), both kernels
@@ -200,7 +203,7 @@ __device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], 
 //      in which P leaves the S^T accumulators).
 // ----------------------------------------------------------------------------
 template <int R>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(sel_threads(R))
 prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
                const float* __restrict__ bias, int32_t* __restrict__ sel_idx,
@@ -223,6 +226,8 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const size_t row0 = (size_t)bkv * g.Lkv + (size_t)win * kS;
   const uint16_t* Vc = v + row0 * kD;
   const uint16_t* Kc = k + row0 * kD;
+  constexpr int kThreads = sel_threads(R);
+  constexpr int kSelWaves = kThreads / kWave;
   for (int x = tid; x < kS * kD / 8; x += kThreads)
     reinterpret_cast<uint4*>(vs)[x] = reinterpret_cast<const uint4*>(Vc)[x];
 
@@ -230,7 +235,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   // other batch of 8 column tiles (half w / 4), so the two waves of a SIMD share
   // the landmark loads of a row group and each searches its own 8 rows below
   // A operand: 16 queries of this row group x 4 heads x 4 k-steps
-  const int rg = w & 3, ch = w >> 2;
+  const int rg = w & 3, ch = w >> 2;        // (four waves: ch = 0, every batch)
   bf16x8 a[kG][4];
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
@@ -242,7 +247,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   const float sc = g.scale / (float)kG;
   const int ntile = (ncand + 15) / 16;
-  for (int nt0 = 8 * ch; nt0 < ntile; nt0 += 16) {
+  for (int nt0 = 8 * ch; nt0 < ntile; nt0 += 8 * (kSelWaves / 4)) {
     bf16x8 bv[8][4];   // the loads of up to 8 column tiles in flight together
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
@@ -789,7 +794,7 @@ template <int R>
 void launch_select(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const uint16_t* lmk, const float* bias, int32_t* sel_idx, uint16_t* kvf,
                    hipStream_t st) {
-  hipLaunchKernelGGL(prefill_select<R>, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(prefill_select<R>, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(sel_threads(R)), 0, st,
                      g, q, k, v, lmk, bias, sel_idx, kvf);
 }
 
