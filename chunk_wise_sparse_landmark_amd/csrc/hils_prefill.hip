@@ -247,17 +247,20 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
   const float sc = g.scale / (float)kG;
   const int ntile = (ncand + 15) / 16;
-  for (int nt0 = 8 * ch; nt0 < ntile; nt0 += 8 * (kSelWaves / 4)) {
-    bf16x8 bv[8][4];   // the loads of up to 8 column tiles in flight together
+  // column tiles per batch: 8 loads in flight with the score table filling the
+  // LDS; 4 with small tables, so that three workgroups fit a CU's registers
+  constexpr int kTiles = R >= 4 ? 8 : 4;
+  for (int nt0 = kTiles * ch; nt0 < ntile; nt0 += kTiles * (kSelWaves / 4)) {
+    bf16x8 bv[kTiles][4];   // the loads of up to kTiles column tiles in flight together
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < kTiles; ++x) {
       const int c = (nt0 + x) * 16 + r16;
       const int cl = c < ncand ? c : 0;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) bv[x][ks] = ld8(L + (size_t)cl * kD + g4 * 8 + ks * 32);
     }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < kTiles; ++x) {
       const int nt = nt0 + x;
       if (nt >= ntile) break;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};

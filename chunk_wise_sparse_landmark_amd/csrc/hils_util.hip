@@ -10,27 +10,27 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One thread per (b, kv head, query) row of K slots: an id is kept only when it
-// is a candidate of that query (a complete chunk before its local window,
-// [0, ncand)) and no earlier slot of the row holds it; anything else becomes -1,
-// which every backward kernel skips.  Positions are kept (a blanked slot stays
-// where it was).
+// One thread per selection entry (b, kv head, query, slot): the id is kept only
+// when it is a candidate of that query (a complete chunk before its local
+// window, [0, ncand)) and no earlier slot of the row holds it; anything else
+// becomes -1, which every backward kernel skips.  Positions are kept (a blanked
+// slot stays where it was).  The earlier slots of a row are the same cache lines
+// the neighbouring threads read.
 __global__ void __launch_bounds__(kThreads)
 sanitize_selection(Geometry g, const int32_t* __restrict__ in, int32_t* __restrict__ out,
-                   long long nrows) {
-  const long long r = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= nrows) return;
+                   long long nent) {
+  const long long e = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= nent) return;
+  const long long r = e / g.K;
+  const int s = (int)(e - r * g.K);
   const int i = (int)(r % g.Lq);
   int ncand, own, own_b;
   g.layout(i, ncand, own, own_b);
   const int32_t* src = in + r * g.K;
-  int32_t* dst = out + r * g.K;
-  for (int s = 0; s < g.K; ++s) {
-    const int c = src[s];
-    bool keep = c >= 0 && c < ncand;
-    for (int t = 0; t < s && keep; ++t) keep = src[t] != c;
-    dst[s] = keep ? c : -1;
-  }
+  const int c = src[s];
+  bool keep = c >= 0 && c < ncand;
+  for (int t = 0; t < s && keep; ++t) keep = src[t] != c;
+  out[e] = keep ? c : -1;
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -49,10 +49,10 @@ size_t sanitized_selection_bytes(const Geometry& g) {
 
 hipError_t launch_sanitize_selection(const Geometry& g, const int32_t* in, int32_t* out,
                                      hipStream_t st) {
-  const long long nrows = (long long)g.B * g.Hkv * g.Lq;
-  if (nrows == 0) return hipSuccess;
-  const unsigned nb = (unsigned)((nrows + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(sanitize_selection, dim3(nb), dim3(kThreads), 0, st, g, in, out, nrows);
+  const long long nent = (long long)g.B * g.Hkv * g.Lq * g.K;
+  if (nent == 0) return hipSuccess;
+  const unsigned nb = (unsigned)((nent + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(sanitize_selection, dim3(nb), dim3(kThreads), 0, st, g, in, out, nent);
   return hipGetLastError();
 }
 
