@@ -208,7 +208,8 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x)
-      if (j0 + x * kMergeWaves < nsplit) run = wave_merge_into(run, key[x], g.K, buf[w]);
+      if (j0 + x * kMergeWaves < nsplit)
+        run = (j0 == w && x == 0) ? key[0] : wave_merge_into(run, key[x], g.K, buf[w]);
   }
   wl[w][lane] = lane < g.K ? run : 0ull;
   __syncthreads();
@@ -222,9 +223,10 @@ decode_merge(Geometry g, int nsplit, const uint64_t* __restrict__ lists,
     __syncthreads();
   }
   if (w == 0) {
+    // ascending ids: a rank sort of the complemented ids (unique, 0 = none)
     const uint64_t top = wl[0][lane];
     uint64_t asc = (lane < g.K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
-    asc = wave_sort64_desc(asc);
+    asc = wave_rank_sort64(asc, buf[0]);
     if (lane < g.K) sel_idx[(size_t)bkv * g.K + lane] = asc ? (int)(0xffffffffull - (asc - 1)) : -1;
   }
 }
