@@ -50,14 +50,20 @@ __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
 }
 
 // ----------------------------------------------------------------------------
-// 1. scores + local top-K.  A workgroup owns cps = nit * 256 consecutive
-//    candidates (nit <= kMaxIt); in iteration i wave w scores a block of 64
+// 1. scores + local top-K.  A workgroup owns cps = NIT * 256 consecutive
+//    candidates (NIT <= kMaxIt); in iteration i wave w scores a block of 64
 //    rows (16 lanes x 16 B per 256 B row, each load instruction covering 4
 //    consecutive rows = 1 KB, the next block's loads issued before
 //    this one is scored) and keeps the block's keys in registers.  The wave's
 //    exact top-K is then found by a bit-by-bit search for the K-th largest key
 //    (wave ballots, no sorting), compacted, sorted once, and the four wave
 //    lists are merged.
+//    No load is predicated: a row past the split's end re-reads the split's
+//    last row (its key is dropped).  A predicated load puts a branch around
+//    it, and the compiler then waits for every outstanding load after the
+//    branch, so the next block would no longer be in flight while one is
+//    scored; the block count and the bias are template parameters for the
+//    same reason.
 // ----------------------------------------------------------------------------
 constexpr int kMaxIt = 4;
 
@@ -65,13 +71,14 @@ constexpr int kMaxIt = 4;
 // K of them, else a value no larger than the smallest valid key.  The low word
 // of a key is the complemented chunk id; ids below 2^idbits leave its bits
 // idbits..31 set, so only the 32 score bits and idbits id bits are searched.
-__device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&kk)[kMaxIt], int K, int idbits) {
+template <int N>
+__device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&kk)[N], int K, int idbits) {
   uint64_t p = 0;
   for (int bit = 63; bit >= 32; --bit) {
     const uint64_t t = p | (1ull << bit);
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < kMaxIt; ++r) cnt += __popcll(__ballot(kk[r] >= t));
+    for (int r = 0; r < N; ++r) cnt += __popcll(__ballot(kk[r] >= t));
     if (cnt >= K) p = t;
   }
   p |= (uint64_t)(0xffffffffu << idbits);
@@ -79,16 +86,17 @@ __device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&kk)[kMaxIt], i
     const uint64_t t = p | (1ull << bit);
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < kMaxIt; ++r) cnt += __popcll(__ballot(kk[r] >= t));
+    for (int r = 0; r < N; ++r) cnt += __popcll(__ballot(kk[r] >= t));
     if (cnt >= K) p = t;
   }
   return p;
 }
 
+template <int NIT, bool kBias>
 __global__ void __launch_bounds__(kThreads)
 decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ lmk,
-                    const float* __restrict__ bias, int ncand, int cps, int nit, int nsplit,
-                    int idbits, uint64_t* __restrict__ lists) {
+                    const float* __restrict__ bias, int ncand, int cps, int nsplit, int idbits,
+                    uint64_t* __restrict__ lists) {
   __shared__ uint64_t buf[4][kWave];
   __shared__ uint64_t wl[4][kWave];
   const int split = blockIdx.x, bkv = blockIdx.y;
@@ -99,39 +107,62 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
 
   const int c0 = split * cps;
   const int c1 = min(c0 + cps, ncand);
+  uint64_t* dst = lists + ((size_t)bkv * nsplit + split) * K;
+  if (c1 <= c0) {                          // no candidates: an empty list
+    if (w == 0 && lane < K) dst[lane] = 0ull;
+    return;
+  }
   const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
-  const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
+  // the row this lane scores in iteration it (x == sub below), clamped
+  auto my_row = [&](int it) { return c0 + (it * 4 + w) * kWave + 4 * sub + grp; };
   auto load_block = [&](int it, uint4 (&raw)[16]) {
     const int base = c0 + (it * 4 + w) * kWave;   // this wave's block of 64
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const int c = base + 4 * x + grp;           // 4 consecutive rows (1 KB) per load
-      raw[x] = c < c1 ? *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8)
-                      : make_uint4(0, 0, 0, 0);
+      const int c = min(base + 4 * x + grp, c1 - 1);   // 4 consecutive rows (1 KB) per load
+      raw[x] = *reinterpret_cast<const uint4*>(L + (size_t)c * kD + sub * 8);
     }
   };
+  // retrieval query: the first four heads' loads go out with the first block's
+  const uint16_t* qg = q + (size_t)(b * g.Hq + kvh * g.G) * kD + sub * 8;
+  uint4 qh[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) qh[h] = *reinterpret_cast<const uint4*>(qg + (size_t)min(h, g.G - 1) * kD);
+  float qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int h = 4; h < g.G; ++h) {          // heads past four (G > 4 only)
+    float x[8];
+    load_bf16x8(qg + (size_t)h * kD, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[e] += x[e];
+  }
+  float bv[NIT];
+  if (kBias) {
+    const float* bb = bias + (size_t)bkv * g.NCcap;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) bv[it] = bb[min(my_row(it), c1 - 1)];
+  }
   uint4 cur[16], nxt[16];
   load_block(0, cur);
 
   // this lane's 8 dims of the mean query
-  float qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int h = 0; h < g.G; ++h) {
-    float x[8];
-    load_bf16x8(q + (size_t)(b * g.Hq + kvh * g.G + h) * kD + sub * 8, x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qb[e] += x[e];
+  for (int h = 0; h < 4; ++h) {
+    const float f = h < g.G ? 1.f : 0.f;
+    const uint32_t u[4] = {qh[h].x, qh[h].y, qh[h].z, qh[h].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qb[2 * e] += f * __uint_as_float(u[e] << 16);
+      qb[2 * e + 1] += f * __uint_as_float(u[e] & 0xffff0000u);
+    }
   }
   const float inv = g.scale / (float)g.G;
 #pragma unroll
   for (int e = 0; e < 8; ++e) qb[e] *= inv;
 
-  uint64_t kk[kMaxIt];
+  uint64_t kk[NIT];
 #pragma unroll
-  for (int it = 0; it < kMaxIt; ++it) {
-    kk[it] = 0ull;
-    if (it >= nit) continue;
-    if (it + 1 < nit) load_block(it + 1, nxt);
-    const int base = c0 + (it * 4 + w) * kWave;
+  for (int it = 0; it < NIT; ++it) {
+    if (it + 1 < NIT) load_block(it + 1, nxt);
     float mine = 0.f;
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -147,16 +178,18 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
       sc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sc), 0x121, 0xf, 0xf, false));
       if (x == sub) mine = sc;
     }
-    const int c = base + 4 * sub + grp;   // the row this lane scored (x == sub)
-    kk[it] = c < c1 ? make_key(mine + (bb ? bb[c] : 0.f), c) : 0ull;
+    const int c = my_row(it);
+    kk[it] = c < c1 ? make_key(mine + (kBias ? bv[it] : 0.f), c) : 0ull;
+    if (it + 1 < NIT) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) cur[x] = nxt[x];
+      for (int x = 0; x < 16; ++x) cur[x] = nxt[x];
+    }
   }
   // exact top-K of the wave's keys: the keys >= the K-th largest, compacted and sorted
   const uint64_t p = wave_kth_key(kk, K, idbits);
   int cntk = 0;
 #pragma unroll
-  for (int it = 0; it < kMaxIt; ++it) {
+  for (int it = 0; it < NIT; ++it) {
     const bool pred = kk[it] != 0ull && kk[it] >= p;
     const uint64_t m = __ballot(pred);
     if (pred) buf[w][cntk + mask_rank(m)] = kk[it];
@@ -177,8 +210,20 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   __syncthreads();
   if (w == 0) {
     const uint64_t t = wave_merge_into(wl[0][lane], wl[2][lane], K, buf[0]);
-    if (lane < K) lists[((size_t)bkv * nsplit + split) * K + lane] = t;
+    if (lane < K) dst[lane] = t;
   }
+}
+
+template <int NIT>
+void launch_score(dim3 grid, hipStream_t st, const Geometry& g, const uint16_t* q,
+                  const uint16_t* lmk, const float* bias, int ncand, int cps, int nsplit,
+                  int idbits, uint64_t* lists) {
+  if (bias)
+    hipLaunchKernelGGL((decode_score_select<NIT, true>), grid, dim3(kThreads), 0, st, g, q, lmk,
+                       bias, ncand, cps, nsplit, idbits, lists);
+  else
+    hipLaunchKernelGGL((decode_score_select<NIT, false>), grid, dim3(kThreads), 0, st, g, q, lmk,
+                       bias, ncand, cps, nsplit, idbits, lists);
 }
 
 // ----------------------------------------------------------------------------
@@ -706,8 +751,13 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
   const uint16_t* Lm = (const uint16_t*)lmk;
   dim3 g1(p.nsplit, bkv);
   prof_begin(kDecodeScore, st);
-  hipLaunchKernelGGL(decode_score_select, g1, dim3(kThreads), 0, st, g, QR, Lm, bias, p.ncand,
-                     p.cps, p.nit, p.nsplit, p.idbits, d.lists);
+  static_assert(kMaxIt == 4, "one scoring instance per block count");
+  switch (p.nit) {
+    case 1: launch_score<1>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
+    case 2: launch_score<2>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
+    case 3: launch_score<3>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
+    default: launch_score<4>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
+  }
   prof_end(kDecodeScore, st);
   prof_begin(kDecodeMerge, st);
   if (p.nsplit <= 8)
