@@ -5,18 +5,20 @@
 // "Sparse training", GQA-shared selection §4 "Architecture", per-chunk softmax
 // and score-weighted fusion §3 "Hierarchical softmax".
 //
-// Four launches on the caller's stream:
+// Four launches on the caller's stream (three when one scoring workgroup per
+// (b, kv head) covers every candidate):
 //  1. score_select  grid (nsplit, B*Hkv): each workgroup streams a contiguous
 //     range of landmark rows (16 lanes x 16 B per 256 B row, coalesced), forms
 //     the group score scale*<mean_h q_h, lmk_c> + bias_c (the group mean is
-//     linear in q), and keeps its local top-K as composite keys.
+//     linear in q), and keeps its local top-K as composite keys; with a
+//     single split it writes the ascending chunk ids itself.
 //  2. merge         grid (B*Hkv): top-K of the nsplit local lists; writes the
 //     ascending chunk ids.
 //  3. attend        grid (nsplit', B*Hkv): each workgroup walks one or a few
 //     of the K+1 fusion slots (selected chunks and the own chunk), reading
-//     each chunk's 16 KB of K and 16 KB of V once for all G heads with the
-//     next chunk's loads in flight, and folds the chunk outputs into a running
-//     (max score, weight sum, weighted output) per head.
+//     each chunk's 16 KB of K and 16 KB of V once for all G heads, and folds
+//     the chunk outputs into a running (max score, weight sum, weighted
+//     output) per head.
 //  4. fuse          one wave per (b, q head): log-sum-exp merge of the
 //     nsplit' partials.  (A separate launch: on this multi-XCD part a
 //     device-scope fence per workgroup -- needed for a last-workgroup
@@ -92,13 +94,16 @@ __device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&kk)[N], int K,
   return p;
 }
 
-template <int NIT, bool kBias>
-__global__ void __launch_bounds__(kThreads)
+// W waves per workgroup.  kFinal: one workgroup covers every candidate of its
+// (b, kv head) and writes the selection itself (ascending ids into sel_idx),
+// so no merge launch follows.
+template <int W, int NIT, bool kBias, bool kFinal>
+__global__ void __launch_bounds__(W * kWave)
 decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ lmk,
                     const float* __restrict__ bias, int ncand, int cps, int nsplit, int idbits,
-                    uint64_t* __restrict__ lists) {
-  __shared__ uint64_t buf[4][kWave];
-  __shared__ uint64_t wl[4][kWave];
+                    uint64_t* __restrict__ lists, int32_t* __restrict__ sel_idx) {
+  __shared__ uint64_t buf[W][kWave];
+  __shared__ uint64_t wl[W][kWave];
   const int split = blockIdx.x, bkv = blockIdx.y;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -107,16 +112,19 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
 
   const int c0 = split * cps;
   const int c1 = min(c0 + cps, ncand);
-  uint64_t* dst = lists + ((size_t)bkv * nsplit + split) * K;
+  uint64_t* dst = kFinal ? nullptr : lists + ((size_t)bkv * nsplit + split) * K;
   if (c1 <= c0) {                          // no candidates: an empty list
-    if (w == 0 && lane < K) dst[lane] = 0ull;
+    if (w == 0 && lane < K) {
+      if (kFinal) sel_idx[(size_t)bkv * K + lane] = -1;
+      else dst[lane] = 0ull;
+    }
     return;
   }
   const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
   // the row this lane scores in iteration it (x == sub below), clamped
-  auto my_row = [&](int it) { return c0 + (it * 4 + w) * kWave + 4 * sub + grp; };
+  auto my_row = [&](int it) { return c0 + (it * W + w) * kWave + 4 * sub + grp; };
   auto load_block = [&](int it, uint4 (&raw)[16]) {
-    const int base = c0 + (it * 4 + w) * kWave;   // this wave's block of 64
+    const int base = c0 + (it * W + w) * kWave;   // this wave's block of 64
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       const int c = min(base + 4 * x + grp, c1 - 1);   // 4 consecutive rows (1 KB) per load
@@ -204,26 +212,38 @@ decode_score_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint64_t run = wave_rank_sort64(sel, buf[w]);
   wl[w][lane] = lane < K ? run : 0ull;
-  __syncthreads();
-  // the four wave lists merged in a tree: waves 0 and 2 in parallel, then wave 0
-  if (w == 0 || w == 2) wl[w][lane] = wave_merge_into(wl[w][lane], wl[w + 1][lane], K, buf[w]);
-  __syncthreads();
+  // the wave lists merged pairwise in a tree (waves 0, 2, .. then 0, 4, ..)
+#pragma unroll
+  for (int st = 1; st < W; st <<= 1) {
+    __syncthreads();
+    if (w % (2 * st) == 0) {
+      const uint64_t mg = wave_merge_into(wl[w][lane], wl[w + st][lane], K, buf[w]);
+      wl[w][lane] = lane < K ? mg : 0ull;
+    }
+  }
   if (w == 0) {
-    const uint64_t t = wave_merge_into(wl[0][lane], wl[2][lane], K, buf[0]);
-    if (lane < K) dst[lane] = t;
+    const uint64_t top = wl[0][lane];
+    if (kFinal) {
+      // ascending ids: a rank sort of the complemented ids (unique, 0 = none)
+      uint64_t asc = (lane < K && top != 0) ? (0xffffffffull - (uint64_t)key_index(top)) + 1 : 0;
+      asc = wave_rank_sort64(asc, buf[0]);
+      if (lane < K) sel_idx[(size_t)bkv * K + lane] = asc ? (int)(0xffffffffull - (asc - 1)) : -1;
+    } else if (lane < K) {
+      dst[lane] = top;
+    }
   }
 }
 
-template <int NIT>
+template <int W, int NIT, bool kFinal>
 void launch_score(dim3 grid, hipStream_t st, const Geometry& g, const uint16_t* q,
                   const uint16_t* lmk, const float* bias, int ncand, int cps, int nsplit,
-                  int idbits, uint64_t* lists) {
+                  int idbits, uint64_t* lists, int32_t* sel_idx) {
   if (bias)
-    hipLaunchKernelGGL((decode_score_select<NIT, true>), grid, dim3(kThreads), 0, st, g, q, lmk,
-                       bias, ncand, cps, nsplit, idbits, lists);
+    hipLaunchKernelGGL((decode_score_select<W, NIT, true, kFinal>), grid, dim3(W * kWave), 0, st, g,
+                       q, lmk, bias, ncand, cps, nsplit, idbits, lists, sel_idx);
   else
-    hipLaunchKernelGGL((decode_score_select<NIT, false>), grid, dim3(kThreads), 0, st, g, q, lmk,
-                       bias, ncand, cps, nsplit, idbits, lists);
+    hipLaunchKernelGGL((decode_score_select<W, NIT, false, kFinal>), grid, dim3(W * kWave), 0, st,
+                       g, q, lmk, bias, ncand, cps, nsplit, idbits, lists, sel_idx);
 }
 
 // ----------------------------------------------------------------------------
@@ -689,6 +709,7 @@ decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* _
 
 struct DecodePlan {
   int ncand, nit, cps, nsplit, idbits;
+  bool fused;           // one 8-wave scoring workgroup per (b, kv head) writes the selection
   int apc, asplit;      // attention: fusion slots per workgroup, workgroups per (b, kv head)
 };
 
@@ -701,11 +722,21 @@ DecodePlan plan(const Geometry& g) {
   // blocks of 64 candidates per wave; fewer, longer splits leave fewer lists
   // to merge (at 16 x 8 (b, kv head) pairs and 2047 candidates, two splits of
   // four blocks per wave beat four splits of two by about 2 us per step)
-  const int want_splits = max(1, 256 / max(1, bkv));
-  const int per = (p.ncand + want_splits - 1) / want_splits;
-  p.nit = min(kMaxIt, max(1, (per + 255) / 256));
-  p.cps = 256 * p.nit;
-  p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
+  // When eight waves of up to kMaxIt blocks cover a pair's candidates and
+  // the pairs fill at least half the CUs, one workgroup per pair scores,
+  // selects and writes the ascending ids itself: no list merge launch.
+  p.fused = p.ncand <= 8 * kMaxIt * kWave && bkv >= 128;
+  if (p.fused) {
+    p.nit = max(1, (p.ncand + 8 * kWave - 1) / (8 * kWave));
+    p.cps = 8 * kWave * p.nit;
+    p.nsplit = 1;
+  } else {
+    const int want_splits = max(1, 256 / max(1, bkv));
+    const int per = (p.ncand + want_splits - 1) / want_splits;
+    p.nit = min(kMaxIt, max(1, (per + 255) / 256));
+    p.cps = 256 * p.nit;
+    p.nsplit = max(1, (p.ncand + p.cps - 1) / p.cps);
+  }
   p.idbits = 1;
   while (p.idbits < 32 && (1ll << p.idbits) < (long long)max(p.ncand, 1)) ++p.idbits;
   // attention: one fusion slot per workgroup (latency hidden by parallelism)
@@ -752,20 +783,31 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
   dim3 g1(p.nsplit, bkv);
   prof_begin(kDecodeScore, st);
   static_assert(kMaxIt == 4, "one scoring instance per block count");
-  switch (p.nit) {
-    case 1: launch_score<1>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
-    case 2: launch_score<2>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
-    case 3: launch_score<3>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
-    default: launch_score<4>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists); break;
+  if (p.fused) {
+    switch (p.nit) {
+      case 1: launch_score<8, 1, true>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, 1, p.idbits, d.lists, sel_idx); break;
+      case 2: launch_score<8, 2, true>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, 1, p.idbits, d.lists, sel_idx); break;
+      case 3: launch_score<8, 3, true>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, 1, p.idbits, d.lists, sel_idx); break;
+      default: launch_score<8, 4, true>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, 1, p.idbits, d.lists, sel_idx); break;
+    }
+  } else {
+    switch (p.nit) {
+      case 1: launch_score<4, 1, false>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists, sel_idx); break;
+      case 2: launch_score<4, 2, false>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists, sel_idx); break;
+      case 3: launch_score<4, 3, false>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists, sel_idx); break;
+      default: launch_score<4, 4, false>(g1, st, g, QR, Lm, bias, p.ncand, p.cps, p.nsplit, p.idbits, d.lists, sel_idx); break;
+    }
   }
   prof_end(kDecodeScore, st);
-  prof_begin(kDecodeMerge, st);
-  if (p.nsplit <= 8)
-    hipLaunchKernelGGL(decode_merge<1>, dim3(bkv), dim3(kWave), 0, st, g, p.nsplit, d.lists, sel_idx);
-  else
-    hipLaunchKernelGGL(decode_merge<16>, dim3(bkv), dim3(16 * kWave), 0, st, g, p.nsplit, d.lists,
-                       sel_idx);
-  prof_end(kDecodeMerge, st);
+  if (!p.fused) {
+    prof_begin(kDecodeMerge, st);
+    if (p.nsplit <= 8)
+      hipLaunchKernelGGL(decode_merge<1>, dim3(bkv), dim3(kWave), 0, st, g, p.nsplit, d.lists, sel_idx);
+    else
+      hipLaunchKernelGGL(decode_merge<16>, dim3(bkv), dim3(16 * kWave), 0, st, g, p.nsplit, d.lists,
+                         sel_idx);
+    prof_end(kDecodeMerge, st);
+  }
   prof_begin(kDecodeAttend, st);
   if (g.G == 4)
     hipLaunchKernelGGL(decode_attend4, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,

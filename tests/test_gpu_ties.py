@@ -131,9 +131,13 @@ def test_prefill_ties(hl, name):
     assert check_forward(host, cfg, out, idx, lse, queries=qs) == 0
 
 
-# decode: 8 score splits (single-wave merge) and 128 splits (16-wave merge);
-# the tied chunks sit in different splits
+# decode: 8 score splits (single-wave merge), 128 splits (16-wave merge), and
+# one eight-wave scoring workgroup per (b, kv head) that writes the selection
+# itself (16 x 8 pairs, at most 2048 candidates); the tied chunks sit in
+# different splits or waves
 DECODE = {
+    "fused_all_equal": (config("decode_128k", lmk="iid", seed=57), "all_equal"),
+    "fused_kth": (config("decode_128k", Lkv=70000, lmk="iid", seed=58), "kth"),
     "split8_all_equal": (config("decode_128k", B=2, Hkv=2, Hq=8, lmk="iid", seed=51), "all_equal"),
     "split8_kth": (config("decode_128k", B=2, Hkv=2, Hq=8, lmk="iid", seed=52), "kth"),
     "split128_all_equal_k64": (config("decode_4m", Hkv=2, Hq=8, Lkv=1 << 21, lmk="iid", seed=53),
@@ -160,11 +164,12 @@ def test_decode_ties(hl, name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("G,win", [(4, 1), (4, 8), (2, 3)])
-def test_decode_values_one_give_output_one(hl, G, win):
-    """V = 1 gives O = 1 through the split decode path: the fusion weights of the
-    selected chunks and the window sum to one (bf16 P and O rounding only)."""
-    cfg = config("decode_128k", B=2, Hkv=2, Hq=2 * G, Lkv=70000, K=32, win=win, seed=56)
+@pytest.mark.parametrize("G,win,B,Hkv", [(4, 1, 2, 2), (4, 8, 2, 2), (2, 3, 2, 2), (4, 1, 16, 8)])
+def test_decode_values_one_give_output_one(hl, G, win, B, Hkv):
+    """V = 1 gives O = 1 through the split decode path (and, at 16 x 8 pairs, the
+    single-workgroup selection): the fusion weights of the selected chunks and
+    the window sum to one (bf16 P and O rounding only)."""
+    cfg = config("decode_128k", B=B, Hkv=Hkv, Hq=Hkv * G, Lkv=70000, K=32, win=win, seed=56)
     host, dev = make_device_inputs(cfg)
     dev["v"] = torch.ones_like(dev["v"])
     out, idx, lse = _run(hl, cfg, dev, "decode")
