@@ -264,6 +264,25 @@ def copy_calibration():
     torch.cuda.empty_cache()
 
 
+def hbm_read_probe(ev, nwg=1024, window_mib=128, total_mib=2048, launches=48):
+    """GB/s of a plain streaming read (hils_inputs' read_u4) over rotating 128 MiB
+    windows of a 2 GiB buffer: a window is read again only after 1.9 GiB of other
+    reads, so the last-level cache cannot serve it.  This is the read rate the part
+    sustains by itself, beside the 8 TB/s peak the rooflines use."""
+    import torch
+    from hils_inputs.device import device_read
+    buf = torch.empty(total_mib * 2 ** 20, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(nwg * 256, dtype=torch.int32, device="cuda")
+    nwin, wb = total_mib // window_mib, window_mib * 2 ** 20
+    ms, n = timed_batch(lambda i: device_read(buf[(i % nwin) * wb:], wb, sink, nwg), launches, ev)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"read_GBps": wb / (ms * 1e-3) / 1e9, "bytes_per_launch": wb, "workgroups": nwg,
+            "launches": n, "buffer_bytes": total_mib * 2 ** 20,
+            "kernel": "read_u4 (hils_inputs): 4 x 16 B loads in flight per thread"}
+
+
 # --------------------------------------------------------------------------- runners
 def timed(step, steps, warmup, ev, kernel, hl):
     """Run warmup + timed steps; returns (ms per step, avg ms of `kernel` launches)."""
@@ -741,6 +760,8 @@ def main():
             if key in r:
                 line[key] = r[key]
     line["extra"] = extra
+    line["hbm_read_probe"] = hbm_read_probe(ev)
+    log("hbm read probe: %.0f GB/s" % line["hbm_read_probe"]["read_GBps"])
     if args.calibrate_copy:
         copy_calibration()
     if not args.no_cpu:

@@ -30,6 +30,9 @@ def _fill_lib():
         _lib.hils_inputs_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                           ctypes.c_void_p]
         _lib.hils_inputs_copy.restype = ctypes.c_int
+        _lib.hils_inputs_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+        _lib.hils_inputs_read.restype = ctypes.c_int
     return _lib
 
 
@@ -120,3 +123,14 @@ def make_decode_inputs_on_device(cfg, device="cuda", kv_from=None):
         fill_normal(t, cfg["seed"], name)
         dev[name] = t
     return dev
+
+
+def device_read(src, nbytes, sink, nwg):
+    """Streaming read of the first `nbytes` of contiguous device tensor `src` by
+    `nwg` workgroups (one word per thread into `sink`, nwg * 256 int32)."""
+    assert src.is_contiguous() and sink.is_contiguous()
+    assert nbytes <= src.numel() * src.element_size() and sink.numel() * sink.element_size() >= nwg * 1024
+    st = torch.cuda.current_stream().cuda_stream
+    if _fill_lib().hils_inputs_read(ctypes.c_void_p(src.data_ptr()), nbytes,
+                                    ctypes.c_void_p(sink.data_ptr()), nwg, ctypes.c_void_p(st)) != 0:
+        raise RuntimeError("device read failed")

@@ -93,3 +93,28 @@ extern "C" int hils_inputs_copy(void* dst, const void* src, uint64_t bytes, void
                      (uint4*)dst, n);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
+
+// Plain streaming read of whole 16-byte words: workgroup g reads the g-th of
+// `nwg` equal contiguous segments, four 16-byte loads in flight per thread, and
+// writes one word per thread to `sink` (nwg * 256 words) so the loads are kept.
+// It measures the read bandwidth the part sustains on its own, next to which the
+// kernels' own rates are read.
+__global__ void __launch_bounds__(256) read_u4(const uint4* __restrict__ src, uint64_t seg,
+                                               uint32_t* __restrict__ sink) {
+  const uint4* p = src + (uint64_t)blockIdx.x * seg;
+  uint32_t acc = 0;
+  for (uint64_t i = threadIdx.x; i < seg; i += 4 * 256) {
+    const uint4 a = p[i], b = p[i + 256], c = p[i + 512], d = p[i + 768];
+    acc ^= a.x ^ b.y ^ c.z ^ d.w;
+  }
+  sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+extern "C" int hils_inputs_read(const void* src, uint64_t bytes, void* sink, int nwg, void* stream) {
+  // whole segments of 4 x 256 words per workgroup, 16-byte aligned
+  if (nwg <= 0 || ((uintptr_t)src % 16) != 0 || bytes % ((uint64_t)nwg * 4 * 256 * 16) != 0) return 1;
+  const uint64_t seg = bytes / 16 / (uint64_t)nwg;
+  hipLaunchKernelGGL(read_u4, dim3(nwg), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, seg,
+                     (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
