@@ -283,6 +283,20 @@ def hbm_read_probe(ev, nwg=1024, window_mib=128, total_mib=2048, launches=48):
             "kernel": "read_u4 (hils_inputs): 4 x 16 B loads in flight per thread"}
 
 
+def mfma_probe(ev, iters=2048, launches=6):
+    """TFLOP/s of a plain dense bf16 MFMA loop (hils_inputs' mfma_loop: 256
+    workgroups x 8 waves, eight independent 16x16x32 chains per wave, operands
+    in registers): the matrix rate the part sustains by itself, beside the
+    2.5 PFLOP/s peak the rooflines use."""
+    import torch
+    from hils_inputs.device import device_mfma_loop
+    sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    ms, n = timed_batch(lambda i: device_mfma_loop(iters, sink), launches, ev)
+    flops = 256 * 8 * iters * 8 * 2.0 * 16 * 16 * 32
+    return {"TFLOPs": flops / (ms * 1e-3) / 1e12, "flops_per_launch": flops, "launches": n,
+            "kernel": "mfma_loop (hils_inputs): 16x16x32 bf16, 8 chains per wave, 2 waves per SIMD"}
+
+
 # --------------------------------------------------------------------------- runners
 def timed(step, steps, warmup, ev, kernel, hl):
     """Run warmup + timed steps; returns (ms per step, avg ms of `kernel` launches)."""
@@ -762,6 +776,8 @@ def main():
     line["extra"] = extra
     line["hbm_read_probe"] = hbm_read_probe(ev)
     log("hbm read probe: %.0f GB/s" % line["hbm_read_probe"]["read_GBps"])
+    line["mfma_probe"] = mfma_probe(ev)
+    log("mfma probe: %.0f TFLOP/s" % line["mfma_probe"]["TFLOPs"])
     if args.calibrate_copy:
         copy_calibration()
     if not args.no_cpu:

@@ -33,6 +33,8 @@ def _fill_lib():
         _lib.hils_inputs_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                           ctypes.c_int, ctypes.c_void_p]
         _lib.hils_inputs_read.restype = ctypes.c_int
+        _lib.hils_inputs_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        _lib.hils_inputs_mfma_loop.restype = ctypes.c_int
     return _lib
 
 
@@ -134,3 +136,13 @@ def device_read(src, nbytes, sink, nwg):
     if _fill_lib().hils_inputs_read(ctypes.c_void_p(src.data_ptr()), nbytes,
                                     ctypes.c_void_p(sink.data_ptr()), nwg, ctypes.c_void_p(st)) != 0:
         raise RuntimeError("device read failed")
+
+
+def device_mfma_loop(iters, sink):
+    """256 workgroups x 8 waves of eight independent 16x16x32 bf16 MFMA chains,
+    `iters` rounds each (one word per thread into `sink`, 256 * 512 floats)."""
+    assert sink.is_contiguous() and sink.numel() * sink.element_size() >= 256 * 512 * 4
+    st = torch.cuda.current_stream().cuda_stream
+    if _fill_lib().hils_inputs_mfma_loop(int(iters), ctypes.c_void_p(sink.data_ptr()),
+                                         ctypes.c_void_p(st)) != 0:
+        raise RuntimeError("device MFMA loop failed")

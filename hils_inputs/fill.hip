@@ -118,3 +118,36 @@ extern "C" int hils_inputs_read(const void* src, uint64_t bytes, void* sink, int
                      (uint32_t*)sink);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
+
+// Plain matrix-core loop: every wave of 256 workgroups x 8 waves runs `iters`
+// rounds of eight independent 16x16x32 bf16 MFMA chains on register operands
+// and writes one word per thread to `sink` (256 * 512 words).  It measures the
+// dense bf16 rate the part sustains by itself, beside the 2.5 PFLOP/s peak.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 probe_bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float probe_f32x4;
+__global__ void __launch_bounds__(512) mfma_loop(int iters, float seed, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  probe_bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (float)(lane + i));
+    b[i] = (__bf16)(seed * (float)(lane - i));
+  }
+  probe_f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = probe_f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][3];
+  sink[(uint64_t)blockIdx.x * 512 + threadIdx.x] = s;
+}
+
+extern "C" int hils_inputs_mfma_loop(int iters, void* sink, void* stream) {
+  if (iters <= 0) return 1;
+  hipLaunchKernelGGL(mfma_loop, dim3(256), dim3(512), 0, (hipStream_t)stream, iters, 1e-3f,
+                     (float*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
