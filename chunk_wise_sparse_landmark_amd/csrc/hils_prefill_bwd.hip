@@ -624,7 +624,7 @@ struct TileBuf {
   float4 st[32];
 };
 struct ChunkSmem {
-  TileBuf tb[2];
+  TileBuf tb[4];                    // two tiles computed while the next two are copied in
   uint16_t eq[kTilesPerItem * 8];   // tile entries: query
   uint8_t es[kTilesPerItem * 8];    // slot (K + j = window member j), 0xff = padding
   int scan[kChunkThreads];
@@ -683,17 +683,13 @@ __device__ __forceinline__ uint2 tile_heads_at_dim(const uint4* __restrict__ til
   return u;
 }
 
-// One tile: start copying the next tile into `nxt`, then accumulate this one.
-// `tb` and `nxt` are restrict (distinct buffers), so the LDS reads of this
-// tile need not wait for the copy.
-__device__ __forceinline__ void chunk_tile_step(
-    const Geometry& g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-    const BwdWs& ws, int b, int kvh, int bkv, int w, int lane, int key, float sc2, int t,
-    bool more, const TileBuf* __restrict__ tbp, TileBuf* __restrict__ nxt,
-    const uint16_t* __restrict__ eq, const uint8_t* __restrict__ es, const bf16x8 (&kB)[4],
-    const bf16x8 (&vB)[4], f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[8], float& dbt) {
+// Accumulate one staged tile.
+__device__ __forceinline__ void chunk_tile_compute(
+    const Geometry& g, int w, int lane, int key, float sc2, int t,
+    const TileBuf* __restrict__ tbp, const uint16_t* __restrict__ eq,
+    const uint8_t* __restrict__ es, const bf16x8 (&kB)[4], const bf16x8 (&vB)[4],
+    f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[8], float& dbt) {
   const TileBuf& tb = *tbp;
-  if (more) stage_tile(g, q, dout, ws, b, kvh, bkv, eq, es, t + 1, *nxt);
   // S and U for this wave's keys; D layout rows (mt, qq = l/16, h = i), key l%16
   f32x4 s[2], u[2];
 #pragma unroll
@@ -756,7 +752,26 @@ __device__ __forceinline__ void chunk_tile_step(
   }
 }
 
-__global__ void __launch_bounds__(kChunkThreads)
+// Tiles t and t + 1 (staged in a, b) are accumulated while tiles t + 2 and
+// t + 3 are copied into c, d: two tiles of each workgroup in flight while it
+// computes (with one, the gather of q and dO waits on its latency).  All four
+// buffers are restrict, so the LDS reads of a and b need not wait for the
+// copies into c and d.
+__device__ __forceinline__ void chunk_pair_step(
+    const Geometry& g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
+    const BwdWs& ws, int b, int kvh, int bkv, int w, int lane, int key, float sc2, int t,
+    int ntile, const TileBuf* __restrict__ ta, const TileBuf* __restrict__ tb,
+    TileBuf* __restrict__ tc, TileBuf* __restrict__ td, const uint16_t* __restrict__ eq,
+    const uint8_t* __restrict__ es, const bf16x8 (&kB)[4], const bf16x8 (&vB)[4],
+    f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[8], float& dbt) {
+  if (t + 2 < ntile) stage_tile(g, q, dout, ws, b, kvh, bkv, eq, es, t + 2, *tc);
+  if (t + 3 < ntile) stage_tile(g, q, dout, ws, b, kvh, bkv, eq, es, t + 3, *td);
+  chunk_tile_compute(g, w, lane, key, sc2, t, ta, eq, es, kB, vB, dv, dk, dlm, dbt);
+  __builtin_amdgcn_sched_barrier(0);     // one tile's registers at a time
+  if (t + 1 < ntile) chunk_tile_compute(g, w, lane, key, sc2, t + 1, tb, eq, es, kB, vB, dv, dk, dlm, dbt);
+}
+
+__global__ void __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, BwdWs ws,
                    uint16_t* __restrict__ dk_out, uint16_t* __restrict__ dv_out,
@@ -813,12 +828,19 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
         if (pos >= r0 && pos < r1) {
           const int qq = (wret + tid) * kWin + bit;
           sm.eq[rbase + pos - r0] = (uint16_t)qq;
-          sm.es[rbase + pos - r0] = ws.slot[((size_t)bkv * L + qq) * g.NC + c];
         }
         ++pos;
       }
     }
   }
+  __syncthreads();
+  // the retrieved entries' slots: one independent load per entry, all in
+  // flight together (a load inside the per-window bit loop above would wait
+  // for each one in turn)
+  // (entries past the last retrieving query pad the last tile and keep 0xff)
+  const int rend = rbase + min(r1, sm.scan[kChunkThreads - 1]) - r0;
+  for (int e = rbase + tid; e < rend; e += kChunkThreads)
+    sm.es[e] = ws.slot[((size_t)bkv * L + sm.eq[e]) * g.NC + c];
   __syncthreads();
 
   // this wave's 16 keys of the chunk as B fragments of S = Q K^T and U = dO V^T
@@ -843,11 +865,14 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
   const int key = c * kS + 16 * w + (lane & 15);
 
   if (ntile > 0) stage_tile(g, q, dout, ws, b, kvh, bkv, sm.eq, sm.es, 0, sm.tb[0]);
+  if (ntile > 1) stage_tile(g, q, dout, ws, b, kvh, bkv, sm.eq, sm.es, 1, sm.tb[1]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    chunk_tile_step(g, q, dout, ws, b, kvh, bkv, w, lane, key, sc2, t, t + 1 < ntile,
-                    &sm.tb[t & 1], &sm.tb[(t + 1) & 1], sm.eq, sm.es, kB, vB, dv, dk, dlm, dbt);
+  for (int t = 0; t < ntile; t += 2) {
+    const int s = t & 2;                  // tiles t, t + 1 in buffers s, s + 1
+    chunk_pair_step(g, q, dout, ws, b, kvh, bkv, w, lane, key, sc2, t, ntile, &sm.tb[s],
+                    &sm.tb[s + 1], &sm.tb[s ^ 2], &sm.tb[(s ^ 2) + 1], sm.eq, sm.es, kB, vB, dv,
+                    dk, dlm, dbt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -978,11 +1003,14 @@ prefill_bwd_dlmk_qret(Geometry g, const uint16_t* __restrict__ qr, BwdWs ws,
       mm &= mm - 1;
       const int qq = (wret + tid) * kWin + bit;
       eq[pos] = (uint16_t)qq;
-      es[pos] = ws.slot[((size_t)bkv * L + qq) * g.NC + c];
       ++pos;
     }
   }
   const int total = scan[kQrThreads - 1];
+  __syncthreads();
+  // slots: one independent load per entry, all in flight together
+  for (int n = tid; n < total; n += kQrThreads)
+    es[n] = ws.slot[((size_t)bkv * L + eq[n]) * g.NC + c];
   __syncthreads();
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll 4
