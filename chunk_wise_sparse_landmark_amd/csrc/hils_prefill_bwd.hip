@@ -688,7 +688,7 @@ __device__ __forceinline__ void chunk_tile_compute(
     const Geometry& g, int w, int lane, int key, float sc2, int t,
     const TileBuf* __restrict__ tbp, const uint16_t* __restrict__ eq,
     const uint8_t* __restrict__ es, const bf16x8 (&kB)[4], const bf16x8 (&vB)[4],
-    f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[8], float& dbt) {
+    f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[2], float& dbt) {
   const TileBuf& tb = *tbp;
   // S and U for this wave's keys; D layout rows (mt, qq = l/16, h = i), key l%16
   f32x4 s[2], u[2];
@@ -733,15 +733,15 @@ __device__ __forceinline__ void chunk_tile_compute(
     const uint2 d1 = tile_heads_at_dim(tb.dn, qs1, db);
     dv[db] = mfma(Awp, as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dv[db]);
     dk[db] = mfma(Adl, as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dk[db]);
-    if (w == 0) {
+    if ((db >> 1) == w) {                 // wave w: landmark-gradient dims 32w .. 32w + 31
       const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
-      float tacc = dlm[db];
+      float tacc = dlm[db & 1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2], __uint_as_float(qw[e] << 16), tacc);
         tacc = __builtin_fmaf(ds[e / 2][(e % 2) * 2 + 1], __uint_as_float(qw[e] & 0xffff0000u), tacc);
       }
-      dlm[db] = tacc;
+      dlm[db & 1] = tacc;
     }
   }
   if (w == 0 && (lane & 15) == 0) {
@@ -763,7 +763,7 @@ __device__ __forceinline__ void chunk_pair_step(
     int ntile, const TileBuf* __restrict__ ta, const TileBuf* __restrict__ tb,
     TileBuf* __restrict__ tc, TileBuf* __restrict__ td, const uint16_t* __restrict__ eq,
     const uint8_t* __restrict__ es, const bf16x8 (&kB)[4], const bf16x8 (&vB)[4],
-    f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[8], float& dbt) {
+    f32x4 (&dv)[8], f32x4 (&dk)[8], float (&dlm)[2], float& dbt) {
   if (t + 2 < ntile) stage_tile(g, q, dout, ws, b, kvh, bkv, eq, es, t + 2, *tc);
   if (t + 3 < ntile) stage_tile(g, q, dout, ws, b, kvh, bkv, eq, es, t + 3, *td);
   chunk_tile_compute(g, w, lane, key, sc2, t, ta, eq, es, kB, vB, dv, dk, dlm, dbt);
@@ -854,14 +854,14 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
     }
   }
   f32x4 dv[8], dk[8];
-  float dlm[8];
+  float dlm[2];                       // landmark gradient, dims 16 (2w + x) + l % 16
   float dbt = 0.f;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dlm[db] = 0.f;
   }
+  dlm[0] = dlm[1] = 0.f;
   const int key = c * kS + 16 * w + (lane & 15);
 
   if (ntile > 0) stage_tile(g, q, dout, ws, b, kvh, bkv, sm.eq, sm.es, 0, sm.tb[0]);
@@ -878,11 +878,9 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
   }
 
   // ---- outputs: lane holds dX[key 16w + 4(l/16) + i][16db + l%16]
-  if (w == 0) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) dlm[db] = rowgroup_sum(dlm[db]);
-    dbt = rowgroup_sum(dbt);
-  }
+  for (int x = 0; x < 2; ++x) dlm[x] = rowgroup_sum(dlm[x]);
+  if (w == 0) dbt = rowgroup_sum(dbt);
   if (part < 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -893,12 +891,10 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
         dk_out[row + 16 * db] = f32_to_bf16(scale * dk[db][i]);
       }
     }
-    if (w == 0) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        if (lane < 16) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + 16 * db + lane] = f32_to_bf16(scale * dlm[db]);
-      if (lane == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = dbt;
-    }
+    for (int x = 0; x < 2; ++x)
+      if (lane < 16) dlmk_out[((size_t)bkv * g.NCcap + c) * kD + 16 * (2 * w + x) + lane] = f32_to_bf16(scale * dlm[x]);
+    if (w == 0 && lane == 0 && dbias_out) dbias_out[(size_t)bkv * g.NCcap + c] = dbt;
   } else {
     float* pp = ws.part + ((size_t)bkv * ws.max_items + part) * kPartFloats;
 #pragma unroll
@@ -910,12 +906,10 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
         pp[kS * kD + kr * kD + 16 * db + (lane & 15)] = dk[db][i];
       }
     }
-    if (w == 0) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        if (lane < 16) pp[2 * kS * kD + 16 * db + lane] = dlm[db];
-      if (lane == 0) pp[2 * kS * kD + kD] = dbt;
-    }
+    for (int x = 0; x < 2; ++x)
+      if (lane < 16) pp[2 * kS * kD + 16 * (2 * w + x) + lane] = dlm[x];
+    if (w == 0 && lane == 0) pp[2 * kS * kD + kD] = dbt;
   }
 }
 
