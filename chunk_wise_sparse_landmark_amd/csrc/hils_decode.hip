@@ -718,13 +718,13 @@ DecodePlan plan(const Geometry& g) {
   const int t = g.Lkv - 1;
   p.ncand = max(0, min(t / kS - max(g.win - 1, 0), g.NC));   // chunks before the window
   const int bkv = g.B * g.Hkv;
-  // scoring: about 256 workgroups (one per CU), each streaming up to kMaxIt
-  // blocks of 64 candidates per wave; fewer, longer splits leave fewer lists
-  // to merge (at 16 x 8 (b, kv head) pairs and 2047 candidates, two splits of
-  // four blocks per wave beat four splits of two by about 2 us per step)
-  // When eight waves of up to kMaxIt blocks cover a pair's candidates and
-  // the pairs fill at least half the CUs, one workgroup per pair scores,
-  // selects and writes the ascending ids itself: no list merge launch.
+  // scoring, fused: when eight waves of up to kMaxIt blocks cover a pair's
+  // candidates and the pairs fill at least half the CUs, one workgroup per
+  // pair scores, selects and writes the ascending ids itself (no list merge
+  // launch).  Split: about 256 workgroups (one per CU), each streaming up to
+  // kMaxIt blocks of 64 candidates per wave; fewer, longer splits leave fewer
+  // lists to merge (at 16 x 8 (b, kv head) pairs and 2047 candidates, two
+  // splits of four blocks per wave beat four splits of two by about 2 us).
   p.fused = p.ncand <= 8 * kMaxIt * kWave && bkv >= 128;
   if (p.fused) {
     p.nit = max(1, (p.ncand + 8 * kWave - 1) / (8 * kWave));
