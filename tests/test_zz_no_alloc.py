@@ -51,6 +51,9 @@ def _both(hl, cfg):
     # G = 2 (general attention), many score splits then few
     (dict(B=2, Hq=8, Hkv=4, Lkv=300000, K=64, win=3, seed=73),
      dict(B=1, Hq=8, Hkv=4, Lkv=5000, K=8, win=1, seed=74)),
+    # 16 x 8 pairs: one scoring workgroup per pair writes the selection (no
+    # merge launch), then a split call
+    (dict(Lkv=70000, K=32, win=1, seed=75), dict(B=2, Lkv=20000, K=16, win=2, seed=76)),
 ])
 def test_noalloc_decode_matches_decode(hl, first, second):
     _both(hl, config("decode_128k", **first))
