@@ -778,6 +778,16 @@ def main():
     log("hbm read probe: %.0f GB/s" % line["hbm_read_probe"]["read_GBps"])
     line["mfma_probe"] = mfma_probe(ev)
     log("mfma probe: %.0f TFLOP/s" % line["mfma_probe"]["TFLOPs"])
+    # each roofline also against the rate the part sustains by itself
+    for r in [line] + extra:
+        rf = r.get("roofline")
+        if not rf or not rf.get("achieved"):
+            continue
+        ceil = (line["mfma_probe"]["TFLOPs"] if rf.get("bound") == "mfma"
+                else line["hbm_read_probe"]["read_GBps"] if rf.get("bound") == "hbm" else None)
+        if ceil:
+            rf["measured_peak"] = ceil
+            rf["frac_of_measured"] = rf["achieved"] / ceil
     if args.calibrate_copy:
         copy_calibration()
     if not args.no_cpu:
