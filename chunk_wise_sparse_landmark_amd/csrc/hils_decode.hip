@@ -69,10 +69,12 @@ __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&x)[8]) {
 // ----------------------------------------------------------------------------
 constexpr int kMaxIt = 4;
 
-// The K-th largest of the wave's valid keys (0 = empty) when there are at least
-// K of them, else a value no larger than the smallest valid key.  The low word
-// of a key is the complemented chunk id; ids below 2^idbits leave its bits
-// idbits..31 set, so only the 32 score bits and idbits id bits are searched.
+// A floor p for the wave's valid keys (0 = empty): when there are at least K of
+// them, the keys >= p are exactly the K largest (p is the K-th largest key, or
+// the first prefix that exactly K keys reach: the search stops there); else p
+// is no larger than the smallest valid key.  The low word of a key is the
+// complemented chunk id; ids below 2^idbits leave its bits idbits..31 set, so
+// only the 32 score bits and idbits id bits are searched.
 template <int N>
 __device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&kk)[N], int K, int idbits) {
   uint64_t p = 0;
@@ -82,6 +84,7 @@ __device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&kk)[N], int K,
 #pragma unroll
     for (int r = 0; r < N; ++r) cnt += __popcll(__ballot(kk[r] >= t));
     if (cnt >= K) p = t;
+    if (cnt == K) return p;
   }
   p |= (uint64_t)(0xffffffffu << idbits);
   for (int bit = idbits - 1; bit >= 0; --bit) {

@@ -75,19 +75,28 @@ constexpr int kChunkElems = kChunkFrags * kFrag;   // 16384 bf16 = 32 KB
 template <int R, int NR, int kIdBits>
 __device__ __forceinline__ void floor_search(const uint64_t (&keys)[NR][R], int K, uint64_t (&p)[NR]) {
   // the score word first, with 32-bit compares of the keys' high words
+  // A prefix that exactly K keys reach already decides the row (the keys at or
+  // above it are its top K), so the search stops there; for scores that are
+  // not tied near the K-th that happens well before the last bit.
   uint32_t ph[NR];
   int nge[NR];
+  bool done[NR];
 #pragma unroll
-  for (int n = 0; n < NR; ++n) { ph[n] = 0u; nge[n] = 0; }
+  for (int n = 0; n < NR; ++n) { ph[n] = 0u; nge[n] = 0; done[n] = false; }
   for (int bit = 31; bit >= 0; --bit) {
+    bool all = true;
 #pragma unroll
     for (int n = 0; n < NR; ++n) {
+      if (done[n]) continue;
       const uint32_t th = ph[n] | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(static_cast<uint32_t>(keys[n][r] >> 32) >= th));
       if (cnt >= K) { ph[n] = th; nge[n] = cnt; }
+      done[n] = cnt == K;
+      all = all && done[n];
     }
+    if (all) break;
   }
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
@@ -203,7 +212,7 @@ __device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], 
 //      in which P leaves the S^T accumulators).
 // ----------------------------------------------------------------------------
 template <int R>
-__global__ void __launch_bounds__(sel_threads(R))
+__global__ void __launch_bounds__(sel_threads(R), R >= 4 ? 2 : 3)
 prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
                const float* __restrict__ bias, int32_t* __restrict__ sel_idx,
@@ -228,8 +237,36 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const uint16_t* Kc = k + row0 * kD;
   constexpr int kThreads = sel_threads(R);
   constexpr int kSelWaves = kThreads / kWave;
-  for (int x = tid; x < kS * kD / 8; x += kThreads)
-    reinterpret_cast<uint4*>(vs)[x] = reinterpret_cast<const uint4*>(Vc)[x];
+  // the loads of the chunk's own K and V go out first, so that their latency
+  // overlaps the query and landmark loads of the scores: V by direct
+  // global->LDS copies (lane i of a wave lands at the wave's base + 16 i; they
+  // have landed at the wait before the V rewrite below), K into registers for
+  // its fragment rewrite (below 8 candidate blocks per lane; at 8 the
+  // registers are taken by the landmark batches, and K is loaded at the
+  // rewrite)
+  {
+    const int wbase = w * kWave;
+#pragma unroll
+    for (int j = 0; j < kS * kD / 8 / kThreads; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(reinterpret_cast<const uint4*>(Vc) + j * kThreads + tid),
+          (__attribute__((address_space(3))) void*)(reinterpret_cast<uint4*>(vs) + j * kThreads + wbase),
+          16, 0, 0);
+  }
+  constexpr int kKf = 16 * kWave / kThreads;   // K fragment words per thread
+  constexpr bool kEarlyK = R < 8;
+  // K word i of this thread: fragment f = tid + i * kThreads, lane fl, k-step
+  // ks, key tile mt
+  auto kf_src = [&](int i) {
+    const int f = tid + i * kThreads;
+    const int fl = f % kWave, ks = (f / kWave) % 4, mt = f / (4 * kWave);
+    return reinterpret_cast<const bf16x8*>(Kc + (size_t)(16 * mt + fl % 16) * kD + 32 * ks + 8 * (fl / 16));
+  };
+  bf16x8 kfr[kKf];
+  if constexpr (kEarlyK) {
+#pragma unroll
+    for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
+  }
 
   // scores: wave w computes the 16 rows of row group w % 4 against every
   // other batch of 8 column tiles (half w / 4), so the two waves of a SIMD share
@@ -244,7 +281,11 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int ks = 0; ks < 4; ++ks) a[h][ks] = ld8(qr + ks * 32);
   }
   const uint16_t* L = lmk + (size_t)bkv * g.NCcap * kD;
-  const float* bb = bias ? bias + (size_t)bkv * g.NCcap : nullptr;
+  // the biases are read with the landmark rows, unpredicated (without a bias
+  // the loads read a landmark word and are discarded): a predicated load would
+  // make the compiler wait for every load in flight after it
+  const bool use_bias = bias != nullptr;
+  const float* bsrc = use_bias ? bias + (size_t)bkv * g.NCcap : reinterpret_cast<const float*>(L);
   const float sc = g.scale / (float)kG;
   const int ntile = (ncand + 15) / 16;
   // column tiles per batch: 8 loads in flight with the score table filling the
@@ -252,36 +293,43 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   constexpr int kTiles = R >= 4 ? 8 : 4;
   for (int nt0 = kTiles * ch; nt0 < ntile; nt0 += kTiles * (kSelWaves / 4)) {
     bf16x8 bv[kTiles][4];   // the loads of up to kTiles column tiles in flight together
+    float bx[kTiles];
 #pragma unroll
     for (int x = 0; x < kTiles; ++x) {
       const int c = (nt0 + x) * 16 + r16;
       const int cl = c < ncand ? c : 0;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) bv[x][ks] = ld8(L + (size_t)cl * kD + g4 * 8 + ks * 32);
+      bx[x] = bsrc[use_bias ? cl : 0];
     }
+    // every tile of the batch is multiplied and stored, a tile past the last
+    // one (clamped rows) into the padding column: no branch, so that no load
+    // of the batch is sunk after one
 #pragma unroll
     for (int x = 0; x < kTiles; ++x) {
       const int nt = nt0 + x;
-      if (nt >= ntile) break;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int h = 0; h < kG; ++h)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) acc = mfma(a[h][ks], bv[x][ks], acc);
       const int c = nt * 16 + r16;
-      const float bc = (bb && c < ncand) ? bb[c] : 0.f;
+      const float bc = (use_bias && c < ncand) ? bx[x] : 0.f;
+      const int cs = nt < ntile ? c : NCP;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gs[rg * 16 + g4 * 4 + i][c] = acc[i] * sc + bc;
+      for (int i = 0; i < 4; ++i) gs[rg * 16 + g4 * 4 + i][cs] = acc[i] * sc + bc;
     }
   }
 
   // K fragments of this chunk: straight 16-B copies
   uint16_t* kdst = kvf + ((size_t)bkv * g.NC + win) * kChunkElems;
-  for (int f = tid; f < 16 * kWave; f += kThreads) {
-    const int fl = f % kWave, ks = (f / kWave) % 4, mt = f / (4 * kWave);
-    reinterpret_cast<uint4*>(kdst)[f] = *reinterpret_cast<const uint4*>(
-        Kc + (size_t)(16 * mt + fl % 16) * kD + 32 * ks + 8 * (fl / 16));
+  if constexpr (!kEarlyK) {
+#pragma unroll
+    for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
   }
+#pragma unroll
+  for (int i = 0; i < kKf; ++i) reinterpret_cast<bf16x8*>(kdst)[tid + i * kThreads] = kfr[i];
+  __builtin_amdgcn_s_waitcnt(0);           // this thread's V copies have landed
   __syncthreads();
 
   // V fragments of this chunk
