@@ -77,12 +77,14 @@ __device__ __forceinline__ void floor_search(const uint64_t (&keys)[NR][R], int 
   // the score word first, with 32-bit compares of the keys' high words
   // A prefix that exactly K keys reach already decides the row (the keys at or
   // above it are its top K), so the search stops there; for scores that are
-  // not tied near the K-th that happens well before the last bit.
+  // not tied near the K-th that happens well before the last bit.  A search
+  // that runs through bit 0 without that ended on a tie at the K-th score word
+  // (the count at its floor is above K), or found no nonzero floor.
   uint32_t ph[NR];
-  int nge[NR];
   bool done[NR];
 #pragma unroll
-  for (int n = 0; n < NR; ++n) { ph[n] = 0u; nge[n] = 0; done[n] = false; }
+  for (int n = 0; n < NR; ++n) { ph[n] = 0u; done[n] = false; }
+#pragma unroll
   for (int bit = 31; bit >= 0; --bit) {
     bool all = true;
 #pragma unroll
@@ -92,7 +94,7 @@ __device__ __forceinline__ void floor_search(const uint64_t (&keys)[NR][R], int 
       int cnt = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(static_cast<uint32_t>(keys[n][r] >> 32) >= th));
-      if (cnt >= K) { ph[n] = th; nge[n] = cnt; }
+      if (cnt >= K) ph[n] = th;
       done[n] = cnt == K;
       all = all && done[n];
     }
@@ -101,15 +103,16 @@ __device__ __forceinline__ void floor_search(const uint64_t (&keys)[NR][R], int 
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
     p[n] = static_cast<uint64_t>(ph[n]) << 32;
+    bool tie = !done[n];
     if (ph[n] == 0u) {
       // fewer than K valid keys (then all of them), or a zero score word among the top K
       p[n] = 1ull;
       int nvalid = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) nvalid += __popcll(__ballot(keys[n][r] != 0ull));
-      if (nvalid > K) nge[n] = K + 1;
+      tie = nvalid > K;
     }
-    if (nge[n] > K) {
+    if (tie) {
       // a tie at the K-th score word: the id bits decide
       uint64_t q = (p[n] == 1ull ? 0ull : p[n]) | static_cast<uint64_t>(0xffffffffu << kIdBits);
       for (int bit = kIdBits - 1; bit >= 0; --bit) {
@@ -124,81 +127,206 @@ __device__ __forceinline__ void floor_search(const uint64_t (&keys)[NR][R], int 
   }
 }
 
+// The largest 32-bit floor th with at least K of the words >= th (0 when fewer
+// than K words are nonzero), from the top bit down with wave ballots; stops at
+// the first prefix that exactly K words reach.
+template <int NR>
+__device__ __forceinline__ void word_floor(const uint32_t (&h)[NR], int K, uint32_t (&ph)[NR]) {
+  bool done[NR];
+#pragma unroll
+  for (int n = 0; n < NR; ++n) { ph[n] = 0u; done[n] = false; }
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    bool all = true;
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+      if (done[n]) continue;
+      const uint32_t th = ph[n] | (1u << bit);
+      const int cnt = __popcll(__ballot(h[n] >= th));
+      if (cnt >= K) ph[n] = th;
+      done[n] = cnt == K;
+      all = all && done[n];
+    }
+    if (all) break;
+  }
+}
+
+// The nonzero keys >= p of R keys per lane (candidate r*64 + lane), in
+// ascending candidate order, as chunk ids into d[0, K); -1 past the last.
+template <int R>
+__device__ __forceinline__ void write_ascending(const uint64_t (&keys)[R], uint64_t p, int K, int32_t* d,
+                                                int lane) {
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool pred = keys[r] != 0ull && keys[r] >= p;
+    const uint64_t m = __ballot(pred);
+    const int at = base + mask_rank(m);
+    if (pred && at < K) d[at] = key_index(keys[r]);   // (exactly min(K, valid) keys pass)
+    base += __popcll(m);
+  }
+  for (int x = base + lane; x < K; x += kWave) d[x] = -1;
+}
+
 template <int R, int NR>
 __device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], int K, int32_t* dst,
                                                  size_t dstride, uint64_t* buf) {
   const int lane = lane_id();
   constexpr int kIdBits = R == 1 ? 6 : (R == 2 ? 7 : (R == 4 ? 8 : 9));
   uint64_t p[NR];
-  if (R >= 4) {
-    // every top-K key is >= the K-th largest lane maximum; when at most 64 keys
-    // are, the search runs over those alone, one per lane
-    uint64_t lm[NR][1];
+  if constexpr (R >= 4) {
+    static_assert(NR == 1, "one row at a time with wide rows");
+    // Prefilter: every top-K key has a score word >= the K-th largest of the 64
+    // lanes' maximum score words (at least K lanes hold a key that reaches it).
+    // The keys that reach it (about K for untied scores) are compacted in
+    // candidate order and, when at most 64 do, each one's rank among them is
+    // counted from LDS broadcasts: the top K are those of rank < K, with no
+    // further bit search.  Lanes that hold no key of a batch write it to a slot
+    // of their own at 64 + lane, so that no store is predicated.
+    uint32_t lm[1];
+    lm[0] = static_cast<uint32_t>(keys[0][0] >> 32);
 #pragma unroll
-    for (int n = 0; n < NR; ++n) {
-      lm[n][0] = keys[n][0];
+    for (int r = 1; r < R; ++r) lm[0] = max(lm[0], static_cast<uint32_t>(keys[0][r] >> 32));
+    uint32_t ph[1];
+    word_floor<1>(lm, K, ph);
+    const uint64_t tau = ph[0] ? static_cast<uint64_t>(ph[0]) << 32 : 1ull;
+    uint64_t m[R];
+    int pre[R];
+    int cnt = 0;
 #pragma unroll
-      for (int r = 1; r < R; ++r) lm[n][0] = keys[n][r] > lm[n][0] ? keys[n][r] : lm[n][0];
+    for (int r = 0; r < R; ++r) {
+      m[r] = __ballot(keys[0][r] >= tau);
+      pre[r] = cnt;
+      cnt += __popcll(m[r]);
     }
-    uint64_t tau[NR];
-    floor_search<1, NR, kIdBits>(lm, K, tau);
-    int most = 0;
-    int cnt[NR];
+    if (cnt <= kWave) {
 #pragma unroll
-    for (int n = 0; n < NR; ++n) {
-      cnt[n] = 0;
+      for (int r = 0; r < R; ++r) {
+        const bool pr = keys[0][r] >= tau;
+        const int at = pre[r] + mask_rank(m[r]);
+        buf[pr ? at : kWave + lane] = keys[0][r];
+      }
+      if (lane >= cnt) buf[lane] = 0ull;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // keys are unique, so the ranks are distinct; empty slots (0) rank nothing
+      const uint64_t mine = buf[lane];
+      int rank = 0;
+      const ulonglong2* b2 = reinterpret_cast<const ulonglong2*>(buf);
+      for (int j = 0; j < cnt; j += 8) {
+        ulonglong2 kk[4];
 #pragma unroll
-      for (int r = 0; r < R; ++r) cnt[n] += __popcll(__ballot(keys[n][r] != 0ull && keys[n][r] >= tau[n]));
-      most = cnt[n] > most ? cnt[n] : most;
-    }
-    if (most <= kWave) {
-      uint64_t k1[NR][1];
+        for (int x = 0; x < 4; ++x) kk[x] = b2[j / 2 + x];
 #pragma unroll
-      for (int n = 0; n < NR; ++n) {
-        int base = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const bool pred = keys[n][r] != 0ull && keys[n][r] >= tau[n];
-          const uint64_t m = __ballot(pred);
-          if (pred) buf[n * kWave + base + mask_rank(m)] = keys[n][r];
-          base += __popcll(m);
-        }
-        if (lane >= base) buf[n * kWave + lane] = 0ull;
+        for (int x = 0; x < 4; ++x) rank += (kk[x].x > mine) + (kk[x].y > mine);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int n = 0; n < NR; ++n) k1[n][0] = buf[n * kWave + lane];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      floor_search<1, NR, kIdBits>(k1, K, p);
-      // p separates the top K within the compacted keys only (it can stop at a
-      // score word when the compacted set holds no tie there); the keys outside
-      // it are all below tau, so over every key the floor is max(p, tau)
-#pragma unroll
-      for (int n = 0; n < NR; ++n) p[n] = p[n] > tau[n] ? p[n] : tau[n];
-    } else {
-      floor_search<R, NR, kIdBits>(keys, K, p);
+      const bool sel = mine != 0ull && rank < K;
+      const uint64_t ms = __ballot(sel);
+      if (sel) dst[mask_rank(ms)] = key_index(mine);
+      for (int x = __popcll(ms) + lane; x < K; x += kWave) dst[x] = -1;
+      return;
     }
-  } else {
-    floor_search<R, NR, kIdBits>(keys, K, p);
   }
+  floor_search<R, NR, kIdBits>(keys, K, p);
 #pragma unroll
-  for (int n = 0; n < NR; ++n) {
-    int32_t* d = dst + n * dstride;
-    int base = 0;
+  for (int n = 0; n < NR; ++n) write_ascending<R>(keys[n], p[n], K, dst + n * dstride, lane);
+}
+
+// Sums over the four lanes of a quad (lane & ~3 .. lane | 3), by DPP quad
+// permutes: all four lanes receive the total, or the sum over the quad's lanes
+// below their own.
+__device__ __forceinline__ int quad_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);   // lanes [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);   // lanes [2,3,0,1]
+  return x;
+}
+__device__ __forceinline__ int quad_below(int x, int q) {
+  const int v0 = __builtin_amdgcn_update_dpp(0, x, 0x00, 0xf, 0xf, false);   // lane 0 of the quad
+  const int v1 = __builtin_amdgcn_update_dpp(0, x, 0x55, 0xf, 0xf, false);   // lane 1
+  const int v2 = __builtin_amdgcn_update_dpp(0, x, 0xAA, 0xf, 0xf, false);   // lane 2
+  return (q > 0 ? v0 : 0) + (q > 1 ? v1 : 0) + (q > 2 ? v2 : 0);
+}
+
+// Top K of the 64R candidates of 16 score rows (rows 0..15 at `row0`, `stride`
+// floats apart), written as ascending chunk ids (-1 past the last) to the 16
+// consecutive K-entry rows at `dst`.  Four lanes share a row: lane part q holds
+// candidates q*n .. q*n + n - 1 as order-preserving score words in registers.
+// The K-th largest word is found bit by bit, each row's count of words >= the
+// trial floor summed over its quad; the rows' searches run side by side in the
+// lanes, so a round costs two vector instructions per word and no scalar
+// chain.  The search stops once every row has met a floor that exactly K words
+// reach.  Equal words at the floor are taken lowest id first, which is the
+// composite-key order.  `stage` is 16*32 + 64 ints of LDS private to the wave.
+template <int R>
+__device__ __forceinline__ void narrow_rows_topk(const float* row0, int stride, int ncand, int K, int32_t* dst,
+                                                 int* stage) {
+  constexpr int P = 4, kRows = kWave / P, n = R * kWave / P;
+  const int lane = lane_id(), rl = lane / P, q = lane % P;
+  const float* src = row0 + rl * stride + q * n;
+  uint32_t wd[n];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const bool pred = keys[n][r] != 0ull && keys[n][r] >= p[n];
-      const uint64_t m = __ballot(pred);
-      const int at = base + mask_rank(m);
-      if (pred && at < K) d[at] = r * kWave + lane;   // (exactly min(K, valid) keys pass)
-      base += __popcll(m);
+  for (int j = 0; j < n; ++j) {
+    const uint32_t u = __float_as_uint(src[j]);
+    const uint32_t o = u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+    // valid words are kept nonzero (word 0 is one NaN pattern, ranked with the
+    // NaN next to it) so that 0 marks the candidates past ncand
+    wd[j] = q * n + j < ncand ? max(o, 1u) : 0u;
+  }
+  // ph: the largest floor that at least K of the row's words reach (0 when
+  // fewer than K words are valid; with ncand <= K every candidate is taken)
+  uint32_t ph = 0u;
+  if (ncand > K) {
+    uint64_t done = 0ull;
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t th = ph | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < n; ++j) cnt += wd[j] >= th ? 1 : 0;
+      cnt = quad_sum(cnt);
+      ph = cnt >= K ? th : ph;
+      // a floor reached by exactly K words stays so as the search goes on
+      done |= __ballot(cnt == K);
+      if (done == ~0ull) break;
     }
-    for (int x = base + lane; x < K; x += kWave) d[x] = -1;
   }
+  // the words above the floor, then the lowest-id words at it, up to K
+  // (with ph = 0 every valid word is above it and no word is taken at it)
+  const bool at_ok = ph != 0u;
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    ngt += wd[j] > ph ? 1 : 0;
+    neq += (at_ok && wd[j] == ph) ? 1 : 0;
+  }
+  const int need = K - quad_sum(ngt);
+  const int teq = min(max(need - quad_below(neq, q), 0), neq);
+  const int mine = ngt + teq;
+  const int total = quad_sum(mine);
+  int* st = stage + rl * K;
+  int* trash = stage + kRows * kMaxKf + lane;
+  for (int x = total + q; x < K; x += P) st[x] = -1;
+  int pos = quad_below(mine, q), eqs = 0;
+  // the same floor through an identity lane permute, so that the compares are
+  // made again here rather than 2n lane masks kept in scalar registers
+  const uint32_t pf = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(ph), 0xE4, 0xf, 0xf, false));
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    const bool e = at_ok && wd[j] == pf;
+    const bool t = wd[j] > pf || (e && eqs < teq);
+    *(t ? st + pos : trash) = q * n + j;
+    pos += t ? 1 : 0;
+    eqs += e ? 1 : 0;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int x = lane; x < kRows * K; x += kWave) dst[x] = stage[x];
 }
 
 // ----------------------------------------------------------------------------
@@ -351,25 +479,33 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     reinterpret_cast<uint4*>(vdst)[f] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 
-  // the wave's 8 rows, one at a time; the V staging area is each wave's
-  // compaction buffer from here on
-  constexpr int NR = 1;
+  // the selection of the window's 64 rows; the V staging area is each wave's
+  // work buffer from here on
   __syncthreads();
   uint64_t* sbuf = reinterpret_cast<uint64_t*>(vs) + w * (kS * kD / 4 / (kThreads / kWave));
-  static_assert(NR * kWave <= kS * kD / 4 / (kThreads / kWave), "compaction buffer");
   constexpr int kRowsPerWave = kWin / (kThreads / kWave);
-  for (int q0 = 0; q0 < kRowsPerWave; q0 += NR) {
-    const int row = w * kRowsPerWave + q0;
-    uint64_t keys[NR][R];
-#pragma unroll
-    for (int n = 0; n < NR; ++n)
+  if constexpr (R <= 2) {
+    static_assert(kRowsPerWave == kWave / 4, "four lanes per row");
+    static_assert(kRowsPerWave * kMaxKf + kWave <= 2 * (kS * kD / 4 / (kThreads / kWave)), "staging");
+    narrow_rows_topk<R>(&gs[w * kRowsPerWave][0], NCP + 1, ncand, g.K,
+                        sel_idx + ((size_t)bkv * g.Lq + i0 + w * kRowsPerWave) * g.K,
+                        reinterpret_cast<int*>(sbuf));
+  } else {
+    // one row at a time over the whole wave
+    for (int q0 = 0; q0 < kRowsPerWave; ++q0) {
+      const int row = w * kRowsPerWave + q0;
+      uint64_t keys[1][R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
+        // read unconditionally (the table is NCP + 1 wide), masked after: a
+        // predicated read would be waited for before the next one is issued
         const int c = r * kWave + lane;
-        keys[n][r] = c < ncand ? make_key(gs[row + n][c], c) : 0ull;
+        const uint64_t kk = make_key(gs[row][c], c);
+        keys[0][r] = kk & (c < ncand ? ~0ull : 0ull);
       }
-    select_ascending<R, NR>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + row) * g.K,
-                            (size_t)g.K, sbuf);
+      select_ascending<R, 1>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + row) * g.K,
+                             (size_t)g.K, sbuf);
+    }
   }
 }
 
