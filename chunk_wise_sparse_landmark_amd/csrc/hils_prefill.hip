@@ -236,9 +236,9 @@ __device__ __forceinline__ void select_ascending(const uint64_t (&keys)[NR][R], 
   for (int n = 0; n < NR; ++n) write_ascending<R>(keys[n], p[n], K, dst + n * dstride, lane);
 }
 
-// Sums over the four lanes of a quad (lane & ~3 .. lane | 3), by DPP quad
-// permutes: all four lanes receive the total, or the sum over the quad's lanes
-// below their own.
+// Sums over the four lanes of a quad (lane & ~3 .. lane | 3) by DPP quad
+// permutes: every lane of the quad receives the total, or the sum over the
+// quad's lanes below its own (q = lane % 4).
 __device__ __forceinline__ int quad_sum(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);   // lanes [1,0,3,2]
   x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);   // lanes [2,3,0,1]
@@ -251,16 +251,18 @@ __device__ __forceinline__ int quad_below(int x, int q) {
   return (q > 0 ? v0 : 0) + (q > 1 ? v1 : 0) + (q > 2 ? v2 : 0);
 }
 
-// Top K of the 64R candidates of 16 score rows (rows 0..15 at `row0`, `stride`
-// floats apart), written as ascending chunk ids (-1 past the last) to the 16
-// consecutive K-entry rows at `dst`.  Four lanes share a row: lane part q holds
-// candidates q*n .. q*n + n - 1 as order-preserving score words in registers.
-// The K-th largest word is found bit by bit, each row's count of words >= the
-// trial floor summed over its quad; the rows' searches run side by side in the
-// lanes, so a round costs two vector instructions per word and no scalar
-// chain.  The search stops once every row has met a floor that exactly K words
-// reach.  Equal words at the floor are taken lowest id first, which is the
-// composite-key order.  `stage` is 16*32 + 64 ints of LDS private to the wave.
+// Top K of the 64R (R <= 2) candidates of 16 score rows (rows 0..15 at `row0`,
+// `stride` floats apart), written as ascending chunk ids (-1 past the last) to
+// the 16 consecutive K-entry rows at `dst`.  Four lanes share a row: lane part
+// q holds candidates q*n .. q*n + n - 1 as order-preserving score words in
+// registers.  The K-th largest word is found bit by bit, each row's count of
+// words >= the trial floor summed over its quad; the rows' searches run side
+// by side in the lanes, so a round costs two vector instructions per word and
+// no scalar chain.  A floor that exactly K words reach stays so as the search
+// goes on, and the search stops once every row of the wave has met one.  The
+// words above the floor are taken, then the lowest-id words at it up to K,
+// which is the composite-key order.  `stage` is 16*32 + 64 ints of LDS private
+// to the wave.
 template <int R>
 __device__ __forceinline__ void narrow_rows_topk(const float* row0, int stride, int ncand, int K, int32_t* dst,
                                                  int* stage) {
@@ -270,16 +272,20 @@ __device__ __forceinline__ void narrow_rows_topk(const float* row0, int stride, 
   uint32_t wd[n];
 #pragma unroll
   for (int j = 0; j < n; ++j) {
-    const uint32_t u = __float_as_uint(src[j]);
-    const uint32_t o = u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+    // read unconditionally (a predicated read is waited for before the next);
     // valid words are kept nonzero (word 0 is one NaN pattern, ranked with the
     // NaN next to it) so that 0 marks the candidates past ncand
-    wd[j] = q * n + j < ncand ? max(o, 1u) : 0u;
+    const uint32_t u = __float_as_uint(src[j]);
+    const uint32_t o = max(u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u), 1u);
+    wd[j] = q * n + j < ncand ? o : 0u;
   }
-  // ph: the largest floor that at least K of the row's words reach (0 when
-  // fewer than K words are valid; with ncand <= K every candidate is taken)
-  uint32_t ph = 0u;
-  if (ncand > K) {
+  int* st = stage + rl * K;
+  if (ncand <= K) {
+    // every candidate is taken
+    for (int x = q; x < K; x += P) st[x] = x < ncand ? x : -1;
+  } else {
+    // ph: the largest floor that at least K of the row's words reach
+    uint32_t ph = 0u;
     uint64_t done = 0ull;
 #pragma unroll
     for (int bit = 31; bit >= 0; --bit) {
@@ -289,39 +295,34 @@ __device__ __forceinline__ void narrow_rows_topk(const float* row0, int stride, 
       for (int j = 0; j < n; ++j) cnt += wd[j] >= th ? 1 : 0;
       cnt = quad_sum(cnt);
       ph = cnt >= K ? th : ph;
-      // a floor reached by exactly K words stays so as the search goes on
       done |= __ballot(cnt == K);
       if (done == ~0ull) break;
     }
-  }
-  // the words above the floor, then the lowest-id words at it, up to K
-  // (with ph = 0 every valid word is above it and no word is taken at it)
-  const bool at_ok = ph != 0u;
-  int ngt = 0, neq = 0;
+    int ngt = 0, neq = 0;
 #pragma unroll
-  for (int j = 0; j < n; ++j) {
-    ngt += wd[j] > ph ? 1 : 0;
-    neq += (at_ok && wd[j] == ph) ? 1 : 0;
-  }
-  const int need = K - quad_sum(ngt);
-  const int teq = min(max(need - quad_below(neq, q), 0), neq);
-  const int mine = ngt + teq;
-  const int total = quad_sum(mine);
-  int* st = stage + rl * K;
-  int* trash = stage + kRows * kMaxKf + lane;
-  for (int x = total + q; x < K; x += P) st[x] = -1;
-  int pos = quad_below(mine, q), eqs = 0;
-  // the same floor through an identity lane permute, so that the compares are
-  // made again here rather than 2n lane masks kept in scalar registers
-  const uint32_t pf = static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(ph), 0xE4, 0xf, 0xf, false));
+    for (int j = 0; j < n; ++j) {
+      ngt += wd[j] > ph ? 1 : 0;
+      neq += wd[j] == ph ? 1 : 0;
+    }
+    const int need = K - quad_sum(ngt);
+    const int teq = min(max(need - quad_below(neq, q), 0), neq);
+    const int mine = ngt + teq;
+    const int total = quad_sum(mine);
+    for (int x = total + q; x < K; x += P) st[x] = -1;
+    int pos = quad_below(mine, q), eqs = 0;
+    int* trash = stage + kRows * kMaxKf + lane;
+    // the same floor through an identity lane permute, so that the compares
+    // are made again here rather than 2n lane masks kept in scalar registers
+    const uint32_t pf = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(ph), 0xE4, 0xf, 0xf, false));
 #pragma unroll
-  for (int j = 0; j < n; ++j) {
-    const bool e = at_ok && wd[j] == pf;
-    const bool t = wd[j] > pf || (e && eqs < teq);
-    *(t ? st + pos : trash) = q * n + j;
-    pos += t ? 1 : 0;
-    eqs += e ? 1 : 0;
+    for (int j = 0; j < n; ++j) {
+      const bool e = wd[j] == pf;
+      const bool t = wd[j] > pf || (e && eqs < teq);
+      *(t ? st + pos : trash) = q * n + j;
+      pos += t ? 1 : 0;
+      eqs += e ? 1 : 0;
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
