@@ -186,13 +186,33 @@ __device__ __forceinline__ uint64_t wave_rank_sort64(uint64_t key, uint64_t* buf
 // Top 64 of the union of two lists sorted descending (one key per lane, keys
 // unique apart from 0): max(a_i, b_{63-i}) is a bitonic sequence holding
 // exactly the 64 largest keys of both, which a rank sort then orders.
+// Value held by lane l ^ J for J = 1, 2, 4, 8, by DPP: quad permutes for 1
+// and 2, a rotation by 8 within each 16-lane row for 8, and for 4 a shift by
+// four lanes up or down within the row, chosen by the lane's bit 2.
+template <int J>
+__device__ __forceinline__ uint32_t dpp_xor_u32(uint32_t x) {
+  const int v = static_cast<int>(x);
+  if constexpr (J == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
+  } else if constexpr (J == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+  } else if constexpr (J == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false));
+  } else {
+    static_assert(J == 4, "lane distance");
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0xf, false);   // from lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // from lane - 4
+    return static_cast<uint32_t>((lane_id() & 4) ? dn : up);
+  }
+}
+
 // Value held by lane l ^ J (J a power of two), for 64-bit keys: the lane-swap
-// VALU instructions for J = 32, 16, LDS permutes below.
+// VALU instructions for J = 32, 16, DPP below.
 template <int J>
 __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
   const int lane = lane_id();
   uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
-  if (J == 32 || J == 16) {
+  if constexpr (J == 32 || J == 16) {
     const auto a = J == 32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
                            : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
     const auto b = J == 32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
@@ -201,8 +221,8 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
     lo = up ? a[0] : a[1];
     hi = up ? b[0] : b[1];
   } else {
-    lo = __shfl_xor(lo, J, kWave);
-    hi = __shfl_xor(hi, J, kWave);
+    lo = dpp_xor_u32<J>(lo);
+    hi = dpp_xor_u32<J>(hi);
   }
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
