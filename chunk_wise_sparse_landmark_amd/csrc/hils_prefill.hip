@@ -44,9 +44,9 @@ constexpr int kD = 128;
 constexpr int kS = 64;
 constexpr int kG = 4;            // query heads per KV group on this path
 // prefill_select: with 4+ candidate blocks per row the score table fills the
-// LDS (one workgroup per CU), so eight waves (two per SIMD) interleave their
-// serial searches; with fewer, two workgroups of four waves share a CU
-constexpr int sel_threads(int R) { return R >= 4 ? 512 : 256; }
+// LDS (one workgroup per CU), so sixteen waves (four per SIMD) interleave their
+// serial searches; with fewer, three workgroups of four waves share a CU
+constexpr int sel_threads(int R) { return R >= 4 ? 1024 : 256; }
 constexpr int kAttWaves = 8;             // prefill_attend: two waves per SIMD
 constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kWin = 64;         // queries per window (one chunk), both kernels
@@ -341,7 +341,7 @@ __device__ __forceinline__ void narrow_rows_topk(const float* row0, int stride, 
 //      in which P leaves the S^T accumulators).
 // ----------------------------------------------------------------------------
 template <int R>
-__global__ void __launch_bounds__(sel_threads(R), R >= 4 ? 2 : 3)
+__global__ void __launch_bounds__(sel_threads(R), R >= 4 ? 1 : 3)
 prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
                const float* __restrict__ bias, int32_t* __restrict__ sel_idx,
@@ -397,9 +397,9 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
   }
 
-  // scores: wave w computes the 16 rows of row group w % 4 against every
-  // other batch of 8 column tiles (half w / 4), so the two waves of a SIMD share
-  // the landmark loads of a row group and each searches its own 8 rows below
+  // scores: wave w computes the 16 rows of row group w % 4 against batch
+  // w / 4, w / 4 + nw / 4, ... of the column tiles (nw waves), and each wave
+  // then selects for its own 64 / nw rows below
   // A operand: 16 queries of this row group x 4 heads x 4 k-steps
   const int rg = w & 3, ch = w >> 2;        // (four waves: ch = 0, every batch)
   bf16x8 a[kG][4];
@@ -417,9 +417,9 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   const float* bsrc = use_bias ? bias + (size_t)bkv * g.NCcap : reinterpret_cast<const float*>(L);
   const float sc = g.scale / (float)kG;
   const int ntile = (ncand + 15) / 16;
-  // column tiles per batch: 8 loads in flight with the score table filling the
-  // LDS; 4 with small tables, so that three workgroups fit a CU's registers
-  constexpr int kTiles = R >= 4 ? 8 : 4;
+  // column tiles per batch: 2 with sixteen waves (128 registers each), 4 with
+  // small tables, so that three workgroups fit a CU's registers
+  constexpr int kTiles = R >= 4 ? 2 : 4;
   for (int nt0 = kTiles * ch; nt0 < ntile; nt0 += kTiles * (kSelWaves / 4)) {
     bf16x8 bv[kTiles][4];   // the loads of up to kTiles column tiles in flight together
     float bx[kTiles];
