@@ -51,14 +51,60 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
   hi = __shfl(hi, src, kWave);
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
+// Value held by lane l ^ J for J = 1, 2, 4, 8, by DPP: quad permutes for 1
+// and 2, a rotation by 8 within each 16-lane row for 8, and for 4 a shift by
+// four lanes up or down within the row, chosen by the lane's bit 2.
+template <int J>
+__device__ __forceinline__ uint32_t dpp_xor_u32(uint32_t x) {
+  const int v = static_cast<int>(x);
+  if constexpr (J == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
+  } else if constexpr (J == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+  } else if constexpr (J == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false));
+  } else {
+    static_assert(J == 4, "lane distance");
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0xf, false);   // from lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // from lane - 4
+    return static_cast<uint32_t>((lane_id() & 4) ? dn : up);
+  }
+}
+
+// Value held by lane l ^ J (J a power of two): the lane-swap VALU
+// instructions for J = 32 and 16, DPP below.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  if constexpr (J == 32 || J == 16) {
+    const auto a = J == 32 ? __builtin_amdgcn_permlane32_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane_id() & J) ? a[0] : a[1];
+  } else {
+    return dpp_xor_u32<J>(x);
+  }
+}
+template <int J>
+__device__ __forceinline__ float lane_xor_f32(float x) {
+  return __uint_as_float(lane_xor_u32<J>(__float_as_uint(x)));
+}
+// Butterfly reductions over the wave (lane distances 32, 16, ..., 1, every lane
+// receiving the result), without LDS permutes.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  x += lane_xor_f32<32>(x);
+  x += lane_xor_f32<16>(x);
+  x += lane_xor_f32<8>(x);
+  x += lane_xor_f32<4>(x);
+  x += lane_xor_f32<2>(x);
+  x += lane_xor_f32<1>(x);
   return x;
 }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  x = fmaxf(x, lane_xor_f32<32>(x));
+  x = fmaxf(x, lane_xor_f32<16>(x));
+  x = fmaxf(x, lane_xor_f32<8>(x));
+  x = fmaxf(x, lane_xor_f32<4>(x));
+  x = fmaxf(x, lane_xor_f32<2>(x));
+  x = fmaxf(x, lane_xor_f32<1>(x));
   return x;
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
@@ -183,47 +229,11 @@ __device__ __forceinline__ uint64_t wave_rank_sort64(uint64_t key, uint64_t* buf
   return out;
 }
 
-// Top 64 of the union of two lists sorted descending (one key per lane, keys
-// unique apart from 0): max(a_i, b_{63-i}) is a bitonic sequence holding
-// exactly the 64 largest keys of both, which a rank sort then orders.
-// Value held by lane l ^ J for J = 1, 2, 4, 8, by DPP: quad permutes for 1
-// and 2, a rotation by 8 within each 16-lane row for 8, and for 4 a shift by
-// four lanes up or down within the row, chosen by the lane's bit 2.
-template <int J>
-__device__ __forceinline__ uint32_t dpp_xor_u32(uint32_t x) {
-  const int v = static_cast<int>(x);
-  if constexpr (J == 1) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
-  } else if constexpr (J == 2) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
-  } else if constexpr (J == 8) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false));
-  } else {
-    static_assert(J == 4, "lane distance");
-    const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0xf, false);   // from lane + 4
-    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // from lane - 4
-    return static_cast<uint32_t>((lane_id() & 4) ? dn : up);
-  }
-}
-
-// Value held by lane l ^ J (J a power of two), for 64-bit keys: the lane-swap
-// VALU instructions for J = 32, 16, DPP below.
+// The same for a 64-bit key, word by word.
 template <int J>
 __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
-  const int lane = lane_id();
-  uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
-  if constexpr (J == 32 || J == 16) {
-    const auto a = J == 32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
-                           : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    const auto b = J == 32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
-                           : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    const bool up = (lane & J) != 0;
-    lo = up ? a[0] : a[1];
-    hi = up ? b[0] : b[1];
-  } else {
-    lo = dpp_xor_u32<J>(lo);
-    hi = dpp_xor_u32<J>(hi);
-  }
+  const uint32_t lo = lane_xor_u32<J>(static_cast<uint32_t>(x));
+  const uint32_t hi = lane_xor_u32<J>(static_cast<uint32_t>(x >> 32));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 template <int J>

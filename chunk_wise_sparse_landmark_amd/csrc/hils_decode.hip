@@ -659,13 +659,18 @@ decode_attend4(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16
 
 // ----------------------------------------------------------------------------
 // 4. merge of the nsplit partials of each (b, q head): one workgroup per row;
-//    wave w takes splits w, w+4, ...; lane -> dims 2l, 2l+1.
+//    wave w of W takes splits w, w + W, ...; lane -> dims 2l, 2l+1.  With few
+//    rows (fewer workgroups than CUs) sixteen waves keep each wave's chain of
+//    partial loads short (at most five of the 65 partials of a decode_4m row);
+//    with many rows four waves per row launch faster.
 //    O = sum_s e^{M_s - M} O_s / sum_s e^{M_s - M} Z_s,  LSE = M + log(...).
 // ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads)
+template <int W>
+__global__ void __launch_bounds__(W * kWave)
 decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* __restrict__ out,
             float* __restrict__ lse_out) {
-  __shared__ float red[4][2 * kWave + 2];
+  constexpr int kFuseWaves = W;
+  __shared__ float red[kFuseWaves][2 * kWave + 2];
   const int row = blockIdx.x;                  // b * Hq + hq
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int b = row / g.Hq, hq = row % g.Hq;
@@ -681,7 +686,7 @@ decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* _
   float z = 0.f, o0 = 0.f, o1 = 0.f;
   if (m != -INFINITY) {
 #pragma unroll 4
-    for (int s = w; s < nsplit; s += 4) {
+    for (int s = w; s < nsplit; s += kFuseWaves) {
       const float* ps = pb + s * sstride;
       const float2 ov = reinterpret_cast<const float2*>(ps)[lane];
       const float ms = ps[kD];
@@ -698,7 +703,7 @@ decode_fuse(Geometry g, int nsplit, const float* __restrict__ parts, uint16_t* _
   if (w == 0) {
     float zt = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < kFuseWaves; ++x) {
       zt += red[x][2 * kWave];
       a0 += red[x][2 * lane];
       a1 += red[x][2 * lane + 1];
@@ -819,8 +824,12 @@ hipError_t launch_decode_fast(const Geometry& g, const void* q, const void* qr, 
     hipLaunchKernelGGL(decode_attend, dim3(p.asplit, bkv), dim3(kThreads), 0, st, g, p.apc,
                        Q, QR, (const uint16_t*)k, (const uint16_t*)v, Lm, bias, sel_idx, d.parts);
   prof_end(kDecodeAttend, st);
-  hipLaunchKernelGGL(decode_fuse, dim3(g.B * g.Hq), dim3(kThreads), 0, st, g, p.asplit, d.parts,
-                     (uint16_t*)out, lse);
+  if (g.B * g.Hq < 256)
+    hipLaunchKernelGGL(decode_fuse<16>, dim3(g.B * g.Hq), dim3(16 * kWave), 0, st, g, p.asplit, d.parts,
+                       (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL(decode_fuse<4>, dim3(g.B * g.Hq), dim3(4 * kWave), 0, st, g, p.asplit, d.parts,
+                       (uint16_t*)out, lse);
   return hipGetLastError();
 }
 
