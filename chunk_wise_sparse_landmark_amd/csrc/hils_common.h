@@ -39,18 +39,6 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------- wave primitives
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
-  lo = __shfl_xor(lo, m, kWave);
-  hi = __shfl_xor(hi, m, kWave);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
-  uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
-  lo = __shfl(lo, src, kWave);
-  hi = __shfl(hi, src, kWave);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 // Value held by lane l ^ J for J = 1, 2, 4, 8, by DPP: quad permutes for 1
 // and 2, a rotation by 8 within each 16-lane row for 8, and for 4 a shift by
 // four lanes up or down within the row, chosen by the lane's bit 2.
@@ -87,6 +75,67 @@ template <int J>
 __device__ __forceinline__ float lane_xor_f32(float x) {
   return __uint_as_float(lane_xor_u32<J>(__float_as_uint(x)));
 }
+// The same for a 64-bit key, word by word.
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
+  const uint32_t lo = lane_xor_u32<J>(static_cast<uint32_t>(x));
+  const uint32_t hi = lane_xor_u32<J>(static_cast<uint32_t>(x >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+// The same with the distance as an argument; it must fold to a constant (an
+// unrolled loop over the distances).
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x, int j) {
+  switch (j) {
+    case 32: return lane_xor_u64<32>(x);
+    case 16: return lane_xor_u64<16>(x);
+    case 8: return lane_xor_u64<8>(x);
+    case 4: return lane_xor_u64<4>(x);
+    case 2: return lane_xor_u64<2>(x);
+    default: return lane_xor_u64<1>(x);
+  }
+}
+__device__ __forceinline__ float lane_xor_f32(float x, int j) {
+  switch (j) {
+    case 32: return lane_xor_f32<32>(x);
+    case 16: return lane_xor_f32<16>(x);
+    case 8: return lane_xor_f32<8>(x);
+    case 4: return lane_xor_f32<4>(x);
+    case 2: return lane_xor_f32<2>(x);
+    default: return lane_xor_f32<1>(x);
+  }
+}
+// Lane i (0..15) of this lane's 16-lane row, by DPP (row broadcast); i must
+// fold to a constant (an unrolled loop).
+template <int I>
+__device__ __forceinline__ float row_bcast_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_bcast_f32(float x, int i) {
+  switch (i) {
+    case 0: return row_bcast_f32<0>(x);
+    case 1: return row_bcast_f32<1>(x);
+    case 2: return row_bcast_f32<2>(x);
+    case 3: return row_bcast_f32<3>(x);
+    case 4: return row_bcast_f32<4>(x);
+    case 5: return row_bcast_f32<5>(x);
+    case 6: return row_bcast_f32<6>(x);
+    case 7: return row_bcast_f32<7>(x);
+    case 8: return row_bcast_f32<8>(x);
+    case 9: return row_bcast_f32<9>(x);
+    case 10: return row_bcast_f32<10>(x);
+    case 11: return row_bcast_f32<11>(x);
+    case 12: return row_bcast_f32<12>(x);
+    case 13: return row_bcast_f32<13>(x);
+    case 14: return row_bcast_f32<14>(x);
+    default: return row_bcast_f32<15>(x);
+  }
+}
+// Lane `src`'s key in every lane; `src` must be the same in all lanes.
+__device__ __forceinline__ uint64_t bcast_u64(uint64_t x, int src) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), src));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x >> 32), src));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 // Butterfly reductions over the wave (lane distances 32, 16, ..., 1, every lane
 // receiving the result), without LDS permutes.
 __device__ __forceinline__ float wave_sum(float x) {
@@ -110,7 +159,7 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t y = shfl_xor_u64(x, m);
+    uint64_t y = lane_xor_u64(x, m);
     x = y > x ? y : x;
   }
   return x;
@@ -146,7 +195,7 @@ __device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t key) {
   for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t other = shfl_xor_u64(key, j);
+      uint64_t other = lane_xor_u64(key, j);
       bool lower = (lane & j) == 0;
       bool keep_max = lower == ((lane & k) == 0);
       uint64_t mx = other > key ? other : key;
@@ -183,7 +232,7 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&keys)[R]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int e = r * kWave + lane;
-          uint64_t other = shfl_xor_u64(keys[r], j);
+          uint64_t other = lane_xor_u64(keys[r], j);
           bool lower = (e & j) == 0;
           bool keep_max = lower == ((e & k) == 0);
           uint64_t mx = other > keys[r] ? other : keys[r];
@@ -229,13 +278,6 @@ __device__ __forceinline__ uint64_t wave_rank_sort64(uint64_t key, uint64_t* buf
   return out;
 }
 
-// The same for a 64-bit key, word by word.
-template <int J>
-__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
-  const uint32_t lo = lane_xor_u32<J>(static_cast<uint32_t>(x));
-  const uint32_t hi = lane_xor_u32<J>(static_cast<uint32_t>(x >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 template <int J>
 __device__ __forceinline__ uint64_t bitonic_step_desc(uint64_t c) {
   const uint64_t o = lane_xor_u64<J>(c);
@@ -285,7 +327,7 @@ __device__ __forceinline__ uint64_t wave_topk(uint64_t (&keys)[R], int K, uint64
 #pragma unroll
     for (int r = 1; r < R; ++r) lm = keys[r] > lm ? keys[r] : lm;
     uint64_t srt = wave_rank_sort64(lm, buf);
-    uint64_t tau = shfl_u64(srt, K - 1);
+    uint64_t tau = bcast_u64(srt, K - 1);
     if (tau == 0) tau = 1;
     int base = 0;
 #pragma unroll
@@ -304,7 +346,7 @@ __device__ __forceinline__ uint64_t wave_topk(uint64_t (&keys)[R], int K, uint64
   uint64_t run = wave_rank_sort64(keys[0], buf);
 #pragma unroll
   for (int r = 1; r < R; ++r) {
-    const uint64_t kth = shfl_u64(run, K - 1);
+    const uint64_t kth = bcast_u64(run, K - 1);
     if (wave_max_u64(keys[r]) > kth) run = wave_merge_sorted(run, wave_rank_sort64(keys[r], buf), buf);
   }
   return run;
@@ -314,8 +356,8 @@ __device__ __forceinline__ uint64_t wave_topk(uint64_t (&keys)[R], int K, uint64
 // top list `run`, unless its head cannot beat the current K-th key.
 __device__ __forceinline__ uint64_t wave_merge_into(uint64_t run, uint64_t list, int K,
                                                     uint64_t* buf) {
-  const uint64_t kth = shfl_u64(run, K - 1);
-  const uint64_t head = shfl_u64(list, 0);
+  const uint64_t kth = bcast_u64(run, K - 1);
+  const uint64_t head = bcast_u64(list, 0);
   return head > kth ? wave_merge_sorted(run, list, buf) : run;
 }
 
@@ -332,7 +374,7 @@ __device__ __forceinline__ float reduce_scatter16(float (&v)[16], int t) {
     for (int i = 0; i < h; ++i) {
       float a = v[i], b = v[i + h];
       asm("" : "+v"(a), "+v"(b));   // keep the selects on registers (no indexed array access)
-      v[i] = (up ? b : a) + __shfl_xor(up ? a : b, h, kWave);
+      v[i] = (up ? b : a) + lane_xor_f32(up ? a : b, h);
     }
   }
   return v[0];

@@ -418,8 +418,8 @@ decode_attend(Geometry g, int apc, const uint16_t* __restrict__ q, const uint16_
 #pragma unroll
         for (int e = 0; e < 32; ++e) d4[e & 3] = __builtin_fmaf(qs[h][qd * 32 + e], kx[e], d4[e & 3]);
         float d = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-        d += __shfl_xor(d, 1, kWave);
-        d += __shfl_xor(d, 2, kWave);
+        d += lane_xor_f32<1>(d);
+        d += lane_xor_f32<2>(d);
         if (qd == 0) lg[h][j] = j < n ? g.scale * d : -INFINITY;
       }
     }

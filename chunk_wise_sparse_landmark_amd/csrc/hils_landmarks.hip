@@ -201,7 +201,7 @@ __device__ __forceinline__ float2 reduce_groups(float (&acc)[8], int lane) {
       for (int e = 0; e < 2; ++e) {
         float lo = acc[2 * pr + e], hi = acc[2 * (pr + np) + e];
         asm("" : "+v"(lo), "+v"(hi));
-        acc[2 * pr + e] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, h, kWave);
+        acc[2 * pr + e] = (up ? hi : lo) + lane_xor_f32(up ? lo : hi, h);
       }
     }
   }
@@ -220,7 +220,7 @@ __device__ __forceinline__ float2 weighted_keys(const uint4 (&kr)[16], float w, 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float wi = __shfl(w, (lane & 48) | i, kWave);
+    const float wi = row_bcast_f32(w, i);
     float kf[8];
     unpack8(kr[i], kf);
 #pragma unroll
@@ -305,8 +305,8 @@ landmark_backward_fast(Geometry g, int nx, const uint16_t* __restrict__ lq,
   const float sdl = g.scale * dl;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float a = __shfl(sdl, (lane & 48) | i, kWave);
-    const float b = __shfl(p, (lane & 48) | i, kWave);
+    const float a = row_bcast_f32(sdl, i);
+    const float b = row_bcast_f32(p, i);
     float y[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) y[x] = __builtin_fmaf(a, qf[x], b * df[x]);
