@@ -46,7 +46,11 @@ constexpr int kG = 4;            // query heads per KV group on this path
 // prefill_select: with 4+ candidate blocks per row the score table fills the
 // LDS (one workgroup per CU), so sixteen waves (four per SIMD) interleave their
 // serial searches; with fewer, three workgroups of four waves share a CU
-constexpr int sel_threads(int R) { return R >= 4 ? 1024 : 256; }
+// prefill_select: four waves over a whole window below four candidate blocks
+// per lane; eight waves over half a window (32 rows) from four blocks up, so
+// that two workgroups (each with a 66 KB score table) share a CU
+constexpr int sel_threads(int R) { return R >= 4 ? 512 : 256; }
+constexpr int sel_rows(int R) { return R >= 4 ? 32 : 64; }
 constexpr int kAttWaves = 8;             // prefill_attend: two waves per SIMD
 constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kWin = 64;         // queries per window (one chunk), both kernels
@@ -341,20 +345,28 @@ __device__ __forceinline__ void narrow_rows_topk(const float* row0, int stride, 
 //      in which P leaves the S^T accumulators).
 // ----------------------------------------------------------------------------
 template <int R>
-__global__ void __launch_bounds__(sel_threads(R), R >= 4 ? 1 : 3)
+__global__ void __launch_bounds__(sel_threads(R), R >= 4 ? 2 : 3)
 prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const uint16_t* __restrict__ lmk,
                const float* __restrict__ bias, int32_t* __restrict__ sel_idx,
                uint16_t* __restrict__ kvf) {
   constexpr int NCP = R * kWave;
-  __shared__ float gs[kWin][NCP + 1];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kS * kD];
+  constexpr int kRows = sel_rows(R);          // score rows (queries) of this workgroup
+  constexpr int kHalves = kWin / kRows;
+  constexpr bool kStageV = R < 4;             // V rewritten through LDS (else gathered)
+  __shared__ __attribute__((aligned(16))) float gs[kRows][NCP + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kStageV ? kS * kD : 8];
+  // wide rows: each wave's work buffer for its row searches (128 keys)
+  __shared__ __attribute__((aligned(16))) uint64_t wbuf[kStageV ? 1 : sel_threads(R) / kWave][2 * kWave];
   const int nbkv = g.B * g.Hkv;            // (b, kv head) fastest: one head per XCD
   const int bkv = blockIdx.x % nbkv;
-  const int win = (g.Lq / kWin - 1) - blockIdx.x / nbkv;
+  const int wh = blockIdx.x / nbkv;
+  const int win = (g.Lq / kWin - 1) - wh / kHalves, half = wh % kHalves;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const int i0 = win * kWin;
+  const int i0 = win * kWin + half * kRows;
+  // the window's own chunk is rewritten in fragment order by its first half
+  const bool rewrite = half == 0;
   // candidates: complete chunks before the local window (own chunk `win` and the
   // g.win - 1 chunks before it)
   const int ncand = max(0, min(win - max(g.win - 1, 0), g.NC));
@@ -373,7 +385,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   // its fragment rewrite (below 8 candidate blocks per lane; at 8 the
   // registers are taken by the landmark batches, and K is loaded at the
   // rewrite)
-  {
+  if constexpr (kStageV) {
     const int wbase = w * kWave;
 #pragma unroll
     for (int j = 0; j < kS * kD / 8 / kThreads; ++j)
@@ -392,7 +404,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     return reinterpret_cast<const bf16x8*>(Kc + (size_t)(16 * mt + fl % 16) * kD + 32 * ks + 8 * (fl / 16));
   };
   bf16x8 kfr[kKf];
-  if constexpr (kEarlyK) {
+  if (kEarlyK && rewrite) {
 #pragma unroll
     for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
   }
@@ -401,7 +413,8 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   // w / 4, w / 4 + nw / 4, ... of the column tiles (nw waves), and each wave
   // then selects for its own 64 / nw rows below
   // A operand: 16 queries of this row group x 4 heads x 4 k-steps
-  const int rg = w & 3, ch = w >> 2;        // (four waves: ch = 0, every batch)
+  constexpr int kRG = kRows / 16;           // row groups of 16 queries
+  const int rg = w % kRG, ch = w / kRG;     // (four waves: ch = 0, every batch)
   bf16x8 a[kG][4];
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
@@ -420,7 +433,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   // column tiles per batch: 2 with sixteen waves (128 registers each), 4 with
   // small tables, so that three workgroups fit a CU's registers
   constexpr int kTiles = R >= 4 ? 2 : 4;
-  for (int nt0 = kTiles * ch; nt0 < ntile; nt0 += kTiles * (kSelWaves / 4)) {
+  for (int nt0 = kTiles * ch; nt0 < ntile; nt0 += kTiles * (kSelWaves / kRG)) {
     bf16x8 bv[kTiles][4];   // the loads of up to kTiles column tiles in flight together
     float bx[kTiles];
 #pragma unroll
@@ -452,40 +465,61 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
 
   // K fragments of this chunk: straight 16-B copies
   uint16_t* kdst = kvf + ((size_t)bkv * g.NC + win) * kChunkElems;
-  if constexpr (!kEarlyK) {
-#pragma unroll
-    for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
-  }
-#pragma unroll
-  for (int i = 0; i < kKf; ++i) reinterpret_cast<bf16x8*>(kdst)[tid + i * kThreads] = kfr[i];
-  __builtin_amdgcn_s_waitcnt(0);           // this thread's V copies have landed
-  __syncthreads();
-
-  // V fragments of this chunk
   uint16_t* vdst = kdst + 16 * kFrag;
-  for (int f = tid; f < 16 * kWave; f += kThreads) {
-    const int fl = f % kWave, ks = (f / kWave) % 2, db = f / (2 * kWave);
-    uint32_t wd[4];
+  // V fragment f, lane fl, element j: V[32ks + 16(j/4) + 4(fl/16) + j%4][16db + fl%16]
+  auto v_key = [](int f, int j) {
+    const int fl = f % kWave, ks = (f / kWave) % 2;
+    return 32 * ks + 16 * (j / 4) + 4 * (fl / 16) + (j % 4);
+  };
+  auto v_col = [](int f) { return 16 * (f / (2 * kWave)) + (f % kWave) % 16; };
+  if constexpr (kStageV) {
+    if constexpr (!kEarlyK) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      uint32_t h2[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int j = jj * 2 + e;
-        const int key = 32 * ks + 16 * (j / 4) + 4 * (fl / 16) + (j % 4);
-        h2[e] = vs[key * kD + 16 * db + (fl % 16)];
-      }
-      wd[jj] = h2[0] | (h2[1] << 16);
+      for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
     }
-    reinterpret_cast<uint4*>(vdst)[f] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+#pragma unroll
+    for (int i = 0; i < kKf; ++i) reinterpret_cast<bf16x8*>(kdst)[tid + i * kThreads] = kfr[i];
+    __builtin_amdgcn_s_waitcnt(0);           // this thread's V copies have landed
+    __syncthreads();
+    // V fragments of this chunk, from the LDS copy
+    for (int f = tid; f < 16 * kWave; f += kThreads) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        wd[jj] = (uint32_t)vs[v_key(f, 2 * jj) * kD + v_col(f)] |
+                 ((uint32_t)vs[v_key(f, 2 * jj + 1) * kD + v_col(f)] << 16);
+      reinterpret_cast<uint4*>(vdst)[f] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+  } else if (rewrite) {
+    if constexpr (!kEarlyK) {
+#pragma unroll
+      for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
+    }
+#pragma unroll
+    for (int i = 0; i < kKf; ++i) reinterpret_cast<bf16x8*>(kdst)[tid + i * kThreads] = kfr[i];
+    // V fragments gathered straight from the V rows (a wave's 2-byte loads
+    // cover 32 contiguous bytes of each of four rows), all issued together
+    constexpr int kVf = 16 * kWave / kThreads;
+    uint16_t hv[kVf][8];
+#pragma unroll
+    for (int i = 0; i < kVf; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[i][j] = Vc[v_key(tid + i * kThreads, j) * kD + v_col(tid + i * kThreads)];
+#pragma unroll
+    for (int i = 0; i < kVf; ++i) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) wd[jj] = (uint32_t)hv[i][2 * jj] | ((uint32_t)hv[i][2 * jj + 1] << 16);
+      reinterpret_cast<uint4*>(vdst)[tid + i * kThreads] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
   }
 
-  // the selection of the window's 64 rows; the V staging area is each wave's
-  // work buffer from here on
+  // the selection of the workgroup's rows
   __syncthreads();
-  uint64_t* sbuf = reinterpret_cast<uint64_t*>(vs) + w * (kS * kD / 4 / (kThreads / kWave));
-  constexpr int kRowsPerWave = kWin / (kThreads / kWave);
+  constexpr int kRowsPerWave = kRows / (kThreads / kWave);
   if constexpr (R <= 2) {
+    // the V staging area is each wave's work buffer from here on
+    uint64_t* sbuf = reinterpret_cast<uint64_t*>(vs) + w * (kS * kD / 4 / (kThreads / kWave));
     static_assert(kRowsPerWave == kWave / 4, "four lanes per row");
     static_assert(kRowsPerWave * kMaxKf + kWave <= 2 * (kS * kD / 4 / (kThreads / kWave)), "staging");
     narrow_rows_topk<R>(&gs[w * kRowsPerWave][0], NCP + 1, ncand, g.K,
@@ -505,7 +539,7 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
         keys[0][r] = kk & (c < ncand ? ~0ull : 0ull);
       }
       select_ascending<R, 1>(keys, g.K, sel_idx + ((size_t)bkv * g.Lq + i0 + row) * g.K,
-                             (size_t)g.K, sbuf);
+                             (size_t)g.K, &wbuf[w][0]);
     }
   }
 }
@@ -982,7 +1016,8 @@ template <int R>
 void launch_select(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const uint16_t* lmk, const float* bias, int32_t* sel_idx, uint16_t* kvf,
                    hipStream_t st) {
-  hipLaunchKernelGGL(prefill_select<R>, dim3((g.Lq / kWin) * g.B * g.Hkv), dim3(sel_threads(R)), 0, st,
+  hipLaunchKernelGGL(prefill_select<R>, dim3((g.Lq / kWin) * (kWin / sel_rows(R)) * g.B * g.Hkv),
+                     dim3(sel_threads(R)), 0, st,
                      g, q, k, v, lmk, bias, sel_idx, kvf);
 }
 
