@@ -21,7 +21,8 @@ top-K retrieval.  `prefill_8k_corr` repeats prefill_8k with correlated adjacent
 queries (first-order autoregressive along the sequence, rho = 0.98), the regime
 in which the query-block union kernel saves work; its line reports the measured
 share of chunks that adjacent queries have in common.  `train_8k_qcal` repeats the
-training step with a separate rank-8 retrieval query (score gradients to it).
+training step with a separate rank-8 retrieval query (score gradients to it), and
+`train_32k` runs it at 32K tokens (batch 1, 512 chunks).
 
 Every input is resident in HBM before timing.  Per-kernel durations come from
 HIP events the library records around each launch of the dominant kernel on
@@ -676,6 +677,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", default=None, help="run one workload: prefill_8k, decode_128k, "
                                                      "decode_4m, train_8k, landmarks_8k, prefill_32k, "
+                                                     "train_32k, train_8k_qcal, prefill_8k_corr, "
                                                      "or prefill_8k, decode_128k, train_8k + _swa512")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain %d MiB device copy (HBM counter calibration)" % COPY_MIB)
@@ -733,9 +735,10 @@ def main():
     if not args.no_extra and args.only is None:
         todo = ["decode_128k", "decode_4m", "prefill_32k", "train_8k", "landmarks_8k",
                 "prefill_8k_swa512", "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr",
-                "train_8k_qcal"]
+                "train_8k_qcal", "train_32k"]
     elif args.only in ("decode_128k", "decode_4m", "train_8k", "landmarks_8k", "prefill_8k_swa512",
-                       "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr", "train_8k_qcal"):
+                       "decode_128k_swa512", "train_8k_swa512", "prefill_8k_corr", "train_8k_qcal",
+                       "train_32k"):
         todo = [args.only]
     for name in todo:
         cfg = dict(config("train_8k"), name=name) if name == "landmarks_8k" else config(name)

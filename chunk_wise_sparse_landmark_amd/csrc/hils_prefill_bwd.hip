@@ -1,5 +1,6 @@
 // MFMA backward of the prefill path: bf16, head_dim 128, chunk 64, GQA group
-// of 4, causal, seq_q == seq_kv (the shapes the MFMA forward covers).
+// of 4, causal, seq_q == seq_kv (the shapes the MFMA forward covers), up to 256
+// chunks with K <= 32 and up to 512 chunks (32K tokens) with K <= 16.
 //
 // Method: Hierarchical Sparse Attention Done Right (arXiv 2607.02980v1, summary
 // page), §3 "Hierarchical softmax" (gradients of the LM loss reach the chunk
@@ -43,8 +44,12 @@ constexpr int kS = 64;
 constexpr int kG = 4;
 constexpr int kWin = 64;
 constexpr int kMaxKb = 32;
-constexpr int kMaxNCb = 256;
-constexpr int kMaxL = kMaxNCb * kS;
+constexpr int kMaxNCb = 512;                       // chunks bound on this path (L <= 32768)
+// the rows pass keeps per-(query, slot) and per-(query, chunk) tables in LDS
+// next to two 48 KB chunk buffers: up to 256 chunks with K <= 32, up to 512
+// chunks with K <= 16
+constexpr int kRowsNarrowNC = 256;
+constexpr int kRowsWideK = 16;
 constexpr int kFragE = kWave * 8;                  // bf16 per fragment
 constexpr int kBwdFrags = 48;                      // K (A), V (A), K (B, P order)
 constexpr int kBwdChunkElems = kBwdFrags * kFragE; // 48 KB per chunk
@@ -53,6 +58,7 @@ constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowBlocks = kWin / 4 / kRowWaves;   // query blocks per wave
 constexpr int kPrepThreads = 256;
 constexpr int kChunkThreads = 256;
+constexpr int kPlanThreads = kMaxNCb;              // one thread per chunk
 constexpr int kTilesPerItem = 64;                  // 512 (query, chunk) pairs per work item
 constexpr int kPartFloats = 2 * kS * kD + kD + 4;  // dV, dK, dlmk, dbias (+pad to 16 B)
 
@@ -116,6 +122,7 @@ BwdWs carve(const Geometry& g, void* base, size_t* total) {
 //      f <  48 (32+db*2+ks): K[32ks + 16(j/4) + 4(l/16) + j%4][16db + l%16]
 //                            B of dQ = dL K, keys in the order dL leaves S^T
 // ----------------------------------------------------------------------------
+template <int NCB>
 __global__ void __launch_bounds__(kPrepThreads)
 prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ out,
@@ -123,8 +130,8 @@ prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
                  BwdWs ws) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_[kS * kD];
   __shared__ __attribute__((aligned(16))) uint16_t vs_[kS * kD];
-  __shared__ uint64_t qmask[kMaxNCb];
-  __shared__ uint8_t slots[kWin * kMaxNCb];
+  __shared__ uint64_t qmask[NCB];
+  __shared__ uint8_t slots[kWin * NCB];
   const int nbkv = g.B * g.Hkv;
   const int bkv = blockIdx.x % nbkv, win = blockIdx.x / nbkv;
   const int b = bkv / g.Hkv, kvh = bkv % g.Hkv;
@@ -135,8 +142,8 @@ prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     reinterpret_cast<uint4*>(ks_)[x] = reinterpret_cast<const uint4*>(k + row0 * kD)[x];
     reinterpret_cast<uint4*>(vs_)[x] = reinterpret_cast<const uint4*>(v + row0 * kD)[x];
   }
-  for (int c = tid; c < kMaxNCb; c += kPrepThreads) qmask[c] = 0ull;
-  for (int x = tid; x < kWin * kMaxNCb / 4; x += kPrepThreads)
+  for (int c = tid; c < NCB; c += kPrepThreads) qmask[c] = 0ull;
+  for (int x = tid; x < kWin * NCB / 4; x += kPrepThreads)
     reinterpret_cast<uint32_t*>(slots)[x] = 0xffffffffu;
   __syncthreads();
 
@@ -193,7 +200,7 @@ prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     const int c = sel_idx[((size_t)bkv * L + win * kWin + qq) * g.K + s];
     if (c >= 0) {
       atomicOr((unsigned long long*)&qmask[c], 1ull << qq);
-      slots[qq * kMaxNCb + c] = (uint8_t)s;
+      slots[qq * NCB + c] = (uint8_t)s;
     }
   }
   __syncthreads();
@@ -201,24 +208,27 @@ prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     ws.qm[((size_t)bkv * NW + win) * g.NC + c] = qmask[c];
   for (int x = tid; x < kWin * g.NC; x += kPrepThreads) {
     const int qq = x / g.NC, c = x % g.NC;
-    ws.slot[((size_t)bkv * L + win * kWin + qq) * g.NC + c] = slots[qq * kMaxNCb + c];
+    ws.slot[((size_t)bkv * L + win * kWin + qq) * g.NC + c] = slots[qq * NCB + c];
   }
 }
 
 // ----------------------------------------------------------------------------
 // 2. rows: dq and the per-(row, slot) table
 // ----------------------------------------------------------------------------
+template <int KB, int NCB>
 struct RowsSmem {
   uint4 kv[2][kBwdFrags * kWave];     // 2 x 48 KB of chunk fragments
-  float wts[kWin * kMaxKb * kG];      // (query, slot, head): weight, then ds
-  uint8_t slotmap[kWin * kMaxNCb];    // (query, chunk) -> slot
-  int sel[kWin * kMaxKb];
-  uint64_t qmask[kMaxNCb];
-  uint16_t ulist[kMaxNCb];
+  float wts[kWin * KB * kG];          // (query, slot, head): weight, then ds
+  uint8_t slotmap[kWin * NCB];        // (query, chunk) -> slot
+  int sel[kWin * KB];
+  uint64_t qmask[NCB];
+  uint16_t ulist[NCB];
   float Dr[kWin * kG];
   float LSE2[kWin * kG];              // forward LSE in log2 units
   int wcount[kRowWaves];
 };
+static_assert(sizeof(RowsSmem<kMaxKb, kRowsNarrowNC>) <= 160 * 1024, "rows pass LDS");
+static_assert(sizeof(RowsSmem<kRowsWideK, kMaxNCb>) <= 160 * 1024, "rows pass LDS");
 
 __device__ __forceinline__ void stage48(const uint16_t* __restrict__ src, uint4* __restrict__ dst) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
@@ -347,6 +357,7 @@ __device__ __forceinline__ float4 block_bwd(const uint4* kvb, const bf16x8 (&qf)
 // masked), every block takes part.  jwin < 0: a union chunk; blocks none of
 // whose queries selected it are skipped, and each selecting row's ds_c replaces
 // its weight in `wts`.
+template <int NCB>
 __device__ __forceinline__ void rows_step(
     const Geometry& g, const uint4* __restrict__ kvb, uint4* __restrict__ nxt,
     const uint16_t* __restrict__ nsrc, const uint8_t* __restrict__ slotmap,
@@ -363,7 +374,7 @@ __device__ __forceinline__ void rows_step(
     const int blk = w * kRowBlocks + j;
     if (((qmk >> (blk * 4)) & 0xfull) == 0) continue;
     const int qi = blk * 4 + (r16 >> 2), h = r16 & 3;
-    const int slot = local ? K + jwin : slotmap[qi * kMaxNCb + c];
+    const int slot = local ? K + jwin : slotmap[qi * NCB + c];
     const float wv = (!local && slot != 0xff) ? wts[(qi * K + slot) * kG + h] : 0.f;
     const float dr = Dr[qi * kG + h];
     float4 st = block_bwd(kvb, qf[j], df[j], sc2, jwin == 0 ? qi + 1 : kS, local, wv, dr,
@@ -376,6 +387,7 @@ __device__ __forceinline__ void rows_step(
   }
 }
 
+template <int KB, int NCB>
 __global__ void __launch_bounds__(kRowThreads)
 prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
                  const uint16_t* __restrict__ dout, const uint16_t* __restrict__ lmk,
@@ -383,7 +395,8 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
                  const float* __restrict__ lse, BwdWs ws, uint16_t* __restrict__ dq_out,
                  uint16_t* __restrict__ dqr_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  RowsSmem& sm = *reinterpret_cast<RowsSmem*>(smem_raw);
+  RowsSmem<KB, NCB>& sm = *reinterpret_cast<RowsSmem<KB, NCB>*>(smem_raw);
+  static_assert(NCB <= kRowThreads, "one thread per chunk in the union list");
   const int nbkv = g.B * g.Hkv;
   const int bkv = blockIdx.x % nbkv;
   const int win = (g.Lq / kWin - 1) - blockIdx.x / nbkv;
@@ -404,9 +417,9 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
   // ---- selection tables and the window's chunk union
   for (int x = tid; x < kWin * K; x += kRowThreads)
     sm.sel[x] = sel_idx[((size_t)bkv * L + i0 + x / K) * K + x % K];
-  for (int x = tid; x < kWin * kMaxNCb / 4; x += kRowThreads)
+  for (int x = tid; x < kWin * NCB / 4; x += kRowThreads)
     reinterpret_cast<uint32_t*>(sm.slotmap)[x] = 0xffffffffu;
-  for (int c = tid; c < kMaxNCb; c += kRowThreads) sm.qmask[c] = 0ull;
+  for (int c = tid; c < NCB; c += kRowThreads) sm.qmask[c] = 0ull;
   if (tid < kWin * kG) {
     const int qq = tid >> 2, h = tid & 3;
     const size_t row = (size_t)(b * g.Hq + kvh * kG + h) * L + i0 + qq;
@@ -418,13 +431,13 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     const int c = sm.sel[x];
     if (c >= 0) {
       atomicOr((unsigned long long*)&sm.qmask[c], 1ull << (x / K));
-      sm.slotmap[(x / K) * kMaxNCb + c] = (uint8_t)(x % K);
+      sm.slotmap[(x / K) * NCB + c] = (uint8_t)(x % K);
     }
   }
   __syncthreads();
   {
     const int c = tid;
-    const bool f = c < ncand && sm.qmask[c] != 0ull;
+    const bool f = c < ncand && c < NCB && sm.qmask[c < NCB ? c : 0] != 0ull;
     const uint64_t m = __ballot(f);
     if (lane == 0) sm.wcount[w] = __popcll(m);
     __syncthreads();
@@ -486,7 +499,7 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
       for (int i = 0; i < 4; ++i) {
         const int rr = g4 * 4 + i;
         const int qi = (w * kRowBlocks + j) * 4 + (rr >> 2), h = rr & 3;
-        const int slot = uu < nunion ? sm.slotmap[qi * kMaxNCb + c] : 0xff;
+        const int slot = uu < nunion ? sm.slotmap[qi * NCB + c] : 0xff;
         if (slot != 0xff)
           sm.wts[(qi * K + slot) * kG + h] = __builtin_amdgcn_exp2f(
               (scale * acc[i] + bc) * 1.4426950408889634f - sm.LSE2[qi * kG + h]);
@@ -505,7 +518,7 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
   int cur = 0;
   int x0 = 0;
   if (nwin > 0) {   // the own chunk (straight-line: its mode is known here)
-    rows_step(g, sm.kv[0], sm.kv[1], seq_src(1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2, ~0ull, own, 0,
+    rows_step<NCB>(g, sm.kv[0], sm.kv[1], seq_src(1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2, ~0ull, own, 0,
               qf, df, sc2, ws, b, kvh, i0, w, dq);
     stage_wait_all();
     __syncthreads();
@@ -513,14 +526,14 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
     x0 = 1;
   }
   for (int x = x0; x < nwin; ++x, cur ^= 1) {
-    rows_step(g, sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2,
+    rows_step<NCB>(g, sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2,
               ~0ull, own - x, x, qf, df, sc2, ws, b, kvh, i0, w, dq);
     stage_wait_all();
     __syncthreads();
   }
   for (int x = nwin; x < nseq; ++x, cur ^= 1) {
     const int c = sm.ulist[x - nwin];
-    rows_step(g, sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2,
+    rows_step<NCB>(g, sm.kv[cur], sm.kv[cur ^ 1], seq_src(x + 1), sm.slotmap, sm.wts, sm.Dr, sm.LSE2,
               sm.qmask[c], c, -1, qf, df, sc2, ws, b, kvh, i0, w, dq);
     stage_wait_all();
     __syncthreads();
@@ -575,9 +588,9 @@ prefill_bwd_rows(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
 //      tiles per window, then the retrieving queries in query order, 8 per
 //      tile) cut into items of kTilesPerItem.
 //      One workgroup per (b, kv head).
-__global__ void __launch_bounds__(kChunkThreads)
+__global__ void __launch_bounds__(kPlanThreads)
 prefill_bwd_plan(Geometry g, BwdWs ws) {
-  __shared__ int scan[kChunkThreads];
+  __shared__ int scan[kPlanThreads];
   const int bkv = blockIdx.x, tid = threadIdx.x;
   const int NW = g.Lq / kWin;
   int nseg = 0, tiles = 0;
@@ -591,7 +604,7 @@ prefill_bwd_plan(Geometry g, BwdWs ws) {
   }
   scan[tid] = nseg;
   __syncthreads();
-  for (int off = 1; off < kChunkThreads; off <<= 1) {
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
     const int t = tid >= off ? scan[tid - off] : 0;
     __syncthreads();
     scan[tid] += t;
@@ -606,7 +619,7 @@ prefill_bwd_plan(Geometry g, BwdWs ws) {
     }
     ws.chunkseg[(size_t)bkv * g.NC + tid] = make_int2(base, nseg);
   }
-  if (tid == 0) ws.nitems[bkv] = scan[kChunkThreads - 1];
+  if (tid == 0) ws.nitems[bkv] = scan[kPlanThreads - 1];
 }
 
 // One tile of 8 queries x 4 heads = 32 rows, staged in LDS by the four waves
@@ -771,6 +784,8 @@ __device__ __forceinline__ void chunk_pair_step(
   if (t + 1 < ntile) chunk_tile_compute(g, w, lane, key, sc2, t + 1, tb, eq, es, kB, vB, dv, dk, dlm, dbt);
 }
 
+// WPT: query windows listed per thread (one up to 256 windows, two up to 512)
+template <int WPT>
 __global__ void __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, BwdWs ws,
@@ -807,9 +822,15 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
   const int rbase = 8 * max(0, own_tiles - t0);   // entry index of the first retrieved query
   const int wret = c + max(g.win, 1);        // first window that may retrieve chunk c
   const int nlater = NW - wret;
-  uint64_t m = 0;
-  if (tid < nlater && r1 > r0) m = ws.qm[((size_t)bkv * NW + wret + tid) * g.NC + c];
-  const int cnt = __popcll(m);
+  // thread t lists windows wret + WPT t .. + WPT - 1
+  uint64_t m[WPT];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int wi = tid * WPT + j;
+    m[j] = (wi < nlater && r1 > r0) ? ws.qm[((size_t)bkv * NW + wret + wi) * g.NC + c] : 0ull;
+    cnt += __popcll(m[j]);
+  }
   sm.scan[tid] = cnt;
   __syncthreads();
   for (int off = 1; off < kChunkThreads; off <<= 1) {
@@ -821,15 +842,18 @@ prefill_bwd_chunks(Geometry g, const uint16_t* __restrict__ q, const uint16_t* _
   {
     int pos = sm.scan[tid] - cnt;
     if (pos < r1 && pos + cnt > r0) {
-      uint64_t mm = m;
-      while (mm) {
-        const int bit = __ffsll((long long)mm) - 1;
-        mm &= mm - 1;
-        if (pos >= r0 && pos < r1) {
-          const int qq = (wret + tid) * kWin + bit;
-          sm.eq[rbase + pos - r0] = (uint16_t)qq;
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        uint64_t mm = m[j];
+        while (mm) {
+          const int bit = __ffsll((long long)mm) - 1;
+          mm &= mm - 1;
+          if (pos >= r0 && pos < r1) {
+            const int qq = (wret + tid * WPT + j) * kWin + bit;
+            sm.eq[rbase + pos - r0] = (uint16_t)qq;
+          }
+          ++pos;
         }
-        ++pos;
       }
     }
   }
@@ -964,11 +988,13 @@ prefill_bwd_reduce(Geometry g, BwdWs ws, uint16_t* __restrict__ dk_out,
 //      added in wave order, so the result does not depend on timing.
 constexpr int kQrThreads = 256;
 
+template <int NCB>
 __global__ void __launch_bounds__(kQrThreads)
 prefill_bwd_dlmk_qret(Geometry g, const uint16_t* __restrict__ qr, BwdWs ws,
                       uint16_t* __restrict__ dlmk_out) {
-  __shared__ uint16_t eq[kMaxL];
-  __shared__ uint8_t es[kMaxL];
+  // the chunk's retrieving queries (at most L <= 64 NCB): ids and slots
+  __shared__ uint16_t eq[NCB * kS];
+  __shared__ uint8_t es[NCB * kS];
   __shared__ int scan[kQrThreads];
   __shared__ float red[kQrThreads / kWave][kD];
   const int nbkv = g.B * g.Hkv;
@@ -979,8 +1005,16 @@ prefill_bwd_dlmk_qret(Geometry g, const uint16_t* __restrict__ qr, BwdWs ws,
   const size_t nslot = (size_t)(g.K + g.win);
   const int wret = c + max(g.win, 1);       // first window that may retrieve chunk c
   const int nlater = NW - wret;
-  const uint64_t m = tid < nlater ? ws.qm[((size_t)bkv * NW + wret + tid) * g.NC + c] : 0ull;
-  const int cnt = __popcll(m);
+  // thread t lists windows wret + kWpt t .. + kWpt - 1
+  constexpr int kWpt = NCB / kQrThreads;
+  uint64_t m[kWpt];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kWpt; ++j) {
+    const int wi = tid * kWpt + j;
+    m[j] = wi < nlater ? ws.qm[((size_t)bkv * NW + wret + wi) * g.NC + c] : 0ull;
+    cnt += __popcll(m[j]);
+  }
   scan[tid] = cnt;
   __syncthreads();
   for (int off = 1; off < kQrThreads; off <<= 1) {
@@ -991,13 +1025,15 @@ prefill_bwd_dlmk_qret(Geometry g, const uint16_t* __restrict__ qr, BwdWs ws,
   }
   {
     int pos = scan[tid] - cnt;
-    uint64_t mm = m;
-    while (mm) {
-      const int bit = __ffsll((long long)mm) - 1;
-      mm &= mm - 1;
-      const int qq = (wret + tid) * kWin + bit;
-      eq[pos] = (uint16_t)qq;
-      ++pos;
+#pragma unroll
+    for (int j = 0; j < kWpt; ++j) {
+      uint64_t mm = m[j];
+      while (mm) {
+        const int bit = __ffsll((long long)mm) - 1;
+        mm &= mm - 1;
+        eq[pos] = (uint16_t)((wret + tid * kWpt + j) * kWin + bit);
+        ++pos;
+      }
     }
   }
   const int total = scan[kQrThreads - 1];
@@ -1035,7 +1071,7 @@ prefill_bwd_dlmk_qret(Geometry g, const uint16_t* __restrict__ qr, BwdWs ws,
 bool prefill_bwd_fast_supported(const Geometry& g, int bf16) {
   return bf16 && g.d == kD && g.S == kS && g.G == kG && g.causal && g.Lq == g.Lkv &&
          g.Lq % kWin == 0 && g.K <= kMaxKb && g.NC <= kMaxNCb && g.NC >= 1 &&
-         g.K + g.win < 0xff;
+         (g.NC <= kRowsNarrowNC || g.K <= kRowsWideK) && g.K + g.win < 0xff;
 }
 
 size_t prefill_bwd_fast_ws(const Geometry& g) {
@@ -1053,27 +1089,51 @@ hipError_t launch_prefill_bwd_fast(const Geometry& g, const void* q, const void*
   const int nbkv = g.B * g.Hkv, NW = g.Lq / kWin;
   const uint16_t* Q = (const uint16_t*)q;
   const uint16_t* DO = (const uint16_t*)dout;
-  hipLaunchKernelGGL(prefill_bwd_prep, dim3(nbkv * NW), dim3(kPrepThreads), 0, st, g, Q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)out, DO, sel_idx, ws);
-  hipError_t e = hipFuncSetAttribute((const void*)prefill_bwd_rows,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(RowsSmem));
+  const bool narrow = g.NC <= kRowsNarrowNC;
+  if (narrow)
+    hipLaunchKernelGGL(prefill_bwd_prep<kRowsNarrowNC>, dim3(nbkv * NW), dim3(kPrepThreads), 0, st, g, Q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)out, DO, sel_idx, ws);
+  else
+    hipLaunchKernelGGL(prefill_bwd_prep<kMaxNCb>, dim3(nbkv * NW), dim3(kPrepThreads), 0, st, g, Q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)out, DO, sel_idx, ws);
+  // dynamic LDS above 64 KB must be enabled for each kernel (per device; cheap)
+  const void* rows_fn = narrow ? (const void*)prefill_bwd_rows<kMaxKb, kRowsNarrowNC>
+                               : (const void*)prefill_bwd_rows<kRowsWideK, kMaxNCb>;
+  const size_t rows_lds = narrow ? sizeof(RowsSmem<kMaxKb, kRowsNarrowNC>)
+                                 : sizeof(RowsSmem<kRowsWideK, kMaxNCb>);
+  hipError_t e = hipFuncSetAttribute(rows_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rows_lds);
   if (e != hipSuccess) return e;
   prof_begin(kPrefillBwdRows, st);
-  hipLaunchKernelGGL(prefill_bwd_rows, dim3(nbkv * NW), dim3(kRowThreads), sizeof(RowsSmem), st, g,
-                     Q, (const uint16_t*)qr, DO, (const uint16_t*)lmk, bias, sel_idx, lse, ws,
-                     (uint16_t*)dq, (uint16_t*)dqr);
+  if (narrow)
+    hipLaunchKernelGGL((prefill_bwd_rows<kMaxKb, kRowsNarrowNC>), dim3(nbkv * NW), dim3(kRowThreads),
+                       rows_lds, st, g, Q, (const uint16_t*)qr, DO, (const uint16_t*)lmk, bias, sel_idx,
+                       lse, ws, (uint16_t*)dq, (uint16_t*)dqr);
+  else
+    hipLaunchKernelGGL((prefill_bwd_rows<kRowsWideK, kMaxNCb>), dim3(nbkv * NW), dim3(kRowThreads),
+                       rows_lds, st, g, Q, (const uint16_t*)qr, DO, (const uint16_t*)lmk, bias, sel_idx,
+                       lse, ws, (uint16_t*)dq, (uint16_t*)dqr);
   prof_end(kPrefillBwdRows, st);
-  hipLaunchKernelGGL(prefill_bwd_plan, dim3(nbkv), dim3(kChunkThreads), 0, st, g, ws);
+  hipLaunchKernelGGL(prefill_bwd_plan, dim3(nbkv), dim3(kPlanThreads), 0, st, g, ws);
   prof_begin(kPrefillBwdChunks, st);
-  hipLaunchKernelGGL(prefill_bwd_chunks, dim3(nbkv * ws.max_items), dim3(kChunkThreads), 0, st, g,
-                     Q, (const uint16_t*)k, (const uint16_t*)v, DO, ws, (uint16_t*)dk,
-                     (uint16_t*)dv, (uint16_t*)dlmk, dbias);
+  if (narrow)
+    hipLaunchKernelGGL(prefill_bwd_chunks<1>, dim3(nbkv * ws.max_items), dim3(kChunkThreads), 0, st,
+                       g, Q, (const uint16_t*)k, (const uint16_t*)v, DO, ws, (uint16_t*)dk,
+                       (uint16_t*)dv, (uint16_t*)dlmk, dbias);
+  else
+    hipLaunchKernelGGL(prefill_bwd_chunks<kMaxNCb / kChunkThreads>, dim3(nbkv * ws.max_items),
+                       dim3(kChunkThreads), 0, st, g, Q, (const uint16_t*)k, (const uint16_t*)v, DO,
+                       ws, (uint16_t*)dk, (uint16_t*)dv, (uint16_t*)dlmk, dbias);
   prof_end(kPrefillBwdChunks, st);
   hipLaunchKernelGGL(prefill_bwd_reduce, dim3(nbkv * g.NCcap), dim3(kChunkThreads), 0, st, g, ws,
                      (uint16_t*)dk, (uint16_t*)dv, (uint16_t*)dlmk, dbias);
-  if (dqr)
-    hipLaunchKernelGGL(prefill_bwd_dlmk_qret, dim3(nbkv * g.NC), dim3(kQrThreads), 0, st, g,
-                       (const uint16_t*)qr, ws, (uint16_t*)dlmk);
+  if (dqr) {
+    if (narrow)
+      hipLaunchKernelGGL(prefill_bwd_dlmk_qret<kRowsNarrowNC>, dim3(nbkv * g.NC), dim3(kQrThreads), 0,
+                         st, g, (const uint16_t*)qr, ws, (uint16_t*)dlmk);
+    else
+      hipLaunchKernelGGL(prefill_bwd_dlmk_qret<kMaxNCb>, dim3(nbkv * g.NC), dim3(kQrThreads), 0, st, g,
+                         (const uint16_t*)qr, ws, (uint16_t*)dlmk);
+  }
   return hipGetLastError();
 }
 

@@ -57,6 +57,8 @@ for _name in ("prefill_8k", "decode_128k", "train_8k"):
 CONFIGS["prefill_8k_corr"] = dict(CONFIGS["prefill_8k"], qcorr=0.98)
 # the training step with a separate rank-8 retrieval query
 CONFIGS["train_8k_qcal"] = dict(CONFIGS["train_8k"], qret=8)
+# the training step at 32K tokens (512 chunks), batch 1
+CONFIGS["train_32k"] = dict(CONFIGS["train_8k"], B=1, Lq=32768, Lkv=32768, seed=6)
 
 
 def config(name, **overrides):

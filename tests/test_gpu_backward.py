@@ -155,6 +155,42 @@ def test_train_8k_full_group(hl):
         assert_close("dlmk chunk %d" % c, to_np(dl)[b, g, c], rdl[c], "norm", 2e-2)
 
 
+@pytest.mark.parametrize("over", [dict(bias=0.3), dict(qret=8, win=8)])
+def test_backward_past_256_chunks_full_group(hl, over):
+    """The MFMA backward past 256 chunks (20480 tokens = 320 chunks, where it takes
+    K <= 16 and lists two query windows per thread): one (batch, kv head) group
+    over all its queries, so every gradient is complete, with a per-chunk bias,
+    and with a separate retrieval query next to a 512-token local window (the
+    landmark gradients then come from the q_ret pass)."""
+    from bench import HipEvents, launched
+    from oracle.pool import default_workers, group_backward, make_pool
+    cfg = dict(config("train_8k"), B=1, Hq=4, Hkv=1, Lq=20480, Lkv=20480, seed=41)
+    cfg.update(over)
+    host, dev = make_device_inputs(cfg)
+    kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=True,
+              local_chunks=cfg.get("win"))
+    qr = dev.get("q_ret")
+    out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"], q_ret=qr,
+                                    **kw)
+
+    def bwd():
+        return hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], dev["bias"], out,
+                                dev["dout"], idx, lse, need_dbias=True, q_ret=qr, **kw)
+
+    assert launched(hl, HipEvents(), "prefill_bwd_rows", bwd), "the MFMA backward path ran"
+    grads = bwd()
+    torch.cuda.synchronize()
+    L = cfg["Lq"]
+    gi = idx.cpu().numpy().astype(np.int64)[0, 0]
+    workers = default_workers()
+    with make_pool(workers) as pool:
+        ref = group_backward(pool, host, 0, 0, np.arange(L), gi, 4 * workers, **kw)
+    names = ("dq", "dk", "dv", "dlmk", "dbias", "dq_ret")
+    for n, (name, got, want) in enumerate(zip(names, grads, ref)):
+        g = to_np(got)[0] if n in (0, 5) else to_np(got)[0, 0]
+        assert_close(name + " group", g, want, "norm", 2e-2)
+
+
 def test_train_8k_swa512_sampled(hl):
     """Training shape with a 512-token local window: dq on sampled rows; dk, dv of
     the last two chunks, which only the queries of the last two windows reach
