@@ -430,6 +430,8 @@ def run_prefill(hl, cfg, steps, warmup, ev):
 
     kern = "prefill_attend" if launched(hl, ev, "prefill_attend", lambda: step(0)) else "generic_attend"
     ms, kms, n = timed(step, steps, warmup, ev, kern, hl)
+    sel = "prefill_select" if kern == "prefill_attend" else "generic_select"
+    _, sel_ms, _ = timed(step, steps, 1, ev, sel, hl)
     flops = forward_flops(cfg)
     ncand, nsel, nown = query_counts(cfg)
     G, d, S = cfg["Hq"] // cfg["Hkv"], cfg["d"], cfg["S"]
@@ -441,6 +443,7 @@ def run_prefill(hl, cfg, steps, warmup, ev):
                              traffic=recorded_traffic(kern, cfg.get("name", "")),
                              per_launch_flops=attn_flops))
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_BF16_TFLOPS
+    res["kernels_ms"] = {kern: kms, sel: sel_ms}
     res["selection"] = sel_stats
     del dev
     return res
@@ -481,6 +484,11 @@ def run_decode(hl, cfg, steps, warmup, ev, nsets):
                              per_launch_bytes=kbytes))
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBS
     res["frac_of_hbm_peak"] = res["value"] / PEAK_HBM_GBS
+    # the step's other timed launches (the fuse launch after the attention has no hook)
+    res["kernels_ms"] = {kern: kms}
+    for other in ("decode_score", "decode_merge", "decode_attend"):
+        if other != kern and launched(hl, ev, other, lambda: step(0)):
+            res["kernels_ms"][other] = timed(step, max(20, steps // 4), 2, ev, other, hl)[1]
     # the generated queries and landmarks of set 0, for the CPU baseline
     res["_host"] = (sets[0]["q"].float().cpu().numpy(), sets[0]["lmk"].float().cpu().numpy())
     del sets, outs
@@ -730,7 +738,8 @@ def main():
                            "heads_kv": cfg["Hkv"], "head_dim": cfg["d"], "seq_len": cfg["Lq"],
                            "chunk_size": cfg["S"], "top_k": cfg["K"], "causal": True,
                            "keep_own_chunk": True, "parallelism": "single GPU"},
-                "roofline": r["roofline"], "selection": r.get("selection")}
+                "roofline": r["roofline"], "kernels_ms": r.get("kernels_ms"),
+                "selection": r.get("selection")}
     todo = []
     if not args.no_extra and args.only is None:
         todo = ["decode_128k", "decode_4m", "prefill_32k", "train_8k", "landmarks_8k",
@@ -773,7 +782,8 @@ def main():
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                 "data": "synthetic", "config": {"workload": r["workload"]},
                 "roofline": r.get("roofline")}
-        for key in ("selection", "backward_kernels", "forward_kernel", "frac_of_hbm_peak", "_host"):
+        for key in ("kernels_ms", "selection", "backward_kernels", "forward_kernel", "frac_of_hbm_peak",
+                    "_host"):
             if key in r:
                 line[key] = r[key]
     line["extra"] = extra
