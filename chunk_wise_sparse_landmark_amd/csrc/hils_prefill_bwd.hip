@@ -206,9 +206,19 @@ prefill_bwd_prep(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __r
   __syncthreads();
   for (int c = tid; c < g.NC; c += kPrepThreads)
     ws.qm[((size_t)bkv * NW + win) * g.NC + c] = qmask[c];
-  for (int x = tid; x < kWin * g.NC; x += kPrepThreads) {
-    const int qq = x / g.NC, c = x % g.NC;
-    ws.slot[((size_t)bkv * L + win * kWin + qq) * g.NC + c] = slots[qq * NCB + c];
+  // the window's 64 x NC slot bytes are one contiguous range that starts at a
+  // multiple of 64 bytes (L and the window start are multiples of 64): four
+  // bytes per store
+  uint32_t* sw = reinterpret_cast<uint32_t*>(ws.slot + ((size_t)bkv * L + win * kWin) * g.NC);
+  for (int x4 = tid; x4 < kWin * g.NC / 4; x4 += kPrepThreads) {
+    uint32_t wd = 0;
+    int qq = (4 * x4) / g.NC, c = 4 * x4 - qq * g.NC;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wd |= (uint32_t)slots[qq * NCB + c] << (8 * e);
+      if (++c == g.NC) { c = 0; ++qq; }
+    }
+    sw[x4] = wd;
   }
 }
 
