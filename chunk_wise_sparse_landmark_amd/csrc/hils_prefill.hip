@@ -9,14 +9,16 @@
 // queries x G heads as one (M x G, d) x (d, S) product over the union of their
 // chunks, M x G >= 16), rebuilt for 64-wide waves and 16x16x32 bf16 MFMA.
 //
-//  1. prefill_select  one workgroup per chunk-aligned 64-query window.  Group
-//     scores sum_h q_h . lmk_c are one MFMA chain (the G heads extend the
-//     reduction), then each query's top-K is found without sorting: tau = K-th
-//     largest lane maximum, keys >= tau are compacted in chunk order and a rank
-//     count keeps K, which come out in ascending id.  The same workgroup also
-//     rewrites its chunk of K and V in MFMA operand-fragment order (16 B per
-//     lane per fragment), so the attention kernel stages a chunk with plain
-//     coalesced copies and reads conflict-free 16-B fragments from LDS.
+//  1. prefill_select  one workgroup per chunk-aligned 64-query window (two,
+//     one per 32-query half, from 256 candidates on).  Group scores
+//     sum_h q_h . lmk_c are one MFMA chain (the G heads extend the reduction),
+//     then each query's top-K is found without sorting (narrow rows: a bit
+//     search four lanes per row; wide rows: tau = K-th largest lane maximum,
+//     keys >= tau compacted in chunk order and a rank count keeps K, which come
+//     out in ascending id).  The (first) workgroup also rewrites the window's
+//     chunk of K and V in MFMA operand-fragment order (16 B per lane per
+//     fragment), so the attention kernel stages a chunk with plain coalesced
+//     copies and reads conflict-free 16-B fragments from LDS.
 //  2. prefill_attend  one workgroup per 64-query window = 16 query blocks of
 //     M = 4 queries x G = 4 heads = 16 rows.  Each of the eight waves owns two
 //     blocks and keeps their fp32 output tiles in MFMA accumulators across all
@@ -409,12 +411,13 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     for (int i = 0; i < kKf; ++i) kfr[i] = *kf_src(i);
   }
 
-  // scores: wave w computes the 16 rows of row group w % 4 against batch
-  // w / 4, w / 4 + nw / 4, ... of the column tiles (nw waves), and each wave
-  // then selects for its own 64 / nw rows below
+  // scores: with nw waves over kRows rows (kRG row groups of 16), wave w
+  // computes the rows of row group w % kRG against batches w / kRG,
+  // w / kRG + nw / kRG, ... of the column tiles, and each wave then selects
+  // for its own kRows / nw rows below
   // A operand: 16 queries of this row group x 4 heads x 4 k-steps
   constexpr int kRG = kRows / 16;           // row groups of 16 queries
-  const int rg = w % kRG, ch = w / kRG;     // (four waves: ch = 0, every batch)
+  const int rg = w % kRG, ch = w / kRG;     // (four waves over 64 rows: ch = 0)
   bf16x8 a[kG][4];
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
