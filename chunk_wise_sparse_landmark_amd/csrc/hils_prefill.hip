@@ -933,16 +933,29 @@ prefill_attend(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
   if (tid < kWin * kG) {
     const int qi = tid >> 2, h = tid & 3;     // 64 queries x 4 heads
     const float lo = nwin > 0 ? sm.lsewin[tid] : -INFINITY;
+    // the row's selection and scores read once, all reads in flight together
+    // (slots past K re-read slot 0 and are dropped)
+    float sv[kMaxKf];
+    uint32_t valid = 0u;
+#pragma unroll
+    for (int slot = 0; slot < kMaxKf; ++slot) {
+      const int ss = slot < K ? slot : 0;
+      const bool ok = slot < K && sm.sel[qi * K + ss] >= 0;
+      sv[slot] = sm.wts[(qi * K + ss) * kG + h];
+      valid |= ok ? 1u << slot : 0u;
+    }
     float m = lo;
-    for (int slot = 0; slot < K; ++slot)
-      if (sm.sel[qi * K + slot] >= 0) m = fmaxf(m, sm.wts[(qi * K + slot) * kG + h]);
+#pragma unroll
+    for (int slot = 0; slot < kMaxKf; ++slot)
+      if ((valid >> slot) & 1u) m = fmaxf(m, sv[slot]);
     float z = nwin > 0 ? __expf(lo - m) : 0.f;
-    for (int slot = 0; slot < K; ++slot)
-      if (sm.sel[qi * K + slot] >= 0) z += __expf(sm.wts[(qi * K + slot) * kG + h] - m);
+#pragma unroll
+    for (int slot = 0; slot < kMaxKf; ++slot)
+      if ((valid >> slot) & 1u) z += __expf(sv[slot] - m);
     const float LSE = z > 0.f ? m + __logf(z) : -INFINITY;
-    for (int slot = 0; slot < K; ++slot)
-      if (sm.sel[qi * K + slot] >= 0)
-        sm.wts[(qi * K + slot) * kG + h] = __expf(sm.wts[(qi * K + slot) * kG + h] - LSE);
+#pragma unroll
+    for (int slot = 0; slot < kMaxKf; ++slot)
+      if ((valid >> slot) & 1u) sm.wts[(qi * K + slot) * kG + h] = __expf(sv[slot] - LSE);
     sm.lse2[tid] = LSE * 1.4426950408889634f;
     if (lse_out) lse_out[(size_t)(b * g.Hq + kvh * kG + h) * g.Lq + i0 + qi] = LSE;
   }
