@@ -197,6 +197,10 @@ def test_prefill_8k_sampled(hl):
 @pytest.mark.parametrize("name,over", [
     ("prefill_32k", {}),                                   # 512 chunks: the widest selection
     ("prefill_8k", dict(Hq=8, Hkv=2, Lq=19200, Lkv=19200, seed=11)),   # 300 chunks, ragged 64-block
+    # 272 chunks with a per-chunk bias, a separate retrieval query, a 3-slot
+    # local window and K = 32 (both halves of every window select)
+    ("prefill_8k", dict(Hq=8, Hkv=2, Lq=17408, Lkv=17408, K=32, bias=0.3, qret=8, win=3,
+                        seed=23)),
 ])
 def test_prefill_long_sampled(hl, name, over):
     """The MFMA prefill path past 256 chunks (8 candidate blocks of 64 per row)."""
@@ -209,8 +213,10 @@ def test_prefill_long_sampled(hl, name, over):
                 | set(range(L - 6, L)))
     check_forward(host, cfg, out, idx, lse, queries=qs, heads_kv=[0, cfg["Hkv"] - 1])
     own = np.arange(L) // cfg["S"]
+    win = cfg.get("win") or 1
     nsel = (idx[0] >= 0).sum(-1)
-    np.testing.assert_array_equal(nsel, np.minimum(own, cfg["K"])[None, :].repeat(cfg["Hkv"], 0))
+    np.testing.assert_array_equal(nsel, np.minimum(np.maximum(own - (win - 1), 0), cfg["K"])[None, :]
+                                  .repeat(cfg["Hkv"], 0))
 
 
 def test_prefill_8k_swa512_sampled(hl):
