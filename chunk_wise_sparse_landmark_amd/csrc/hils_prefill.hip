@@ -285,6 +285,11 @@ __device__ __forceinline__ void narrow_rows_topk(const float* row0, int stride, 
     const uint32_t o = max(u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u), 1u);
     wd[j] = q * n + j < ncand ? o : 0u;
   }
+  // the words are in registers before `stage` (which may be the rows just
+  // read) is written
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int* st = stage + rl * K;
   if (ncand <= K) {
     // every candidate is taken
@@ -466,6 +471,22 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     }
   }
 
+  constexpr int kRowsPerWave = kRows / (kThreads / kWave);
+  if constexpr (R <= 2) {
+    // Narrow rows: wave w scored its own 16 rows against every column tile, so
+    // it searches them now, without waiting for the other waves or the chunk
+    // rewrite below; its table rows, dead once their words are in registers,
+    // are its work space.
+    static_assert(kSelWaves == kRG && kRowsPerWave == kWave / 4, "a wave owns its rows");
+    static_assert(kRowsPerWave * kMaxKf + kWave <= kRowsPerWave * (NCP + 1), "staging");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    narrow_rows_topk<R>(&gs[w * kRowsPerWave][0], NCP + 1, ncand, g.K,
+                        sel_idx + ((size_t)bkv * g.Lq + i0 + w * kRowsPerWave) * g.K,
+                        reinterpret_cast<int*>(&gs[w * kRowsPerWave][0]));
+  }
+
   // K fragments of this chunk: straight 16-B copies
   uint16_t* kdst = kvf + ((size_t)bkv * g.NC + win) * kChunkElems;
   uint16_t* vdst = kdst + 16 * kFrag;
@@ -517,18 +538,9 @@ prefill_select(Geometry g, const uint16_t* __restrict__ q, const uint16_t* __res
     }
   }
 
-  // the selection of the workgroup's rows
-  __syncthreads();
-  constexpr int kRowsPerWave = kRows / (kThreads / kWave);
-  if constexpr (R <= 2) {
-    // the V staging area is each wave's work buffer from here on
-    uint64_t* sbuf = reinterpret_cast<uint64_t*>(vs) + w * (kS * kD / 4 / (kThreads / kWave));
-    static_assert(kRowsPerWave == kWave / 4, "four lanes per row");
-    static_assert(kRowsPerWave * kMaxKf + kWave <= 2 * (kS * kD / 4 / (kThreads / kWave)), "staging");
-    narrow_rows_topk<R>(&gs[w * kRowsPerWave][0], NCP + 1, ncand, g.K,
-                        sel_idx + ((size_t)bkv * g.Lq + i0 + w * kRowsPerWave) * g.K,
-                        reinterpret_cast<int*>(sbuf));
-  } else {
+  // the selection of the wide rows (the narrow ones are done above)
+  if constexpr (R >= 4) {
+    __syncthreads();
     // one row at a time over the whole wave
     for (int q0 = 0; q0 < kRowsPerWave; ++q0) {
       const int row = w * kRowsPerWave + q0;
