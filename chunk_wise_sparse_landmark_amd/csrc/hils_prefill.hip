@@ -751,11 +751,12 @@ __device__ __forceinline__ void chunk_step(bool lag, const uint4* __restrict__ k
                                            bf16x8 (&pa)[kBlocksPerWave][2],
                                            f32x4 (&o)[kBlocksPerWave][8]) {
   if (nsrc) stage_async(nsrc, knx, vnx);
+  // a wave none of whose blocks takes part reads no fragments
   if (lag) {
     if (pact) chunk_pv(vprev, pact, pa, o);
     __builtin_amdgcn_sched_barrier(0);
-    chunk_probs<kMasked, kDirect>(kbuf, qf, sc2, act, vis, rw, pa);
-  } else {
+    if (act) chunk_probs<kMasked, kDirect>(kbuf, qf, sc2, act, vis, rw, pa);
+  } else if (act) {
     chunk_probs<kMasked, kDirect>(kbuf, qf, sc2, act, vis, rw, pa);
     // keep the V fragment loads after the softmax (register pressure)
     __builtin_amdgcn_sched_barrier(0);
