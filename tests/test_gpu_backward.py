@@ -82,20 +82,26 @@ def test_backward_shapes(hl, over):
     _grad_case(hl, cfg)
 
 
-@pytest.mark.parametrize("name", ["train_8k", "train_8k_qcal"])
-def test_train_8k_sampled(hl, name):
-    """Full training shape through the product path (and with a separate retrieval
-    query).  dq (and dq_ret) are checked on sampled query rows; dk, dv of the last
-    two chunks and dlmk, dbias of the second-to-last one are complete once every
-    query of the last two windows is included (no earlier query can reach those
-    chunks)."""
+@pytest.mark.parametrize("name", ["train_8k", "train_8k_qcal", "train_32k"])
+def test_train_sampled(hl, name):
+    """Full training shapes through the product path (8K tokens, also with a
+    separate retrieval query, and 32K tokens = 512 chunks).  dq (and dq_ret) are
+    checked on sampled query rows; dk, dv of the last two chunks and dlmk, dbias
+    of the second-to-last one are complete once every query of the last two
+    windows is included (no earlier query can reach those chunks)."""
     cfg = config(name)
     host, dev = make_device_inputs(cfg)
     kw = dict(chunk_size=cfg["S"], top_k=cfg["K"], causal=True, keep_own_chunk=True)
     qr = dev.get("q_ret")
     out, idx, lse = hl.hils_forward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, q_ret=qr, **kw)
-    grads = hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out, dev["dout"], idx,
-                             lse, need_dbias=True, q_ret=qr, **kw)
+
+    def bwd():
+        return hl.hils_backward(dev["q"], dev["k"], dev["v"], dev["lmk"], None, out, dev["dout"],
+                                idx, lse, need_dbias=True, q_ret=qr, **kw)
+
+    from bench import HipEvents, launched
+    assert launched(hl, HipEvents(), "prefill_bwd_rows", bwd), "the MFMA backward path ran"
+    grads = bwd()
     dq, dk, dv, dl, db = grads[:5]
     torch.cuda.synchronize()
     L, S = cfg["Lq"], cfg["S"]
