@@ -704,7 +704,7 @@ def main():
         summarize_stats(args.stats_summary[0], args.stats_summary[1], " ; ".join(args.command))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
         sys.exit(2)
 

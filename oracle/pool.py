@@ -29,7 +29,7 @@ def _init_worker():
 
 
 def default_workers():
-    """Host cores to use: all of them, capped at 16 (a GPU machine's CPU share)."""
+    """Host cores to use: all of them, capped at 16 (the host share of one GPU)."""
     return max(1, min(os.cpu_count() or 1, 16))
 
 
